@@ -1,0 +1,21 @@
+"""Parallax attention forward on AMD Instinct MI355X (gfx950).
+
+Python entry points over the C ABI of ``libplx_attn.so`` (include/plx_attn.h):
+
+* ``prefill(q, k, v, rho, scale=None)`` -- causal prefill, [B,H,T,d] tensors;
+* ``decode(q, rho, k_cache, v_cache, seqlens, scale=None, num_splits=0)`` -- one decode
+  step over a contiguous per-sequence KV cache;
+* ``decode_num_splits`` / ``decode_workspace_size`` -- the split plan of a decode call.
+
+All arithmetic runs in the HIP kernels; torch only supplies device memory and streams.
+"""
+from ._lib import (  # noqa: F401
+    LIB_PATH,
+    PlxError,
+    decode,
+    decode_num_splits,
+    decode_workspace_size,
+    header_functions,
+    load,
+    prefill,
+)

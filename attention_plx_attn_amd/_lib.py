@@ -1,0 +1,170 @@
+"""ctypes binding of libplx_attn.so: argument marshalling only.
+
+Every step of the forward runs in the HIP kernels behind the C ABI (include/plx_attn.h).
+Torch provides device memory and the current stream; nothing here computes attention,
+and there is no fallback: if the library is missing or a call fails, an error is raised.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+import re
+from typing import Optional
+
+import torch
+
+_PKG = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_PKG, "libplx_attn.so")
+HEADER_PATH = os.path.join(os.path.dirname(_PKG), "include", "plx_attn.h")
+
+PLX_F32, PLX_BF16 = 0, 1
+_STATUS = {0: "PLX_OK", 1: "PLX_ERR_NULL_POINTER", 2: "PLX_ERR_INVALID_SHAPE",
+           3: "PLX_ERR_INVALID_ARG", 4: "PLX_ERR_UNSUPPORTED", 5: "PLX_ERR_MISALIGNED",
+           6: "PLX_ERR_WORKSPACE_TOO_SMALL", 7: "PLX_ERR_HIP"}
+
+_lib = None
+
+
+class PlxError(RuntimeError):
+    def __init__(self, code: int, where: str):
+        self.code = code
+        msg = _lib.plx_status_string(code).decode() if _lib is not None else ""
+        super().__init__(f"{where}: {_STATUS.get(code, code)} ({msg})")
+
+
+def load() -> ctypes.CDLL:
+    """Load libplx_attn.so; raises if it has not been built (no fallback path exists)."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(LIB_PATH):
+        raise RuntimeError(f"{LIB_PATH} is missing: build it with "
+                           "`python -c 'import __graft_entry__ as g; g.build()'`")
+    lib = ctypes.CDLL(LIB_PATH)
+    i32, vp, f32 = ctypes.c_int32, ctypes.c_void_p, ctypes.c_float
+    lib.plx_attn_prefill.argtypes = [ctypes.c_int] + [i32] * 5 + [vp] * 5 + [f32, vp]
+    lib.plx_attn_prefill.restype = ctypes.c_int
+    lib.plx_attn_decode_num_splits.argtypes = [i32] * 4 + [ctypes.POINTER(i32)]
+    lib.plx_attn_decode_num_splits.restype = ctypes.c_int
+    lib.plx_attn_decode_workspace_size.argtypes = [i32] * 5 + [ctypes.POINTER(ctypes.c_size_t)]
+    lib.plx_attn_decode_workspace_size.restype = ctypes.c_int
+    lib.plx_attn_decode.argtypes = ([ctypes.c_int] + [i32] * 5 + [vp] * 6 +
+                                    [f32, i32, vp, ctypes.c_size_t, vp])
+    lib.plx_attn_decode.restype = ctypes.c_int
+    lib.plx_status_string.argtypes = [ctypes.c_int]
+    lib.plx_status_string.restype = ctypes.c_char_p
+    _lib = lib
+    return lib
+
+
+def header_functions():
+    """Names of the functions include/plx_attn.h declares."""
+    text = open(HEADER_PATH).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(plx_\w+)\s*\(", text)))
+
+
+def _dtype_code(t: torch.Tensor) -> int:
+    if t.dtype == torch.bfloat16:
+        return PLX_BF16
+    if t.dtype == torch.float32:
+        return PLX_F32
+    raise TypeError(f"unsupported dtype {t.dtype}")
+
+
+def _check(t: torch.Tensor, name: str, dtype, device, shape=None):
+    if not isinstance(t, torch.Tensor):
+        raise TypeError(f"{name} must be a torch.Tensor")
+    if t.device.type != "cuda" or (device is not None and t.device != device):
+        raise ValueError(f"{name} must be on the same GPU as q ({t.device})")
+    if dtype is not None and t.dtype != dtype:
+        raise TypeError(f"{name} has dtype {t.dtype}, expected {dtype}")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    if shape is not None and tuple(t.shape) != tuple(shape):
+        raise ValueError(f"{name} has shape {tuple(t.shape)}, expected {tuple(shape)}")
+
+
+def _stream_handle(stream: Optional[torch.cuda.Stream], device) -> int:
+    s = stream if stream is not None else torch.cuda.current_stream(device)
+    return ctypes.c_void_p(s.cuda_stream).value or 0
+
+
+def prefill(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, rho: torch.Tensor,
+            scale: Optional[float] = None, out: Optional[torch.Tensor] = None,
+            stream: Optional[torch.cuda.Stream] = None) -> torch.Tensor:
+    """Causal Parallax prefill. q, k, rho [B,H,T,d_qk]; v [B,H,T,d_v] -> o [B,H,T,d_v]."""
+    lib = load()
+    if q.dim() != 4:
+        raise ValueError("q must be [B, H, T, d_qk]")
+    B, H, T, dqk = q.shape
+    dv = v.shape[-1]
+    _check(q, "q", None, None)
+    _check(k, "k", q.dtype, q.device, (B, H, T, dqk))
+    _check(rho, "rho", q.dtype, q.device, (B, H, T, dqk))
+    _check(v, "v", q.dtype, q.device, (B, H, T, dv))
+    if out is None:
+        out = torch.empty((B, H, T, dv), dtype=q.dtype, device=q.device)
+    _check(out, "out", q.dtype, q.device, (B, H, T, dv))
+    if scale is None:
+        scale = dqk ** -0.5
+    rc = lib.plx_attn_prefill(_dtype_code(q), B, H, T, dqk, dv, q.data_ptr(), k.data_ptr(),
+                              v.data_ptr(), rho.data_ptr(), out.data_ptr(), float(scale),
+                              _stream_handle(stream, q.device))
+    if rc != 0:
+        raise PlxError(rc, "plx_attn_prefill")
+    return out
+
+
+def decode_num_splits(B: int, H: int, L_max: int, num_splits: int = 0) -> int:
+    lib = load()
+    s = ctypes.c_int32(0)
+    rc = lib.plx_attn_decode_num_splits(B, H, L_max, num_splits, ctypes.byref(s))
+    if rc != 0:
+        raise PlxError(rc, "plx_attn_decode_num_splits")
+    return s.value
+
+
+def decode_workspace_size(B: int, H: int, L_max: int, d_v: int, num_splits: int = 0) -> int:
+    lib = load()
+    n = ctypes.c_size_t(0)
+    rc = lib.plx_attn_decode_workspace_size(B, H, L_max, d_v, num_splits, ctypes.byref(n))
+    if rc != 0:
+        raise PlxError(rc, "plx_attn_decode_workspace_size")
+    return n.value
+
+
+def decode(q: torch.Tensor, rho: torch.Tensor, k_cache: torch.Tensor, v_cache: torch.Tensor,
+           seqlens: torch.Tensor, scale: Optional[float] = None, num_splits: int = 0,
+           out: Optional[torch.Tensor] = None, workspace: Optional[torch.Tensor] = None,
+           stream: Optional[torch.cuda.Stream] = None) -> torch.Tensor:
+    """One decode step. q, rho [B,H,d]; caches [B,H,L_max,d]; seqlens int32 [B] -> [B,H,d]."""
+    lib = load()
+    if q.dim() != 3:
+        raise ValueError("q must be [B, H, d_qk]")
+    B, H, dqk = q.shape
+    L_max, dv = v_cache.shape[2], v_cache.shape[3]
+    _check(q, "q", None, None)
+    _check(rho, "rho", q.dtype, q.device, (B, H, dqk))
+    _check(k_cache, "k_cache", q.dtype, q.device, (B, H, L_max, dqk))
+    _check(v_cache, "v_cache", q.dtype, q.device, (B, H, L_max, dv))
+    _check(seqlens, "seqlens", torch.int32, q.device, (B,))
+    if out is None:
+        out = torch.empty((B, H, dv), dtype=q.dtype, device=q.device)
+    _check(out, "out", q.dtype, q.device, (B, H, dv))
+    need = decode_workspace_size(B, H, L_max, dv, num_splits)
+    if workspace is None and need > 0:
+        workspace = torch.empty(need // 4, dtype=torch.float32, device=q.device)
+    ws_ptr, ws_bytes = 0, 0
+    if workspace is not None:
+        _check(workspace, "workspace", None, q.device)
+        ws_ptr, ws_bytes = workspace.data_ptr(), workspace.numel() * workspace.element_size()
+    if scale is None:
+        scale = dqk ** -0.5
+    rc = lib.plx_attn_decode(_dtype_code(q), B, H, L_max, dqk, dv, q.data_ptr(), rho.data_ptr(),
+                             k_cache.data_ptr(), v_cache.data_ptr(), seqlens.data_ptr(),
+                             out.data_ptr(), float(scale), int(num_splits), ws_ptr, ws_bytes,
+                             _stream_handle(stream, q.device))
+    if rc != 0:
+        raise PlxError(rc, "plx_attn_decode")
+    return out

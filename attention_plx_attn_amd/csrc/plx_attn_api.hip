@@ -1,0 +1,189 @@
+// plx_attn_api.hip -- the exported C ABI: argument validation, dispatch, split planning.
+//
+// Every entry point validates on the host before touching the HIP runtime, so an invalid
+// call enqueues nothing. The only device query is the compute-unit count (cached per
+// device) used by the decode split heuristic.
+#include <atomic>
+#include <climits>
+#include <cmath>
+
+#include "plx_attn.h"
+#include "plx_kernels.hpp"
+
+namespace {
+
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+constexpr int kMaxDevices = 64;
+std::atomic<int> g_cu_count[kMaxDevices];
+
+// Compute units of the current device, queried once per device.
+plx_status_t current_cu_count(int* out) {
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess) return PLX_ERR_HIP;
+    if (dev >= 0 && dev < kMaxDevices) {
+        const int cached = g_cu_count[dev].load(std::memory_order_relaxed);
+        if (cached > 0) {
+            *out = cached;
+            return PLX_OK;
+        }
+    }
+    int cus = 0;
+    if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
+        cus < 1)
+        return PLX_ERR_HIP;
+    if (dev >= 0 && dev < kMaxDevices) g_cu_count[dev].store(cus, std::memory_order_relaxed);
+    *out = cus;
+    return PLX_OK;
+}
+
+constexpr int kDecodeWaveKeys = 64;      // keys one wave consumes per step
+constexpr int kDecodeMinChunk = 256;     // at least one step per wave of a 4-wave workgroup
+constexpr int kDecodeMaxSplits = 4096;
+constexpr int kDecodeWgPerCu = 2;        // target resident workgroups per compute unit
+
+int ceil_div(long long a, long long b) { return (int)((a + b - 1) / b); }
+
+// Keys per chunk for a requested split count (a multiple of 64) and the chunks that result.
+void chunk_plan(int L_max, int splits, int* chunk, int* launched) {
+    int c = ceil_div(L_max, splits);
+    c = ceil_div(c, kDecodeWaveKeys) * kDecodeWaveKeys;
+    *chunk = c;
+    *launched = ceil_div(L_max, c);
+}
+
+plx_status_t plan_splits(int B, int H, int L_max, int num_splits, int* splits) {
+    if (num_splits < 0 || num_splits > kDecodeMaxSplits) return PLX_ERR_INVALID_ARG;
+    if (num_splits > 0) {
+        *splits = num_splits;
+        return PLX_OK;
+    }
+    int cus = 0;
+    const plx_status_t st = current_cu_count(&cus);
+    if (st != PLX_OK) return st;
+    const long long bh = (long long)B * H;
+    long long s = (kDecodeWgPerCu * (long long)cus + bh - 1) / bh;  // fill the chip once
+    const long long smax = (L_max + kDecodeMinChunk - 1) / kDecodeMinChunk;
+    if (s > smax) s = smax;
+    if (s < 1) s = 1;
+    if (s > kDecodeMaxSplits) s = kDecodeMaxSplits;
+    *splits = (int)s;
+    return PLX_OK;
+}
+
+plx_status_t check_decode_shape(int B, int H, int L_max, int d_v) {
+    if (B < 1 || H < 1 || L_max < 1 || d_v < 1) return PLX_ERR_INVALID_SHAPE;
+    if ((long long)B * H > INT_MAX / 4) return PLX_ERR_INVALID_SHAPE;
+    if ((long long)L_max * 256 >= (1LL << 31)) return PLX_ERR_INVALID_SHAPE;
+    if (B > 65535 || H > 65535) return PLX_ERR_INVALID_SHAPE;  // grid y/z limits
+    return PLX_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+const char* plx_status_string(plx_status_t s) {
+    switch (s) {
+        case PLX_OK: return "ok";
+        case PLX_ERR_NULL_POINTER: return "a required pointer is NULL";
+        case PLX_ERR_INVALID_SHAPE: return "invalid or too large shape";
+        case PLX_ERR_INVALID_ARG: return "invalid argument (dtype, scale or split count)";
+        case PLX_ERR_UNSUPPORTED: return "unsupported dtype / head-dim combination";
+        case PLX_ERR_MISALIGNED: return "pointer not 16-byte aligned";
+        case PLX_ERR_WORKSPACE_TOO_SMALL: return "decode workspace too small";
+        case PLX_ERR_HIP: return "HIP runtime error";
+    }
+    return "unknown status";
+}
+
+plx_status_t plx_attn_prefill(plx_dtype_t dtype, int32_t B, int32_t H, int32_t T,
+                              int32_t d_qk, int32_t d_v, const void* q, const void* k,
+                              const void* v, const void* rho, void* o, float softmax_scale,
+                              void* stream) {
+    if (dtype != PLX_F32 && dtype != PLX_BF16) return PLX_ERR_INVALID_ARG;
+    if (!q || !k || !v || !rho || !o) return PLX_ERR_NULL_POINTER;
+    if (B < 1 || H < 1 || T < 1 || d_qk < 1 || d_v < 1) return PLX_ERR_INVALID_SHAPE;
+    if (!std::isfinite(softmax_scale) || softmax_scale < 0.f) return PLX_ERR_INVALID_ARG;
+    const long long esize = dtype == PLX_BF16 ? 2 : 4;
+    if ((long long)T * d_qk * esize >= (1LL << 31) || (long long)T * d_v * esize >= (1LL << 31))
+        return PLX_ERR_INVALID_SHAPE;
+    if ((long long)B * H > INT_MAX / 2) return PLX_ERR_INVALID_SHAPE;
+    if (d_qk != d_v) return PLX_ERR_UNSUPPORTED;
+    const bool ok = (dtype == PLX_BF16 && d_qk == 128) ||
+                    (dtype == PLX_F32 && plx::prefill_f32_supported(d_qk));
+    if (!ok) return PLX_ERR_UNSUPPORTED;
+    if (dtype == PLX_F32 && (B > 65535 || H > 65535)) return PLX_ERR_INVALID_SHAPE;
+    if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(rho) || !aligned16(o))
+        return PLX_ERR_MISALIGNED;
+
+    plx::PrefillArgs a{B, H, T, d_qk, q, k, v, rho, o, softmax_scale};
+    const hipStream_t st = static_cast<hipStream_t>(stream);
+    const hipError_t e = dtype == PLX_BF16 ? plx::launch_prefill_bf16_d128(a, st)
+                                           : plx::launch_prefill_f32(a, st);
+    return e == hipSuccess ? PLX_OK : PLX_ERR_HIP;
+}
+
+plx_status_t plx_attn_decode_num_splits(int32_t B, int32_t H, int32_t L_max,
+                                        int32_t num_splits, int32_t* splits_out) {
+    if (!splits_out) return PLX_ERR_NULL_POINTER;
+    plx_status_t st = check_decode_shape(B, H, L_max, 1);
+    if (st != PLX_OK) return st;
+    int s = 0;
+    st = plan_splits(B, H, L_max, num_splits, &s);
+    if (st != PLX_OK) return st;
+    int chunk = 0, launched = 0;
+    chunk_plan(L_max, s, &chunk, &launched);
+    *splits_out = launched;
+    return PLX_OK;
+}
+
+plx_status_t plx_attn_decode_workspace_size(int32_t B, int32_t H, int32_t L_max,
+                                            int32_t d_v, int32_t num_splits,
+                                            size_t* bytes_out) {
+    if (!bytes_out) return PLX_ERR_NULL_POINTER;
+    plx_status_t st = check_decode_shape(B, H, L_max, d_v);
+    if (st != PLX_OK) return st;
+    int s = 0;
+    st = plx_attn_decode_num_splits(B, H, L_max, num_splits, &s);
+    if (st != PLX_OK) return st;
+    *bytes_out = s > 1 ? (size_t)B * H * s * (size_t)(2 * d_v + 4) * sizeof(float) : 0;
+    return PLX_OK;
+}
+
+plx_status_t plx_attn_decode(plx_dtype_t dtype, int32_t B, int32_t H, int32_t L_max,
+                             int32_t d_qk, int32_t d_v, const void* q, const void* rho,
+                             const void* k_cache, const void* v_cache,
+                             const int32_t* seqlens, void* o, float softmax_scale,
+                             int32_t num_splits, void* workspace, size_t workspace_bytes,
+                             void* stream) {
+    if (dtype != PLX_F32 && dtype != PLX_BF16) return PLX_ERR_INVALID_ARG;
+    if (!q || !rho || !k_cache || !v_cache || !seqlens || !o) return PLX_ERR_NULL_POINTER;
+    plx_status_t st = check_decode_shape(B, H, L_max, d_v);
+    if (st != PLX_OK) return st;
+    if (d_qk < 1) return PLX_ERR_INVALID_SHAPE;
+    if (!std::isfinite(softmax_scale) || softmax_scale < 0.f) return PLX_ERR_INVALID_ARG;
+    if (num_splits < 0 || num_splits > kDecodeMaxSplits) return PLX_ERR_INVALID_ARG;
+    if (!(dtype == PLX_BF16 && d_qk == 128 && d_v == 128)) return PLX_ERR_UNSUPPORTED;
+    if (!aligned16(q) || !aligned16(rho) || !aligned16(k_cache) || !aligned16(v_cache) ||
+        !aligned16(o) || (reinterpret_cast<uintptr_t>(seqlens) & 3u) != 0)
+        return PLX_ERR_MISALIGNED;
+
+    int splits = 0;
+    st = plan_splits(B, H, L_max, num_splits, &splits);
+    if (st != PLX_OK) return st;
+    int chunk = 0, launched = 0;
+    chunk_plan(L_max, splits, &chunk, &launched);
+    if (launched > 1) {
+        const size_t need = (size_t)B * H * launched * (size_t)(2 * d_v + 4) * sizeof(float);
+        if (!workspace) return PLX_ERR_NULL_POINTER;
+        if (workspace_bytes < need) return PLX_ERR_WORKSPACE_TOO_SMALL;
+        if (!aligned16(workspace)) return PLX_ERR_MISALIGNED;
+    }
+    plx::DecodeArgs a{B, H, L_max, d_qk, q, rho, k_cache, v_cache, seqlens, o, softmax_scale,
+                      launched, chunk, static_cast<float*>(workspace)};
+    const hipError_t e = plx::launch_decode_bf16_d128(a, static_cast<hipStream_t>(stream));
+    return e == hipSuccess ? PLX_OK : PLX_ERR_HIP;
+}
+
+}  // extern "C"

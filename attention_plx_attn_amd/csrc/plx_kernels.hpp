@@ -1,0 +1,40 @@
+// plx_kernels.hpp -- host-side launch interface of the Parallax kernels (internal).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace plx {
+
+struct PrefillArgs {
+    int B, H, T, d;
+    const void* q;
+    const void* k;
+    const void* v;
+    const void* rho;
+    void* o;
+    float scale;
+};
+
+struct DecodeArgs {
+    int B, H, L_max, d;
+    const void* q;
+    const void* rho;
+    const void* k;
+    const void* v;
+    const int32_t* seqlens;
+    void* o;
+    float scale;
+    int splits;  // chunks per (b, h) actually launched
+    int chunk;   // keys per chunk (multiple of 64)
+    float* ws;   // split partials, [B*H*splits][kDecodeRecord] floats (unused if splits == 1)
+};
+
+constexpr int kDecodeRecord = 2 * 128 + 4;  // A1[128], A2[128], m, l, beta, pad
+
+bool prefill_f32_supported(int d);
+hipError_t launch_prefill_f32(const PrefillArgs& a, hipStream_t stream);
+hipError_t launch_prefill_bf16_d128(const PrefillArgs& a, hipStream_t stream);
+hipError_t launch_decode_bf16_d128(const DecodeArgs& a, hipStream_t stream);
+
+}  // namespace plx

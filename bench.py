@@ -1,0 +1,299 @@
+#!/usr/bin/env python3
+"""Benchmark of the Parallax attention forward on one MI355X.
+
+One step = one pass of the whole hot path over one batch of synthetic inputs:
+  * causal prefill, bf16 in/out, B=4, H=16, T=2048, d=128 (fp32 accumulation), then
+  * one decode step, bf16, B=1, H=16, d=128 over a 32768-row KV cache (split-KV partials
+    plus the combine kernel).
+Inputs are resident in HBM before the timed region. The decode cache is rotated over
+several device copies so that successive steps cannot be served from the 256 MB
+last-level cache.
+
+Prints ONE JSON line. `value` is the prefill's algorithmic throughput in TFLOP/s
+(8*d FLOPs per visible causal (query, key) pair: Q K^T, R K^T, P V and (P*T) V);
+the decode figures (tokens/s, algorithmic HBM GB/s) ride along in the same line.
+`roofline` describes the dominant kernel (the prefill), timed with HIP events on the
+stream it runs on; `traffic` comes from committed rocprofv3 counter summaries and is
+null when the kernel source changed since they were taken. `cpu_baseline` times the
+fp64 oracle's streaming form on the host cores.
+
+Extra modes (used to produce the committed rocprofv3 summaries):
+  --calibrate-copy        also run a plain 1 GiB device copy, the reference for counters
+  --summarize-counters F W  fold rocprofv3 --pmc CSVs (FETCH_SIZE run F, WRITE_SIZE run W)
+                            into profiles/prefill_bf16_d128_counters.json
+"""
+from __future__ import annotations
+
+import argparse
+import csv
+import glob
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBPS = 8000.0
+BF16_PEAK_TFLOPS = 2500.0
+COUNTERS_JSON = os.path.join(ROOT, "profiles", "prefill_bf16_d128_counters.json")
+PREFILL_KERNEL = "prefill_bf16_d128_kernel"
+COPY_BYTES = 1 << 30
+PREFILL_SOURCES = ("attention_plx_attn_amd/csrc/prefill_bf16.hip",
+                   "attention_plx_attn_amd/csrc/plx_device.hpp")
+
+
+def source_hash(files=PREFILL_SOURCES) -> str:
+    h = hashlib.sha256()
+    for f in files:
+        with open(os.path.join(ROOT, f), "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()
+
+
+def prefill_flops(B, H, T, d) -> int:
+    return 8 * d * B * H * T * (T + 1) // 2
+
+
+def decode_bytes(seqlens, H, d) -> int:
+    kv = int(sum(int(s) for s in seqlens)) * H * (2 * d) * 2
+    return kv + len(seqlens) * H * 3 * d * 2  # + q, rho in and o out
+
+
+# ------------------------------------------------------------------------------ counters
+
+def _pmc_rows(path_glob, counter):
+    out = {}
+    for path in glob.glob(path_glob, recursive=True):
+        with open(path, newline="") as fh:
+            for row in csv.DictReader(fh):
+                if row.get("Counter_Name") != counter:
+                    continue
+                name = row.get("Kernel_Name", "")
+                out.setdefault(name, []).append(float(row["Counter_Value"]))
+    return out
+
+
+def summarize_counters(fetch_glob, write_glob, out_path=COUNTERS_JSON):
+    """Per-dispatch FETCH_SIZE / WRITE_SIZE (KiB) of the prefill kernel, calibrated by a
+    plain copy of known size run in the same process."""
+    fetch = _pmc_rows(fetch_glob, "FETCH_SIZE")
+    write = _pmc_rows(write_glob, "WRITE_SIZE")
+
+    def pick(d, key):
+        vals = [v for k, vs in d.items() if key(k) for v in vs]
+        return sum(vals) / len(vals) if vals else None
+
+    is_prefill = lambda k: PREFILL_KERNEL in k  # noqa: E731
+    is_copy = lambda k: "copy" in k.lower() or "elementwise" in k.lower()  # noqa: E731
+    f_k, w_k = pick(fetch, is_prefill), pick(write, is_prefill)
+    # the calibration copy is the largest-traffic copy-like kernel in the run
+    f_c = max((sum(v) / len(v) for k, v in fetch.items() if is_copy(k)), default=None)
+    w_c = max((sum(v) / len(v) for k, v in write.items() if is_copy(k)), default=None)
+    if None in (f_k, w_k, f_c, w_c):
+        raise SystemExit(f"missing counters: prefill {f_k} {w_k} copy {f_c} {w_c}")
+    copy_kib = COPY_BYTES / 1024.0
+    fetch_scale, write_scale = copy_kib / f_c, copy_kib / w_c
+    rec = {
+        "kernel": PREFILL_KERNEL,
+        "workload": "prefill B4 H16 T2048 d128 bf16 causal",
+        "fetch_kib_per_dispatch_raw": f_k,
+        "write_kib_per_dispatch_raw": w_k,
+        "copy_fetch_kib_raw": f_c,
+        "copy_write_kib_raw": w_c,
+        "fetch_scale": fetch_scale,
+        "write_scale": write_scale,
+        "hbm_bytes_per_dispatch": (f_k * fetch_scale + w_k * write_scale) * 1024.0,
+        "source_sha256": source_hash(),
+    }
+    with open(out_path, "w") as fh:
+        json.dump(rec, fh, indent=1)
+        fh.write("\n")
+    print(json.dumps(rec))
+
+
+def committed_traffic():
+    try:
+        with open(COUNTERS_JSON) as fh:
+            rec = json.load(fh)
+    except (OSError, ValueError):
+        return None
+    if rec.get("source_sha256") != source_hash():
+        return None
+    return rec.get("hbm_bytes_per_dispatch")
+
+
+# ------------------------------------------------------------------------------ CPU baseline
+
+def cpu_baseline(px, dx):
+    import oracle
+
+    cores = oracle.threads()
+    t0 = time.perf_counter()
+    oracle.prefill(px["q"], px["k"], px["v"], px["rho"], px["scale"], form="stream", block=64)
+    t_pre = time.perf_counter() - t0
+    B, H, T, d = px["q"].shape
+    t0 = time.perf_counter()
+    oracle.decode(dx["q"], dx["rho"], dx["k_cache"], dx["v_cache"], dx["seqlens"], dx["scale"],
+                  form="stream", block=64)
+    t_dec = time.perf_counter() - t0
+    return {
+        "value": prefill_flops(B, H, T, d) / t_pre / 1e12,
+        "unit": "TFLOP/s",
+        "cores": cores,
+        "kind": "oracle",
+        "sample": (f"the full prefill workload B{B} H{H} T{T} d{d} in the oracle's fp64 "
+                   f"streaming form ({t_pre:.2f} s); decode B1 H16 L32768 in the same form "
+                   f"({t_dec:.2f} s)"),
+        "decode_tokens_per_s": dx["q"].shape[0] / t_dec,
+    }
+
+
+# ------------------------------------------------------------------------------ main
+
+def main():
+    ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=100)
+    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--copies", type=int, default=4, help="decode cache copies to rotate")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--calibrate-copy", action="store_true")
+    ap.add_argument("--summarize-counters", nargs=2, metavar=("FETCH_CSV_GLOB", "WRITE_CSV_GLOB"))
+    args = ap.parse_args()
+
+    if args.summarize_counters:
+        summarize_counters(*args.summarize_counters)
+        return 0
+    world = int(os.environ.get("WORLD_SIZE", "1"))
+    if args.gpus != 1 or world != 1:
+        print("bench.py measures the Parallax forward on one GPU only; runs on more than "
+              f"one GPU (--gpus {args.gpus}, WORLD_SIZE {world}) are not supported.",
+              file=sys.stderr, flush=True)
+        return 2
+
+    import torch
+
+    import attention_plx_attn_amd as plx
+    from plx_synth import CONFIGS, decode_inputs, prefill_inputs
+
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    pcfg, dcfg = CONFIGS["prefill_bf16"], CONFIGS["decode_32k"]
+    px = prefill_inputs(pcfg, seed=0)
+    dx = decode_inputs(dcfg, seed=0)
+    pd = {k: px[k].to(dev) for k in ("q", "k", "v", "rho")}
+    dd = {k: dx[k].to(dev) for k in ("q", "rho", "seqlens")}
+    caches = [(dx["k_cache"].to(dev), dx["v_cache"].to(dev))]
+    for _ in range(1, max(1, args.copies)):
+        caches.append((caches[0][0].clone(), caches[0][1].clone()))
+    o_p = torch.empty_like(pd["q"])
+    o_d = torch.empty_like(dd["q"])
+    splits = plx.decode_num_splits(dcfg.B, dcfg.H, dcfg.L_max, 0)
+    ws_bytes = plx.decode_workspace_size(dcfg.B, dcfg.H, dcfg.L_max, dcfg.d, 0)
+    ws = torch.empty(max(ws_bytes // 4, 1), dtype=torch.float32, device=dev)
+    stream = torch.cuda.current_stream(dev)
+
+    def run_prefill():
+        plx.prefill(pd["q"], pd["k"], pd["v"], pd["rho"], pcfg.scale, out=o_p)
+
+    def run_decode(i):
+        kc, vc = caches[i % len(caches)]
+        plx.decode(dd["q"], dd["rho"], kc, vc, dd["seqlens"], dcfg.scale, out=o_d, workspace=ws)
+
+    if args.calibrate_copy:
+        src = torch.empty(COPY_BYTES, dtype=torch.uint8, device=dev).fill_(1)
+        dst = torch.empty_like(src)
+        for _ in range(3):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        del src, dst
+
+    for i in range(args.warmup):
+        run_prefill()
+        run_decode(i)
+    torch.cuda.synchronize()
+
+    K = args.steps
+    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(K)]
+    start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    start.record(stream)
+    for i in range(K):
+        ev[i][0].record(stream)
+        run_prefill()
+        ev[i][1].record(stream)
+        run_decode(i)
+        ev[i][2].record(stream)
+    end.record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    total_ms = start.elapsed_time(end)
+    pre_ms = sorted(e[0].elapsed_time(e[1]) for e in ev)
+    dec_ms = sorted(e[1].elapsed_time(e[2]) for e in ev)
+    avg = lambda xs: sum(xs) / len(xs)  # noqa: E731
+    pct = lambda xs, p: xs[min(len(xs) - 1, int(p * len(xs)))]  # noqa: E731
+
+    flops = prefill_flops(pcfg.B, pcfg.H, pcfg.T, pcfg.d)
+    pre_avg_s = avg(pre_ms) / 1e3
+    tflops = flops / pre_avg_s / 1e12
+    dbytes = decode_bytes(dx["seqlens"].tolist(), dcfg.H, dcfg.d)
+    dec_avg_s = avg(dec_ms) / 1e3
+    dec_gbps = dbytes / dec_avg_s / 1e9
+
+    traffic = committed_traffic()
+    result = {
+        "metric": "decode tokens/s & HBM GB/s frac; prefill TFLOP/s & MFMA util (B,H,T,d=128)",
+        "value": round(tflops, 2),
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": K,
+        "warmup": args.warmup,
+        "ms_per_step": round(total_ms / K, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic (seeded N(0,1) q, k, v; probe 0.1*RMSNorm(N(0,1)) for prefill, "
+                "RMSNorm(W_R x) for decode)",
+        "config": {"workload": "parallax forward: causal prefill B4 H16 T2048 d128 + "
+                               "decode B1 H16 L32768 d128",
+                   "prefill": {"B": pcfg.B, "H": pcfg.H, "T": pcfg.T, "d": pcfg.d},
+                   "decode": {"B": dcfg.B, "H": dcfg.H, "L": dcfg.L_max, "d": dcfg.d,
+                              "splits": splits, "cache_copies": len(caches)}},
+        "prefill": {"us_avg": round(avg(pre_ms) * 1e3, 2),
+                    "us_p10": round(pct(pre_ms, 0.1) * 1e3, 2),
+                    "us_p90": round(pct(pre_ms, 0.9) * 1e3, 2),
+                    "tflops": round(tflops, 2),
+                    "mfma_frac": round(tflops / BF16_PEAK_TFLOPS, 4),
+                    "tokens_per_s": round(pcfg.B * pcfg.T / pre_avg_s, 1)},
+        "decode": {"us_avg": round(avg(dec_ms) * 1e3, 2),
+                   "us_p10": round(pct(dec_ms, 0.1) * 1e3, 2),
+                   "us_p90": round(pct(dec_ms, 0.9) * 1e3, 2),
+                   "tokens_per_s": round(dcfg.B / dec_avg_s, 1),
+                   "hbm_gbps": round(dec_gbps, 1),
+                   "hbm_frac": round(dec_gbps / HBM_PEAK_GBPS, 4),
+                   "bytes": dbytes},
+        "roofline": {"bound": "mfma", "achieved": round(tflops, 2), "peak": BF16_PEAK_TFLOPS,
+                     "unit": "TFLOP/s", "frac": round(tflops / BF16_PEAK_TFLOPS, 4),
+                     "traffic": traffic, "kernel": PREFILL_KERNEL,
+                     "work_per_launch": flops},
+        "roofline_decode": {"bound": "hbm", "achieved": round(dec_gbps, 1),
+                            "peak": HBM_PEAK_GBPS, "unit": "GB/s",
+                            "frac": round(dec_gbps / HBM_PEAK_GBPS, 4), "traffic": None,
+                            "work_per_launch": dbytes},
+        "wall_s_timed": round(wall, 3),
+    }
+    if not args.no_cpu_baseline:
+        result["cpu_baseline"] = cpu_baseline(px, dx)
+    else:
+        result["cpu_baseline"] = None
+    print(json.dumps(result), flush=True)
+    return 0
+
+
+if __name__ == "__main__":
+    sys.exit(main())

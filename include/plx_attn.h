@@ -1,0 +1,128 @@
+/*
+ * plx_attn.h -- C ABI of the Parallax attention forward on AMD Instinct MI355X (gfx950).
+ *
+ * Parallax adds a covariance-correction branch to causal softmax attention. For query i
+ * over its visible keys j, with softmax weights p_ij of the scores a_ij = scale <q_i, k_j>:
+ *
+ *     o_i = o_SA_i - Sigma_KV^(i) rho_i                                        (1)
+ *
+ * where o_SA_i = sum_j p_ij v_j is the softmax-attention output and Sigma_KV^(i) is the
+ * softmax-weighted covariance of the values against the keys, applied to the per-query
+ * probe rho_i (the row of the extra R matrix). Equation (1) is the central equation of the
+ * method [Resumen Tecnico: Parallax - Atencion Lineal Local Parametrizada para Modelado de
+ * Lenguaje, section "Mecanismo Central"]; the covariance is the softmax-weighted KV
+ * covariance [Parallax: Parameterized Local Linear Attention for Language Modeling,
+ * agihunt.info review, method paragraph]. Expanded, (1) is the corrected-weight sum
+ *
+ *     o_i = sum_j p_ij (1 - (t_ij - tbar_i)) v_j,  t_ij = <rho_i, k_j>,  tbar_i = sum_j p_ij t_ij
+ *
+ * [Parallax (paper.rainbus.top summary), section "方法步骤详情" (method steps 2-6)], which
+ * the kernels evaluate in streaming form: one pass over the keys with one running max and
+ * one rescale factor shared by both branches, accumulating sum w v, sum w t v, sum w and
+ * sum w t together (same section's streaming sentences; agihunt review, hardware paragraph).
+ * The boundary-amplification factor of exact local linear attention is fixed at zero.
+ * The probe rho is an input: its projection W_R x and normalisation happen before the call.
+ *
+ * Conventions shared by every entry point
+ *   - All tensors are device pointers to contiguous, row-major arrays, 16-byte aligned.
+ *   - The caller allocates and owns every buffer, including the decode workspace; the
+ *     library allocates nothing and keeps no per-call state. It caches the device's
+ *     compute-unit count on first use.
+ *   - Calls are asynchronous: work is enqueued on `stream` (a hipStream_t passed as
+ *     void*; NULL = the default stream). Buffers must stay valid until the stream reaches
+ *     the work. The output must not alias any input.
+ *   - Arguments are validated on the host first; an invalid call returns its status code
+ *     without enqueuing anything. A launch failure returns PLX_ERR_HIP. No exception
+ *     crosses the ABI and the library never aborts.
+ *   - Arithmetic: bf16 inputs are multiplied on the matrix cores with fp32 accumulation;
+ *     the softmax weights and the weight*probe products are rounded to bf16 (RNE) before
+ *     the value products, and the row sums are taken from the same rounded values. Output
+ *     is rounded to the input dtype (RNE). fp32 inputs use fp32 throughout.
+ *   - softmax_scale multiplies q.k only (t is unscaled); it must be finite and >= 0
+ *     (0 gives uniform weights).
+ */
+#ifndef PLX_ATTN_H
+#define PLX_ATTN_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+    PLX_OK = 0,
+    PLX_ERR_NULL_POINTER = 1,        /* a required pointer is NULL */
+    PLX_ERR_INVALID_SHAPE = 2,       /* a size is < 1 or too large for 32-bit slice offsets */
+    PLX_ERR_INVALID_ARG = 3,         /* scale not finite or negative; bad split count; bad dtype */
+    PLX_ERR_UNSUPPORTED = 4,         /* (dtype, d_qk, d_v) combination not built */
+    PLX_ERR_MISALIGNED = 5,          /* a pointer is not 16-byte aligned */
+    PLX_ERR_WORKSPACE_TOO_SMALL = 6, /* decode workspace smaller than required */
+    PLX_ERR_HIP = 7                  /* a HIP runtime call or kernel launch failed */
+} plx_status_t;
+
+typedef enum { PLX_F32 = 0, PLX_BF16 = 1 } plx_dtype_t;
+
+/*
+ * Causal prefill: every query row of every (batch, head) against keys 0..i.
+ *
+ *   q, k, rho : [B, H, T, d_qk]   v, o : [B, H, T, d_v]   (dtype for all five)
+ *   Key j is visible to query i iff j <= i (top-left aligned, T_q = T_k = T).
+ *
+ * Built combinations: (PLX_BF16, d_qk = d_v = 128) on the matrix cores;
+ * (PLX_F32, d_qk = d_v in {16, 32, 64}) on the vector ALUs.
+ * Limits: B*H <= 2^31-1 and T * d * sizeof(dtype) < 2^31 (one (b,h) slice per buffer).
+ */
+plx_status_t plx_attn_prefill(plx_dtype_t dtype, int32_t B, int32_t H, int32_t T,
+                              int32_t d_qk, int32_t d_v, const void* q, const void* k,
+                              const void* v, const void* rho, void* o, float softmax_scale,
+                              void* stream);
+
+/*
+ * Split count the decode call will use: num_splits if > 0, otherwise a heuristic from
+ * B*H, L_max and the current device's compute-unit count. Writes it to *splits_out.
+ */
+plx_status_t plx_attn_decode_num_splits(int32_t B, int32_t H, int32_t L_max,
+                                        int32_t num_splits, int32_t* splits_out);
+
+/*
+ * Bytes of fp32 workspace plx_attn_decode needs for the same (B, H, L_max, d_v,
+ * num_splits): B*H*S*(2*d_v + 4)*4 for S > 1 split partials, 0 when S == 1.
+ */
+plx_status_t plx_attn_decode_workspace_size(int32_t B, int32_t H, int32_t L_max,
+                                            int32_t d_v, int32_t num_splits,
+                                            size_t* bytes_out);
+
+/*
+ * One decode step over a contiguous per-sequence KV cache.
+ *
+ *   q, rho   : [B, H, d_qk]            k_cache : [B, H, L_max, d_qk]
+ *   v_cache  : [B, H, L_max, d_v]      o       : [B, H, d_v]
+ *   seqlens  : device int32 [B]; query b attends to cache rows [0, n_b) with
+ *              n_b = min(max(seqlens[b], 0), L_max); n_b == 0 gives o[b] = 0.
+ *              Rows at or beyond n_b are never read, so they may hold anything.
+ *   num_splits : 0 = heuristic, else the number of KV chunks per (b, h); each chunk's
+ *              partial state (running max, normaliser, sum w t, sum w v, sum w t v) goes
+ *              to the workspace and a second kernel merges them.
+ *   workspace  : device buffer of at least plx_attn_decode_workspace_size() bytes
+ *              (may be NULL when that size is 0).
+ *
+ * Built combination: (PLX_BF16, d_qk = d_v = 128).
+ * Limits: L_max * d * 2 < 2^31; num_splits <= 4096.
+ */
+plx_status_t plx_attn_decode(plx_dtype_t dtype, int32_t B, int32_t H, int32_t L_max,
+                             int32_t d_qk, int32_t d_v, const void* q, const void* rho,
+                             const void* k_cache, const void* v_cache,
+                             const int32_t* seqlens, void* o, float softmax_scale,
+                             int32_t num_splits, void* workspace, size_t workspace_bytes,
+                             void* stream);
+
+/* Static, NUL-terminated description of a status code. */
+const char* plx_status_string(plx_status_t s);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* PLX_ATTN_H */

@@ -65,6 +65,7 @@ def _load():
         lib.plx_oracle_decode.argtypes = [ctypes.c_int] * 6 + [dp] * 4 + [
             ctypes.POINTER(ctypes.c_int32), ctypes.c_double, ctypes.c_int, ctypes.c_int, dp]
         lib.plx_oracle_decode.restype = ctypes.c_int
+        lib.plx_oracle_threads.restype = ctypes.c_int
         _lib = lib
     return _lib
 
@@ -128,4 +129,9 @@ def decode(q, rho, k_cache, v_cache, seqlens, scale: float, form: str = "cov", b
     return out
 
 
-__all__ = ["build", "prefill", "decode"]
+def threads() -> int:
+    """OpenMP threads the oracle runs on."""
+    return int(_load().plx_oracle_threads())
+
+
+__all__ = ["build", "prefill", "decode", "threads"]

@@ -317,3 +317,15 @@ int plx_oracle_decode(int form, int B, int H, int L_max, int dqk, int dv, const 
     }
     return bad ? -1 : 0;
 }
+
+/* Threads the OpenMP loops above will use (reported next to CPU timings). */
+#ifdef _OPENMP
+#include <omp.h>
+#endif
+int plx_oracle_threads(void) {
+#ifdef _OPENMP
+    return omp_get_max_threads();
+#else
+    return 1;
+#endif
+}

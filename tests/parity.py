@@ -1,0 +1,74 @@
+"""Comparison helpers for GPU-vs-oracle parity (shared by the GPU tests and smoke()).
+
+Tolerances
+  * fp32 path: max |g - r| <= 1e-5 and ||g - r||_2 / ||r||_2 <= 1e-5.
+  * bf16 path (bf16 inputs, fp32 accumulation, bf16 output):
+      elementwise |g - r| <= 1e-2 + ulp_bf16(r) / 2  and  rel-L2 <= 5e-3,
+    where r is the unrounded fp64 oracle. The half-ulp term is the rounding of the
+    output itself to bf16 (2^-6 / 2 = 0.0078 for |r| in [2, 4)), which no kernel can
+    avoid; the 1e-2 budget is what the kernel's arithmetic may add on top.
+"""
+from __future__ import annotations
+
+import numpy as np
+import torch
+
+BF16_ABS, BF16_REL_L2 = 1e-2, 5e-3
+F32_ABS, F32_REL_L2 = 1e-5, 1e-5
+
+
+def to_f64(t) -> np.ndarray:
+    if isinstance(t, torch.Tensor):
+        return t.detach().to("cpu", torch.float64).numpy()
+    return np.asarray(t, dtype=np.float64)
+
+
+def ulp_bf16(r: np.ndarray) -> np.ndarray:
+    a = np.maximum(np.abs(r), 2.0 ** -126)
+    return 2.0 ** (np.floor(np.log2(a)) - 7)
+
+
+def metrics(got, ref) -> dict:
+    g, r = to_f64(got), to_f64(ref)
+    err = np.abs(g - r)
+    denom = max(np.linalg.norm(r), 1e-300)
+    return {
+        "max_abs": float(err.max()) if err.size else 0.0,
+        "rel_l2": float(np.linalg.norm(g - r) / denom) if err.size else 0.0,
+        "excess_over_half_ulp": float((err - 0.5 * ulp_bf16(r)).max()) if err.size else 0.0,
+        "finite": bool(np.isfinite(g).all()),
+    }
+
+
+def check_bf16(got, ref, what: str = "") -> dict:
+    m = metrics(got, ref)
+    assert m["finite"], f"{what}: non-finite output"
+    assert m["excess_over_half_ulp"] <= BF16_ABS, f"{what}: {m}"
+    assert m["rel_l2"] <= BF16_REL_L2, f"{what}: {m}"
+    return m
+
+
+def check_f32(got, ref, what: str = "") -> dict:
+    m = metrics(got, ref)
+    assert m["finite"], f"{what}: non-finite output"
+    assert m["max_abs"] <= F32_ABS, f"{what}: {m}"
+    assert m["rel_l2"] <= F32_REL_L2, f"{what}: {m}"
+    return m
+
+
+def sample_rows(B: int, H: int, T: int, n_random: int = 64, seed: int = 0) -> np.ndarray:
+    """Flat row ids (b*H + h)*T + i: first rows, tile boundaries, last rows, random rows."""
+    rng = np.random.default_rng(seed)
+    per_head = set(range(min(8, T)))
+    for edge in range(63, T, 64):
+        per_head.update({edge, min(edge + 1, T - 1)})
+    per_head.update({T - 2, T - 1} if T > 1 else {0})
+    per_head = np.array(sorted(i for i in per_head if 0 <= i < T))
+    rows = []
+    for bh in range(B * H):
+        pick = per_head
+        if len(pick) > 40:  # keep the explicit-covariance cost bounded on long sequences
+            pick = np.concatenate([per_head[:8], per_head[-4:],
+                                   rng.choice(per_head, 28, replace=False)])
+        rows.append(bh * T + np.unique(np.concatenate([pick, rng.integers(0, T, n_random)])))
+    return np.concatenate(rows)

@@ -1,0 +1,95 @@
+"""The C-ABI library loads, exports what include/plx_attn.h declares, and rejects bad
+arguments on the host before any HIP call (these tests need no GPU)."""
+import ctypes
+import subprocess
+
+import pytest
+
+import attention_plx_attn_amd as plx
+from attention_plx_attn_amd import _lib
+
+A = 1 << 20  # a 16-byte aligned fake address: validation must reject before using it
+
+
+@pytest.fixture(scope="module")
+def lib():
+    return plx.load()
+
+
+def test_exports_every_declared_symbol(lib):
+    declared = plx.header_functions()
+    assert set(declared) == {"plx_attn_prefill", "plx_attn_decode", "plx_attn_decode_num_splits",
+                             "plx_attn_decode_workspace_size", "plx_status_string"}
+    out = subprocess.run(["nm", "-D", "--defined-only", plx.LIB_PATH], capture_output=True,
+                         text=True, check=True).stdout
+    exported = {line.split()[-1] for line in out.splitlines() if " T " in line}
+    for name in declared:
+        assert name in exported, name
+        assert getattr(lib, name) is not None
+
+
+def test_status_strings(lib):
+    for code in range(8):
+        s = lib.plx_status_string(code)
+        assert isinstance(s, bytes) and len(s) > 0
+    assert lib.plx_status_string(99) == b"unknown status"
+
+
+def _prefill(lib, dtype=1, B=1, H=1, T=8, dqk=128, dv=128, ptrs=(A,) * 5, scale=0.1):
+    return lib.plx_attn_prefill(dtype, B, H, T, dqk, dv, *ptrs, ctypes.c_float(scale), None)
+
+
+def test_prefill_validation(lib):
+    assert _prefill(lib, ptrs=(0, A, A, A, A)) == 1
+    assert _prefill(lib, ptrs=(A, A, A, A, 0)) == 1
+    assert _prefill(lib, T=0) == 2
+    assert _prefill(lib, B=-1) == 2
+    assert _prefill(lib, H=0) == 2
+    assert _prefill(lib, T=1 << 24) == 2                 # slice > 2^31 bytes
+    assert _prefill(lib, scale=float("nan")) == 3
+    assert _prefill(lib, scale=float("inf")) == 3
+    assert _prefill(lib, scale=-1.0) == 3
+    assert _prefill(lib, dtype=7) == 3
+    assert _prefill(lib, dqk=64, dv=64) == 4              # bf16 only at d = 128
+    assert _prefill(lib, dqk=128, dv=64) == 4
+    assert _prefill(lib, dtype=0, dqk=128, dv=128) == 4   # f32 only at d in {16, 32, 64}
+    assert _prefill(lib, dtype=0, dqk=48, dv=48) == 4
+    assert _prefill(lib, ptrs=(A + 8, A, A, A, A)) == 5
+    assert _prefill(lib, dtype=0, dqk=16, dv=16, ptrs=(A, A, A, A + 4, A)) == 5
+
+
+def _decode(lib, dtype=1, B=2, H=2, L=64, dqk=128, dv=128, q=A, rho=A, kc=A, vc=A, sl=A, o=A,
+            scale=0.1, splits=1, ws=0, wsb=0):
+    return lib.plx_attn_decode(dtype, B, H, L, dqk, dv, q, rho, kc, vc, sl, o,
+                               ctypes.c_float(scale), splits, ws, wsb, None)
+
+
+def test_decode_validation(lib):
+    assert _decode(lib, sl=0) == 1
+    assert _decode(lib, kc=0) == 1
+    assert _decode(lib, L=0) == 2
+    assert _decode(lib, L=1 << 23) == 2
+    assert _decode(lib, B=70000) == 2
+    assert _decode(lib, scale=float("nan")) == 3
+    assert _decode(lib, splits=-2) == 3
+    assert _decode(lib, splits=5000) == 3
+    assert _decode(lib, dtype=0) == 4
+    assert _decode(lib, dqk=64, dv=64) == 4
+    assert _decode(lib, vc=A + 2) == 5
+    assert _decode(lib, sl=A + 2) == 5
+    # split run: the workspace is required and must be large enough
+    assert _decode(lib, L=1024, splits=4) == 1
+    assert _decode(lib, L=1024, splits=4, ws=A, wsb=100) == 6
+    need = 2 * 2 * 4 * (2 * 128 + 4) * 4
+    assert _decode(lib, L=1024, splits=4, ws=A + 4, wsb=need) == 5
+
+
+def test_split_plan_explicit(lib):
+    assert plx.decode_num_splits(1, 16, 32768, 32) == 32
+    assert plx.decode_num_splits(1, 16, 1000, 3) == 3       # chunks of 384 keys
+    assert plx.decode_num_splits(1, 16, 100, 8) == 2        # chunks round up to 64 keys
+    assert plx.decode_num_splits(4, 4, 64, 1) == 1
+    assert plx.decode_workspace_size(2, 3, 4096, 128, 1) == 0
+    assert plx.decode_workspace_size(2, 3, 4096, 128, 4) == 2 * 3 * 4 * 260 * 4
+    with pytest.raises(_lib.PlxError):
+        plx.decode_num_splits(0, 1, 10, 1)

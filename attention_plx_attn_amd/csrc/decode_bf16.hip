@@ -128,7 +128,9 @@ __global__ __launch_bounds__(NT, 2) void decode_split_bf16_d128_kernel(
 #pragma unroll
             for (int i = 0; i < 4; ++i) {
                 const float own = sc[t][i];
-                const float score = col == 1 ? swap_adjacent(own) : own;
+                // DPP must run with every lane active: take the neighbour's value first.
+                const float partner = swap_adjacent(own);
+                const float score = col == 1 ? partner : own;
                 const bool valid = kb0 + 16 * t + 4 * g + i < j1;
                 const float wgt = valid ? exp2_fast(fmaf(score, c, -m_run)) : 0.f;
                 u[i] = col == 0 ? wgt : (col == 1 ? wgt * own : 0.f);

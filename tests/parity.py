@@ -56,6 +56,41 @@ def check_f32(got, ref, what: str = "") -> dict:
     return m
 
 
+U_BF16 = 2.0 ** -8  # unit roundoff of bf16 (8-bit significand)
+
+
+def weight_rounding_bound(q, k, v, rho, scale) -> np.ndarray:
+    """First-order bound on what rounding the weights to bf16 adds to a causal prefill.
+
+    The kernels round w_j and w_j t_j to bf16 (relative errors e_j, d_j with |e|,|d| <= u)
+    and take l and beta from the rounded values. Differentiating
+    o = (A1/l)(1 + beta/l) - A2/l gives
+        do = sum_j p_j [ e_j ((v_j - vbar)(1 + tbar) + C) + d_j t_j (vbar - v_j) ],
+    with C = sum_j p_j (t_j - tbar) v_j, hence
+        |do| <= u sum_j p_j ( |v_j - vbar| (|1 + tbar| + |t_j|) + |C| ).
+    Returns that bound per output element, [B, H, T, d_v]. It is a worst case (every
+    rounding error aligned) and grows with |t|, i.e. with the probe norm; actual errors
+    are several times smaller because the individual roundings have random signs.
+    """
+    q, k, v, rho = (to_f64(x) for x in (q, k, v, rho))
+    B, H, T, _ = q.shape
+    out = np.zeros(v.shape)
+    for b in range(B):
+        for h in range(H):
+            a = scale * q[b, h] @ k[b, h].T
+            a = np.where(np.tril(np.ones((T, T), bool)), a, -np.inf)
+            p = np.exp(a - a.max(1, keepdims=True))
+            p /= p.sum(1, keepdims=True)
+            t = rho[b, h] @ k[b, h].T
+            tbar = (p * t).sum(1)
+            vbar = p @ v[b, h]
+            C = (p * (t - tbar[:, None])) @ v[b, h]
+            dev = np.abs(v[b, h][None, :, :] - vbar[:, None, :])  # [i, j, c]
+            fac = np.abs(1 + tbar)[:, None] + np.abs(t)             # [i, j]
+            out[b, h] = U_BF16 * (np.einsum("ij,ijc->ic", p * fac, dev) + np.abs(C))
+    return out
+
+
 def sample_rows(B: int, H: int, T: int, n_random: int = 64, seed: int = 0) -> np.ndarray:
     """Flat row ids (b*H + h)*T + i: first rows, tile boundaries, last rows, random rows."""
     rng = np.random.default_rng(seed)

@@ -13,7 +13,11 @@
 //     keys on the 32 rows and the wave's queries on the 32 lanes of each half-wave;
 //   * K and V tiles of 64 keys are staged in LDS, double-buffered: K row-major (rows stored
 //     in a permuted order, below), V transposed (d rows x 64 keys) so that a value operand
-//     is one 16-byte LDS read;
+//     is one 16-byte LDS read. In the transposed tile the 16-byte key chunk of dim row d is
+//     XOR-swizzled with bits 4..6 of d: the transposing 8-byte stores of 16 lanes (16 dims
+//     8 apart) would otherwise all hit one bank pair. gfx950's LDS serves 16 lanes of a
+//     16-byte access per clock over 64 banks; with the 144-byte row pitch and this swizzle
+//     both the stores and the operand reads are conflict-free;
 //   * the score tile's accumulator layout is reused directly as the P operand of the value
 //     products O^T += V^T P^T: storing key rows with bits 2 and 3 of the row index swapped
 //     makes each lane's eight consecutive accumulator registers hold eight consecutive
@@ -27,6 +31,8 @@
 // Workgroups are issued longest query block first; with B*H a multiple of 8 all blocks of
 // one (b, h) land on the same XCD (dispatch is round-robin over the 8 XCDs), so its K/V
 // stay in that XCD's L2.
+#include <type_traits>
+
 #include "plx_device.hpp"
 #include "plx_kernels.hpp"
 
@@ -87,9 +93,6 @@ __global__ __launch_bounds__(NT, 1) void prefill_bf16_d128_kernel(
 
     const int kend = min(q0 + BR, T);
     const int ntiles = (kend + BC - 1) / BC;
-    const int wave_q_first = q0 + 32 * w;
-    const int wave_q_last = min(q0 + 32 * w + 31, T - 1);
-    const bool wave_active = wave_q_first < T;
 
     f32x16 acc1[4], acc2[4];
 #pragma unroll
@@ -129,60 +132,41 @@ __global__ __launch_bounds__(NT, 1) void prefill_bf16_d128_kernel(
             const uint32_t lo23 = __builtin_amdgcn_perm(vst[3][p], vst[2][p], 0x05040100u);
             const uint32_t hi01 = __builtin_amdgcn_perm(vst[1][p], vst[0][p], 0x07060302u);
             const uint32_t hi23 = __builtin_amdgcn_perm(vst[3][p], vst[2][p], 0x07060302u);
-            const int d0 = 8 * vdc + 2 * p;
-            *(u32x2*)(Vl + d0 * VS + 4 * vkg) = u32x2{lo01, lo23};
-            *(u32x2*)(Vl + (d0 + 1) * VS + 4 * vkg) = u32x2{hi01, hi23};
+            const int d0 = 8 * vdc + 2 * p;  // d0 and d0 + 1 share bits 4..6 (= vdc >> 1)
+            const int cs = 8 * ((vkg >> 1) ^ ((vdc >> 1) & 7)) + 4 * (vkg & 1);
+            *(u32x2*)(Vl + d0 * VS + cs) = u32x2{lo01, lo23};
+            *(u32x2*)(Vl + (d0 + 1) * VS + cs) = u32x2{hi01, hi23};
         }
     };
 
-    // Key offset (within a 32-key half tile) of accumulator register i in this half-wave.
-    int koff[16];
-#pragma unroll
-    for (int i = 0; i < 16; ++i) koff[i] = perm_row(8 * (i >> 2) + 4 * h + (i & 3));
-
-    gload(0);
-    lstore(0);
-    __syncthreads();
-
     const int qi = q0 + 32 * w + n;
-    for (int kt = 0; kt < ntiles; ++kt) {
-        const int buf = kt & 1;
-        const bool more = kt + 1 < ntiles;
-        if (more) gload(kt + 1);
 
-        if (wave_active && kt * BC <= wave_q_last) {
-            const __bf16* Kl = lds + buf * BUF_ELEMS;
-            const __bf16* Vl = Kl + K_ELEMS;
-
-            // S^T and T^T for the two 32-key halves of the tile (shared K operand).
-            f32x16 S[2], Tt[2];
+    // One 64-key tile: scores on the shared K operand, online softmax with the lazy
+    // running max, value products on the shared V operand. DIAG: the tile reaches past
+    // some row of the block, so keys after the row are masked (weight exactly 0).
+    auto tile = [&](int kt, auto diag_tag) {
+        constexpr bool DIAG = decltype(diag_tag)::value;
+        const __bf16* Kl = lds + (kt & 1) * BUF_ELEMS;
+        const __bf16* Vl = Kl + K_ELEMS;
 #pragma unroll
-            for (int hc = 0; hc < 2; ++hc) {
-                S[hc] = f32x16{};
-                Tt[hc] = f32x16{};
+        for (int hc = 0; hc < 2; ++hc) {
+            f32x16 S = f32x16{}, Tt = f32x16{};
 #pragma unroll
-                for (int s = 0; s < 8; ++s) {
-                    const bf16x8 kf = *(const bf16x8*)(Kl + (32 * hc + n) * KS + 16 * s + 8 * h);
-                    S[hc] = mfma32(kf, qf[s], S[hc]);
-                    Tt[hc] = mfma32(kf, rf[s], Tt[hc]);
-                }
+            for (int s = 0; s < 8; ++s) {
+                const bf16x8 kf = *(const bf16x8*)(Kl + (32 * hc + n) * KS + 16 * s + 8 * h);
+                S = mfma32(kf, qf[s], S);
+                Tt = mfma32(kf, rf[s], Tt);
             }
-
-            // Causal mask (key > query) on tiles that reach past the wave's first row.
-            const bool diag = kt * BC + BC - 1 > wave_q_first;
-            if (diag) {
+            // Register i of this half-wave holds key 64 kt + 32 hc + perm_row(8 (i/4) + 4 h + i%4).
+            if constexpr (DIAG) {
+                const int lim = qi - (kt * BC + 32 * hc);
 #pragma unroll
-                for (int hc = 0; hc < 2; ++hc)
-#pragma unroll
-                    for (int i = 0; i < 16; ++i)
-                        if (kt * BC + 32 * hc + koff[i] > qi) S[hc][i] = -INFINITY;
+                for (int i = 0; i < 16; ++i)
+                    if (perm_row(8 * (i >> 2) + 4 * h + (i & 3)) > lim) S[i] = -INFINITY;
             }
-
-            float mt = -INFINITY;
+            float mt = S[0];
 #pragma unroll
-            for (int hc = 0; hc < 2; ++hc)
-#pragma unroll
-                for (int i = 0; i < 16; ++i) mt = fmaxf(mt, S[hc][i]);
+            for (int i = 1; i < 16; ++i) mt = fmaxf(mt, S[i]);
             mt = fmaxf(mt, shfl_xor(mt, 32));
             const float ms = mt > -INFINITY ? mt * c : -INFINITY;
 
@@ -200,46 +184,56 @@ __global__ __launch_bounds__(NT, 1) void prefill_bf16_d128_kernel(
                 m_run = mn;
             }
 
-            // P1 = exp2(S c - m), P2 = P1 * T, rounded to bf16; row sums from rounded values.
-            bf16x8 pf[4], p2f[4];
+            // P1 = exp2(S c - m), P2 = P1 * T, rounded to bf16 (row sums from the rounded
+            // values), then O1^T += V^T P1^T and O2^T += V^T P2^T on a shared V operand.
 #pragma unroll
-            for (int hc = 0; hc < 2; ++hc) {
+            for (int r = 0; r < 2; ++r) {
+                float wv[8];
 #pragma unroll
-                for (int r = 0; r < 2; ++r) {
-                    u32x4 pw, p2w;
-#pragma unroll
-                    for (int e = 0; e < 8; e += 2) {
-                        const int i0 = 8 * r + e, i1 = i0 + 1;
-                        const float w0 = S[hc][i0] == -INFINITY
-                                             ? 0.f
-                                             : exp2_fast(fmaf(S[hc][i0], c, -m_run));
-                        const float w1 = S[hc][i1] == -INFINITY
-                                             ? 0.f
-                                             : exp2_fast(fmaf(S[hc][i1], c, -m_run));
-                        pw[e >> 1] = pack_bf16x2(w0, w1);
-                        p2w[e >> 1] = pack_bf16x2(w0 * Tt[hc][i0], w1 * Tt[hc][i1]);
-                        lsum = add_bf16x2(pw[e >> 1], lsum);
-                        bsum = add_bf16x2(p2w[e >> 1], bsum);
-                    }
-                    pf[2 * hc + r] = as_bf16x8(pw);
-                    p2f[2 * hc + r] = as_bf16x8(p2w);
+                for (int e = 0; e < 8; ++e) {
+                    wv[e] = exp2_fast(fmaf(S[8 * r + e], c, -m_run));
+                    if constexpr (DIAG) wv[e] = S[8 * r + e] == -INFINITY ? 0.f : wv[e];
                 }
-            }
-
-            // O1^T += V^T P1^T and O2^T += V^T P2^T (shared V operand).
+                u32x4 pw, p2w;
 #pragma unroll
-            for (int ks = 0; ks < 4; ++ks) {
+                for (int e = 0; e < 8; e += 2) {
+                    pw[e >> 1] = pack_bf16x2(wv[e], wv[e + 1]);
+                    p2w[e >> 1] = pack_bf16x2(wv[e] * Tt[8 * r + e], wv[e + 1] * Tt[8 * r + e + 1]);
+                    lsum = add_bf16x2(pw[e >> 1], lsum);
+                    bsum = add_bf16x2(p2w[e >> 1], bsum);
+                }
+                const bf16x8 pf = as_bf16x8(pw), p2f = as_bf16x8(p2w);
+                const int ks = 2 * hc + r;
 #pragma unroll
                 for (int nb = 0; nb < 4; ++nb) {
-                    const bf16x8 vf = *(const bf16x8*)(Vl + (32 * nb + n) * VS + 16 * ks + 8 * h);
-                    acc1[nb] = mfma32(vf, pf[ks], acc1[nb]);
-                    acc2[nb] = mfma32(vf, p2f[ks], acc2[nb]);
+                    const int vr = 32 * nb + n;
+                    const bf16x8 vf =
+                        *(const bf16x8*)(Vl + vr * VS + 8 * ((2 * ks + h) ^ ((vr >> 4) & 7)));
+                    acc1[nb] = mfma32(vf, pf, acc1[nb]);
+                    acc2[nb] = mfma32(vf, p2f, acc2[nb]);
                 }
             }
         }
-
-        if (more) lstore(buf ^ 1);
+        // Stage the next tile (prefetched into registers at the top of the iteration).
+        lstore((kt & 1) ^ 1);
         __syncthreads();
+    };
+
+    gload(0);
+    lstore(0);
+    __syncthreads();
+    // Tiles entirely below the block's first row need no mask; the last one or two do.
+    // The next tile is prefetched unconditionally: after the last tile this reads one
+    // tile past the block (zeros past T through the buffer range) into an LDS buffer
+    // nobody reads again, which keeps branches out of the loop body.
+    const int nfull = min(ntiles, q0 / BC);
+    for (int kt = 0; kt < nfull; ++kt) {
+        gload(kt + 1);
+        tile(kt, std::false_type{});
+    }
+    for (int kt = nfull; kt < ntiles; ++kt) {
+        gload(kt + 1);
+        tile(kt, std::true_type{});
     }
 
     // Epilogue: combine the half-waves' sums, o = (A1/l)(1 + beta/l) - A2/l, RNE to bf16.

@@ -1,31 +1,33 @@
 // prefill_bf16.hip -- causal Parallax prefill, bf16 in/out, d_qk = d_v = 128, gfx950.
 //
 // Method [Parallax (paper.rainbus.top summary), "方法步骤详情": per KV block compute the
-// scores S1 = Q K^T and the probe products S2 = R K^T sharing one matrix instruction's
-// operand, then P1 = exp(S1 - m) and P2 = P1 * S2, and accumulate O1 += P1 V and O2 += P2 V
-// in parallel; agihunt review, hardware paragraph: both branches share one KV stream, one
-// running max and one rescale factor]. Final combine o = (1 + tbar) O1 - O2 with
-// tbar = sum P2 / sum P1 (method step 6).
+// scores S1 = Q K^T and the probe products S2 = R K^T, then P1 = exp(S1 - m) and
+// P2 = P1 * S2, and accumulate O1 += P1 V and O2 += P2 V in parallel; agihunt review,
+// hardware paragraph: both branches share one KV stream, one running max and one rescale
+// factor]. Final combine o = (1 + tbar) O1 - O2 with tbar = sum P2 / sum P1 (step 6).
 //
-// Work decomposition (one workgroup = 4 waves = 128 query rows of one (b, h)):
-//   * every wave owns 32 query rows; its Q and R fragments stay in registers as the
-//     B operand of v_mfma_f32_32x32x16_bf16, so the product tile is S^T = K [Q|R]^T with
-//     keys on the 32 rows and the wave's queries on the 32 lanes of each half-wave;
-//   * K and V tiles of 64 keys are staged in LDS, double-buffered: K row-major (rows stored
-//     in a permuted order, below), V transposed (d rows x 64 keys) so that a value operand
-//     is one 16-byte LDS read. In the transposed tile the 16-byte key chunk of dim row d is
-//     XOR-swizzled with bits 4..6 of d: the transposing 8-byte stores of 16 lanes (16 dims
-//     8 apart) would otherwise all hit one bank pair. gfx950's LDS serves 16 lanes of a
-//     16-byte access per clock over 64 banks; with the 144-byte row pitch and this swizzle
-//     both the stores and the operand reads are conflict-free;
+// Work decomposition: one workgroup = 128 query rows of one (b, h) = 4 query groups of 32
+// rows, and 8 waves, two per SIMD. For query group g, wave g runs the softmax branch
+// (Q K^T, running max, P1, O1 += P1 V) and wave g + 4, on the same SIMD, runs the probe
+// branch (R K^T, P2 = P1 * T, O2 += P2 V) one tile behind, reading the softmax wave's
+// rounded weights and rescale factors from LDS. Both waves issue the same number of
+// matrix instructions, so each SIMD's matrix pipe is fed by two independent instruction
+// streams while either one waits on LDS or on its vector work. Details:
+//   * a wave's Q (or R) fragments stay in registers as the B operand of
+//     v_mfma_f32_32x32x16_bf16, so the product tile is S^T = K Q^T (or T^T = K R^T) with
+//     keys on the 32 rows and the group's queries on the 32 lanes of each half-wave;
+//   * K and V tiles of 64 keys are staged in LDS, three buffers each (the probe wave reads
+//     the tile before the softmax wave's): K row-major with rows stored in a permuted order,
+//     V transposed (d rows x 64 keys) so a value operand is one 16-byte LDS read; the
+//     16-byte key chunks of dim row d are XOR-swizzled with bits 4..6 of d, which makes the
+//     transposing 8-byte stores and the operand reads conflict-free on gfx950's 64-bank LDS;
 //   * the score tile's accumulator layout is reused directly as the P operand of the value
 //     products O^T += V^T P^T: storing key rows with bits 2 and 3 of the row index swapped
 //     makes each lane's eight consecutive accumulator registers hold eight consecutive
 //     keys, exactly the operand layout, so no cross-lane traffic is needed;
-//   * lane <-> query throughout, so max, rescale and normaliser stay lane-local except one
-//     exchange with the other half-wave per tile (the two halves hold the two key halves);
-//   * P1 and P2 are rounded to bf16 and the sums l = sum P1, beta = sum P2 are taken from
-//     the rounded values, so the effective corrected weights sum to exactly one;
+//   * P1 and P2 are rounded to bf16 and l = sum P1, beta = sum P2 are taken from the rounded
+//     values, so the effective corrected weights sum to exactly one; P2 is formed from the
+//     rounded P1 the softmax wave hands over;
 //   * the running max is updated lazily (only when a row's tile max exceeds it by more than
 //     2^8); the result is the same exact expression, with far fewer rescales.
 // Workgroups are issued longest query block first; with B*H a multiple of 8 all blocks of
@@ -42,13 +44,21 @@ namespace {
 constexpr int D = 128;
 constexpr int BR = 128;  // query rows per workgroup
 constexpr int BC = 64;   // keys per LDS tile
-constexpr int NT = 256;  // threads per workgroup (4 waves)
-constexpr int KS = D + 8;               // LDS row stride of the K tile (bf16 elements)
-constexpr int VS = BC + 8;              // LDS row stride of the transposed V tile
-constexpr int K_ELEMS = BC * KS;        // 8704
-constexpr int V_ELEMS = D * VS;         // 9216
-constexpr int BUF_ELEMS = K_ELEMS + V_ELEMS;
-constexpr float kLazyTau = 8.0f;        // log2 headroom before the running max moves
+constexpr int NT = 512;  // threads per workgroup (8 waves)
+constexpr int KS = D + 8;         // LDS row stride of a K tile (bf16 elements)
+constexpr int VS = BC + 8;        // LDS row stride of a transposed V tile
+constexpr int K_ELEMS = BC * KS;  // 8704 bf16
+constexpr int V_ELEMS = D * VS;   // 9216 bf16
+constexpr int NBUF = 3;
+constexpr int W_BYTES = 4 * 4 * 64 * 16;  // rounded P1 of one tile: 4 groups x 4 k-steps x 64 lanes
+// LDS byte layout: K buffers | V buffers | 2 x P1 hand-over | 2 x rescale factors
+constexpr int OFF_V = NBUF * K_ELEMS * 2;
+constexpr int OFF_W = OFF_V + NBUF * V_ELEMS * 2;
+constexpr int OFF_A = OFF_W + 2 * W_BYTES;
+constexpr int LDS_BYTES = OFF_A + 2 * 4 * 32 * 4;
+static_assert(LDS_BYTES <= 160 * 1024, "LDS budget");
+static_assert(4 * 64 * 64 * 4 <= OFF_W, "epilogue hand-over must fit in the K/V buffers");
+constexpr float kLazyTau = 8.0f;  // log2 headroom before the running max moves
 
 // Row order inside each 32-key half of a K tile: bits 2 and 3 swapped (an involution).
 __device__ __forceinline__ int perm_row(int r) {
@@ -62,7 +72,7 @@ __device__ __forceinline__ f32x16 mfma32(bf16x8 a, bf16x8 b, f32x16 c) {
 __global__ __launch_bounds__(NT, 1) void prefill_bf16_d128_kernel(
     const __bf16* __restrict__ q, const __bf16* __restrict__ k, const __bf16* __restrict__ v,
     const __bf16* __restrict__ rho, __bf16* __restrict__ o, int BH, int T, int nqb, float c) {
-    __shared__ __attribute__((aligned(16))) __bf16 lds[2 * BUF_ELEMS];
+    __shared__ __attribute__((aligned(16))) unsigned char lds[LDS_BYTES];
 
     const int wid = blockIdx.x;
     const int bh = wid % BH;
@@ -70,188 +80,253 @@ __global__ __launch_bounds__(NT, 1) void prefill_bf16_d128_kernel(
     const int q0 = qb * BR;
     const int tid = threadIdx.x;
     const int lane = tid & 63;
-    const int w = tid >> 6;
-    const int n = lane & 31;  // query within the wave's 32 rows
-    const int h = lane >> 5;  // half-wave: which 8-element k-slice of an operand
+    const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const bool probe = w >= 4;  // wave-uniform role
+    const int g = w & 3;        // query group
+    const int n = lane & 31;    // query within the group
+    const int h = lane >> 5;    // half-wave: which 8-element k-slice of an operand
+    const int qi = q0 + 32 * g + n;
 
     const size_t slice = (size_t)bh * (size_t)T * D;
     const uint32_t slice_bytes = (uint32_t)T * D * 2u;
-    const auto rq = make_rsrc(q + slice, slice_bytes);
-    const auto rr = make_rsrc(rho + slice, slice_bytes);
     const auto rk = make_rsrc(k + slice, slice_bytes);
     const auto rv = make_rsrc(v + slice, slice_bytes);
 
-    // Q and R fragments: B operand, lane holds dims 16 s + 8 h .. +7 of its query row.
-    const int qrow = q0 + 32 * w + n;
-    bf16x8 qf[8], rf[8];
+    auto kbuf = [&](int t) { return (__bf16*)(lds + (t % NBUF) * K_ELEMS * 2); };
+    auto vbuf = [&](int t) { return (__bf16*)(lds + OFF_V + (t % NBUF) * V_ELEMS * 2); };
+    auto wbuf = [&](int t) { return (u32x4*)(lds + OFF_W + (t & 1) * W_BYTES) + g * 256; };
+    auto abuf = [&](int t) { return (float*)(lds + OFF_A) + ((t & 1) * 4 + g) * 32; };
+
+    // Q (softmax waves) or R (probe waves) fragments: B operand, lane holds dims
+    // 16 s + 8 h .. +7 of its query row.
+    bf16x8 xf[8];
+    {
+        const auto rx = make_rsrc((probe ? rho : q) + slice, slice_bytes);
 #pragma unroll
-    for (int s = 0; s < 8; ++s) {
-        const uint32_t off = (uint32_t)qrow * 256u + 32u * s + 16u * h;
-        qf[s] = as_bf16x8(load16(rq, off));
-        rf[s] = as_bf16x8(load16(rr, off));
+        for (int s = 0; s < 8; ++s)
+            xf[s] = as_bf16x8(load16(rx, (uint32_t)qi * 256u + 32u * s + 16u * h));
     }
 
     const int kend = min(q0 + BR, T);
     const int ntiles = (kend + BC - 1) / BC;
 
-    f32x16 acc1[4], acc2[4];
+    f32x16 acc[4];
 #pragma unroll
-    for (int nb = 0; nb < 4; ++nb) {
-        acc1[nb] = f32x16{};
-        acc2[nb] = f32x16{};
-    }
-    float m_run = -INFINITY, lsum = 0.f, bsum = 0.f;
+    for (int nb = 0; nb < 4; ++nb) acc[nb] = f32x16{};
+    float rsum = 0.f;  // softmax waves: l = sum P1; probe waves: beta = sum P2
 
-    // ---- global -> registers -> LDS staging of one 64-key tile
-    u32x4 kst[4], vst[4];
-    const int vdc = tid & 15;  // V: dims 8 vdc .. +7
-    const int vkg = tid >> 4;  // V: keys 4 vkg .. +3
+    // ---- staging: softmax waves (threads 0..255) load K tiles, probe waves load V tiles.
+    const int st = tid & 255;
+    u32x4 stg[4];
     auto gload = [&](int kt) {
+        if (!probe) {
 #pragma unroll
-        for (int j = 0; j < 4; ++j) {
-            const int chunk = tid + NT * j;
-            const int row = chunk >> 4, col = chunk & 15;
-            kst[j] = load16(rk, (uint32_t)(kt * BC + row) * 256u + 16u * col);
-            vst[j] = load16(rv, (uint32_t)(kt * BC + 4 * vkg + j) * 256u + 16u * vdc);
-        }
-    };
-    auto lstore = [&](int buf) {
-        __bf16* Kl = lds + buf * BUF_ELEMS;
-        __bf16* Vl = Kl + K_ELEMS;
-#pragma unroll
-        for (int j = 0; j < 4; ++j) {
-            const int chunk = tid + NT * j;
-            const int row = chunk >> 4, col = chunk & 15;
-            const int prow = (row & 32) | perm_row(row & 31);
-            *(u32x4*)(Kl + prow * KS + col * 8) = kst[j];
-        }
-        // Transpose 4 keys x 8 dims into 8 dims x 4 keys (byte permutes), 8-byte stores.
-#pragma unroll
-        for (int p = 0; p < 4; ++p) {
-            const uint32_t lo01 = __builtin_amdgcn_perm(vst[1][p], vst[0][p], 0x05040100u);
-            const uint32_t lo23 = __builtin_amdgcn_perm(vst[3][p], vst[2][p], 0x05040100u);
-            const uint32_t hi01 = __builtin_amdgcn_perm(vst[1][p], vst[0][p], 0x07060302u);
-            const uint32_t hi23 = __builtin_amdgcn_perm(vst[3][p], vst[2][p], 0x07060302u);
-            const int d0 = 8 * vdc + 2 * p;  // d0 and d0 + 1 share bits 4..6 (= vdc >> 1)
-            const int cs = 8 * ((vkg >> 1) ^ ((vdc >> 1) & 7)) + 4 * (vkg & 1);
-            *(u32x2*)(Vl + d0 * VS + cs) = u32x2{lo01, lo23};
-            *(u32x2*)(Vl + (d0 + 1) * VS + cs) = u32x2{hi01, hi23};
-        }
-    };
-
-    const int qi = q0 + 32 * w + n;
-
-    // One 64-key tile: scores on the shared K operand, online softmax with the lazy
-    // running max, value products on the shared V operand. DIAG: the tile reaches past
-    // some row of the block, so keys after the row are masked (weight exactly 0).
-    auto tile = [&](int kt, auto diag_tag) {
-        constexpr bool DIAG = decltype(diag_tag)::value;
-        const __bf16* Kl = lds + (kt & 1) * BUF_ELEMS;
-        const __bf16* Vl = Kl + K_ELEMS;
-#pragma unroll
-        for (int hc = 0; hc < 2; ++hc) {
-            f32x16 S = f32x16{}, Tt = f32x16{};
-#pragma unroll
-            for (int s = 0; s < 8; ++s) {
-                const bf16x8 kf = *(const bf16x8*)(Kl + (32 * hc + n) * KS + 16 * s + 8 * h);
-                S = mfma32(kf, qf[s], S);
-                Tt = mfma32(kf, rf[s], Tt);
+            for (int j = 0; j < 4; ++j) {
+                const int chunk = st + 256 * j;
+                stg[j] = load16(rk, (uint32_t)(kt * BC + (chunk >> 4)) * 256u + 16u * (chunk & 15));
             }
-            // Register i of this half-wave holds key 64 kt + 32 hc + perm_row(8 (i/4) + 4 h + i%4).
-            if constexpr (DIAG) {
+        } else {
+            const int vdc = st & 15, vkg = st >> 4;  // dims 8 vdc .. +7, keys 4 vkg .. +3
+#pragma unroll
+            for (int j = 0; j < 4; ++j)
+                stg[j] = load16(rv, (uint32_t)(kt * BC + 4 * vkg + j) * 256u + 16u * vdc);
+        }
+    };
+    auto lstore = [&](int kt) {
+        if (!probe) {
+            __bf16* Kl = kbuf(kt);
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+                const int chunk = st + 256 * j;
+                const int row = chunk >> 4, col = chunk & 15;
+                const int prow = (row & 32) | perm_row(row & 31);
+                *(u32x4*)(Kl + prow * KS + col * 8) = stg[j];
+            }
+        } else {
+            __bf16* Vl = vbuf(kt);
+            const int vdc = st & 15, vkg = st >> 4;
+            // Transpose 4 keys x 8 dims into 8 dims x 4 keys (byte permutes), 8-byte stores.
+#pragma unroll
+            for (int p = 0; p < 4; ++p) {
+                const uint32_t lo01 = __builtin_amdgcn_perm(stg[1][p], stg[0][p], 0x05040100u);
+                const uint32_t lo23 = __builtin_amdgcn_perm(stg[3][p], stg[2][p], 0x05040100u);
+                const uint32_t hi01 = __builtin_amdgcn_perm(stg[1][p], stg[0][p], 0x07060302u);
+                const uint32_t hi23 = __builtin_amdgcn_perm(stg[3][p], stg[2][p], 0x07060302u);
+                const int d0 = 8 * vdc + 2 * p;  // d0 and d0 + 1 share bits 4..6 (= vdc >> 1)
+                const int cs = 8 * ((vkg >> 1) ^ ((vdc >> 1) & 7)) + 4 * (vkg & 1);
+                *(u32x2*)(Vl + d0 * VS + cs) = u32x2{lo01, lo23};
+                *(u32x2*)(Vl + (d0 + 1) * VS + cs) = u32x2{hi01, hi23};
+            }
+        }
+    };
+
+    // Product tile for one 32-key half (hc) of K tile kt against this wave's fragments.
+    auto scores = [&](int kt, int hc) {
+        const __bf16* Kl = kbuf(kt) + (32 * hc + n) * KS + 8 * h;
+        f32x16 S = f32x16{};
+#pragma unroll
+        for (int s = 0; s < 8; ++s) S = mfma32(*(const bf16x8*)(Kl + 16 * s), xf[s], S);
+        return S;
+    };
+    // O^T += V^T P^T for k-step ks (keys 16 ks .. +15) of V tile kt.
+    auto value_products = [&](int kt, int ks, bf16x8 pf) {
+        const __bf16* Vl = vbuf(kt);
+#pragma unroll
+        for (int nb = 0; nb < 4; ++nb) {
+            const int vr = 32 * nb + n;
+            const bf16x8 vf = *(const bf16x8*)(Vl + vr * VS + 8 * ((2 * ks + h) ^ ((vr >> 4) & 7)));
+            acc[nb] = mfma32(vf, pf, acc[nb]);
+        }
+    };
+
+    // ---- softmax branch: tile kt.
+    float m_run = -INFINITY;
+    auto softmax_tile = [&](int kt, auto diag_tag) {
+        constexpr bool DIAG = decltype(diag_tag)::value;
+        f32x16 S[2];
+        S[0] = scores(kt, 0);
+        S[1] = scores(kt, 1);
+        // Register i of half hc holds key 64 kt + 32 hc + perm_row(8 (i/4) + 4 h + i%4).
+        if constexpr (DIAG) {
+#pragma unroll
+            for (int hc = 0; hc < 2; ++hc) {
                 const int lim = qi - (kt * BC + 32 * hc);
 #pragma unroll
                 for (int i = 0; i < 16; ++i)
-                    if (perm_row(8 * (i >> 2) + 4 * h + (i & 3)) > lim) S[i] = -INFINITY;
-            }
-            float mt = S[0];
-#pragma unroll
-            for (int i = 1; i < 16; ++i) mt = fmaxf(mt, S[i]);
-            mt = fmaxf(mt, shfl_xor(mt, 32));
-            const float ms = mt > -INFINITY ? mt * c : -INFINITY;
-
-            const bool need = ms > m_run + kLazyTau;
-            if (wave_any(need)) {
-                const float mn = need ? ms : m_run;
-                const float alpha = exp2_fast(m_run - mn);
-                lsum *= alpha;
-                bsum *= alpha;
-#pragma unroll
-                for (int nb = 0; nb < 4; ++nb) {
-                    acc1[nb] *= alpha;
-                    acc2[nb] *= alpha;
-                }
-                m_run = mn;
-            }
-
-            // P1 = exp2(S c - m), P2 = P1 * T, rounded to bf16 (row sums from the rounded
-            // values), then O1^T += V^T P1^T and O2^T += V^T P2^T on a shared V operand.
-#pragma unroll
-            for (int r = 0; r < 2; ++r) {
-                float wv[8];
-#pragma unroll
-                for (int e = 0; e < 8; ++e) {
-                    wv[e] = exp2_fast(fmaf(S[8 * r + e], c, -m_run));
-                    if constexpr (DIAG) wv[e] = S[8 * r + e] == -INFINITY ? 0.f : wv[e];
-                }
-                u32x4 pw, p2w;
-#pragma unroll
-                for (int e = 0; e < 8; e += 2) {
-                    pw[e >> 1] = pack_bf16x2(wv[e], wv[e + 1]);
-                    p2w[e >> 1] = pack_bf16x2(wv[e] * Tt[8 * r + e], wv[e + 1] * Tt[8 * r + e + 1]);
-                    lsum = add_bf16x2(pw[e >> 1], lsum);
-                    bsum = add_bf16x2(p2w[e >> 1], bsum);
-                }
-                const bf16x8 pf = as_bf16x8(pw), p2f = as_bf16x8(p2w);
-                const int ks = 2 * hc + r;
-#pragma unroll
-                for (int nb = 0; nb < 4; ++nb) {
-                    const int vr = 32 * nb + n;
-                    const bf16x8 vf =
-                        *(const bf16x8*)(Vl + vr * VS + 8 * ((2 * ks + h) ^ ((vr >> 4) & 7)));
-                    acc1[nb] = mfma32(vf, pf, acc1[nb]);
-                    acc2[nb] = mfma32(vf, p2f, acc2[nb]);
-                }
+                    if (perm_row(8 * (i >> 2) + 4 * h + (i & 3)) > lim) S[hc][i] = -INFINITY;
             }
         }
-        // Stage the next tile (prefetched into registers at the top of the iteration).
-        lstore((kt & 1) ^ 1);
-        __syncthreads();
+        float mt = fmaxf(S[0][0], S[1][0]);
+#pragma unroll
+        for (int i = 1; i < 16; ++i) mt = fmaxf(mt, fmaxf(S[0][i], S[1][i]));
+        mt = fmaxf(mt, shfl_xor(mt, 32));
+        const float ms = mt > -INFINITY ? mt * c : -INFINITY;
+        const bool need = ms > m_run + kLazyTau;
+        float alpha = 1.f;
+        if (wave_any(need)) {
+            const float mn = need ? ms : m_run;
+            alpha = exp2_fast(m_run - mn);
+            rsum *= alpha;
+#pragma unroll
+            for (int nb = 0; nb < 4; ++nb) acc[nb] *= alpha;
+            m_run = mn;
+        }
+        if (h == 0) abuf(kt)[n] = alpha;  // the probe wave applies the same rescale
+        u32x4* wout = wbuf(kt);
+#pragma unroll
+        for (int ks = 0; ks < 4; ++ks) {
+            const int hc = ks >> 1, r = ks & 1;
+            u32x4 pw;
+#pragma unroll
+            for (int e = 0; e < 8; e += 2) {
+                float w0 = exp2_fast(fmaf(S[hc][8 * r + e], c, -m_run));
+                float w1 = exp2_fast(fmaf(S[hc][8 * r + e + 1], c, -m_run));
+                if constexpr (DIAG) {  // masked keys: weight exactly 0 (also when c == 0)
+                    w0 = S[hc][8 * r + e] == -INFINITY ? 0.f : w0;
+                    w1 = S[hc][8 * r + e + 1] == -INFINITY ? 0.f : w1;
+                }
+                pw[e >> 1] = pack_bf16x2(w0, w1);
+                rsum = add_bf16x2(pw[e >> 1], rsum);
+            }
+            wout[ks * 64 + lane] = pw;
+            value_products(kt, ks, as_bf16x8(pw));
+        }
     };
 
+    // ---- probe branch: tile kt (one tile behind the softmax branch).
+    auto probe_tile = [&](int kt) {
+        const float alpha = abuf(kt)[n];
+        if (wave_any(alpha != 1.f)) {
+            rsum *= alpha;
+#pragma unroll
+            for (int nb = 0; nb < 4; ++nb) acc[nb] *= alpha;
+        }
+        const u32x4* win = wbuf(kt);
+#pragma unroll
+        for (int hc = 0; hc < 2; ++hc) {
+            const f32x16 Tt = scores(kt, hc);
+#pragma unroll
+            for (int r = 0; r < 2; ++r) {
+                const int ks = 2 * hc + r;
+                const u32x4 pw = win[ks * 64 + lane];
+                u32x4 p2w;
+#pragma unroll
+                for (int e = 0; e < 8; e += 2) {
+                    const uint32_t x = pw[e >> 1];
+                    p2w[e >> 1] = pack_bf16x2(bf16_lo(x) * Tt[8 * r + e], bf16_hi(x) * Tt[8 * r + e + 1]);
+                    rsum = add_bf16x2(p2w[e >> 1], rsum);
+                }
+                value_products(kt, ks, as_bf16x8(p2w));
+            }
+        }
+    };
+
+    // ---- pipeline. Iteration it: the softmax waves process tile it, the probe waves tile
+    // it - 1; tile it + 1 is prefetched into registers at the top and stored into buffer
+    // (it + 1) % 3 at the bottom, before the one barrier per iteration. That buffer last
+    // held tile it - 2, read by the softmax waves in iteration it - 2 and by the probe waves
+    // in iteration it - 1. Loads past the block (or past T: zeros through the buffer range)
+    // land in buffers nobody reads again. Both roles run ntiles + 1 iterations.
     gload(0);
     lstore(0);
     __syncthreads();
-    // Tiles entirely below the block's first row need no mask; the last one or two do.
-    // The next tile is prefetched unconditionally: after the last tile this reads one
-    // tile past the block (zeros past T through the buffer range) into an LDS buffer
-    // nobody reads again, which keeps branches out of the loop body.
-    const int nfull = min(ntiles, q0 / BC);
-    for (int kt = 0; kt < nfull; ++kt) {
-        gload(kt + 1);
-        tile(kt, std::false_type{});
-    }
-    for (int kt = nfull; kt < ntiles; ++kt) {
-        gload(kt + 1);
-        tile(kt, std::true_type{});
+    const int nfull = min(ntiles, q0 / BC);  // tiles entirely below the block's first row
+    if (!probe) {
+        for (int it = 0; it < nfull; ++it) {
+            gload(it + 1);
+            softmax_tile(it, std::false_type{});
+            lstore(it + 1);
+            __syncthreads();
+        }
+        for (int it = nfull; it < ntiles; ++it) {
+            gload(it + 1);
+            softmax_tile(it, std::true_type{});
+            lstore(it + 1);
+            __syncthreads();
+        }
+        __syncthreads();  // the probe waves' last iteration
+    } else {
+        gload(1);
+        lstore(1);
+        __syncthreads();
+        for (int it = 1; it <= ntiles; ++it) {
+            gload(it + 1);
+            probe_tile(it - 1);
+            lstore(it + 1);
+            __syncthreads();
+        }
     }
 
-    // Epilogue: combine the half-waves' sums, o = (A1/l)(1 + beta/l) - A2/l, RNE to bf16.
-    lsum += shfl_xor(lsum, 32);
-    bsum += shfl_xor(bsum, 32);
-    if (qi < T) {
-        const float inv = 1.f / lsum;
-        const float one_tb = 1.f + bsum * inv;
+    // ---- epilogue: probe waves hand O2 and beta over through LDS; the softmax waves
+    // combine o = (A1/l)(1 + beta/l) - A2/l and round to bf16.
+    rsum += shfl_xor(rsum, 32);  // both key halves of each row
+    u32x4* hand = (u32x4*)lds + g * 64 * 16;
+    float* bhand = (float*)(lds + OFF_W) + g * 32;
+    if (probe) {
+#pragma unroll
+        for (int nb = 0; nb < 4; ++nb)
+#pragma unroll
+            for (int j = 0; j < 4; ++j)
+                hand[(4 * nb + j) * 64 + lane] =
+                    __builtin_bit_cast(u32x4, f32x4{acc[nb][4 * j], acc[nb][4 * j + 1],
+                                                   acc[nb][4 * j + 2], acc[nb][4 * j + 3]});
+        if (h == 0) bhand[n] = rsum;
+    }
+    __syncthreads();
+    if (!probe && qi < T) {
+        const float inv = 1.f / rsum;
+        const float one_tb = 1.f + bhand[n] * inv;
         __bf16* orow = o + slice + (size_t)qi * D;
 #pragma unroll
         for (int nb = 0; nb < 4; ++nb) {
 #pragma unroll
-            for (int g = 0; g < 4; ++g) {
+            for (int j = 0; j < 4; ++j) {
+                const f32x4 a2 = __builtin_bit_cast(f32x4, hand[(4 * nb + j) * 64 + lane]);
                 float y[4];
 #pragma unroll
-                for (int r = 0; r < 4; ++r)
-                    y[r] = inv * (acc1[nb][4 * g + r] * one_tb - acc2[nb][4 * g + r]);
-                const int d0 = 32 * nb + 8 * g + 4 * h;
+                for (int r = 0; r < 4; ++r) y[r] = inv * (acc[nb][4 * j + r] * one_tb - a2[r]);
+                // register 4 j + r holds dim 32 nb + 8 j + 4 h + r
+                const int d0 = 32 * nb + 8 * j + 4 * h;
                 *(u32x2*)(orow + d0) = u32x2{pack_bf16x2(y[0], y[1]), pack_bf16x2(y[2], y[3])};
             }
         }

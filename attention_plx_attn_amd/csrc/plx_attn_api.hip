@@ -37,10 +37,10 @@ plx_status_t current_cu_count(int* out) {
     return PLX_OK;
 }
 
-constexpr int kDecodeWaveKeys = 64;      // keys one wave consumes per step
+constexpr int kDecodeWaveKeys = 64;      // chunk granularity (keys)
 constexpr int kDecodeMinChunk = 256;     // at least one step per wave of a 4-wave workgroup
 constexpr int kDecodeMaxSplits = 4096;
-constexpr int kDecodeWgPerCu = 2;        // target resident workgroups per compute unit
+constexpr int kDecodeWgPerCu = 1;        // one streaming workgroup per compute unit (measured best)
 
 int ceil_div(long long a, long long b) { return (int)((a + b - 1) / b); }
 

@@ -32,6 +32,11 @@ __device__ __forceinline__ u32x4 load16(__amdgpu_buffer_rsrc_t r, uint32_t off) 
     return __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, 0);
 }
 
+// Same, marked non-temporal (streamed once; do not keep in the caches).
+__device__ __forceinline__ u32x4 load16_nt(__amdgpu_buffer_rsrc_t r, uint32_t off) {
+    return __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, 2);
+}
+
 // ----------------------------------------------------------------------------- bf16
 __device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
     bf16x2 v = {(__bf16)lo, (__bf16)hi};  // v_cvt_pk_bf16_f32, round to nearest even

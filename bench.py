@@ -18,7 +18,8 @@ null when the kernel source changed since they were taken. `cpu_baseline` times 
 fp64 oracle's streaming form on the host cores.
 
 Extra modes (used to produce the committed rocprofv3 summaries):
-  --calibrate-copy        also run a plain 1 GiB device copy, the reference for counters
+  --calibrate-copy        also run a reference kernel of known traffic (1 GiB read + 1 GiB
+                          written), which scales the counters
   --summarize-counters F W  fold rocprofv3 --pmc CSVs (FETCH_SIZE run F, WRITE_SIZE run W)
                             into profiles/prefill_bf16_d128_counters.json
 """
@@ -87,11 +88,9 @@ def summarize_counters(fetch_glob, write_glob, out_path=COUNTERS_JSON):
         return sum(vals) / len(vals) if vals else None
 
     is_prefill = lambda k: PREFILL_KERNEL in k  # noqa: E731
-    is_copy = lambda k: "copy" in k.lower() or "elementwise" in k.lower()  # noqa: E731
+    is_ref = lambda k: "neg" in k.lower()  # the --calibrate-copy reference kernel  # noqa: E731
     f_k, w_k = pick(fetch, is_prefill), pick(write, is_prefill)
-    # the calibration copy is the largest-traffic copy-like kernel in the run
-    f_c = max((sum(v) / len(v) for k, v in fetch.items() if is_copy(k)), default=None)
-    w_c = max((sum(v) / len(v) for k, v in write.items() if is_copy(k)), default=None)
+    f_c, w_c = pick(fetch, is_ref), pick(write, is_ref)
     if None in (f_k, w_k, f_c, w_c):
         raise SystemExit(f"missing counters: prefill {f_k} {w_k} copy {f_c} {w_c}")
     copy_kib = COPY_BYTES / 1024.0
@@ -204,10 +203,12 @@ def main():
         plx.decode(dd["q"], dd["rho"], kc, vc, dd["seqlens"], dcfg.scale, out=o_d, workspace=ws)
 
     if args.calibrate_copy:
-        src = torch.empty(COPY_BYTES, dtype=torch.uint8, device=dev).fill_(1)
+        # Reference for the traffic counters: an elementwise negation of 1 GiB of fp32
+        # reads exactly COPY_BYTES and writes COPY_BYTES.
+        src = torch.ones(COPY_BYTES // 4, dtype=torch.float32, device=dev)
         dst = torch.empty_like(src)
         for _ in range(3):
-            dst.copy_(src)
+            torch.neg(src, out=dst)
         torch.cuda.synchronize()
         del src, dst
 

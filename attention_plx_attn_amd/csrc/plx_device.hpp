@@ -68,6 +68,22 @@ __device__ __forceinline__ float swap_adjacent(float x) {
     return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), 0xB1, 0xF, 0xF, false));
 }
 
+// max(x, x of the lane 32 away): v_permlane32_swap hands each half-wave the other half's
+// value (entry 1 holds the upper half's x in lanes 0..31, entry 0 the lower half's x in
+// lanes 32..63), a VALU exchange instead of an LDS round trip.
+__device__ __forceinline__ float max_with_other_half(float x) {
+    const auto r = __builtin_amdgcn_permlane32_swap(__float_as_int(x), __float_as_int(x), false,
+                                                    false);
+    return fmaxf(__int_as_float(r[0]), __int_as_float(r[1]));
+}
+
+// max(a, b, c): the NaN-propagating maximum, which gfx950 executes as one v_maximum3_f32. The
+// fmaxf chain would first canonicalize every operand that comes from a matrix instruction (a
+// v_max x, x per element under IEEE mode); for non-NaN inputs both give the same value.
+__device__ __forceinline__ float max3(float a, float b, float c) {
+    return __builtin_elementwise_maximum(__builtin_elementwise_maximum(a, b), c);
+}
+
 __device__ __forceinline__ float wave_max(float x) {
     for (int m = 32; m >= 1; m >>= 1) x = fmaxf(x, shfl_xor(x, m));
     return x;

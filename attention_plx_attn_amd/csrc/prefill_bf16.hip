@@ -11,8 +11,10 @@
 // (Q K^T, running max, P1, O1 += P1 V) and wave g + 4, on the same SIMD, runs the probe
 // branch (R K^T, P2 = P1 * T, O2 += P2 V) one tile behind, reading the softmax wave's
 // rounded weights and rescale factors from LDS. Both waves issue the same number of
-// matrix instructions, so each SIMD's matrix pipe is fed by two independent instruction
-// streams while either one waits on LDS or on its vector work. Details:
+// matrix instructions, and the probe wave is shifted by half a tile (it computes T one
+// iteration ahead and does its vector work first), so each SIMD's matrix pipe alternates
+// between the two instruction streams instead of both waves computing and then both
+// waiting at the same time. Details:
 //   * a wave's Q (or R) fragments stay in registers as the B operand of
 //     v_mfma_f32_32x32x16_bf16, so the product tile is S^T = K Q^T (or T^T = K R^T) with
 //     keys on the 32 rows and the group's queries on the 32 lanes of each half-wave;
@@ -26,8 +28,8 @@
 //     makes each lane's eight consecutive accumulator registers hold eight consecutive
 //     keys, exactly the operand layout, so no cross-lane traffic is needed;
 //   * P1 and P2 are rounded to bf16 and l = sum P1, beta = sum P2 are taken from the rounded
-//     values, so the effective corrected weights sum to exactly one; P2 is formed from the
-//     rounded P1 the softmax wave hands over;
+//     values, so the effective corrected weights sum to exactly one; the probe wave forms
+//     P2 from the rounded P1 the softmax wave hands over and keeps both sums;
 //   * the running max is updated lazily (only when a row's tile max exceeds it by more than
 //     2^8); the result is the same exact expression, with far fewer rescales.
 // Workgroups are issued longest query block first; with B*H a multiple of 8 all blocks of
@@ -113,7 +115,8 @@ __global__ __launch_bounds__(NT, 1) void prefill_bf16_d128_kernel(
     f32x16 acc[4];
 #pragma unroll
     for (int nb = 0; nb < 4; ++nb) acc[nb] = f32x16{};
-    float rsum = 0.f;  // softmax waves: l = sum P1; probe waves: beta = sum P2
+    float rsum = 0.f;  // probe waves: beta = sum P2
+    float lsum = 0.f;  // probe waves: l = sum P1 (from the rounded P1 they receive)
 
     // ---- staging: softmax waves (threads 0..255) load K tiles, probe waves load V tiles.
     const int st = tid & 255;
@@ -166,17 +169,21 @@ __global__ __launch_bounds__(NT, 1) void prefill_bf16_d128_kernel(
         f32x16 S = f32x16{};
 #pragma unroll
         for (int s = 0; s < 8; ++s) S = mfma32(*(const bf16x8*)(Kl + 16 * s), xf[s], S);
+        __builtin_amdgcn_iglp_opt(0);  // interleave the operand reads with the matrix ops
         return S;
     };
-    // O^T += V^T P^T for k-step ks (keys 16 ks .. +15) of V tile kt.
+    // O^T += V^T P^T for k-step ks (keys 16 ks .. +15) of V tile kt. Lane (n, h) of block nb
+    // reads dim row vr = 32 nb + n, chunk (2 ks + h) ^ ((vr >> 4) & 7) = 2 (ks ^ nb) + (h ^ (n >> 4)):
+    // a per-lane base plus a constant per (nb, ks), so every read uses the immediate offset.
+    const int vlane = (n * VS + 8 * (h ^ (n >> 4))) * 2;
     auto value_products = [&](int kt, int ks, bf16x8 pf) {
-        const __bf16* Vl = vbuf(kt);
+        const unsigned char* Vl = (const unsigned char*)vbuf(kt) + vlane;
 #pragma unroll
         for (int nb = 0; nb < 4; ++nb) {
-            const int vr = 32 * nb + n;
-            const bf16x8 vf = *(const bf16x8*)(Vl + vr * VS + 8 * ((2 * ks + h) ^ ((vr >> 4) & 7)));
+            const bf16x8 vf = *(const bf16x8*)(Vl + 32 * nb * VS * 2 + 32 * (ks ^ nb));
             acc[nb] = mfma32(vf, pf, acc[nb]);
         }
+        __builtin_amdgcn_iglp_opt(0);
     };
 
     // ---- softmax branch: tile kt.
@@ -196,17 +203,18 @@ __global__ __launch_bounds__(NT, 1) void prefill_bf16_d128_kernel(
                     if (perm_row(8 * (i >> 2) + 4 * h + (i & 3)) > lim) S[hc][i] = -INFINITY;
             }
         }
-        float mt = fmaxf(S[0][0], S[1][0]);
+        float mt = max3(S[0][0], S[1][0], S[0][1]);
+        mt = max3(mt, S[1][1], S[0][2]);
 #pragma unroll
-        for (int i = 1; i < 16; ++i) mt = fmaxf(mt, fmaxf(S[0][i], S[1][i]));
-        mt = fmaxf(mt, shfl_xor(mt, 32));
+        for (int i = 2; i < 15; ++i) mt = max3(mt, S[1][i], S[0][i + 1]);
+        mt = max3(mt, S[1][15], S[1][15]);
+        mt = max_with_other_half(mt);
         const float ms = mt > -INFINITY ? mt * c : -INFINITY;
         const bool need = ms > m_run + kLazyTau;
         float alpha = 1.f;
         if (wave_any(need)) {
             const float mn = need ? ms : m_run;
             alpha = exp2_fast(m_run - mn);
-            rsum *= alpha;
 #pragma unroll
             for (int nb = 0; nb < 4; ++nb) acc[nb] *= alpha;
             m_run = mn;
@@ -226,38 +234,37 @@ __global__ __launch_bounds__(NT, 1) void prefill_bf16_d128_kernel(
                     w1 = S[hc][8 * r + e + 1] == -INFINITY ? 0.f : w1;
                 }
                 pw[e >> 1] = pack_bf16x2(w0, w1);
-                rsum = add_bf16x2(pw[e >> 1], rsum);
             }
             wout[ks * 64 + lane] = pw;
             value_products(kt, ks, as_bf16x8(pw));
         }
     };
 
-    // ---- probe branch: tile kt (one tile behind the softmax branch).
-    auto probe_tile = [&](int kt) {
+    // ---- probe branch, finishing tile kt: its products T were computed in the previous
+    // iteration (so that this vector work overlaps the softmax wave's score products).
+    auto probe_finish = [&](int kt, const f32x16 (&Tt)[2]) {
         const float alpha = abuf(kt)[n];
         if (wave_any(alpha != 1.f)) {
             rsum *= alpha;
+            lsum *= alpha;
 #pragma unroll
             for (int nb = 0; nb < 4; ++nb) acc[nb] *= alpha;
         }
         const u32x4* win = wbuf(kt);
 #pragma unroll
-        for (int hc = 0; hc < 2; ++hc) {
-            const f32x16 Tt = scores(kt, hc);
+        for (int ks = 0; ks < 4; ++ks) {
+            const int hc = ks >> 1, r = ks & 1;
+            const u32x4 pw = win[ks * 64 + lane];
+            u32x4 p2w;
 #pragma unroll
-            for (int r = 0; r < 2; ++r) {
-                const int ks = 2 * hc + r;
-                const u32x4 pw = win[ks * 64 + lane];
-                u32x4 p2w;
-#pragma unroll
-                for (int e = 0; e < 8; e += 2) {
-                    const uint32_t x = pw[e >> 1];
-                    p2w[e >> 1] = pack_bf16x2(bf16_lo(x) * Tt[8 * r + e], bf16_hi(x) * Tt[8 * r + e + 1]);
-                    rsum = add_bf16x2(p2w[e >> 1], rsum);
-                }
-                value_products(kt, ks, as_bf16x8(p2w));
+            for (int e = 0; e < 8; e += 2) {
+                const uint32_t x = pw[e >> 1];
+                p2w[e >> 1] =
+                    pack_bf16x2(bf16_lo(x) * Tt[hc][8 * r + e], bf16_hi(x) * Tt[hc][8 * r + e + 1]);
+                rsum = add_bf16x2(p2w[e >> 1], rsum);
+                lsum = add_bf16x2(x, lsum);
             }
+            value_products(kt, ks, as_bf16x8(p2w));
         }
     };
 
@@ -286,12 +293,23 @@ __global__ __launch_bounds__(NT, 1) void prefill_bf16_d128_kernel(
         }
         __syncthreads();  // the probe waves' last iteration
     } else {
+        // Probe waves: iteration it finishes tile it - 1 (P2 and its value products) and
+        // then computes the products T of tile it for the next iteration. Their vector
+        // work thus starts while the softmax waves issue score products, and their matrix
+        // work while the softmax waves compute weights.
+        f32x16 Tt[2];
         gload(1);
+        Tt[0] = scores(0, 0);
+        Tt[1] = scores(0, 1);
         lstore(1);
         __syncthreads();
         for (int it = 1; it <= ntiles; ++it) {
             gload(it + 1);
-            probe_tile(it - 1);
+            probe_finish(it - 1, Tt);
+            if (it < ntiles) {
+                Tt[0] = scores(it, 0);
+                Tt[1] = scores(it, 1);
+            }
             lstore(it + 1);
             __syncthreads();
         }
@@ -299,9 +317,8 @@ __global__ __launch_bounds__(NT, 1) void prefill_bf16_d128_kernel(
 
     // ---- epilogue: probe waves hand O2 and beta over through LDS; the softmax waves
     // combine o = (A1/l)(1 + beta/l) - A2/l and round to bf16.
-    rsum += shfl_xor(rsum, 32);  // both key halves of each row
     u32x4* hand = (u32x4*)lds + g * 64 * 16;
-    float* bhand = (float*)(lds + OFF_W) + g * 32;
+    float* bhand = (float*)(lds + OFF_W) + g * 64;  // per group: l[32], beta[32]
     if (probe) {
 #pragma unroll
         for (int nb = 0; nb < 4; ++nb)
@@ -310,12 +327,17 @@ __global__ __launch_bounds__(NT, 1) void prefill_bf16_d128_kernel(
                 hand[(4 * nb + j) * 64 + lane] =
                     __builtin_bit_cast(u32x4, f32x4{acc[nb][4 * j], acc[nb][4 * j + 1],
                                                    acc[nb][4 * j + 2], acc[nb][4 * j + 3]});
-        if (h == 0) bhand[n] = rsum;
+        rsum += shfl_xor(rsum, 32);  // both key halves of each row
+        lsum += shfl_xor(lsum, 32);
+        if (h == 0) {
+            bhand[n] = lsum;
+            bhand[32 + n] = rsum;
+        }
     }
     __syncthreads();
     if (!probe && qi < T) {
-        const float inv = 1.f / rsum;
-        const float one_tb = 1.f + bhand[n] * inv;
+        const float inv = 1.f / bhand[n];
+        const float one_tb = 1.f + bhand[32 + n] * inv;
         __bf16* orow = o + slice + (size_t)qi * D;
 #pragma unroll
         for (int nb = 0; nb < 4; ++nb) {

@@ -5,7 +5,9 @@ One step = one pass of the whole hot path over one batch of synthetic inputs:
   * causal prefill, bf16 in/out, B=4, H=16, T=2048, d=128 (fp32 accumulation), then
   * one decode step, bf16, B=1, H=16, d=128 over a 32768-row KV cache (split-KV partials
     plus the combine kernel).
-Inputs are resident in HBM before the timed region. The decode cache is rotated over
+Inputs are resident in HBM before the timed region, and untimed steps run for --settle-s
+seconds before the --warmup steps, so that the timed region sees the clock the GPU holds
+under sustained load rather than its ramp. The decode cache is rotated over
 several device copies so that successive steps cannot be served from the 256 MB
 last-level cache.
 
@@ -157,6 +159,11 @@ def main():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=100)
     ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--settle-s", type=float, default=0.5,
+                    help="untimed steps run for at least this long before the warm-up steps: "
+                         "the GPU clock ramps up over the first tens of milliseconds of "
+                         "sustained matrix work, and a timed region inside the ramp "
+                         "under-reports the steady rate")
     ap.add_argument("--copies", type=int, default=4, help="decode cache copies to rotate")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--calibrate-copy", action="store_true")
@@ -212,6 +219,14 @@ def main():
         torch.cuda.synchronize()
         del src, dst
 
+    settle_steps = 0
+    t_settle = time.perf_counter()
+    while time.perf_counter() - t_settle < args.settle_s:
+        for _ in range(20):
+            run_prefill()
+            run_decode(settle_steps)
+            settle_steps += 1
+        torch.cuda.synchronize()
     for i in range(args.warmup):
         run_prefill()
         run_decode(i)
@@ -253,6 +268,7 @@ def main():
         "n_gpus": 1,
         "steps": K,
         "warmup": args.warmup,
+        "settle_steps": settle_steps,
         "ms_per_step": round(total_ms / K, 4),
         "higher_is_better": True,
         "scaling": "weak",

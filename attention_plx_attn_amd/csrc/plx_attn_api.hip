@@ -117,7 +117,12 @@ plx_status_t plx_attn_prefill(plx_dtype_t dtype, int32_t B, int32_t H, int32_t T
     if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(rho) || !aligned16(o))
         return PLX_ERR_MISALIGNED;
 
-    plx::PrefillArgs a{B, H, T, d_qk, q, k, v, rho, o, softmax_scale};
+    int cus = 1;
+    if (dtype == PLX_BF16) {
+        const plx_status_t s = current_cu_count(&cus);
+        if (s != PLX_OK) return s;
+    }
+    plx::PrefillArgs a{B, H, T, d_qk, q, k, v, rho, o, softmax_scale, cus};
     const hipStream_t st = static_cast<hipStream_t>(stream);
     const hipError_t e = dtype == PLX_BF16 ? plx::launch_prefill_bf16_d128(a, st)
                                            : plx::launch_prefill_f32(a, st);

@@ -14,6 +14,7 @@ struct PrefillArgs {
     const void* rho;
     void* o;
     float scale;
+    int workers;  // resident workgroups of a persistent launch (the device's compute units)
 };
 
 struct DecodeArgs {

@@ -145,51 +145,50 @@ __global__ __launch_bounds__(NT, 1) void prefill_bf16_d128_kernel(
         float rsum = 0.f;  // probe waves: beta = sum P2
         float lsum = 0.f;  // probe waves: l = sum P1 (from the rounded P1 they receive)
 
-        // ---- staging: softmax waves (threads 0..255) load K tiles, probe waves load V tiles. The
-        // buffer resource starts at the tile, so every tile uses the same per-lane offsets.
+        // ---- staging: the softmax waves (threads 0..255) load and store both the K and the V
+        // tile; the probe waves have the longer dependency chain per slot (P2 = P1 * T and
+        // their products), so they stage nothing. The buffer resource starts at the tile, so
+        // every tile uses the same per-lane offsets.
         const int st = tid & 255;
         const uint32_t koff = (uint32_t)(st >> 4) * 256u + 16u * (st & 15);  // + 4096 j
         const uint32_t voff = (uint32_t)(4 * (st >> 4)) * 256u + 16u * (st & 15);  // + 256 j
-        u32x4 stg[4];
+        u32x4 stg[8];  // K chunks 0..3, V chunks 4..7
         auto gload = [&](int bh, int kt) {
+            if (probe) return;
             const size_t base = slice_of(bh) + (size_t)kt * BC * D;
             const uint32_t bytes = slice_bytes - (uint32_t)kt * BC * 256u;  // kt * BC < T
-            if (!probe) {
-                const auto rk = make_rsrc(k + base, bytes);
+            const auto rk = make_rsrc(k + base, bytes);
 #pragma unroll
-                for (int j = 0; j < 4; ++j) stg[j] = load16(rk, koff + 4096u * j);
-            } else {
-                // dims 8 (st & 15) .. +7 of keys 4 (st >> 4) .. +3
-                const auto rv = make_rsrc(v + base, bytes);
+            for (int j = 0; j < 4; ++j) stg[j] = load16(rk, koff + 4096u * j);
+            // dims 8 (st & 15) .. +7 of keys 4 (st >> 4) .. +3
+            const auto rv = make_rsrc(v + base, bytes);
 #pragma unroll
-                for (int j = 0; j < 4; ++j) stg[j] = load16(rv, voff + 256u * j);
-            }
+            for (int j = 0; j < 4; ++j) stg[4 + j] = load16(rv, voff + 256u * j);
         };
         auto lstore = [&](int t) {
-            if (!probe) {
-                __bf16* Kl = kbuf(t);
+            if (probe) return;
+            __bf16* Kl = kbuf(t);
 #pragma unroll
-                for (int j = 0; j < 4; ++j) {
-                    const int chunk = st + 256 * j;
-                    const int row = chunk >> 4, col = chunk & 15;
-                    const int prow = (row & 32) | perm_row(row & 31);
-                    *(u32x4*)(Kl + prow * KS + col * 8) = stg[j];
-                }
-            } else {
-                __bf16* Vl = vbuf(t);
-                const int vdc = st & 15, vkg = st >> 4;
-                // Transpose 4 keys x 8 dims into 8 dims x 4 keys (byte permutes), 8-byte stores.
+            for (int j = 0; j < 4; ++j) {
+                const int chunk = st + 256 * j;
+                const int row = chunk >> 4, col = chunk & 15;
+                const int prow = (row & 32) | perm_row(row & 31);
+                *(u32x4*)(Kl + prow * KS + col * 8) = stg[j];
+            }
+            __bf16* Vl = vbuf(t);
+            const int vdc = st & 15, vkg = st >> 4;
+            // Transpose 4 keys x 8 dims into 8 dims x 4 keys (byte permutes), 8-byte stores.
+            const u32x4* sv = stg + 4;
 #pragma unroll
-                for (int p = 0; p < 4; ++p) {
-                    const uint32_t lo01 = __builtin_amdgcn_perm(stg[1][p], stg[0][p], 0x05040100u);
-                    const uint32_t lo23 = __builtin_amdgcn_perm(stg[3][p], stg[2][p], 0x05040100u);
-                    const uint32_t hi01 = __builtin_amdgcn_perm(stg[1][p], stg[0][p], 0x07060302u);
-                    const uint32_t hi23 = __builtin_amdgcn_perm(stg[3][p], stg[2][p], 0x07060302u);
-                    const int d0 = 8 * vdc + 2 * p;  // d0 and d0 + 1 share bits 4..6 (= vdc >> 1)
-                    const int cs = 8 * ((vkg >> 1) ^ ((vdc >> 1) & 7)) + 4 * (vkg & 1);
-                    *(u32x2*)(Vl + d0 * VS + cs) = u32x2{lo01, lo23};
-                    *(u32x2*)(Vl + (d0 + 1) * VS + cs) = u32x2{hi01, hi23};
-                }
+            for (int p = 0; p < 4; ++p) {
+                const uint32_t lo01 = __builtin_amdgcn_perm(sv[1][p], sv[0][p], 0x05040100u);
+                const uint32_t lo23 = __builtin_amdgcn_perm(sv[3][p], sv[2][p], 0x05040100u);
+                const uint32_t hi01 = __builtin_amdgcn_perm(sv[1][p], sv[0][p], 0x07060302u);
+                const uint32_t hi23 = __builtin_amdgcn_perm(sv[3][p], sv[2][p], 0x07060302u);
+                const int d0 = 8 * vdc + 2 * p;  // d0 and d0 + 1 share bits 4..6 (= vdc >> 1)
+                const int cs = 8 * ((vkg >> 1) ^ ((vdc >> 1) & 7)) + 4 * (vkg & 1);
+                *(u32x2*)(Vl + d0 * VS + cs) = u32x2{lo01, lo23};
+                *(u32x2*)(Vl + (d0 + 1) * VS + cs) = u32x2{hi01, hi23};
             }
         };
 
@@ -330,7 +329,7 @@ __global__ __launch_bounds__(NT, 1) void prefill_bf16_d128_kernel(
             // item's first tile. Returns whether anything was loaded.
             auto stage = [&](int kt) {
                 const bool inside = kt + 1 < nt;
-                if (!inside && !has_next) return false;
+                if (probe || (!inside && !has_next)) return false;
                 gload(inside ? cur.bh : nx.bh, inside ? kt + 1 : 0);
                 return true;
             };

@@ -18,11 +18,12 @@
 //   * a wave's Q (or R) fragments stay in registers as the B operand of
 //     v_mfma_f32_32x32x16_bf16, so the product tile is S^T = K Q^T (or T^T = K R^T) with
 //     keys on the 32 rows and the group's queries on the 32 lanes of each half-wave;
-//   * K and V tiles of 64 keys are staged in LDS, three buffers each (the probe wave reads
-//     the tile before the softmax wave's): K row-major with rows stored in a permuted order,
-//     V transposed (d rows x 64 keys) so a value operand is one 16-byte LDS read; the
-//     16-byte key chunks of dim row d are XOR-swizzled with bits 4..6 of d, which makes the
-//     transposing 8-byte stores and the operand reads conflict-free on gfx950's 64-bank LDS;
+//   * K and V tiles of 64 keys are staged in LDS by the softmax waves, three buffers each
+//     (while tile t + 1 is stored, the softmax waves read tile t and the probe waves tile
+//     t - 1): K row-major with rows stored in a permuted order, V transposed (d rows x 64
+//     keys) so a value operand is one 16-byte LDS read; the 16-byte key chunks of dim row d
+//     are XOR-swizzled with bits 4..6 of d, which keeps the operand reads conflict-free on
+//     gfx950's 64-bank LDS and spreads the transposing 8-byte stores;
 //   * the score tile's accumulator layout is reused directly as the P operand of the value
 //     products O^T += V^T P^T: storing key rows with bits 2 and 3 of the row index swapped
 //     makes each lane's eight consecutive accumulator registers hold eight consecutive

@@ -33,6 +33,7 @@ import glob
 import hashlib
 import json
 import os
+import re
 import sys
 import time
 
@@ -48,11 +49,18 @@ PREFILL_SOURCES = ("attention_plx_attn_amd/csrc/prefill_bf16.hip",
                    "attention_plx_attn_amd/csrc/plx_device.hpp")
 
 
+def code_only(text: str) -> str:
+    """C++ source without comments and blank lines (what the counters depend on)."""
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    text = re.sub(r"//[^\n]*", "", text)
+    return "\n".join(ln.rstrip() for ln in text.splitlines() if ln.strip())
+
+
 def source_hash(files=PREFILL_SOURCES) -> str:
     h = hashlib.sha256()
     for f in files:
-        with open(os.path.join(ROOT, f), "rb") as fh:
-            h.update(fh.read())
+        with open(os.path.join(ROOT, f), encoding="utf-8") as fh:
+            h.update(code_only(fh.read()).encode())
     return h.hexdigest()
 
 

@@ -212,12 +212,10 @@ __global__ __launch_bounds__(NT, 1) void prefill_bf16_d128_kernel(
         __builtin_amdgcn_iglp_opt(0);
     };
 
-    auto tile = [&](int t, int kt, int qi, auto diag_tag, bool next, const Item& nx) {
+    // Weights and value products of tile t (local index kt) from its products S, Tp.
+    auto finish = [&](int t, int kt, int qi, auto diag_tag, f32x4 (&S)[4], const f32x4 (&Tp)[4]) {
         constexpr bool DIAG = decltype(diag_tag)::value;
-        f32x4 S[4], Tp[4];
-        products(t, S, Tp);
         if constexpr (DIAG) {
-            if (next) load_x(nx);
             // key kt * BC + 8 gq + (32 (kb >> 1) + 4 (kb & 1) + i) is visible iff the constant
             // part is at most lim
             const int lim = qi - kt * BC - 8 * gq;
@@ -299,22 +297,31 @@ __global__ __launch_bounds__(NT, 1) void prefill_bf16_d128_kernel(
         lsum = bsum = 0.f;
         m_run = -INFINITY;
         const int qi = cur.q0 + 16 * w + col;
+        f32x4 S[4], Tp[4];
         for (int kt = 0; kt < cur.nfull; ++kt) {
             const bool staged = stage(kt);
-            tile(t0 + kt, kt, qi, std::false_type{}, false, nx);
+            products(t0 + kt, S, Tp);
+            finish(t0 + kt, kt, qi, std::false_type{}, S, Tp);
             if (staged) lstore(t0 + kt + 1);
             __syncthreads();
         }
         for (int kt = cur.nfull; kt < nt - 1; ++kt) {
             const bool staged = stage(kt);
-            tile(t0 + kt, kt, qi, std::true_type{}, false, nx);
+            products(t0 + kt, S, Tp);
+            finish(t0 + kt, kt, qi, std::true_type{}, S, Tp);
             if (staged) lstore(t0 + kt + 1);
             __syncthreads();
         }
         {
             const int kt = nt - 1;
             const bool staged = stage(kt);
-            tile(t0 + kt, kt, qi, std::true_type{}, has_next, nx);
+            // When every key of the tile lies after every row of the wave (waves 0-3 in a full
+            // item's last tile) the wave has nothing to add; skipping leaves the SIMD's matrix
+            // pipe to the other wave for this slot.
+            const bool skip = kt * BC > cur.q0 + 16 * w + 15;
+            if (!skip) products(t0 + kt, S, Tp);
+            if (has_next) load_x(nx);
+            if (!skip) finish(t0 + kt, kt, qi, std::true_type{}, S, Tp);
             if (staged) lstore(t0 + kt + 1);
             __syncthreads();
         }

@@ -29,9 +29,11 @@
 // favours the older wave for the matrix pipe, and the V stagers have the longer slot).
 // Persistent launch: one workgroup per compute unit, each working through a static list of
 // items, longest first in snake order so that every workgroup gets the same number of tiles.
-// The items of one workgroup form a single stream of K/V tiles in a ring of three LDS
-// buffers: an item's last slot already stages the next item's first tile and requests its Q
-// and R fragments. With B*H a multiple of 8, workgroup x (dispatched to XCD x % 8) serves only
+// The items of one workgroup form a single stream of K/V tiles in a ring of four LDS
+// buffers; tile s + 2 is staged while tile s is processed, so the workgroup synchronizes only
+// after every second tile, and an item's last tiles already stage the next item's first ones.
+// The Q and R fragments of the next item are requested right after the products of an item's
+// last tile. With B*H a multiple of 8, workgroup x (dispatched to XCD x % 8) serves only
 // the heads with bh % 8 == x % 8, so each head's K and V are read through one XCD's L2.
 #include <type_traits>
 
@@ -49,7 +51,7 @@ constexpr int KS = D + 8;         // LDS row stride of a K tile (bf16 elements)
 constexpr int VS = BC + 8;        // LDS row stride of a transposed V tile
 constexpr int K_ELEMS = BC * KS;  // 8704 bf16
 constexpr int V_ELEMS = D * VS;   // 9216 bf16
-constexpr int NBUF = 3;
+constexpr int NBUF = 4;  // stream tiles s + 2 is staged while s is processed
 constexpr int OFF_V = NBUF * K_ELEMS * 2;
 constexpr int LDS_BYTES = OFF_V + NBUF * V_ELEMS * 2;
 static_assert(LDS_BYTES <= 160 * 1024, "LDS budget");
@@ -271,13 +273,41 @@ __global__ __launch_bounds__(NT, 1) void prefill_bf16_d128_kernel(
     };
 
     if (w >= 4) __builtin_amdgcn_s_setprio(1);  // the V stagers carry the longer slot
+    // Stream tile s + 2 is staged while tile s is processed (four buffers), so a barrier is
+    // needed only after every second tile: between the step that last reads a buffer (s - 2)
+    // and the one that refills it (s) lies a barrier, and so does between that refill and the
+    // step that reads it (s + 2).
     int kk = 0;
     int pos = item_position(0, jw, Wc);
     if (pos >= nit_c) return;
     Item cur = item_at(pos, cls, ncls, nbh_c, nqb, T);
+    // Source of the tile `ahead` tiles after local tile kt of item a, given the next two items.
+    auto source = [&](const Item& a, int kt, int ahead, bool h1, const Item& n1, bool h2,
+                      const Item& n2, int* bh, int* tile) {
+        int r = kt + ahead;
+        if (r < a.ntiles) { *bh = a.bh; *tile = r; return true; }
+        r -= a.ntiles;
+        if (!h1) return false;
+        if (r < n1.ntiles) { *bh = n1.bh; *tile = r; return true; }
+        r -= n1.ntiles;
+        if (!h2 || r >= n2.ntiles) return false;
+        *bh = n2.bh; *tile = r;
+        return true;
+    };
     load_x(cur);
-    gload(cur.bh, 0);
-    lstore(0);
+    {
+        const int p1 = item_position(1, jw, Wc), p2 = item_position(2, jw, Wc);
+        const bool h1 = p1 < nit_c, h2 = p2 < nit_c;
+        const Item n1 = item_at(h1 ? p1 : pos, cls, ncls, nbh_c, nqb, T);
+        const Item n2 = item_at(h2 ? p2 : pos, cls, ncls, nbh_c, nqb, T);
+        gload(cur.bh, 0);
+        lstore(0);
+        int sbh = 0, stile = 0;
+        if (source(cur, 0, 1, h1, n1, h2, n2, &sbh, &stile)) {
+            gload(sbh, stile);
+            lstore(1);
+        }
+    }
     __syncthreads();
     __builtin_amdgcn_s_waitcnt(0x0F70);  // the fragments have arrived (see the epilogue)
     int t0 = 0;
@@ -285,12 +315,18 @@ __global__ __launch_bounds__(NT, 1) void prefill_bf16_d128_kernel(
         const int pos_n = item_position(kk + 1, jw, Wc);
         const bool has_next = pos_n < nit_c;
         const Item nx = item_at(has_next ? pos_n : pos, cls, ncls, nbh_c, nqb, T);
+        const int pos_n2 = item_position(kk + 2, jw, Wc);
+        const bool has_next2 = has_next && pos_n2 < nit_c;
+        const Item nx2 = item_at(has_next2 ? pos_n2 : pos, cls, ncls, nbh_c, nqb, T);
         const int nt = cur.ntiles;
         auto stage = [&](int kt) {
-            const bool inside = kt + 1 < nt;
-            if (!inside && !has_next) return false;
-            gload(inside ? cur.bh : nx.bh, inside ? kt + 1 : 0);
+            int sbh = 0, stile = 0;
+            if (!source(cur, kt, 2, has_next, nx, has_next2, nx2, &sbh, &stile)) return false;
+            gload(sbh, stile);
             return true;
+        };
+        auto slot_end = [&](int kt) {
+            if ((t0 + kt) & 1) __syncthreads();
         };
 #pragma unroll
         for (int db = 0; db < 8; ++db) a1[db] = a2[db] = f32x4{};
@@ -302,15 +338,15 @@ __global__ __launch_bounds__(NT, 1) void prefill_bf16_d128_kernel(
             const bool staged = stage(kt);
             products(t0 + kt, S, Tp);
             finish(t0 + kt, kt, qi, std::false_type{}, S, Tp);
-            if (staged) lstore(t0 + kt + 1);
-            __syncthreads();
+            if (staged) lstore(t0 + kt + 2);
+            slot_end(kt);
         }
         for (int kt = cur.nfull; kt < nt - 1; ++kt) {
             const bool staged = stage(kt);
             products(t0 + kt, S, Tp);
             finish(t0 + kt, kt, qi, std::true_type{}, S, Tp);
-            if (staged) lstore(t0 + kt + 1);
-            __syncthreads();
+            if (staged) lstore(t0 + kt + 2);
+            slot_end(kt);
         }
         {
             const int kt = nt - 1;
@@ -322,8 +358,8 @@ __global__ __launch_bounds__(NT, 1) void prefill_bf16_d128_kernel(
             if (!skip) products(t0 + kt, S, Tp);
             if (has_next) load_x(nx);
             if (!skip) finish(t0 + kt, kt, qi, std::true_type{}, S, Tp);
-            if (staged) lstore(t0 + kt + 1);
-            __syncthreads();
+            if (staged) lstore(t0 + kt + 2);
+            slot_end(kt);
         }
         __builtin_amdgcn_s_waitcnt(0x0F70);
         // ---- epilogue: l and beta over the four lanes of each query; o = (A1/l)(1 + beta/l)

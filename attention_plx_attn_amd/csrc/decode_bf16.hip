@@ -49,7 +49,7 @@ template <int KB>
 __global__ __launch_bounds__(NT, KB <= 32 ? 2 : 1) void decode_split_bf16_d128_kernel(
     const __bf16* __restrict__ q, const __bf16* __restrict__ rho, const __bf16* __restrict__ kc,
     const __bf16* __restrict__ vc, const int32_t* __restrict__ seqlens, __bf16* __restrict__ o,
-    float* __restrict__ ws, int H, int L_max, int S, int chunk, float c) {
+    float* __restrict__ ws, int H, int L_max, int S, float c) {
     __shared__ __attribute__((aligned(16))) float ush[NW][2][KB];  // rounded w and w t per key
     __shared__ __attribute__((aligned(16))) float red[NW][2 * D + 4];
 
@@ -60,6 +60,9 @@ __global__ __launch_bounds__(NT, KB <= 32 ? 2 : 1) void decode_split_bf16_d128_k
 
     int nb_keys = seqlens[b];
     nb_keys = nb_keys < 0 ? 0 : (nb_keys > L_max ? L_max : nb_keys);
+    // The S chunks of this sequence split its own length (not L_max) evenly, in whole wave
+    // steps, so that ragged batches keep every split busy; trailing chunks may be empty.
+    const int chunk = (((nb_keys + S - 1) / S) + KB - 1) / KB * KB;
     const int j0 = s * chunk;
     const int j1 = min(j0 + chunk, nb_keys);
     const size_t bh = (size_t)b * H + h;
@@ -349,7 +352,7 @@ hipError_t launch_decode_bf16_d128(const DecodeArgs& a, hipStream_t stream) {
     hipLaunchKernelGGL(decode_split_bf16_d128_kernel<PLX_DECODE_KB>, grid, dim3(NT), 0, stream,
                        (const __bf16*)a.q, (const __bf16*)a.rho, (const __bf16*)a.k,
                        (const __bf16*)a.v, a.seqlens, (__bf16*)a.o, a.ws, a.H, a.L_max, a.splits,
-                       a.chunk, a.scale * kLog2e);
+                       a.scale * kLog2e);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess || a.splits == 1) return e;
     const int BH = a.B * a.H;

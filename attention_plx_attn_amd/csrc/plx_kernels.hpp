@@ -27,7 +27,7 @@ struct DecodeArgs {
     void* o;
     float scale;
     int splits;  // chunks per (b, h) actually launched
-    int chunk;   // keys per chunk (multiple of 64)
+    int chunk;   // keys per chunk of the L_max plan (the kernel splits each sequence evenly)
     float* ws;   // split partials, [B*H*splits][kDecodeRecord] floats (unused if splits == 1)
 };
 

@@ -19,7 +19,10 @@ stream it runs on; `traffic` comes from committed rocprofv3 counter summaries an
 null when the kernel source changed since they were taken. `cpu_baseline` times the
 fp64 oracle's streaming form on the host cores.
 
-Extra modes (used to produce the committed rocprofv3 summaries):
+Extra modes:
+  --sweep [OUT_MD]        time the long prefill (1x32x32768) and the 18 decode grid cells
+                          (H16 d128, B x ctx) instead of the step; one JSON line each
+Used to produce the committed rocprofv3 summaries:
   --calibrate-copy        also run a reference kernel of known traffic (1 GiB read + 1 GiB
                           written), which scales the counters
   --summarize-counters F W  fold rocprofv3 --pmc CSVs (FETCH_SIZE run F, WRITE_SIZE run W)
@@ -160,6 +163,123 @@ def cpu_baseline(px, dx):
     }
 
 
+# ------------------------------------------------------------------------------ sweep
+
+def _stats_us(ms_list):
+    xs = sorted(ms_list)
+    pick = lambda p: xs[min(len(xs) - 1, int(p * len(xs)))] * 1e3  # noqa: E731
+    return {"median_us": round(pick(0.5), 2), "p10_us": round(pick(0.1), 2),
+            "p90_us": round(pick(0.9), 2)}
+
+
+def sweep(out_md):
+    """Times the long prefill (1x32x32768) and every decode grid cell (H16 d128).
+
+    Decode cells: before each timed call a 512 MiB buffer is written, which evicts the L2 and
+    the 256 MB last-level cache, so every call streams its cache from HBM; HIP events bracket
+    the decode call only. Prints one JSON line per workload and writes a markdown table."""
+    import torch
+
+    import attention_plx_attn_amd as plx
+    from plx_synth import CONFIGS, decode_grid_cells, decode_inputs
+
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    stream = torch.cuda.current_stream(dev)
+    lines = []
+
+    # long prefill
+    cfg = CONFIGS["prefill_long"]
+    # Drawn on the device (seeded) with the recipe's distribution: q, k, v ~ N(0,1); rho zero
+    # on the first half of the heads and 0.1 RMSNorm(N(0,1)) on the second half.
+    g = torch.Generator(device=dev)
+    g.manual_seed(5)
+    shp = (cfg.B, cfg.H, cfg.T, cfg.d)
+    d = {k: torch.randn(shp, generator=g, device=dev, dtype=torch.float32).to(torch.bfloat16)
+         for k in ("q", "k", "v")}
+    r = torch.randn(shp, generator=g, device=dev, dtype=torch.float32)
+    r = 0.1 * r * torch.rsqrt(r.pow(2).mean(-1, keepdim=True) + 1e-6)
+    r[:, : cfg.H // 2] = 0
+    d["rho"] = r.to(torch.bfloat16)
+    del r
+    o = torch.empty_like(d["q"])
+    t_end = time.perf_counter() + 0.5
+    while time.perf_counter() < t_end:  # settle the clock
+        plx.prefill(d["q"], d["k"], d["v"], d["rho"], cfg.scale, out=o)
+        torch.cuda.synchronize()
+    times = []
+    for _ in range(7):
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        plx.prefill(d["q"], d["k"], d["v"], d["rho"], cfg.scale, out=o)
+        e1.record(stream)
+        torch.cuda.synchronize()
+        times.append(e0.elapsed_time(e1))
+    st = _stats_us(times)
+    fl = prefill_flops(cfg.B, cfg.H, cfg.T, cfg.d)
+    rec = {"workload": f"prefill B{cfg.B} H{cfg.H} T{cfg.T} d{cfg.d} bf16 causal", **st,
+           "tflops": round(fl / (st["median_us"] * 1e-6) / 1e12, 1),
+           "mfma_frac": round(fl / (st["median_us"] * 1e-6) / 1e12 / BF16_PEAK_TFLOPS, 4),
+           "tokens_per_s": round(cfg.B * cfg.T / (st["median_us"] * 1e-6), 0)}
+    print(json.dumps(rec), flush=True)
+    lines.append(rec)
+    del d, o
+    torch.cuda.empty_cache()
+
+    # decode grid
+    flush = torch.empty(512 * 1024 * 1024 // 4, dtype=torch.float32, device=dev)
+    for cfg in decode_grid_cells():
+        dx = decode_inputs(cfg, seed=0, device=str(dev), device_draw=True)
+        splits = plx.decode_num_splits(cfg.B, cfg.H, cfg.L_max, 0)
+        wsb = plx.decode_workspace_size(cfg.B, cfg.H, cfg.L_max, cfg.d, 0)
+        ws = torch.empty(max(wsb // 4, 1), dtype=torch.float32, device=dev)
+        od = torch.empty_like(dx["q"])
+
+        def call():
+            plx.decode(dx["q"], dx["rho"], dx["k_cache"], dx["v_cache"], dx["seqlens"],
+                       cfg.scale, out=od, workspace=ws)
+
+        for _ in range(3):
+            call()
+        times = []
+        iters = 20
+        for _ in range(iters):
+            flush.fill_(1.0)
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record(stream)
+            call()
+            e1.record(stream)
+            torch.cuda.synchronize()
+            times.append(e0.elapsed_time(e1))
+        st = _stats_us(times)
+        nbytes = decode_bytes(dx["seqlens"].cpu().tolist(), cfg.H, cfg.d)
+        gbps = nbytes / (st["median_us"] * 1e-6) / 1e9
+        rec = {"workload": f"decode B{cfg.B} H{cfg.H} ctx{cfg.L_max} d{cfg.d} bf16", **st,
+               "splits": splits, "bytes": nbytes, "hbm_gbps": round(gbps, 1),
+               "hbm_frac": round(gbps / HBM_PEAK_GBPS, 4),
+               "tokens_per_s": round(cfg.B / (st["median_us"] * 1e-6), 1)}
+        print(json.dumps(rec), flush=True)
+        lines.append(rec)
+        del dx, ws, od
+        torch.cuda.empty_cache()
+
+    if out_md:
+        with open(out_md, "w") as fh:
+            fh.write("| workload | median us | p10 us | p90 us | rate | roofline fraction |\n")
+            fh.write("|---|---|---|---|---|---|\n")
+            for r in lines:
+                if "tflops" in r:
+                    rate = f"{r['tflops']} TFLOP/s, {r['tokens_per_s']:.3g} tokens/s"
+                    frac = f"{100 * r['mfma_frac']:.1f}% of 2.5 PFLOP/s"
+                else:
+                    rate = (f"{r['hbm_gbps']} GB/s, {r['tokens_per_s']:,.0f} tokens/s, "
+                            f"{r['splits']} splits")
+                    frac = f"{100 * r['hbm_frac']:.1f}% of 8 TB/s"
+                fh.write(f"| {r['workload']} | {r['median_us']} | {r['p10_us']} | {r['p90_us']} "
+                         f"| {rate} | {frac} |\n")
+    return 0
+
+
 # ------------------------------------------------------------------------------ main
 
 def main():
@@ -176,6 +296,8 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--calibrate-copy", action="store_true")
     ap.add_argument("--summarize-counters", nargs=2, metavar=("FETCH_CSV_GLOB", "WRITE_CSV_GLOB"))
+    ap.add_argument("--sweep", metavar="OUT_MD", nargs="?", const="",
+                    help="time the long prefill and the decode grid instead of the step")
     args = ap.parse_args()
 
     if args.summarize_counters:
@@ -187,6 +309,9 @@ def main():
               f"one GPU (--gpus {args.gpus}, WORLD_SIZE {world}) are not supported.",
               file=sys.stderr, flush=True)
         return 2
+
+    if args.sweep is not None:
+        return sweep(args.sweep)
 
     import torch
 

@@ -1,52 +1,115 @@
 // decode_bf16.hip -- one Parallax decode step over a contiguous per-sequence KV cache,
 // bf16 in/out, d_qk = d_v = 128, gfx950.
 //
-// Design points taken from the pages and re-made for CDNA4:
-//  * QK and RK in one matrix instruction [agihunt review, hardware paragraph: a decode step
-//    has one query row, so most accumulator rows of a matrix instruction sit idle; Parallax
-//    puts the probe products in the same instruction]. Here each 16-key tile is one
-//    v_mfma_f32_16x16x32_bf16 per 32 dims with the cache keys as the 16 rows and the
-//    columns [q, rho, 0 ... 0]: column 0 yields the scores, column 1 the probe products t,
-//    at no extra instruction cost.
-//  * Persistent KV-loop splitting with a reduction of the partials [Parallax
+// The per-step arithmetic (one matrix instruction yields the scores and the probe products;
+// see decode_step.hpp) is shared by two ways of dividing the cache among waves:
+//
+//  * Split mode: persistent KV-loop splitting with a reduction of the partials [Parallax
 //    (paper.rainbus.top summary), reproducibility section: the decode kernel's optimisations
 //    are instruction sharing, KV-loop splitting and the reduction of the split partials].
-//    Each workgroup streams one chunk of one (b, h) and writes its partial state
-//    (m, l, beta, A1 = sum w v, A2 = sum w t v); a second kernel merges the partials with
-//    one rescale each and applies o = (A1/l)(1 + beta/l) - A2/l. With one chunk per (b, h)
-//    the first kernel writes o directly.
-//  * Decode is bound by HBM bandwidth: the cache is read once with non-temporal 16-byte
-//    buffer loads (every K load is a contiguous 64-byte row segment per 4 lanes, every V
-//    load a 256-byte row per 16 lanes). A wave step covers 32 keys (16 KiB) and the loads
-//    of the next step are issued before the current one is consumed, so each wave keeps
-//    up to 32 KiB in flight; the split heuristic aims at one such 4-wave workgroup per
-//    compute unit, which measured best on MI355X. The buffer range ends at the chunk's
-//    last valid row, so rows at or beyond seqlens are never read (they come back as zeros
-//    and get zero weight).
-// Softmax weights and weight*probe products are rounded to bf16 and the sums l and beta are
-// taken from the rounded values, as in the prefill kernel.
-#include "plx_device.hpp"
+//    Workgroup (s, h, b) streams chunk s of the (b, h) range (the S chunks split that
+//    sequence's own length evenly), its 4 waves interleaving 32-row steps, and writes the
+//    partial state (m, l, beta, A1 = sum w v, A2 = sum w t v); a second kernel merges the S
+//    partials of each (b, h) with one rescale each and applies o = (A1/l)(1 + beta/l) - A2/l.
+//    With S = 1 the first kernel writes o directly. Suits few long sequences.
+//
+//  * Wave-range mode: the (b, h) key ranges, laid end to end (sequence-major, head-minor),
+//    form one flat range of W = H * sum_b n_b rows, and wave g of G streams the slice
+//    [g W / G, (g + 1) W / G). Every wave therefore gets the same number of rows whatever the
+//    mix of sequence lengths, and it prefetches across (b, h) boundaries, so short sequences
+//    cost no pipeline restart. Each workgroup first forms the prefix sums of the clamped
+//    lengths in LDS; a wave finds its first (b, h) with a 64-way search. A (b, h) that lies
+//    inside one slice is finished by its wave (o written); one cut by slice boundaries leaves
+//    a partial per piece, and a combine kernel (one wave per slice boundary) merges them.
+//    With the boundaries moved to the next (b, h) start ("whole" plans, chosen when there are
+//    many (b, h) per wave) nothing is cut and no combine runs. Suits many or ragged sequences.
+//
+// Both stream the cache once with non-temporal 16-byte buffer loads in 32-row steps (16 KiB);
+// split mode keeps two steps in flight per wave, wave-range mode one step per wave with 16
+// waves per compute unit. Buffer ranges end at the last valid row, so rows at or beyond
+// seqlens are never read.
+#include "decode_step.hpp"
 #include "plx_kernels.hpp"
 
 namespace plx {
 namespace {
 
-constexpr int D = 128;
-constexpr int NT = 256;  // 4 waves
-constexpr int NW = 4;
+using decode::Acc;
+using decode::D;
+using decode::Frag;
+using decode::KB;
+using decode::NT;
+using decode::NW;
 constexpr int REC = kDecodeRecord;
-#ifndef PLX_DECODE_KB
-#define PLX_DECODE_KB 32
-#endif
 
-__device__ __forceinline__ f32x4 mfma16(bf16x8 a, bf16x8 b, f32x4 c) {
-    return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
+__device__ __forceinline__ int rfl(int x) { return __builtin_amdgcn_readfirstlane(x); }
+
+__device__ __forceinline__ int clamp_len(int n, int L_max) {
+    return n < 0 ? 0 : (n > L_max ? L_max : n);
 }
 
-// KB: keys per wave per step (a multiple of 16); KT = KB / 16 score tiles per step; each
-// lane group of 16 lanes accumulates KB / 4 value rows per step.
-template <int KB>
-__global__ __launch_bounds__(NT, KB <= 32 ? 2 : 1) void decode_split_bf16_d128_kernel(
+// o = (A1/l)(1 + beta/l) - A2/l; an empty range (l == 0) gives 0.
+__device__ __forceinline__ float combine_out(float a1, float a2, float l, float beta) {
+    if (!(l > 0.f)) return 0.f;
+    const float inv = 1.f / l;
+    return inv * (a1 * (1.f + beta * inv) - a2);
+}
+
+// ------------------------------------------------------------------------- partial merging
+// Online merge of partial records by one wave; lane owns dims 2 lane, 2 lane + 1.
+struct Merge {
+    float m = -INFINITY, l = 0.f, beta = 0.f, a1x = 0.f, a1y = 0.f, a2x = 0.f, a2y = 0.f;
+};
+
+// Fold records rec_at(0 .. n-1) into st, issuing the loads of a batch of 8 records before
+// using any of them (one memory round trip per batch). An empty record has m = -inf.
+template <class RecAt>
+__device__ __forceinline__ void fold_records(Merge& st, int n, RecAt rec_at, int lane) {
+    constexpr int BATCH = 8;
+    for (int u0 = 0; u0 < n; u0 += BATCH) {
+        float ms[BATCH], ls[BATCH], bs[BATCH];
+        float2 x1[BATCH], x2[BATCH];
+#pragma unroll
+        for (int u = 0; u < BATCH; ++u) {
+            const float* rec = rec_at(min(u0 + u, n - 1));
+            ms[u] = u0 + u < n ? rec[2 * D] : -INFINITY;
+            ls[u] = rec[2 * D + 1];
+            bs[u] = rec[2 * D + 2];
+            x1[u] = *(const float2*)(rec + 2 * lane);
+            x2[u] = *(const float2*)(rec + D + 2 * lane);
+        }
+        float mb = st.m;
+#pragma unroll
+        for (int u = 0; u < BATCH; ++u) mb = fmaxf(mb, ms[u]);
+        if (mb == -INFINITY) continue;  // nothing non-empty yet (wave-uniform)
+        const float fo = st.m > -INFINITY ? exp2_fast(st.m - mb) : 0.f;
+        st.l *= fo;
+        st.beta *= fo;
+        st.a1x *= fo;
+        st.a1y *= fo;
+        st.a2x *= fo;
+        st.a2y *= fo;
+#pragma unroll
+        for (int u = 0; u < BATCH; ++u) {
+            const float f = ms[u] > -INFINITY ? exp2_fast(ms[u] - mb) : 0.f;  // empty: 0
+            st.l = fmaf(f, ls[u], st.l);
+            st.beta = fmaf(f, bs[u], st.beta);
+            st.a1x = fmaf(f, x1[u].x, st.a1x);
+            st.a1y = fmaf(f, x1[u].y, st.a1y);
+            st.a2x = fmaf(f, x2[u].x, st.a2x);
+            st.a2y = fmaf(f, x2[u].y, st.a2y);
+        }
+        st.m = mb;
+    }
+}
+
+__device__ __forceinline__ void store_merged(const Merge& st, __bf16* o_bh, int lane) {
+    *(uint32_t*)(o_bh + 2 * lane) = pack_bf16x2(combine_out(st.a1x, st.a2x, st.l, st.beta),
+                                                combine_out(st.a1y, st.a2y, st.l, st.beta));
+}
+
+// ------------------------------------------------------------------------------ split mode
+__global__ __launch_bounds__(NT, 2) void decode_split_bf16_d128_kernel(
     const __bf16* __restrict__ q, const __bf16* __restrict__ rho, const __bf16* __restrict__ kc,
     const __bf16* __restrict__ vc, const int32_t* __restrict__ seqlens, __bf16* __restrict__ o,
     float* __restrict__ ws, int H, int L_max, int S, float c) {
@@ -58,167 +121,51 @@ __global__ __launch_bounds__(NT, KB <= 32 ? 2 : 1) void decode_split_bf16_d128_k
     const int col = lane & 15;  // column of the score tile (0: q, 1: rho); V: dims 8 col ..
     const int g = lane >> 4;    // row group of the score tile; V: key sub-range
 
-    int nb_keys = seqlens[b];
-    nb_keys = nb_keys < 0 ? 0 : (nb_keys > L_max ? L_max : nb_keys);
+    const int nb_keys = clamp_len(seqlens[b], L_max);
     // The S chunks of this sequence split its own length (not L_max) evenly, in whole wave
     // steps, so that ragged batches keep every split busy; trailing chunks may be empty.
     const int chunk = (((nb_keys + S - 1) / S) + KB - 1) / KB * KB;
     const int j0 = s * chunk;
     const int j1 = min(j0 + chunk, nb_keys);
     const size_t bh = (size_t)b * H + h;
-    const __bf16* kbase = kc + bh * (size_t)L_max * D;
-    const __bf16* vbase = vc + bh * (size_t)L_max * D;
     const uint32_t range = j1 > 0 ? (uint32_t)j1 * 256u : 0u;
-    const auto rk = make_rsrc(kbase, range);
-    const auto rv = make_rsrc(vbase, range);
+    const auto rk = make_rsrc(kc + bh * (size_t)L_max * D, range);
+    const auto rv = make_rsrc(vc + bh * (size_t)L_max * D, range);
 
-    // B operand [q | rho | 0...]: lane holds dims 32 st + 8 g .. +7 of column `col`.
     bf16x8 bqr[4];
-    {
-        const auto rq = make_rsrc(q + bh * D, 256u);
-        const auto rr = make_rsrc(rho + bh * D, 256u);
-#pragma unroll
-        for (int st = 0; st < 4; ++st) {
-            const u32x4 xq = load16(rq, 64u * st + 16u * g);
-            const u32x4 xr = load16(rr, 64u * st + 16u * g);
-            bqr[st] = as_bf16x8(col == 0 ? xq : (col == 1 ? xr : u32x4{}));
-        }
-    }
+    decode::load_qr(make_rsrc(q + bh * D, 256u), make_rsrc(rho + bh * D, 256u), col, g, bqr);
 
-    float m_run = -INFINITY;
-    float rsum = 0.f;  // sum of rounded weights: l in column-0 lanes, beta in column-1 lanes
-    float a1[8], a2[8];
-#pragma unroll
-    for (int e = 0; e < 8; ++e) a1[e] = a2[e] = 0.f;
+    Acc acc;
+    acc.reset();
 
-    // Software pipeline over this wave's steps: the loads of step n + 1 are issued before
-    // step n is consumed (two register sets, so the loop is unrolled by two). A prefetch
-    // past the chunk reads beyond the buffer range and returns zeros without touching memory.
-    constexpr int KT = KB / 16, VR = KB / 4;
-    auto load_step = [&](int kb0, u32x4 (&kf)[KT][4], u32x4 (&vf)[VR]) {
-#pragma unroll
-        for (int t = 0; t < KT; ++t)
-#pragma unroll
-            for (int st = 0; st < 4; ++st)
-                kf[t][st] = load16_nt(rk, (uint32_t)(kb0 + 16 * t + col) * 256u + 64u * st + 16u * g);
-#pragma unroll
-        for (int r = 0; r < VR; ++r)
-            vf[r] = load16_nt(rv, (uint32_t)(kb0 + VR * g + r) * 256u + 16u * col);
-    };
-    auto consume = [&](int kb0, const u32x4 (&kf)[KT][4], const u32x4 (&vf)[VR]) {
-        // Score tile: row = key (16 per tile), column 0 = q.k, column 1 = rho.k.
-        f32x4 sc[KT];
-#pragma unroll
-        for (int t = 0; t < KT; ++t) {
-            sc[t] = f32x4{};
-#pragma unroll
-            for (int st = 0; st < 4; ++st) sc[t] = mfma16(as_bf16x8(kf[t][st]), bqr[st], sc[t]);
-        }
-        // Lane (col, g) register i holds key kb0 + 16 t + 4 g + i.
-        float mx = -INFINITY;
-        if (col == 0) {
-#pragma unroll
-            for (int t = 0; t < KT; ++t)
-#pragma unroll
-                for (int i = 0; i < 4; ++i)
-                    if (kb0 + 16 * t + 4 * g + i < j1) mx = fmaxf(mx, sc[t][i] * c);
-        }
-        mx = fmaxf(mx, shfl_xor(mx, 16));
-        mx = fmaxf(mx, shfl_xor(mx, 32));
-        const float mb = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(mx), 0));
-        if (mb > m_run) {  // wave-uniform
-            const float alpha = exp2_fast(m_run - mb);
-            rsum *= alpha;
-#pragma unroll
-            for (int e = 0; e < 8; ++e) {
-                a1[e] *= alpha;
-                a2[e] *= alpha;
-            }
-            m_run = mb;
-        }
-
-        // Column 0 lanes: w; column 1 lanes: w t (score from the adjacent column-0 lane).
-#pragma unroll
-        for (int t = 0; t < KT; ++t) {
-            float u[4];
-#pragma unroll
-            for (int i = 0; i < 4; ++i) {
-                const float own = sc[t][i];
-                // DPP must run with every lane active: take the neighbour's value first.
-                const float partner = swap_adjacent(own);
-                const float score = col == 1 ? partner : own;
-                const bool valid = kb0 + 16 * t + 4 * g + i < j1;
-                const float wgt = valid ? exp2_fast(fmaf(score, c, -m_run)) : 0.f;
-                u[i] = col == 0 ? wgt : (col == 1 ? wgt * own : 0.f);
-            }
-            const uint32_t p01 = pack_bf16x2(u[0], u[1]);
-            const uint32_t p23 = pack_bf16x2(u[2], u[3]);
-            rsum = add_bf16x2(p23, add_bf16x2(p01, rsum));
-            if (col < 2)
-                *(f32x4*)&ush[w][col][16 * t + 4 * g] =
-                    f32x4{bf16_lo(p01), bf16_hi(p01), bf16_lo(p23), bf16_hi(p23)};
-        }
-        __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
-        __builtin_amdgcn_wave_barrier();
-        __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
-
-        // Value accumulation: lane (col, g) takes keys kb0 + VR g .. +VR-1, dims 8 col .. +7.
-#pragma unroll
-        for (int r4 = 0; r4 < VR / 4; ++r4) {
-            const f32x4 u0 = *(const f32x4*)&ush[w][0][VR * g + 4 * r4];
-            const f32x4 u1 = *(const f32x4*)&ush[w][1][VR * g + 4 * r4];
-#pragma unroll
-            for (int rr = 0; rr < 4; ++rr) {
-                const u32x4 x = vf[4 * r4 + rr];
-#pragma unroll
-                for (int p = 0; p < 4; ++p) {
-                    const float vlo = bf16_lo(x[p]), vhi = bf16_hi(x[p]);
-                    a1[2 * p] = fmaf(u0[rr], vlo, a1[2 * p]);
-                    a1[2 * p + 1] = fmaf(u0[rr], vhi, a1[2 * p + 1]);
-                    a2[2 * p] = fmaf(u1[rr], vlo, a2[2 * p]);
-                    a2[2 * p + 1] = fmaf(u1[rr], vhi, a2[2 * p + 1]);
-                }
-            }
-        }
-        __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
-        __builtin_amdgcn_wave_barrier();
-        __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
-    };
-
+    // Software pipeline over this wave's steps (rows j0 + KB w + n STEP): the loads of step
+    // n + 1 are issued before step n is consumed. A prefetch past the chunk reads beyond the
+    // buffer range and returns zeros without touching memory.
     constexpr int STEP = KB * NW;
-    u32x4 kfA[KT][4], vfA[VR], kfB[KT][4], vfB[VR];
+    Frag fa, fb;
     int kb0 = j0 + KB * w;
-    if (kb0 < j1) load_step(kb0, kfA, vfA);
+    if (kb0 < j1) decode::load_step(rk, rv, kb0, col, g, fa);
     for (; kb0 < j1; kb0 += 2 * STEP) {
-        load_step(kb0 + STEP, kfB, vfB);
-        consume(kb0, kfA, vfA);
+        decode::load_step(rk, rv, kb0 + STEP, col, g, fb);
+        decode::consume(acc, fa, bqr, kb0, j1, c, ush[w], col, g);
         if (kb0 + STEP >= j1) break;
-        load_step(kb0 + 2 * STEP, kfA, vfA);
-        consume(kb0 + STEP, kfB, vfB);
+        decode::load_step(rk, rv, kb0 + 2 * STEP, col, g, fa);
+        decode::consume(acc, fb, bqr, kb0 + STEP, j1, c, ush[w], col, g);
     }
 
-    // Wave totals: values over the 4 key sub-ranges; l and beta over the 4 row groups.
-#pragma unroll
-    for (int e = 0; e < 8; ++e) {
-        a1[e] += shfl_xor(a1[e], 16);
-        a1[e] += shfl_xor(a1[e], 32);
-        a2[e] += shfl_xor(a2[e], 16);
-        a2[e] += shfl_xor(a2[e], 32);
-    }
-    rsum += shfl_xor(rsum, 16);
-    rsum += shfl_xor(rsum, 32);
+    decode::wave_totals(acc);
     if (lane < 16) {
 #pragma unroll
         for (int e = 0; e < 8; ++e) {
-            red[w][8 * lane + e] = a1[e];
-            red[w][D + 8 * lane + e] = a2[e];
+            red[w][8 * lane + e] = acc.a1[e];
+            red[w][D + 8 * lane + e] = acc.a2[e];
         }
     }
     if (lane == 0) {
-        red[w][2 * D] = m_run;
-        red[w][2 * D + 1] = rsum;
+        red[w][2 * D] = acc.m_run;
+        red[w][2 * D + 1] = acc.rsum;
     }
-    if (lane == 1) red[w][2 * D + 2] = rsum;
+    if (lane == 1) red[w][2 * D + 2] = acc.rsum;
     __syncthreads();
 
     // Merge the 4 wave states (one rescale each); thread tid < 128 owns dim tid.
@@ -239,12 +186,7 @@ __global__ __launch_bounds__(NT, KB <= 32 ? 2 : 1) void decode_split_bf16_d128_k
             }
         }
         if (S == 1) {
-            float y = 0.f;
-            if (l > 0.f) {
-                const float inv = 1.f / l;
-                y = inv * (A1 * (1.f + beta * inv) - A2);
-            }
-            o[bh * D + tid] = (__bf16)y;
+            o[bh * D + tid] = (__bf16)combine_out(A1, A2, l, beta);
         } else {
             float* rec = ws + (bh * (size_t)S + s) * REC;
             rec[tid] = A1;
@@ -259,103 +201,297 @@ __global__ __launch_bounds__(NT, KB <= 32 ? 2 : 1) void decode_split_bf16_d128_k
     }
 }
 
-// One workgroup per (b, h). Wave w folds the partials s = w, w + 4, ... with an online
-// max/rescale, issuing the loads of a batch of 8 partials before using any of them (one
-// memory round trip per batch); lane owns dims 2 lane, 2 lane + 1. The four wave states are
-// then merged through LDS with one rescale each.
+// One workgroup per (b, h): wave w folds the partials s = w, w + 4, ..., then the four wave
+// states are merged through LDS with one rescale each.
 __global__ __launch_bounds__(NT) void decode_combine_kernel(const float* __restrict__ ws,
                                                             __bf16* __restrict__ o, int S) {
-    constexpr int BATCH = 8;
     __shared__ __attribute__((aligned(16))) float reds[NW][2 * D + 4];
     const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
     const size_t bh = blockIdx.x;
     const float* base = ws + bh * (size_t)S * REC;
 
-    float m = -INFINITY, l = 0.f, beta = 0.f, a1x = 0.f, a1y = 0.f, a2x = 0.f, a2y = 0.f;
-    for (int s0 = w; s0 < S; s0 += NW * BATCH) {
-        float ms[BATCH], ls[BATCH], bs[BATCH];
-        float2 x1[BATCH], x2[BATCH];
-#pragma unroll
-        for (int u = 0; u < BATCH; ++u) {
-            const int s = s0 + NW * u;
-            const float* rec = base + (size_t)min(s, S - 1) * REC;
-            ms[u] = s < S ? rec[2 * D] : -INFINITY;
-            ls[u] = rec[2 * D + 1];
-            bs[u] = rec[2 * D + 2];
-            x1[u] = *(const float2*)(rec + 2 * lane);
-            x2[u] = *(const float2*)(rec + D + 2 * lane);
-        }
-        float mb = m;
-#pragma unroll
-        for (int u = 0; u < BATCH; ++u) mb = fmaxf(mb, ms[u]);
-        if (mb == -INFINITY) continue;  // nothing non-empty yet (wave-uniform)
-        const float fo = m > -INFINITY ? exp2_fast(m - mb) : 0.f;
-        l *= fo;
-        beta *= fo;
-        a1x *= fo;
-        a1y *= fo;
-        a2x *= fo;
-        a2y *= fo;
-#pragma unroll
-        for (int u = 0; u < BATCH; ++u) {
-            const float f = ms[u] > -INFINITY ? exp2_fast(ms[u] - mb) : 0.f;  // empty: 0
-            l = fmaf(f, ls[u], l);
-            beta = fmaf(f, bs[u], beta);
-            a1x = fmaf(f, x1[u].x, a1x);
-            a1y = fmaf(f, x1[u].y, a1y);
-            a2x = fmaf(f, x2[u].x, a2x);
-            a2y = fmaf(f, x2[u].y, a2y);
-        }
-        m = mb;
-    }
-    *(float2*)&reds[w][2 * lane] = float2{a1x, a1y};
-    *(float2*)&reds[w][D + 2 * lane] = float2{a2x, a2y};
+    Merge st;
+    const int n = w < S ? (S - w + NW - 1) / NW : 0;
+    fold_records(st, n, [&](int u) { return base + (size_t)(w + NW * u) * REC; }, lane);
+    *(float2*)&reds[w][2 * lane] = float2{st.a1x, st.a1y};
+    *(float2*)&reds[w][D + 2 * lane] = float2{st.a2x, st.a2y};
     if (lane == 0) {
-        reds[w][2 * D] = m;
-        reds[w][2 * D + 1] = l;
-        reds[w][2 * D + 2] = beta;
+        reds[w][2 * D] = st.m;
+        reds[w][2 * D + 1] = st.l;
+        reds[w][2 * D + 2] = st.beta;
     }
     __syncthreads();
     if (w == 0) {
-        float M = -INFINITY;
-#pragma unroll
-        for (int i = 0; i < NW; ++i) M = fmaxf(M, reds[i][2 * D]);
-        float L = 0.f, Bt = 0.f, A1x = 0.f, A1y = 0.f, A2x = 0.f, A2y = 0.f;
-        if (M > -INFINITY) {
-#pragma unroll
-            for (int i = 0; i < NW; ++i) {
-                const float mi = reds[i][2 * D];
-                const float f = mi > -INFINITY ? exp2_fast(mi - M) : 0.f;
-                L = fmaf(f, reds[i][2 * D + 1], L);
-                Bt = fmaf(f, reds[i][2 * D + 2], Bt);
-                A1x = fmaf(f, reds[i][2 * lane], A1x);
-                A1y = fmaf(f, reds[i][2 * lane + 1], A1y);
-                A2x = fmaf(f, reds[i][D + 2 * lane], A2x);
-                A2y = fmaf(f, reds[i][D + 2 * lane + 1], A2y);
-            }
-        }
-        float yx = 0.f, yy = 0.f;
-        if (L > 0.f) {
-            const float inv = 1.f / L;
-            const float one_tb = 1.f + Bt * inv;
-            yx = inv * (A1x * one_tb - A2x);
-            yy = inv * (A1y * one_tb - A2y);
-        }
-        *(uint32_t*)(o + bh * D + 2 * lane) = pack_bf16x2(yx, yy);
+        Merge all;
+        fold_records(all, NW, [&](int i) { return &reds[i][0]; }, lane);
+        store_merged(all, o + bh * D, lane);
     }
+}
+
+// ------------------------------------------------------------------------ wave-range mode
+// P[0..B]: prefix sums of the clamped sequence lengths, formed by the whole workgroup:
+// thread t sums the block of per = ceil(B / 256) <= 32 sequences from t per (all loads
+// issued before any is used; reads past B return 0), a wave scan and the 4 wave totals give
+// the block offsets. Ends with a workgroup barrier.
+__device__ __forceinline__ void seq_prefix(const int32_t* __restrict__ seqlens, int B, int L_max, int* P) {
+    constexpr int MAXPER = (kDecodeRangeMaxB + NT - 1) / NT;
+    __shared__ int wsum[NW];
+    const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+    const int per = (B + NT - 1) / NT;
+    const auto rs = make_rsrc(seqlens, (uint32_t)B * 4u);
+    int n[MAXPER];
+#pragma unroll
+    for (int i = 0; i < MAXPER; ++i)
+        n[i] = (int)__builtin_amdgcn_raw_buffer_load_b32(
+            rs, i < per ? (uint32_t)(tid * per + i) * 4u : 0x7FFFFFF0u, 0, 0);
+    int sum = 0;
+#pragma unroll
+    for (int i = 0; i < MAXPER; ++i) {
+        n[i] = clamp_len(n[i], L_max);
+        sum += n[i];
+    }
+    int x = sum;  // inclusive scan over the wave
+    for (int d = 1; d < 64; d <<= 1) {
+        const int y = __shfl_up(x, d, 64);
+        if (lane >= d) x += y;
+    }
+    if (lane == 63) wsum[w] = x;
+    __syncthreads();
+    int run = x - sum;
+    for (int i = 0; i < w; ++i) run += wsum[i];
+#pragma unroll
+    for (int i = 0; i < MAXPER; ++i) {
+        run += n[i];
+        const int b = tid * per + i;
+        if (i < per && b < B) P[b + 1] = run;
+    }
+    if (tid == 0) P[0] = 0;
+    __syncthreads();
+}
+
+// First sequence b in [0, B] with H P[b] >= x (requires H P[B] >= x). Each round the 64 lanes
+// test 64 evenly spaced candidates and a ballot keeps the interval holding the answer, so
+// B <= 8192 needs at most 3 rounds. Wave-uniform.
+__device__ __forceinline__ int first_seq_from(const int* P, int B, int H, int x) {
+    const int lane = __lane_id();
+    int lo = 0, hi = B;
+    while (lo < hi) {
+        const int stride = (hi - lo + 62) / 63;  // lane 63 tests hi
+        const bool p = H * P[min(lo + lane * stride, hi)] >= x;
+        const int l = __builtin_ctzll(__builtin_amdgcn_ballot_w64(p));
+        if (l == 0) break;  // the answer is lo
+        const int t_hit = min(lo + l * stride, hi);
+        lo = rfl(lo + (l - 1) * stride + 1);
+        hi = rfl(t_hit);
+    }
+    return lo;
+}
+
+// Position x of the flat range: the (b, h) holding row x, its start F and length n, and the
+// offset j = x - F; when x is a (b, h) start (j = 0) it is the first such (b, h), which may
+// be empty. b == B means x == W with no (b, h) left.
+struct Loc {
+    int b, h, F, n, j;
+};
+__device__ __forceinline__ Loc locate(const int* P, int B, int H, int x) {
+    const int b = first_seq_from(P, B, H, x);
+    const int Pb = rfl(P[b]);
+    Loc L;
+    if (H * Pb == x) {
+        L.b = b;
+        L.h = 0;
+        L.F = x;
+        L.j = 0;
+        L.n = b < B ? rfl(P[b + 1]) - Pb : 0;
+        return L;
+    }
+    const int Pp = rfl(P[b - 1]);  // H P[b-1] < x < H P[b]: sequence b - 1 is not empty
+    L.b = b - 1;
+    L.n = Pb - Pp;
+    L.h = (x - H * Pp) / L.n;
+    L.F = H * Pp + L.h * L.n;
+    L.j = x - L.F;
+    return L;
+}
+
+// Slice boundary g of G over W rows; "whole" plans move it to the next (b, h) start.
+template <bool WHOLE>
+__device__ __forceinline__ int boundary(const int* P, int B, int H, int W, int g, int G) {
+    const int x = (int)((long long)g * W / G);
+    if (!WHOLE) return x;
+    const Loc L = locate(P, B, H, x);
+    return L.j > 0 ? L.F + L.n : x;
+}
+
+template <bool WHOLE>
+__global__ __launch_bounds__(NT, 4) void decode_range_bf16_d128_kernel(
+    const __bf16* __restrict__ q, const __bf16* __restrict__ rho, const __bf16* __restrict__ kc,
+    const __bf16* __restrict__ vc, const int32_t* __restrict__ seqlens, __bf16* __restrict__ o,
+    float* __restrict__ ws, int B, int H, int L_max, float c) {
+    extern __shared__ int P[];  // B + 1 prefix sums
+    __shared__ __attribute__((aligned(16))) float ush[NW][2][KB];
+    seq_prefix(seqlens, B, L_max, P);
+
+    const int lane = threadIdx.x & 63;
+    const int w = rfl(threadIdx.x >> 6);
+    const int col = lane & 15, g = lane >> 4;
+    const int G = gridDim.x * NW, gw = blockIdx.x * NW + w;
+    const bool last = gw == G - 1;  // also takes empty (b, h) at the very end
+    const int W = H * rfl(P[B]);
+    const int r0 = boundary<WHOLE>(P, B, H, W, gw, G);
+    const int r1 = boundary<WHOLE>(P, B, H, W, gw + 1, G);
+
+    // Cursor over this slice: (b, h) with start F and length n; the piece [j, je) of it.
+    const Loc L = locate(P, B, H, r0);
+    int b = L.b, h = L.h, F = L.F, n = L.n, j = L.j, js = L.j;
+    bool more = b < B && (j > 0 || F < r1 || last);
+    int je = last ? n : min(n, r1 - F);
+
+    struct Step {
+        int it, kb0, je, js, n;
+        bool valid, last;
+    };
+    // Next step of KB rows; a piece with no rows (an empty (b, h), or an empty slice inside
+    // a (b, h)) still takes one step so that its output or partial gets written.
+    auto next = [&]() {
+        Step s;
+        s.valid = more;
+        s.it = b * H + h;
+        s.kb0 = j;
+        s.je = je;
+        s.js = js;
+        s.n = n;
+        s.last = j + KB >= je;
+        if (!s.last) {
+            j += KB;
+            return s;
+        }
+        F += n;
+        if (++h == H) {
+            h = 0;
+            ++b;
+            n = b < B ? rfl(P[b + 1]) - rfl(P[b]) : 0;
+        }
+        more = b < B && (F < r1 || last);
+        j = js = 0;
+        je = last ? n : min(n, r1 - F);
+        return s;
+    };
+    Acc acc;
+    acc.reset();
+    // End of a piece: the whole (b, h) range writes o, a cut piece writes its partial to
+    // slot 0 (piece starts inside the (b, h)) or 1 (piece starts at the (b, h) start).
+    auto finish = [&](const Step& s) {
+        decode::wave_totals(acc);
+        const float l = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(acc.rsum), 0));
+        const float beta = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(acc.rsum), 1));
+        if (s.js == 0 && s.je == s.n) {
+            if (lane < 16) {
+                uint32_t pk[4];
+#pragma unroll
+                for (int p = 0; p < 4; ++p)
+                    pk[p] = pack_bf16x2(combine_out(acc.a1[2 * p], acc.a2[2 * p], l, beta),
+                                        combine_out(acc.a1[2 * p + 1], acc.a2[2 * p + 1], l, beta));
+                *(u32x4*)(o + (size_t)s.it * D + 8 * lane) = u32x4{pk[0], pk[1], pk[2], pk[3]};
+            }
+        } else {
+            float* rec = ws + ((size_t)gw * 2 + (s.js > 0 ? 0 : 1)) * REC;
+            if (lane < 16) {
+                *(f32x4*)(rec + 8 * lane) = f32x4{acc.a1[0], acc.a1[1], acc.a1[2], acc.a1[3]};
+                *(f32x4*)(rec + 8 * lane + 4) = f32x4{acc.a1[4], acc.a1[5], acc.a1[6], acc.a1[7]};
+                *(f32x4*)(rec + D + 8 * lane) = f32x4{acc.a2[0], acc.a2[1], acc.a2[2], acc.a2[3]};
+                *(f32x4*)(rec + D + 8 * lane + 4) =
+                    f32x4{acc.a2[4], acc.a2[5], acc.a2[6], acc.a2[7]};
+            }
+            if (lane == 0) *(f32x4*)(rec + 2 * D) = f32x4{acc.m_run, l, beta, 0.f};
+        }
+        acc.reset();
+    };
+
+    // One step in flight per wave; latency is hidden by the other waves of the compute unit
+    // (16 at this kernel's register count).
+    Frag f;
+    bf16x8 bqr[4];
+    while (more) {
+        const Step s = next();
+        // q and rho of the step's (b, h), reloaded every step (cache hits after the first):
+        // lane (col, g) reads column col's dims 32 st + 8 g .. +7 and keeps them for col < 2.
+        const __bf16* qr_src = (col == 1 ? rho : q) + (size_t)s.it * D + 8 * g;
+        u32x4 xq[4];
+#pragma unroll
+        for (int st = 0; st < 4; ++st) xq[st] = *(const u32x4*)(qr_src + 32 * st);
+        const size_t row0 = (size_t)s.it * L_max;
+        const uint32_t range = (uint32_t)s.je * 256u;
+        decode::load_step(make_rsrc(kc + row0 * D, range), make_rsrc(vc + row0 * D, range),
+                          s.kb0, col, g, f);
+        __builtin_amdgcn_sched_barrier(0);  // every load of the step is issued before any wait
+#pragma unroll
+        for (int st = 0; st < 4; ++st) bqr[st] = as_bf16x8(col < 2 ? xq[st] : u32x4{});
+        decode::consume(acc, f, bqr, s.kb0, s.je, c, ush[w], col, g);
+        if (s.last) finish(s);
+    }
+}
+
+// Merges the pieces of every (b, h) that slice boundaries cut: wave g (1 <= g < G) looks at
+// boundary g; if it is the first boundary inside a (b, h), the pieces are wave g-1's slot 1
+// and slot 0 of waves g, g+1, ... whose slices start inside that (b, h).
+__global__ __launch_bounds__(NT) void decode_range_combine_kernel(
+    const float* __restrict__ ws, __bf16* __restrict__ o, const int32_t* __restrict__ seqlens,
+    int B, int H, int L_max, int G) {
+    extern __shared__ int P[];
+    seq_prefix(seqlens, B, L_max, P);
+    const int lane = threadIdx.x & 63;
+    const int gb = blockIdx.x * NW + rfl(threadIdx.x >> 6) + 1;
+    if (gb >= G) return;
+    const int W = H * rfl(P[B]);
+    auto R = [&](int k) { return (int)((long long)k * W / G); };
+    const Loc L = locate(P, B, H, R(gb));
+    if (L.b >= B || L.j == 0 || R(gb - 1) > L.F) return;
+    const int E = L.F + L.n;
+    int np = 1;
+    while (gb + np - 1 < G && R(gb + np - 1) < E) ++np;
+    Merge st;
+    fold_records(st, np,
+                 [&](int u) {
+                     return u == 0 ? ws + ((size_t)(gb - 1) * 2 + 1) * REC
+                                   : ws + ((size_t)(gb + u - 1) * 2) * REC;
+                 },
+                 lane);
+    store_merged(st, o + ((size_t)L.b * H + L.h) * D, lane);
 }
 
 }  // namespace
 
 hipError_t launch_decode_bf16_d128(const DecodeArgs& a, hipStream_t stream) {
+    const float c = a.scale * kLog2e;
+    if (a.waves > 0) {
+        const int grid = a.waves / NW;
+        const size_t lds = (size_t)(a.B + 1) * sizeof(int);
+        if (a.whole)
+            hipLaunchKernelGGL(decode_range_bf16_d128_kernel<true>, dim3(grid), dim3(NT), lds,
+                               stream, (const __bf16*)a.q, (const __bf16*)a.rho,
+                               (const __bf16*)a.k, (const __bf16*)a.v, a.seqlens, (__bf16*)a.o,
+                               a.ws, a.B, a.H, a.L_max, c);
+        else
+            hipLaunchKernelGGL(decode_range_bf16_d128_kernel<false>, dim3(grid), dim3(NT), lds,
+                               stream, (const __bf16*)a.q, (const __bf16*)a.rho,
+                               (const __bf16*)a.k, (const __bf16*)a.v, a.seqlens, (__bf16*)a.o,
+                               a.ws, a.B, a.H, a.L_max, c);
+        hipError_t e = hipGetLastError();
+        if (e != hipSuccess || a.whole || a.waves == 1) return e;
+        hipLaunchKernelGGL(decode_range_combine_kernel, dim3((a.waves - 1 + NW - 1) / NW),
+                           dim3(NT), lds, stream, (const float*)a.ws, (__bf16*)a.o, a.seqlens,
+                           a.B, a.H, a.L_max, a.waves);
+        return hipGetLastError();
+    }
+    const int BH = a.B * a.H;
     dim3 grid(a.splits, a.H, a.B);
-    hipLaunchKernelGGL(decode_split_bf16_d128_kernel<PLX_DECODE_KB>, grid, dim3(NT), 0, stream,
+    hipLaunchKernelGGL(decode_split_bf16_d128_kernel, grid, dim3(NT), 0, stream,
                        (const __bf16*)a.q, (const __bf16*)a.rho, (const __bf16*)a.k,
                        (const __bf16*)a.v, a.seqlens, (__bf16*)a.o, a.ws, a.H, a.L_max, a.splits,
-                       a.scale * kLog2e);
+                       c);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess || a.splits == 1) return e;
-    const int BH = a.B * a.H;
     hipLaunchKernelGGL(decode_combine_kernel, dim3(BH), dim3(NT), 0, stream, (const float*)a.ws,
                        (__bf16*)a.o, a.splits);
     return hipGetLastError();

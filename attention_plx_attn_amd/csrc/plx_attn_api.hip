@@ -41,6 +41,14 @@ constexpr int kDecodeWaveKeys = 64;      // chunk granularity (keys)
 constexpr int kDecodeMinChunk = 256;     // at least one step per wave of a 4-wave workgroup
 constexpr int kDecodeMaxSplits = 4096;
 constexpr int kDecodeWgPerCu = 1;        // one streaming workgroup per compute unit (measured best)
+// Wave-range mode: slices end at (b, h) starts once there are 8 (b, h) per wave. The automatic
+// plan uses it only in that form, for short contexts with enough (b, h) to give every compute
+// unit at least one 4-wave workgroup and at most the 4 its registers allow (measured on
+// MI355X: ahead of split mode for B x ctx = 512 x 128 and 2048 x 128, behind it once the
+// combine of cut (b, h) runs or the contexts are long enough for one workgroup per (b, h)).
+constexpr int kRangeWholeBhPerWave = 8;
+constexpr int kRangeWgPerCu = 4;
+constexpr int kRangeMaxAutoLmax = 512;
 
 int ceil_div(long long a, long long b) { return (int)((a + b - 1) / b); }
 
@@ -52,22 +60,55 @@ void chunk_plan(int L_max, int splits, int* chunk, int* launched) {
     *launched = ceil_div(L_max, c);
 }
 
-plx_status_t plan_splits(int B, int H, int L_max, int num_splits, int* splits) {
-    if (num_splits < 0 || num_splits > kDecodeMaxSplits) return PLX_ERR_INVALID_ARG;
-    if (num_splits > 0) {
-        *splits = num_splits;
+// How a decode call divides the cache: split mode (splits chunks of each (b, h)) or
+// wave-range mode (waves equal slices of all (b, h) laid end to end).
+struct DecodePlan {
+    int splits = 1, chunk = 0;  // split mode
+    int waves = 0;              // > 0: wave-range mode
+    bool whole = false;         // wave-range slices end at (b, h) starts
+    size_t ws_bytes = 0;
+    int reported() const { return waves > 0 ? -waves : splits; }
+};
+
+bool range_mode_fits(int B, int H, int L_max) {
+    return B <= plx::kDecodeRangeMaxB && (long long)B * H * L_max < (1LL << 31);
+}
+
+plx_status_t plan_decode(int B, int H, int L_max, int d_v, int num_splits, DecodePlan* p) {
+    if (num_splits > kDecodeMaxSplits || num_splits < -plx::kDecodeRangeMaxWaves)
+        return PLX_ERR_INVALID_ARG;
+    *p = DecodePlan{};
+    const long long bh = (long long)B * H;
+    const size_t rec_bytes = (size_t)(2 * d_v + 4) * sizeof(float);
+    int waves = 0, splits = num_splits;
+    if (num_splits < 0) {
+        if (!range_mode_fits(B, H, L_max)) return PLX_ERR_UNSUPPORTED;
+        waves = ceil_div(-(long long)num_splits, 4) * 4;
+    } else if (num_splits == 0) {
+        int cus = 0;
+        const plx_status_t st = current_cu_count(&cus);
+        if (st != PLX_OK) return st;
+        long long wg = bh / (4LL * kRangeWholeBhPerWave);
+        if (wg > (long long)kRangeWgPerCu * cus) wg = (long long)kRangeWgPerCu * cus;
+        if (range_mode_fits(B, H, L_max) && L_max <= kRangeMaxAutoLmax && wg >= cus)
+            waves = (int)(4 * wg);
+        if (!waves) {  // split mode: fill the chip once with (b, h, chunk) workgroups
+            long long s = (kDecodeWgPerCu * (long long)cus + bh - 1) / bh;
+            const long long smax = (L_max + kDecodeMinChunk - 1) / kDecodeMinChunk;
+            if (s > smax) s = smax;
+            if (s < 1) s = 1;
+            if (s > kDecodeMaxSplits) s = kDecodeMaxSplits;
+            splits = (int)s;
+        }
+    }
+    if (waves > 0) {
+        p->waves = waves;
+        p->whole = bh >= (long long)kRangeWholeBhPerWave * waves;
+        p->ws_bytes = p->whole ? 0 : (size_t)waves * 2 * rec_bytes;
         return PLX_OK;
     }
-    int cus = 0;
-    const plx_status_t st = current_cu_count(&cus);
-    if (st != PLX_OK) return st;
-    const long long bh = (long long)B * H;
-    long long s = (kDecodeWgPerCu * (long long)cus + bh - 1) / bh;  // fill the chip once
-    const long long smax = (L_max + kDecodeMinChunk - 1) / kDecodeMinChunk;
-    if (s > smax) s = smax;
-    if (s < 1) s = 1;
-    if (s > kDecodeMaxSplits) s = kDecodeMaxSplits;
-    *splits = (int)s;
+    chunk_plan(L_max, splits, &p->chunk, &p->splits);
+    p->ws_bytes = p->splits > 1 ? (size_t)bh * p->splits * rec_bytes : 0;
     return PLX_OK;
 }
 
@@ -134,12 +175,10 @@ plx_status_t plx_attn_decode_num_splits(int32_t B, int32_t H, int32_t L_max,
     if (!splits_out) return PLX_ERR_NULL_POINTER;
     plx_status_t st = check_decode_shape(B, H, L_max, 1);
     if (st != PLX_OK) return st;
-    int s = 0;
-    st = plan_splits(B, H, L_max, num_splits, &s);
+    DecodePlan p;
+    st = plan_decode(B, H, L_max, 128, num_splits, &p);
     if (st != PLX_OK) return st;
-    int chunk = 0, launched = 0;
-    chunk_plan(L_max, s, &chunk, &launched);
-    *splits_out = launched;
+    *splits_out = p.reported();
     return PLX_OK;
 }
 
@@ -149,10 +188,10 @@ plx_status_t plx_attn_decode_workspace_size(int32_t B, int32_t H, int32_t L_max,
     if (!bytes_out) return PLX_ERR_NULL_POINTER;
     plx_status_t st = check_decode_shape(B, H, L_max, d_v);
     if (st != PLX_OK) return st;
-    int s = 0;
-    st = plx_attn_decode_num_splits(B, H, L_max, num_splits, &s);
+    DecodePlan p;
+    st = plan_decode(B, H, L_max, d_v, num_splits, &p);
     if (st != PLX_OK) return st;
-    *bytes_out = s > 1 ? (size_t)B * H * s * (size_t)(2 * d_v + 4) * sizeof(float) : 0;
+    *bytes_out = p.ws_bytes;
     return PLX_OK;
 }
 
@@ -168,25 +207,24 @@ plx_status_t plx_attn_decode(plx_dtype_t dtype, int32_t B, int32_t H, int32_t L_
     if (st != PLX_OK) return st;
     if (d_qk < 1) return PLX_ERR_INVALID_SHAPE;
     if (!std::isfinite(softmax_scale) || softmax_scale < 0.f) return PLX_ERR_INVALID_ARG;
-    if (num_splits < 0 || num_splits > kDecodeMaxSplits) return PLX_ERR_INVALID_ARG;
+    if (num_splits > kDecodeMaxSplits || num_splits < -plx::kDecodeRangeMaxWaves)
+        return PLX_ERR_INVALID_ARG;
     if (!(dtype == PLX_BF16 && d_qk == 128 && d_v == 128)) return PLX_ERR_UNSUPPORTED;
     if (!aligned16(q) || !aligned16(rho) || !aligned16(k_cache) || !aligned16(v_cache) ||
         !aligned16(o) || (reinterpret_cast<uintptr_t>(seqlens) & 3u) != 0)
         return PLX_ERR_MISALIGNED;
 
-    int splits = 0;
-    st = plan_splits(B, H, L_max, num_splits, &splits);
+    DecodePlan p;
+    st = plan_decode(B, H, L_max, d_v, num_splits, &p);
     if (st != PLX_OK) return st;
-    int chunk = 0, launched = 0;
-    chunk_plan(L_max, splits, &chunk, &launched);
-    if (launched > 1) {
-        const size_t need = (size_t)B * H * launched * (size_t)(2 * d_v + 4) * sizeof(float);
+    if (p.ws_bytes > 0) {
         if (!workspace) return PLX_ERR_NULL_POINTER;
-        if (workspace_bytes < need) return PLX_ERR_WORKSPACE_TOO_SMALL;
+        if (workspace_bytes < p.ws_bytes) return PLX_ERR_WORKSPACE_TOO_SMALL;
         if (!aligned16(workspace)) return PLX_ERR_MISALIGNED;
     }
     plx::DecodeArgs a{B, H, L_max, d_qk, q, rho, k_cache, v_cache, seqlens, o, softmax_scale,
-                      launched, chunk, static_cast<float*>(workspace)};
+                      p.splits, p.chunk, static_cast<float*>(workspace), p.waves,
+                      p.whole ? 1 : 0};
     const hipError_t e = plx::launch_decode_bf16_d128(a, static_cast<hipStream_t>(stream));
     return e == hipSuccess ? PLX_OK : PLX_ERR_HIP;
 }

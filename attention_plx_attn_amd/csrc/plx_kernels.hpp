@@ -26,12 +26,17 @@ struct DecodeArgs {
     const int32_t* seqlens;
     void* o;
     float scale;
-    int splits;  // chunks per (b, h) actually launched
+    int splits;  // split mode: chunks per (b, h) actually launched
     int chunk;   // keys per chunk of the L_max plan (the kernel splits each sequence evenly)
-    float* ws;   // split partials, [B*H*splits][kDecodeRecord] floats (unused if splits == 1)
+    float* ws;   // partials: split mode [B*H*splits][kDecodeRecord] floats (unused if
+                 // splits == 1); wave-range mode [waves][2][kDecodeRecord] (unused if whole)
+    int waves;   // > 0: wave-range mode with this many waves (a multiple of 4); 0: split mode
+    int whole;   // wave-range mode: slices end at (b, h) boundaries, no partials
 };
 
 constexpr int kDecodeRecord = 2 * 128 + 4;  // A1[128], A2[128], m, l, beta, pad
+constexpr int kDecodeRangeMaxB = 8192;      // wave-range mode keeps B + 1 prefix sums in LDS
+constexpr int kDecodeRangeMaxWaves = 1 << 16;
 
 bool prefill_f32_supported(int d);
 hipError_t launch_prefill_f32(const PrefillArgs& a, hipStream_t stream);

@@ -80,15 +80,19 @@ plx_status_t plx_attn_prefill(plx_dtype_t dtype, int32_t B, int32_t H, int32_t T
                               void* stream);
 
 /*
- * Split count the decode call will use: num_splits if > 0, otherwise a heuristic from
- * B*H, L_max and the current device's compute-unit count. Writes it to *splits_out.
+ * The plan a decode call with these arguments will use, written to *splits_out in the
+ * encoding of num_splits: S > 0 for split mode with S chunks per (b, h), or -G for
+ * wave-range mode with G waves. num_splits > 0 and < 0 are taken as given (a negative count
+ * is rounded up to a multiple of 4); 0 picks from B*H, L_max and the current device's
+ * compute-unit count.
  */
 plx_status_t plx_attn_decode_num_splits(int32_t B, int32_t H, int32_t L_max,
                                         int32_t num_splits, int32_t* splits_out);
 
 /*
  * Bytes of fp32 workspace plx_attn_decode needs for the same (B, H, L_max, d_v,
- * num_splits): B*H*S*(2*d_v + 4)*4 for S > 1 split partials, 0 when S == 1.
+ * num_splits): split mode B*H*S*(2*d_v + 4)*4 for S > 1 chunks (0 when S == 1);
+ * wave-range mode G*2*(2*d_v + 4)*4 for G waves, or 0 when its slices hold whole (b, h).
  */
 plx_status_t plx_attn_decode_workspace_size(int32_t B, int32_t H, int32_t L_max,
                                             int32_t d_v, int32_t num_splits,
@@ -102,14 +106,21 @@ plx_status_t plx_attn_decode_workspace_size(int32_t B, int32_t H, int32_t L_max,
  *   seqlens  : device int32 [B]; query b attends to cache rows [0, n_b) with
  *              n_b = min(max(seqlens[b], 0), L_max); n_b == 0 gives o[b] = 0.
  *              Rows at or beyond n_b are never read, so they may hold anything.
- *   num_splits : 0 = heuristic, else the number of KV chunks per (b, h); each chunk's
- *              partial state (running max, normaliser, sum w t, sum w v, sum w t v) goes
- *              to the workspace and a second kernel merges them.
+ *   num_splits : how the cache is divided among waves; 0 = heuristic.
+ *              > 0: split mode, that many KV chunks per (b, h) (each sequence's own length
+ *              split evenly); each chunk's partial state (running max, normaliser, sum w t,
+ *              sum w v, sum w t v) goes to the workspace and a second kernel merges them.
+ *              < 0: wave-range mode with -num_splits waves (rounded up to a multiple of 4):
+ *              the (b, h) ranges are laid end to end (sequence-major, head-minor) and each
+ *              wave streams an equal slice, whatever the mix of lengths; a (b, h) cut by
+ *              slice ends leaves partials that a second kernel merges. With at least 8
+ *              (b, h) per wave the slices end at (b, h) starts instead and nothing is merged.
+ *              Needs B <= 8192 and B*H*L_max < 2^31 (else PLX_ERR_UNSUPPORTED).
  *   workspace  : device buffer of at least plx_attn_decode_workspace_size() bytes
  *              (may be NULL when that size is 0).
  *
  * Built combination: (PLX_BF16, d_qk = d_v = 128).
- * Limits: L_max * d * 2 < 2^31; num_splits <= 4096.
+ * Limits: L_max * d * 2 < 2^31; -65536 <= num_splits <= 4096.
  */
 plx_status_t plx_attn_decode(plx_dtype_t dtype, int32_t B, int32_t H, int32_t L_max,
                              int32_t d_qk, int32_t d_v, const void* q, const void* rho,

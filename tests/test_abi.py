@@ -71,7 +71,9 @@ def test_decode_validation(lib):
     assert _decode(lib, L=1 << 23) == 2
     assert _decode(lib, B=70000) == 2
     assert _decode(lib, scale=float("nan")) == 3
-    assert _decode(lib, splits=-2) == 3
+    assert _decode(lib, splits=-70000) == 3
+    assert _decode(lib, B=9000, splits=-8) == 4       # wave-range mode keeps B + 1 sums in LDS
+    assert _decode(lib, B=64, H=64, L=1 << 20, splits=-8) == 4  # flat rows must fit in int32
     assert _decode(lib, splits=5000) == 3
     assert _decode(lib, dtype=0) == 4
     assert _decode(lib, dqk=64, dv=64) == 4
@@ -93,3 +95,14 @@ def test_split_plan_explicit(lib):
     assert plx.decode_workspace_size(2, 3, 4096, 128, 4) == 2 * 3 * 4 * 260 * 4
     with pytest.raises(_lib.PlxError):
         plx.decode_num_splits(0, 1, 10, 1)
+
+
+def test_wave_range_plan_explicit(lib):
+    # num_splits < 0 asks for wave-range mode with that many waves, rounded up to 4; the plan
+    # reports minus the wave count. Slices end at (b, h) starts (no workspace) once there are
+    # at least 8 (b, h) per wave, else each wave has two partial slots.
+    assert plx.decode_num_splits(8, 4, 300, -4) == -4
+    assert plx.decode_num_splits(8, 4, 300, -5) == -8
+    assert plx.decode_workspace_size(8, 4, 300, 128, -4) == 0          # 32 (b, h) >= 8 * 4
+    assert plx.decode_workspace_size(8, 4, 300, 128, -8) == 8 * 2 * 260 * 4
+    assert plx.decode_workspace_size(1, 1, 40, 128, -4096) == 4096 * 2 * 260 * 4

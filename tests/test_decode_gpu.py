@@ -76,6 +76,63 @@ def test_split_counts_deterministic_and_permutation_invariant_batch():
     assert torch.equal(_run(xp, 4).cpu(), o[perm])
 
 
+# Wave-range mode (num_splits < 0: that many waves share the (b, h) ranges laid end to end).
+# (B, H, L_max, waves): whole (b, h) per wave; pieces cut across 2-3 waves; (b, h) cut into
+# ~40 pieces (several merge batches); more waves than rows (empty slices); a single (b, h).
+@pytest.mark.parametrize("B,H,L,waves", [(8, 4, 300, 4), (21, 3, 64, 4), (8, 4, 300, 8),
+                                         (8, 4, 300, 64), (3, 2, 1000, 256), (1, 1, 40, 4096),
+                                         (1, 1, 1000, 8)])
+def test_wave_range_decode(B, H, L, waves):
+    cfg = DecodeConfig("d", 25, B, H, L, 128, "bf16", "scaled", "uniform_half")
+    x = decode_inputs(cfg, seed=B * 7 + L, poison=True)
+    _say("wave-range", B, H, L, waves, "ws", plx.decode_workspace_size(B, H, L, 128, -waves))
+    o = _run(x, -waves)
+    k = torch.nan_to_num(x["k_cache"].float())
+    v = torch.nan_to_num(x["v_cache"].float())
+    ref = oracle.decode(x["q"], x["rho"], k, v, x["seqlens"], x["scale"], form="cov")
+    check_bf16(o, ref, f"wave-range B={B} H={H} L={L} waves={waves}")
+    assert torch.equal(o, _run(x, -waves))
+
+
+@pytest.mark.parametrize("waves", [4, 8, 64])
+def test_wave_range_seqlens_edge_cases(waves):
+    # rho as in the prefill configs: with the strong decode probe (RMSNorm(W_R x), norm ~11)
+    # a 37-row context has outputs near 11, where bf16 output spacing alone is 1/16.
+    cfg = DecodeConfig("d", 22, 7, 3, 200, 128, "bf16", "scaled", "full")
+    x = decode_inputs(cfg, seed=1)
+    sl = torch.tensor([0, -5, 1, 200, 100000, 0, 37], dtype=torch.int32)
+    o = _run(x, -waves, seqlens=sl).cpu()
+    for b in (0, 1, 5):
+        assert torch.all(o[b] == 0)
+    assert torch.equal(o[2], x["v_cache"][2, :, 0])  # one key: exactly its value
+    ref = oracle.decode(x["q"], x["rho"], x["k_cache"], x["v_cache"], sl, x["scale"])
+    check_bf16(o[3:5], ref[3:5], f"edges waves={waves}")
+    check_bf16(o[6:], ref[6:], f"edges waves={waves}")
+    zero = _run(x, -waves, seqlens=torch.zeros(7, dtype=torch.int32)).cpu()
+    assert torch.all(zero == 0)
+
+
+def test_wave_range_permuted_batch():
+    # Permuting the batch moves every slice boundary; each order must match the oracle.
+    cfg = DecodeConfig("d", 24, 6, 4, 777, 128, "bf16", "scaled", "uniform_half")
+    x = decode_inputs(cfg, seed=9)
+    ref = oracle.decode(x["q"], x["rho"], x["k_cache"], x["v_cache"], x["seqlens"], x["scale"])
+    check_bf16(_run(x, -16), ref, "wave-range")
+    perm = torch.tensor([3, 1, 0, 5, 2, 4])
+    xp = {k: (x[k][perm] if k != "scale" else x[k]) for k in x}
+    check_bf16(_run(xp, -16), ref[perm.numpy()], "wave-range permuted")
+
+
+def test_auto_plan_modes():
+    # Automatic choice (needs the device's compute-unit count): many short sequences use
+    # wave-range mode with whole (b, h) per slice (no workspace); the rest use split mode.
+    assert plx.decode_num_splits(2048, 16, 128, 0) < 0
+    assert plx.decode_workspace_size(2048, 16, 128, 128, 0) == 0
+    assert plx.decode_num_splits(1, 16, 32768, 0) > 0
+    assert plx.decode_num_splits(16, 16, 1024, 0) > 0
+    assert plx.decode_num_splits(2048, 16, 1024, 0) > 0
+
+
 @pytest.mark.parametrize("splits", [0, 1, 2, 7, 64, 128])
 def test_config_decode_32k(splits):
     cfg = CONFIGS["decode_32k"]

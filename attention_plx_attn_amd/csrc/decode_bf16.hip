@@ -21,8 +21,8 @@
 //    lengths in LDS; a wave finds its first (b, h) with a 64-way search. A (b, h) that lies
 //    inside one slice is finished by its wave (o written); one cut by slice boundaries leaves
 //    a partial per piece, and a combine kernel (one wave per slice boundary) merges them.
-//    With the boundaries moved to the next (b, h) start ("whole" plans, chosen when there are
-//    many (b, h) per wave) nothing is cut and no combine runs. Suits many or ragged sequences.
+//    With the boundaries moved to the next (b, h) start ("whole" plans, chosen from 2 (b, h)
+//    per wave) nothing is cut and no combine runs. Suits many short sequences.
 //
 // Both stream the cache once with non-temporal 16-byte buffer loads in 32-row steps (16 KiB);
 // split mode keeps two steps in flight per wave, wave-range mode one step per wave with 16

@@ -41,13 +41,14 @@ constexpr int kDecodeWaveKeys = 64;      // chunk granularity (keys)
 constexpr int kDecodeMinChunk = 256;     // at least one step per wave of a 4-wave workgroup
 constexpr int kDecodeMaxSplits = 4096;
 constexpr int kDecodeWgPerCu = 1;        // one streaming workgroup per compute unit (measured best)
-// Wave-range mode: slices end at (b, h) starts once there are 8 (b, h) per wave. The automatic
-// plan uses it only in that form, for short contexts with enough (b, h) to give every compute
-// unit at least one 4-wave workgroup and at most the 4 its registers allow (measured on
-// MI355X: ahead of split mode for B x ctx = 512 x 128 and 2048 x 128, behind it once the
-// combine of cut (b, h) runs or the contexts are long enough for one workgroup per (b, h)).
-constexpr int kRangeWholeBhPerWave = 8;
+// Wave-range mode: slices end at (b, h) starts once there are 2 (b, h) per wave. The automatic
+// plan uses it only in that form, for short contexts with enough (b, h) for at least 2 and at
+// most 4 (the register limit) 4-wave workgroups per compute unit. Measured on MI355X: ahead
+// of split mode for B x ctx = 512 x 128 and 2048 x 128; behind it once a combine of cut (b, h)
+// runs, or when the contexts are long enough for one workgroup per (b, h).
+constexpr int kRangeWholeBhPerWave = 2;
 constexpr int kRangeWgPerCu = 4;
+constexpr int kRangeMinWgPerCu = 2;
 constexpr int kRangeMaxAutoLmax = 512;
 
 int ceil_div(long long a, long long b) { return (int)((a + b - 1) / b); }
@@ -90,7 +91,8 @@ plx_status_t plan_decode(int B, int H, int L_max, int d_v, int num_splits, Decod
         if (st != PLX_OK) return st;
         long long wg = bh / (4LL * kRangeWholeBhPerWave);
         if (wg > (long long)kRangeWgPerCu * cus) wg = (long long)kRangeWgPerCu * cus;
-        if (range_mode_fits(B, H, L_max) && L_max <= kRangeMaxAutoLmax && wg >= cus)
+        if (range_mode_fits(B, H, L_max) && L_max <= kRangeMaxAutoLmax &&
+            wg >= (long long)kRangeMinWgPerCu * cus)
             waves = (int)(4 * wg);
         if (!waves) {  // split mode: fill the chip once with (b, h, chunk) workgroups
             long long s = (kDecodeWgPerCu * (long long)cus + bh - 1) / bh;

@@ -113,7 +113,7 @@ plx_status_t plx_attn_decode_workspace_size(int32_t B, int32_t H, int32_t L_max,
  *              < 0: wave-range mode with -num_splits waves (rounded up to a multiple of 4):
  *              the (b, h) ranges are laid end to end (sequence-major, head-minor) and each
  *              wave streams an equal slice, whatever the mix of lengths; a (b, h) cut by
- *              slice ends leaves partials that a second kernel merges. With at least 8
+ *              slice ends leaves partials that a second kernel merges. With at least 2
  *              (b, h) per wave the slices end at (b, h) starts instead and nothing is merged.
  *              Needs B <= 8192 and B*H*L_max < 2^31 (else PLX_ERR_UNSUPPORTED).
  *   workspace  : device buffer of at least plx_attn_decode_workspace_size() bytes

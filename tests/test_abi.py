@@ -100,9 +100,9 @@ def test_split_plan_explicit(lib):
 def test_wave_range_plan_explicit(lib):
     # num_splits < 0 asks for wave-range mode with that many waves, rounded up to 4; the plan
     # reports minus the wave count. Slices end at (b, h) starts (no workspace) once there are
-    # at least 8 (b, h) per wave, else each wave has two partial slots.
+    # at least 2 (b, h) per wave, else each wave has two partial slots.
     assert plx.decode_num_splits(8, 4, 300, -4) == -4
     assert plx.decode_num_splits(8, 4, 300, -5) == -8
-    assert plx.decode_workspace_size(8, 4, 300, 128, -4) == 0          # 32 (b, h) >= 8 * 4
-    assert plx.decode_workspace_size(8, 4, 300, 128, -8) == 8 * 2 * 260 * 4
+    assert plx.decode_workspace_size(8, 4, 300, 128, -16) == 0         # 32 (b, h) >= 2 * 16
+    assert plx.decode_workspace_size(8, 4, 300, 128, -20) == 20 * 2 * 260 * 4
     assert plx.decode_workspace_size(1, 1, 40, 128, -4096) == 4096 * 2 * 260 * 4

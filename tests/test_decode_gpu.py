@@ -77,11 +77,12 @@ def test_split_counts_deterministic_and_permutation_invariant_batch():
 
 
 # Wave-range mode (num_splits < 0: that many waves share the (b, h) ranges laid end to end).
-# (B, H, L_max, waves): whole (b, h) per wave; pieces cut across 2-3 waves; (b, h) cut into
-# ~40 pieces (several merge batches); more waves than rows (empty slices); a single (b, h).
-@pytest.mark.parametrize("B,H,L,waves", [(8, 4, 300, 4), (21, 3, 64, 4), (8, 4, 300, 8),
-                                         (8, 4, 300, 64), (3, 2, 1000, 256), (1, 1, 40, 4096),
-                                         (1, 1, 1000, 8)])
+# (B, H, L_max, waves): whole (b, h) per slice (8, 16 and 2 (b, h) per wave); pieces cut across
+# 2-3 waves; (b, h) cut into ~40 pieces (several merge batches); more waves than rows (empty
+# slices); a single (b, h).
+@pytest.mark.parametrize("B,H,L,waves", [(8, 4, 300, 4), (21, 3, 64, 4), (8, 4, 300, 16),
+                                         (8, 4, 300, 24), (8, 4, 300, 64), (3, 2, 1000, 256),
+                                         (1, 1, 40, 4096), (1, 1, 1000, 8)])
 def test_wave_range_decode(B, H, L, waves):
     cfg = DecodeConfig("d", 25, B, H, L, 128, "bf16", "scaled", "uniform_half")
     x = decode_inputs(cfg, seed=B * 7 + L, poison=True)
@@ -94,7 +95,7 @@ def test_wave_range_decode(B, H, L, waves):
     assert torch.equal(o, _run(x, -waves))
 
 
-@pytest.mark.parametrize("waves", [4, 8, 64])
+@pytest.mark.parametrize("waves", [4, 12, 64])  # 21 (b, h): whole, cut, cut
 def test_wave_range_seqlens_edge_cases(waves):
     # rho as in the prefill configs: with the strong decode probe (RMSNorm(W_R x), norm ~11)
     # a 37-row context has outputs near 11, where bf16 output spacing alone is 1/16.

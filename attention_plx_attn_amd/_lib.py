@@ -90,10 +90,12 @@ def _stream_handle(stream: Optional[torch.cuda.Stream], device) -> int:
     return ctypes.c_void_p(s.cuda_stream).value or 0
 
 
-def prefill(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, rho: torch.Tensor,
+def prefill(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, rho: Optional[torch.Tensor],
             scale: Optional[float] = None, out: Optional[torch.Tensor] = None,
             stream: Optional[torch.cuda.Stream] = None) -> torch.Tensor:
-    """Causal Parallax prefill. q, k, rho [B,H,T,d_qk]; v [B,H,T,d_v] -> o [B,H,T,d_v]."""
+    """Causal Parallax prefill. q, k, rho [B,H,T,d_qk]; v [B,H,T,d_v] -> o [B,H,T,d_v].
+
+    rho=None means rho = 0 exactly (plain softmax attention, the specialised kernel)."""
     lib = load()
     if q.dim() != 4:
         raise ValueError("q must be [B, H, T, d_qk]")
@@ -101,7 +103,8 @@ def prefill(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, rho: torch.Tensor
     dv = v.shape[-1]
     _check(q, "q", None, None)
     _check(k, "k", q.dtype, q.device, (B, H, T, dqk))
-    _check(rho, "rho", q.dtype, q.device, (B, H, T, dqk))
+    if rho is not None:
+        _check(rho, "rho", q.dtype, q.device, (B, H, T, dqk))
     _check(v, "v", q.dtype, q.device, (B, H, T, dv))
     if out is None:
         out = torch.empty((B, H, T, dv), dtype=q.dtype, device=q.device)
@@ -109,7 +112,8 @@ def prefill(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, rho: torch.Tensor
     if scale is None:
         scale = dqk ** -0.5
     rc = lib.plx_attn_prefill(_dtype_code(q), B, H, T, dqk, dv, q.data_ptr(), k.data_ptr(),
-                              v.data_ptr(), rho.data_ptr(), out.data_ptr(), float(scale),
+                              v.data_ptr(), 0 if rho is None else rho.data_ptr(),
+                              out.data_ptr(), float(scale),
                               _stream_handle(stream, q.device))
     if rc != 0:
         raise PlxError(rc, "plx_attn_prefill")
@@ -134,18 +138,21 @@ def decode_workspace_size(B: int, H: int, L_max: int, d_v: int, num_splits: int 
     return n.value
 
 
-def decode(q: torch.Tensor, rho: torch.Tensor, k_cache: torch.Tensor, v_cache: torch.Tensor,
+def decode(q: torch.Tensor, rho: Optional[torch.Tensor], k_cache: torch.Tensor, v_cache: torch.Tensor,
            seqlens: torch.Tensor, scale: Optional[float] = None, num_splits: int = 0,
            out: Optional[torch.Tensor] = None, workspace: Optional[torch.Tensor] = None,
            stream: Optional[torch.cuda.Stream] = None) -> torch.Tensor:
-    """One decode step. q, rho [B,H,d]; caches [B,H,L_max,d]; seqlens int32 [B] -> [B,H,d]."""
+    """One decode step. q, rho [B,H,d]; caches [B,H,L_max,d]; seqlens int32 [B] -> [B,H,d].
+
+    rho=None means rho = 0 exactly (plain softmax attention, the specialised kernels)."""
     lib = load()
     if q.dim() != 3:
         raise ValueError("q must be [B, H, d_qk]")
     B, H, dqk = q.shape
     L_max, dv = v_cache.shape[2], v_cache.shape[3]
     _check(q, "q", None, None)
-    _check(rho, "rho", q.dtype, q.device, (B, H, dqk))
+    if rho is not None:
+        _check(rho, "rho", q.dtype, q.device, (B, H, dqk))
     _check(k_cache, "k_cache", q.dtype, q.device, (B, H, L_max, dqk))
     _check(v_cache, "v_cache", q.dtype, q.device, (B, H, L_max, dv))
     _check(seqlens, "seqlens", torch.int32, q.device, (B,))
@@ -161,7 +168,8 @@ def decode(q: torch.Tensor, rho: torch.Tensor, k_cache: torch.Tensor, v_cache: t
         ws_ptr, ws_bytes = workspace.data_ptr(), workspace.numel() * workspace.element_size()
     if scale is None:
         scale = dqk ** -0.5
-    rc = lib.plx_attn_decode(_dtype_code(q), B, H, L_max, dqk, dv, q.data_ptr(), rho.data_ptr(),
+    rho_ptr = 0 if rho is None else rho.data_ptr()
+    rc = lib.plx_attn_decode(_dtype_code(q), B, H, L_max, dqk, dv, q.data_ptr(), rho_ptr,
                              k_cache.data_ptr(), v_cache.data_ptr(), seqlens.data_ptr(),
                              out.data_ptr(), float(scale), int(num_splits), ws_ptr, ws_bytes,
                              _stream_handle(stream, q.device))

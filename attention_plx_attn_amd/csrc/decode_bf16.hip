@@ -109,6 +109,8 @@ __device__ __forceinline__ void store_merged(const Merge& st, __bf16* o_bh, int 
 }
 
 // ------------------------------------------------------------------------------ split mode
+// PROBE = false (rho == NULL at the boundary): the softmax-only specialisation, see consume().
+template <bool PROBE>
 __global__ __launch_bounds__(NT, 2) void decode_split_bf16_d128_kernel(
     const __bf16* __restrict__ q, const __bf16* __restrict__ rho, const __bf16* __restrict__ kc,
     const __bf16* __restrict__ vc, const int32_t* __restrict__ seqlens, __bf16* __restrict__ o,
@@ -133,7 +135,8 @@ __global__ __launch_bounds__(NT, 2) void decode_split_bf16_d128_kernel(
     const auto rv = make_rsrc(vc + bh * (size_t)L_max * D, range);
 
     bf16x8 bqr[4];
-    decode::load_qr(make_rsrc(q + bh * D, 256u), make_rsrc(rho + bh * D, 256u), col, g, bqr);
+    decode::load_qr(make_rsrc(q + bh * D, 256u), make_rsrc(PROBE ? rho + bh * D : q, PROBE ? 256u : 0u),
+                    col, g, bqr);
 
     Acc acc;
     acc.reset();
@@ -147,13 +150,13 @@ __global__ __launch_bounds__(NT, 2) void decode_split_bf16_d128_kernel(
     if (kb0 < j1) decode::load_step(rk, rv, kb0, col, g, fa);
     for (; kb0 < j1; kb0 += 2 * STEP) {
         decode::load_step(rk, rv, kb0 + STEP, col, g, fb);
-        decode::consume(acc, fa, bqr, kb0, j1, c, ush[w], col, g);
+        decode::consume<PROBE>(acc, fa, bqr, kb0, j1, c, ush[w], col, g);
         if (kb0 + STEP >= j1) break;
         decode::load_step(rk, rv, kb0 + 2 * STEP, col, g, fa);
-        decode::consume(acc, fb, bqr, kb0 + STEP, j1, c, ush[w], col, g);
+        decode::consume<PROBE>(acc, fb, bqr, kb0 + STEP, j1, c, ush[w], col, g);
     }
 
-    decode::wave_totals(acc);
+    decode::wave_totals<PROBE>(acc);
     if (lane < 16) {
 #pragma unroll
         for (int e = 0; e < 8; ++e) {
@@ -323,7 +326,7 @@ __device__ __forceinline__ int boundary(const int* P, int B, int H, int W, int g
     return L.j > 0 ? L.F + L.n : x;
 }
 
-template <bool WHOLE>
+template <bool WHOLE, bool PROBE>
 __global__ __launch_bounds__(NT, 4) void decode_range_bf16_d128_kernel(
     const __bf16* __restrict__ q, const __bf16* __restrict__ rho, const __bf16* __restrict__ kc,
     const __bf16* __restrict__ vc, const int32_t* __restrict__ seqlens, __bf16* __restrict__ o,
@@ -382,7 +385,7 @@ __global__ __launch_bounds__(NT, 4) void decode_range_bf16_d128_kernel(
     // End of a piece: the whole (b, h) range writes o, a cut piece writes its partial to
     // slot 0 (piece starts inside the (b, h)) or 1 (piece starts at the (b, h) start).
     auto finish = [&](const Step& s) {
-        decode::wave_totals(acc);
+        decode::wave_totals<PROBE>(acc);
         const float l = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(acc.rsum), 0));
         const float beta = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(acc.rsum), 1));
         if (s.js == 0 && s.je == s.n) {
@@ -416,7 +419,7 @@ __global__ __launch_bounds__(NT, 4) void decode_range_bf16_d128_kernel(
         const Step s = next();
         // q and rho of the step's (b, h), reloaded every step (cache hits after the first):
         // lane (col, g) reads column col's dims 32 st + 8 g .. +7 and keeps them for col < 2.
-        const __bf16* qr_src = (col == 1 ? rho : q) + (size_t)s.it * D + 8 * g;
+        const __bf16* qr_src = (PROBE && col == 1 ? rho : q) + (size_t)s.it * D + 8 * g;
         u32x4 xq[4];
 #pragma unroll
         for (int st = 0; st < 4; ++st) xq[st] = *(const u32x4*)(qr_src + 32 * st);
@@ -426,8 +429,9 @@ __global__ __launch_bounds__(NT, 4) void decode_range_bf16_d128_kernel(
                           s.kb0, col, g, f);
         __builtin_amdgcn_sched_barrier(0);  // every load of the step is issued before any wait
 #pragma unroll
-        for (int st = 0; st < 4; ++st) bqr[st] = as_bf16x8(col < 2 ? xq[st] : u32x4{});
-        decode::consume(acc, f, bqr, s.kb0, s.je, c, ush[w], col, g);
+        for (int st = 0; st < 4; ++st)
+            bqr[st] = as_bf16x8(col == 0 || (PROBE && col == 1) ? xq[st] : u32x4{});
+        decode::consume<PROBE>(acc, f, bqr, s.kb0, s.je, c, ush[w], col, g);
         if (s.last) finish(s);
     }
 }
@@ -460,21 +464,22 @@ __global__ __launch_bounds__(NT) void decode_range_combine_kernel(
     store_merged(st, o + ((size_t)L.b * H + L.h) * D, lane);
 }
 
-}  // namespace
 
-hipError_t launch_decode_bf16_d128(const DecodeArgs& a, hipStream_t stream) {
+template <bool PROBE>
+hipError_t launch_decode(const DecodeArgs& a, hipStream_t stream) {
     const float c = a.scale * kLog2e;
+    const __bf16* rho = PROBE ? (const __bf16*)a.rho : (const __bf16*)a.q;
     if (a.waves > 0) {
         const int grid = a.waves / NW;
         const size_t lds = (size_t)(a.B + 1) * sizeof(int);
         if (a.whole)
-            hipLaunchKernelGGL(decode_range_bf16_d128_kernel<true>, dim3(grid), dim3(NT), lds,
-                               stream, (const __bf16*)a.q, (const __bf16*)a.rho,
-                               (const __bf16*)a.k, (const __bf16*)a.v, a.seqlens, (__bf16*)a.o,
-                               a.ws, a.B, a.H, a.L_max, c);
+            hipLaunchKernelGGL((decode_range_bf16_d128_kernel<true, PROBE>), dim3(grid), dim3(NT),
+                               lds, stream, (const __bf16*)a.q, rho, (const __bf16*)a.k,
+                               (const __bf16*)a.v, a.seqlens, (__bf16*)a.o, a.ws, a.B, a.H,
+                               a.L_max, c);
         else
-            hipLaunchKernelGGL(decode_range_bf16_d128_kernel<false>, dim3(grid), dim3(NT), lds,
-                               stream, (const __bf16*)a.q, (const __bf16*)a.rho,
+            hipLaunchKernelGGL((decode_range_bf16_d128_kernel<false, PROBE>), dim3(grid),
+                               dim3(NT), lds, stream, (const __bf16*)a.q, rho,
                                (const __bf16*)a.k, (const __bf16*)a.v, a.seqlens, (__bf16*)a.o,
                                a.ws, a.B, a.H, a.L_max, c);
         hipError_t e = hipGetLastError();
@@ -486,15 +491,20 @@ hipError_t launch_decode_bf16_d128(const DecodeArgs& a, hipStream_t stream) {
     }
     const int BH = a.B * a.H;
     dim3 grid(a.splits, a.H, a.B);
-    hipLaunchKernelGGL(decode_split_bf16_d128_kernel, grid, dim3(NT), 0, stream,
-                       (const __bf16*)a.q, (const __bf16*)a.rho, (const __bf16*)a.k,
-                       (const __bf16*)a.v, a.seqlens, (__bf16*)a.o, a.ws, a.H, a.L_max, a.splits,
-                       c);
+    hipLaunchKernelGGL(decode_split_bf16_d128_kernel<PROBE>, grid, dim3(NT), 0, stream,
+                       (const __bf16*)a.q, rho, (const __bf16*)a.k, (const __bf16*)a.v,
+                       a.seqlens, (__bf16*)a.o, a.ws, a.H, a.L_max, a.splits, c);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess || a.splits == 1) return e;
     hipLaunchKernelGGL(decode_combine_kernel, dim3(BH), dim3(NT), 0, stream, (const float*)a.ws,
                        (__bf16*)a.o, a.splits);
     return hipGetLastError();
+}
+
+}  // namespace
+
+hipError_t launch_decode_bf16_d128(const DecodeArgs& a, hipStream_t stream) {
+    return a.rho ? launch_decode<true>(a, stream) : launch_decode<false>(a, stream);
 }
 
 }  // namespace plx

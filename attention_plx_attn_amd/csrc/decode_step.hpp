@@ -79,6 +79,9 @@ __device__ __forceinline__ void load_qr(__amdgpu_buffer_rsrc_t rq, __amdgpu_buff
 
 // Consume the step whose loads are in f: rows kb0 + ... count while below je.
 // ush: this wave's [2][KB] LDS exchange area (w and w t per row).
+// PROBE = false is the softmax-only specialisation (rho = 0 exactly, column 1 of bqr zero):
+// A2 stays 0 and is not accumulated; every other value is computed as with PROBE and rho = 0.
+template <bool PROBE>
 __device__ __forceinline__ void consume(Acc& s, const Frag& f, const bf16x8 (&bqr)[4], int kb0,
                                         int je, float c, float (*ush)[KB], int col, int g) {
     // Score tile: row = key (16 per tile), column 0 = q.k, column 1 = rho.k.
@@ -105,7 +108,7 @@ __device__ __forceinline__ void consume(Acc& s, const Frag& f, const bf16x8 (&bq
 #pragma unroll
         for (int e = 0; e < 8; ++e) {
             s.a1[e] *= alpha;
-            s.a2[e] *= alpha;
+            if constexpr (PROBE) s.a2[e] *= alpha;
         }
         s.m_run = mb;
     }
@@ -139,7 +142,7 @@ __device__ __forceinline__ void consume(Acc& s, const Frag& f, const bf16x8 (&bq
 #pragma unroll
     for (int r4 = 0; r4 < VR / 4; ++r4) {
         const f32x4 u0 = *(const f32x4*)&ush[0][VR * g + 4 * r4];
-        const f32x4 u1 = *(const f32x4*)&ush[1][VR * g + 4 * r4];
+        const f32x4 u1 = PROBE ? *(const f32x4*)&ush[1][VR * g + 4 * r4] : f32x4{};
 #pragma unroll
         for (int rr = 0; rr < 4; ++rr) {
             const u32x4 x = f.v[4 * r4 + rr];
@@ -148,8 +151,10 @@ __device__ __forceinline__ void consume(Acc& s, const Frag& f, const bf16x8 (&bq
                 const float vlo = bf16_lo(x[p]), vhi = bf16_hi(x[p]);
                 s.a1[2 * p] = fmaf(u0[rr], vlo, s.a1[2 * p]);
                 s.a1[2 * p + 1] = fmaf(u0[rr], vhi, s.a1[2 * p + 1]);
-                s.a2[2 * p] = fmaf(u1[rr], vlo, s.a2[2 * p]);
-                s.a2[2 * p + 1] = fmaf(u1[rr], vhi, s.a2[2 * p + 1]);
+                if constexpr (PROBE) {
+                    s.a2[2 * p] = fmaf(u1[rr], vlo, s.a2[2 * p]);
+                    s.a2[2 * p + 1] = fmaf(u1[rr], vhi, s.a2[2 * p + 1]);
+                }
             }
         }
     }
@@ -160,13 +165,16 @@ __device__ __forceinline__ void consume(Acc& s, const Frag& f, const bf16x8 (&bq
 
 // Wave totals: values over the 4 row groups (lanes 0..15 then hold dims 8 col .. +7), l in
 // lane 0 and beta in lane 1.
+template <bool PROBE>
 __device__ __forceinline__ void wave_totals(Acc& s) {
 #pragma unroll
     for (int e = 0; e < 8; ++e) {
         s.a1[e] += shfl_xor(s.a1[e], 16);
         s.a1[e] += shfl_xor(s.a1[e], 32);
-        s.a2[e] += shfl_xor(s.a2[e], 16);
-        s.a2[e] += shfl_xor(s.a2[e], 32);
+        if constexpr (PROBE) {
+            s.a2[e] += shfl_xor(s.a2[e], 16);
+            s.a2[e] += shfl_xor(s.a2[e], 32);
+        }
     }
     s.rsum += shfl_xor(s.rsum, 16);
     s.rsum += shfl_xor(s.rsum, 32);

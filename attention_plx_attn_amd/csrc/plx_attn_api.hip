@@ -145,7 +145,7 @@ plx_status_t plx_attn_prefill(plx_dtype_t dtype, int32_t B, int32_t H, int32_t T
                               const void* v, const void* rho, void* o, float softmax_scale,
                               void* stream) {
     if (dtype != PLX_F32 && dtype != PLX_BF16) return PLX_ERR_INVALID_ARG;
-    if (!q || !k || !v || !rho || !o) return PLX_ERR_NULL_POINTER;
+    if (!q || !k || !v || !o) return PLX_ERR_NULL_POINTER;  // rho == NULL: softmax only
     if (B < 1 || H < 1 || T < 1 || d_qk < 1 || d_v < 1) return PLX_ERR_INVALID_SHAPE;
     if (!std::isfinite(softmax_scale) || softmax_scale < 0.f) return PLX_ERR_INVALID_ARG;
     const long long esize = dtype == PLX_BF16 ? 2 : 4;
@@ -158,7 +158,7 @@ plx_status_t plx_attn_prefill(plx_dtype_t dtype, int32_t B, int32_t H, int32_t T
     if (!ok) return PLX_ERR_UNSUPPORTED;
     if (dtype == PLX_F32 && (B > 65535 || H > 65535)) return PLX_ERR_INVALID_SHAPE;
     if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(rho) || !aligned16(o))
-        return PLX_ERR_MISALIGNED;
+        return PLX_ERR_MISALIGNED;  // aligned16(NULL) holds
 
     int cus = 1;
     if (dtype == PLX_BF16) {
@@ -204,7 +204,7 @@ plx_status_t plx_attn_decode(plx_dtype_t dtype, int32_t B, int32_t H, int32_t L_
                              int32_t num_splits, void* workspace, size_t workspace_bytes,
                              void* stream) {
     if (dtype != PLX_F32 && dtype != PLX_BF16) return PLX_ERR_INVALID_ARG;
-    if (!q || !rho || !k_cache || !v_cache || !seqlens || !o) return PLX_ERR_NULL_POINTER;
+    if (!q || !k_cache || !v_cache || !seqlens || !o) return PLX_ERR_NULL_POINTER;
     plx_status_t st = check_decode_shape(B, H, L_max, d_v);
     if (st != PLX_OK) return st;
     if (d_qk < 1) return PLX_ERR_INVALID_SHAPE;

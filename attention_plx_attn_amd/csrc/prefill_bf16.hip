@@ -93,6 +93,10 @@ __device__ __forceinline__ float max_across_row_groups(float x) {
     return max_with_other_half(x);
 }
 
+// PROBE = false: the softmax-only specialisation (rho = 0 exactly): no R K^T products, no P2,
+// no O2 and no beta, so o = O1 / l. With rho = 0 the full kernel computes the same values in
+// the same order (P2 = 0, beta = 0, o = O1 (1 + 0) / l - 0), so both give identical bits.
+template <bool PROBE>
 __global__ __launch_bounds__(NT, 1) void prefill_bf16_d128_kernel(
     const __bf16* __restrict__ q, const __bf16* __restrict__ k, const __bf16* __restrict__ v,
     const __bf16* __restrict__ rho, __bf16* __restrict__ o, int BH, int T, int nqb, float c,
@@ -126,7 +130,7 @@ __global__ __launch_bounds__(NT, 1) void prefill_bf16_d128_kernel(
 #pragma unroll
         for (int st = 0; st < 4; ++st) {
             xq[st] = as_bf16x8(load16(rq, qoff + 64u * st));
-            xr[st] = as_bf16x8(load16(rr, qoff + 64u * st));
+            if constexpr (PROBE) xr[st] = as_bf16x8(load16(rr, qoff + 64u * st));
         }
     };
 
@@ -192,7 +196,7 @@ __global__ __launch_bounds__(NT, 1) void prefill_bf16_d128_kernel(
             for (int s = 0; s < 4; ++s) {
                 const bf16x8 kf = *(const bf16x8*)(Kl + 16 * kb * KS * 2 + 64 * s);
                 S[kb] = mfma16(kf, xq[s], S[kb]);
-                Tp[kb] = mfma16(kf, xr[s], Tp[kb]);
+                if constexpr (PROBE) Tp[kb] = mfma16(kf, xr[s], Tp[kb]);
             }
         }
         __builtin_amdgcn_iglp_opt(0);
@@ -209,7 +213,7 @@ __global__ __launch_bounds__(NT, 1) void prefill_bf16_d128_kernel(
             const bf16x8 vf = *(const bf16x8*)(Vl + vlane[db & 3] + 16 * db * VS * 2 +
                                                64 * (G ^ (db >> 2)));
             a1[db] = mfma16(vf, p1, a1[db]);
-            a2[db] = mfma16(vf, p2, a2[db]);
+            if constexpr (PROBE) a2[db] = mfma16(vf, p2, a2[db]);
         }
         __builtin_amdgcn_iglp_opt(0);
     };
@@ -244,10 +248,10 @@ __global__ __launch_bounds__(NT, 1) void prefill_bf16_d128_kernel(
 #pragma unroll
             for (int db = 0; db < 8; ++db) {
                 a1[db] *= alpha;
-                a2[db] *= alpha;
+                if constexpr (PROBE) a2[db] *= alpha;
             }
             lsum *= alpha;
-            bsum *= alpha;
+            if constexpr (PROBE) bsum *= alpha;
             m_run = mn;
         }
 #pragma unroll
@@ -263,9 +267,13 @@ __global__ __launch_bounds__(NT, 1) void prefill_bf16_d128_kernel(
                     w1 = S[kb][i0 + 1] == -INFINITY ? 0.f : w1;
                 }
                 p1[e] = pack_bf16x2(w0, w1);
-                p2[e] = pack_bf16x2(w0 * Tp[kb][i0], w1 * Tp[kb][i0 + 1]);
                 lsum = add_bf16x2(p1[e], lsum);
-                bsum = add_bf16x2(p2[e], bsum);
+                if constexpr (PROBE) {
+                    p2[e] = pack_bf16x2(w0 * Tp[kb][i0], w1 * Tp[kb][i0 + 1]);
+                    bsum = add_bf16x2(p2[e], bsum);
+                } else {
+                    p2[e] = 0u;
+                }
             }
             values(t, G, __builtin_bit_cast(bf16x8, u32x4{p1[0], p1[1], p1[2], p1[3]}),
                    __builtin_bit_cast(bf16x8, u32x4{p2[0], p2[1], p2[2], p2[3]}));
@@ -329,7 +337,7 @@ __global__ __launch_bounds__(NT, 1) void prefill_bf16_d128_kernel(
             if ((t0 + kt) & 1) __syncthreads();
         };
 #pragma unroll
-        for (int db = 0; db < 8; ++db) a1[db] = a2[db] = f32x4{};
+        for (int db = 0; db < 8; ++db) a1[db] = a2[db] = f32x4{};  // a2 stays 0 without PROBE
         lsum = bsum = 0.f;
         m_run = -INFINITY;
         const int qi = cur.q0 + 16 * w + col;
@@ -365,11 +373,13 @@ __global__ __launch_bounds__(NT, 1) void prefill_bf16_d128_kernel(
         // ---- epilogue: l and beta over the four lanes of each query; o = (A1/l)(1 + beta/l)
         // - A2/l, rounded to bf16.
         lsum += __int_as_float(__builtin_amdgcn_ds_swizzle(__float_as_int(lsum), 0x401F));
-        bsum += __int_as_float(__builtin_amdgcn_ds_swizzle(__float_as_int(bsum), 0x401F));
         {
             const auto r1 = __builtin_amdgcn_permlane32_swap(__float_as_int(lsum),
                                                              __float_as_int(lsum), false, false);
             lsum = __int_as_float(r1[0]) + __int_as_float(r1[1]);
+        }
+        if constexpr (PROBE) {
+            bsum += __int_as_float(__builtin_amdgcn_ds_swizzle(__float_as_int(bsum), 0x401F));
             const auto r2 = __builtin_amdgcn_permlane32_swap(__float_as_int(bsum),
                                                              __float_as_int(bsum), false, false);
             bsum = __int_as_float(r2[0]) + __int_as_float(r2[1]);
@@ -382,7 +392,8 @@ __global__ __launch_bounds__(NT, 1) void prefill_bf16_d128_kernel(
             for (int db = 0; db < 8; ++db) {
                 float y[4];
 #pragma unroll
-                for (int i = 0; i < 4; ++i) y[i] = inv * (a1[db][i] * one_tb - a2[db][i]);
+                for (int i = 0; i < 4; ++i)
+                    y[i] = PROBE ? inv * (a1[db][i] * one_tb - a2[db][i]) : inv * a1[db][i];
                 *(u32x2*)(orow + 16 * db + 4 * gq) =
                     u32x2{pack_bf16x2(y[0], y[1]), pack_bf16x2(y[2], y[3])};
             }
@@ -408,9 +419,16 @@ hipError_t launch_prefill_bf16_d128(const PrefillArgs& a, hipStream_t stream) {
         grid -= grid % 8;
     }
     if (grid < 1 || grid > 0x7fffffffLL) return hipErrorInvalidConfiguration;
-    hipLaunchKernelGGL(prefill_bf16_d128_kernel, dim3((unsigned)grid), dim3(NT), 0, stream,
-                       (const __bf16*)a.q, (const __bf16*)a.k, (const __bf16*)a.v,
-                       (const __bf16*)a.rho, (__bf16*)a.o, BH, a.T, nqb, a.scale * kLog2e, ncls);
+    if (a.rho)
+        hipLaunchKernelGGL(prefill_bf16_d128_kernel<true>, dim3((unsigned)grid), dim3(NT), 0,
+                           stream, (const __bf16*)a.q, (const __bf16*)a.k, (const __bf16*)a.v,
+                           (const __bf16*)a.rho, (__bf16*)a.o, BH, a.T, nqb, a.scale * kLog2e,
+                           ncls);
+    else
+        hipLaunchKernelGGL(prefill_bf16_d128_kernel<false>, dim3((unsigned)grid), dim3(NT), 0,
+                           stream, (const __bf16*)a.q, (const __bf16*)a.k, (const __bf16*)a.v,
+                           (const __bf16*)a.q, (__bf16*)a.o, BH, a.T, nqb, a.scale * kLog2e,
+                           ncls);
     return hipGetLastError();
 }
 

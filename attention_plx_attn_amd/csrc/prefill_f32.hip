@@ -29,7 +29,7 @@ __global__ __launch_bounds__(kRows) void prefill_f32_kernel(
 #pragma unroll
     for (int e = 0; e < D; ++e) {
         qi[e] = valid ? q[(slice + i) * D + e] : 0.f;
-        ri[e] = valid ? rho[(slice + i) * D + e] : 0.f;
+        ri[e] = valid && rho ? rho[(slice + i) * D + e] : 0.f;  // no rho: the softmax-only case
         a1[e] = 0.f;
         a2[e] = 0.f;
     }

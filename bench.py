@@ -22,6 +22,8 @@ fp64 oracle's streaming form on the host cores.
 Extra modes:
   --sweep [OUT_MD]        time the long prefill (1x32x32768) and the 18 decode grid cells
                           (H16 d128, B x ctx) instead of the step; one JSON line each
+  --compare [OUT_MD]      time Parallax against softmax-only attention (rho = NULL) with the
+                          same inputs and with twice the heads (equal matrix FLOPs)
 Used to produce the committed rocprofv3 summaries:
   --calibrate-copy        also run a reference kernel of known traffic (1 GiB read + 1 GiB
                           written), which scales the counters
@@ -175,9 +177,9 @@ def _stats_us(ms_list):
 def sweep(out_md):
     """Times the long prefill (1x32x32768) and every decode grid cell (H16 d128).
 
-    Decode cells: before each timed call a 512 MiB buffer is written, which evicts the L2 and
-    the 256 MB last-level cache, so every call streams its cache from HBM; HIP events bracket
-    the decode call only. Prints one JSON line per workload and writes a markdown table."""
+    Decode cells: before each timed call a 1 GiB buffer is read, which evicts the L2s and the
+    256 MB last-level cache, so every call streams its cache from HBM; HIP events bracket the
+    decode call only. Prints one JSON line per workload and writes a markdown table."""
     import torch
 
     import attention_plx_attn_amd as plx
@@ -284,6 +286,90 @@ def sweep(out_md):
     return 0
 
 
+def compare(out_md):
+    """The softmax-only comparisons: Parallax against plain softmax attention (rho = NULL, the
+    specialised kernels) on the same q, k, v and cache (I/O-matched), and against softmax
+    attention with twice the heads, which does the same matrix FLOPs as Parallax
+    (compute-matched: Parallax's two score products and two value products per pair). Prefill
+    4x16x2048 and decode 1x16x32768, bf16, d = 128; HIP events, median of 20 calls (prefill
+    after 0.5 s of untimed calls; decode with a 1 GiB read before each call)."""
+    import torch
+
+    import attention_plx_attn_amd as plx
+
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    stream = torch.cuda.current_stream(dev)
+    g = torch.Generator(device=dev)
+    g.manual_seed(11)
+    flush = torch.ones(1024 * 1024 * 1024 // 4, dtype=torch.float32, device=dev)
+    sink = torch.empty(1, dtype=torch.float32, device=dev)
+
+    def bf(shape, s=1.0):
+        return (s * torch.randn(shape, generator=g, device=dev)).to(torch.bfloat16)
+
+    def timed(call, cold, n=20):
+        if not cold:
+            t_end = time.perf_counter() + 0.5
+            while time.perf_counter() < t_end:
+                call()
+                torch.cuda.synchronize()
+        for _ in range(3):
+            call()
+        ts = []
+        for _ in range(n):
+            if cold:
+                torch.sum(flush, dim=0, keepdim=True, out=sink)
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record(stream)
+            call()
+            e1.record(stream)
+            torch.cuda.synchronize()
+            ts.append(e0.elapsed_time(e1))
+        return _stats_us(ts)["median_us"]
+
+    rows = []
+    B, T, d = 4, 2048, 128
+    for name, H, probe in (("Parallax", 16, True), ("softmax only, I/O-matched", 16, False),
+                           ("softmax only, compute-matched (2x heads)", 32, False)):
+        q, k, v = bf((B, H, T, d)), bf((B, H, T, d)), bf((B, H, T, d))
+        rho = bf((B, H, T, d), 0.1) if probe else None
+        o = torch.empty_like(q)
+        us = timed(lambda: plx.prefill(q, k, v, rho, d ** -0.5, out=o), cold=False)
+        fl = (8 if probe else 4) * d * B * H * T * (T + 1) // 2
+        rows.append({"kernel": "prefill", "variant": name, "shape": f"{B}x{H}x{T} d{d}",
+                     "median_us": us, "tflops": round(fl / us / 1e6, 1)})
+        print(json.dumps(rows[-1]), flush=True)
+        del q, k, v, rho, o
+    L = 32768
+    for name, H, probe in (("Parallax", 16, True), ("softmax only, I/O-matched", 16, False),
+                           ("softmax only, compute-matched (2x heads)", 32, False)):
+        q, kc, vc = bf((1, H, d)), bf((1, H, L, d)), bf((1, H, L, d))
+        rho = bf((1, H, d)) if probe else None
+        sl = torch.full((1,), L, dtype=torch.int32, device=dev)
+        o = torch.empty_like(q)
+        ws = torch.empty(max(plx.decode_workspace_size(1, H, L, d) // 4, 1),
+                         dtype=torch.float32, device=dev)
+        us = timed(lambda: plx.decode(q, rho, kc, vc, sl, d ** -0.5, out=o, workspace=ws),
+                   cold=True)
+        nbytes = decode_bytes([L], H, d) - (0 if probe else H * d * 2)
+        rows.append({"kernel": "decode", "variant": name, "shape": f"1x{H}x{L} d{d}",
+                     "median_us": us, "hbm_gbps": round(nbytes / us / 1e3, 1)})
+        print(json.dumps(rows[-1]), flush=True)
+        del q, kc, vc, rho, o, ws
+        torch.cuda.empty_cache()
+    if out_md:
+        base = {r["kernel"]: r["median_us"] for r in rows if r["variant"] == "Parallax"}
+        with open(out_md, "w") as fh:
+            fh.write("| kernel | variant | shape | median us | rate | time / Parallax |\n")
+            fh.write("|---|---|---|---|---|---|\n")
+            for r in rows:
+                rate = (f"{r['tflops']} TFLOP/s" if "tflops" in r else f"{r['hbm_gbps']} GB/s")
+                fh.write(f"| {r['kernel']} | {r['variant']} | {r['shape']} | {r['median_us']} | "
+                         f"{rate} | {r['median_us'] / base[r['kernel']]:.3f} |\n")
+    return 0
+
+
 # ------------------------------------------------------------------------------ main
 
 def main():
@@ -302,6 +388,9 @@ def main():
     ap.add_argument("--summarize-counters", nargs=2, metavar=("FETCH_CSV_GLOB", "WRITE_CSV_GLOB"))
     ap.add_argument("--sweep", metavar="OUT_MD", nargs="?", const="",
                     help="time the long prefill and the decode grid instead of the step")
+    ap.add_argument("--compare", metavar="OUT_MD", nargs="?", const="",
+                    help="time Parallax against softmax-only attention (I/O- and "
+                         "compute-matched) instead of the step")
     args = ap.parse_args()
 
     if args.summarize_counters:
@@ -316,6 +405,8 @@ def main():
 
     if args.sweep is not None:
         return sweep(args.sweep)
+    if args.compare is not None:
+        return compare(args.compare)
 
     import torch
 

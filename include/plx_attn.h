@@ -69,6 +69,8 @@ typedef enum { PLX_F32 = 0, PLX_BF16 = 1 } plx_dtype_t;
  *
  *   q, k, rho : [B, H, T, d_qk]   v, o : [B, H, T, d_v]   (dtype for all five)
  *   Key j is visible to query i iff j <= i (top-left aligned, T_q = T_k = T).
+ *   rho == NULL means rho = 0 exactly: plain softmax attention, computed by a specialisation
+ *   without the probe branch; its output is bit-identical to a call with an all-zero rho.
  *
  * Built combinations: (PLX_BF16, d_qk = d_v = 128) on the matrix cores;
  * (PLX_F32, d_qk = d_v in {16, 32, 64}) on the vector ALUs.
@@ -103,6 +105,8 @@ plx_status_t plx_attn_decode_workspace_size(int32_t B, int32_t H, int32_t L_max,
  *
  *   q, rho   : [B, H, d_qk]            k_cache : [B, H, L_max, d_qk]
  *   v_cache  : [B, H, L_max, d_v]      o       : [B, H, d_v]
+ *   rho == NULL means rho = 0 exactly (plain softmax attention, a specialisation without
+ *              the probe accumulations; bit-identical to a call with an all-zero rho).
  *   seqlens  : device int32 [B]; query b attends to cache rows [0, n_b) with
  *              n_b = min(max(seqlens[b], 0), L_max); n_b == 0 gives o[b] = 0.
  *              Rows at or beyond n_b are never read, so they may hold anything.

@@ -42,6 +42,7 @@ def _prefill(lib, dtype=1, B=1, H=1, T=8, dqk=128, dv=128, ptrs=(A,) * 5, scale=
 def test_prefill_validation(lib):
     assert _prefill(lib, ptrs=(0, A, A, A, A)) == 1
     assert _prefill(lib, ptrs=(A, A, A, A, 0)) == 1
+    assert _prefill(lib, ptrs=(A, A, A, 0, A), T=0) == 2  # rho may be NULL (softmax only)
     assert _prefill(lib, T=0) == 2
     assert _prefill(lib, B=-1) == 2
     assert _prefill(lib, H=0) == 2
@@ -68,6 +69,7 @@ def test_decode_validation(lib):
     assert _decode(lib, sl=0) == 1
     assert _decode(lib, kc=0) == 1
     assert _decode(lib, L=0) == 2
+    assert _decode(lib, rho=0, L=0) == 2                  # rho may be NULL (softmax only)
     assert _decode(lib, L=1 << 23) == 2
     assert _decode(lib, B=70000) == 2
     assert _decode(lib, scale=float("nan")) == 3

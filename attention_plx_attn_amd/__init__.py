@@ -5,7 +5,8 @@ Python entry points over the C ABI of ``libplx_attn.so`` (include/plx_attn.h):
 * ``prefill(q, k, v, rho, scale=None)`` -- causal prefill, [B,H,T,d] tensors;
 * ``decode(q, rho, k_cache, v_cache, seqlens, scale=None, num_splits=0)`` -- one decode
   step over a contiguous per-sequence KV cache;
-* ``decode_num_splits`` / ``decode_workspace_size`` -- the split plan of a decode call.
+* ``decode_num_splits`` / ``decode_workspace_size`` -- the split plan of a decode call;
+* ``probe(x, w_r, H, ...)`` -- the probe producer rho = gate * RoPE(RMSNorm(x W_R^T)).
 
 All arithmetic runs in the HIP kernels; torch only supplies device memory and streams.
 """
@@ -18,4 +19,5 @@ from ._lib import (  # noqa: F401
     header_functions,
     load,
     prefill,
+    probe,
 )

@@ -51,6 +51,8 @@ def load() -> ctypes.CDLL:
     lib.plx_attn_decode.argtypes = ([ctypes.c_int] + [i32] * 5 + [vp] * 6 +
                                     [f32, i32, vp, ctypes.c_size_t, vp])
     lib.plx_attn_decode.restype = ctypes.c_int
+    lib.plx_attn_probe.argtypes = [ctypes.c_int] + [i32] * 5 + [vp] * 5 + [f32, f32, vp, vp]
+    lib.plx_attn_probe.restype = ctypes.c_int
     lib.plx_status_string.argtypes = [ctypes.c_int]
     lib.plx_status_string.restype = ctypes.c_char_p
     _lib = lib
@@ -175,4 +177,38 @@ def decode(q: torch.Tensor, rho: Optional[torch.Tensor], k_cache: torch.Tensor, 
                              _stream_handle(stream, q.device))
     if rc != 0:
         raise PlxError(rc, "plx_attn_decode")
+    return out
+
+
+def probe(x: torch.Tensor, w_r: torch.Tensor, H: int, gamma: Optional[torch.Tensor] = None,
+          gate: Optional[torch.Tensor] = None, positions: Optional[torch.Tensor] = None,
+          eps: float = 1e-6, rope_base: float = 0.0, out: Optional[torch.Tensor] = None,
+          stream: Optional[torch.cuda.Stream] = None) -> torch.Tensor:
+    """Probe producer: x [B,T,C], w_r [H*d,C] -> rho [B,H,T,d] =
+    gate_h * RoPE(gamma * RMSNorm_head(x W_R^T)). gamma [d], gate [H] float32; positions
+    int32 [B] (token t of sequence b is at positions[b] + t); rope_base 0 = no rotation."""
+    lib = load()
+    if x.dim() != 3:
+        raise ValueError("x must be [B, T, C]")
+    B, T, C = x.shape
+    if w_r.dim() != 2 or w_r.shape[1] != C or w_r.shape[0] % H != 0:
+        raise ValueError(f"w_r has shape {tuple(w_r.shape)}, expected [H*d, {C}]")
+    d = w_r.shape[0] // H
+    _check(x, "x", None, None)
+    _check(w_r, "w_r", x.dtype, x.device, (H * d, C))
+    ptrs = []
+    for t, name, shape, dt in ((gamma, "gamma", (d,), torch.float32),
+                               (gate, "gate", (H,), torch.float32),
+                               (positions, "positions", (B,), torch.int32)):
+        if t is not None:
+            _check(t, name, dt, x.device, shape)
+        ptrs.append(0 if t is None else t.data_ptr())
+    if out is None:
+        out = torch.empty((B, H, T, d), dtype=x.dtype, device=x.device)
+    _check(out, "out", x.dtype, x.device, (B, H, T, d))
+    rc = lib.plx_attn_probe(_dtype_code(x), B, T, C, H, d, x.data_ptr(), w_r.data_ptr(), *ptrs,
+                            float(eps), float(rope_base), out.data_ptr(),
+                            _stream_handle(stream, x.device))
+    if rc != 0:
+        raise PlxError(rc, "plx_attn_probe")
     return out

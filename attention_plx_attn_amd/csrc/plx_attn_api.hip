@@ -231,4 +231,27 @@ plx_status_t plx_attn_decode(plx_dtype_t dtype, int32_t B, int32_t H, int32_t L_
     return e == hipSuccess ? PLX_OK : PLX_ERR_HIP;
 }
 
+plx_status_t plx_attn_probe(plx_dtype_t dtype, int32_t B, int32_t T, int32_t C, int32_t H,
+                            int32_t d, const void* x, const void* w_r, const float* gamma,
+                            const float* gate, const int32_t* positions, float eps,
+                            float rope_base, void* rho, void* stream) {
+    if (dtype != PLX_F32 && dtype != PLX_BF16) return PLX_ERR_INVALID_ARG;
+    if (!x || !w_r || !rho) return PLX_ERR_NULL_POINTER;
+    if (B < 1 || T < 1 || C < 1 || H < 1 || d < 1) return PLX_ERR_INVALID_SHAPE;
+    if ((long long)B * T * C * 2 >= (1LL << 31) || (long long)d * C * 2 >= (1LL << 31) ||
+        H > 65535 || (long long)B * T > (1LL << 36))
+        return PLX_ERR_INVALID_SHAPE;
+    if (!std::isfinite(eps) || eps < 0.f || !std::isfinite(rope_base) ||
+        (rope_base != 0.f && !(rope_base > 1.f)))
+        return PLX_ERR_INVALID_ARG;
+    if (!(dtype == PLX_BF16 && d == 128) || C % 8 != 0) return PLX_ERR_UNSUPPORTED;
+    if (!aligned16(x) || !aligned16(w_r) || !aligned16(rho) || !aligned16(gamma) ||
+        (reinterpret_cast<uintptr_t>(gate) & 3u) ||
+        (reinterpret_cast<uintptr_t>(positions) & 3u))
+        return PLX_ERR_MISALIGNED;
+    plx::ProbeArgs a{B, T, C, H, x, w_r, gamma, gate, positions, rho, eps, rope_base};
+    const hipError_t e = plx::launch_probe_bf16_d128(a, static_cast<hipStream_t>(stream));
+    return e == hipSuccess ? PLX_OK : PLX_ERR_HIP;
+}
+
 }  // extern "C"

@@ -38,9 +38,21 @@ constexpr int kDecodeRecord = 2 * 128 + 4;  // A1[128], A2[128], m, l, beta, pad
 constexpr int kDecodeRangeMaxB = 8192;      // wave-range mode keeps B + 1 prefix sums in LDS
 constexpr int kDecodeRangeMaxWaves = 1 << 16;
 
+struct ProbeArgs {
+    int B, T, C, H;            // tokens [B, T], input width C, heads H (d = 128)
+    const void* x;             // [B, T, C]
+    const void* w_r;           // [H * d, C]
+    const float* gamma;        // [d] RMSNorm weight or nullptr (1)
+    const float* gate;         // [H] per-head multiplier or nullptr (1)
+    const int32_t* positions;  // [B] position of token 0 of each sequence, or nullptr (0)
+    void* rho;                 // [B, H, T, d]
+    float eps, rope_base;      // rope_base 0: no rotation
+};
+
 bool prefill_f32_supported(int d);
 hipError_t launch_prefill_f32(const PrefillArgs& a, hipStream_t stream);
 hipError_t launch_prefill_bf16_d128(const PrefillArgs& a, hipStream_t stream);
 hipError_t launch_decode_bf16_d128(const DecodeArgs& a, hipStream_t stream);
+hipError_t launch_probe_bf16_d128(const ProbeArgs& a, hipStream_t stream);
 
 }  // namespace plx

@@ -24,6 +24,8 @@ Extra modes:
                           (H16 d128, B x ctx) instead of the step; one JSON line each
   --compare [OUT_MD]      time Parallax against softmax-only attention (rho = NULL) with the
                           same inputs and with twice the heads (equal matrix FLOPs)
+  --probe-producer [OUT_MD]  time the probe producer (x W_R^T, RMSNorm, RoPE, gate) on the
+                          prefill step's tokens at C = 32 and C = 2048
 Used to produce the committed rocprofv3 summaries:
   --calibrate-copy        also run a reference kernel of known traffic (1 GiB read + 1 GiB
                           written), which scales the counters
@@ -52,6 +54,8 @@ PREFILL_KERNEL = "prefill_bf16_d128_kernel"
 COPY_BYTES = 1 << 30
 PREFILL_SOURCES = ("attention_plx_attn_amd/csrc/prefill_bf16.hip",
                    "attention_plx_attn_amd/csrc/plx_device.hpp")
+DECODE_SOURCES = ("attention_plx_attn_amd/csrc/decode_bf16.hip",
+                  "attention_plx_attn_amd/csrc/decode_step.hpp")
 
 
 def code_only(text: str) -> str:
@@ -162,7 +166,43 @@ def cpu_baseline(px, dx):
                    f"streaming form ({t_pre:.2f} s); decode B1 H16 L32768 in the same form "
                    f"({t_dec:.2f} s)"),
         "decode_tokens_per_s": dx["q"].shape[0] / t_dec,
+        "cpu_model": _cpu_model(),
     }
+
+
+def _cpu_model() -> str:
+    try:
+        with open("/proc/cpuinfo", encoding="utf-8") as fh:
+            for ln in fh:
+                if ln.startswith("model name"):
+                    return ln.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
+
+
+def streaming_read_gbps(torch, dev, stream) -> float:
+    """Measured HBM read rate of this board: a sum over 1 GiB of fp32 (read once, a few KB
+    written), median of 10 calls after a short warm-up, HIP events on the launch stream."""
+    x = torch.ones(1024 * 1024 * 1024 // 4, dtype=torch.float32, device=dev)
+    sink = torch.empty(1, dtype=torch.float32, device=dev)
+    for _ in range(5):
+        torch.sum(x, dim=0, keepdim=True, out=sink)
+    ts = []
+    for _ in range(10):
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        torch.sum(x, dim=0, keepdim=True, out=sink)
+        e1.record(stream)
+        torch.cuda.synchronize()
+        ts.append(e0.elapsed_time(e1))
+    del x
+    torch.cuda.empty_cache()
+    return x_bytes_gbps(1024 ** 3, sorted(ts)[len(ts) // 2])
+
+
+def x_bytes_gbps(nbytes: int, ms: float) -> float:
+    return nbytes / (ms * 1e-3) / 1e9
 
 
 # ------------------------------------------------------------------------------ sweep
@@ -370,6 +410,67 @@ def compare(out_md):
     return 0
 
 
+def probe_producer(out_md):
+    """Times the probe producer rho = gate * RoPE(gamma * RMSNorm_head(x W_R^T)) on the prefill
+    step's tokens (4 x 2048, H = 16, d = 128) at the configs' input width C = 32 (bound by
+    writing rho) and at C = 2048 (a model-width projection, bound by the matrix cores); HIP
+    events, median of 20 calls after 0.5 s of untimed calls."""
+    import torch
+
+    import attention_plx_attn_amd as plx
+
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    stream = torch.cuda.current_stream(dev)
+    g = torch.Generator(device=dev)
+    g.manual_seed(13)
+    B, T, H, d = 4, 2048, 16, 128
+    rows = []
+    for C in (32, 2048):
+        x = torch.randn((B, T, C), generator=g, device=dev).to(torch.bfloat16)
+        w = (0.05 * torch.randn((H * d, C), generator=g, device=dev)).to(torch.bfloat16)
+        gamma = torch.ones(d, device=dev)
+        gate = torch.full((H,), 0.5, device=dev)
+        rho = torch.empty((B, H, T, d), dtype=torch.bfloat16, device=dev)
+
+        def call():
+            plx.probe(x, w, H, gamma=gamma, gate=gate, eps=1e-6, rope_base=10000.0, out=rho)
+
+        t_end = time.perf_counter() + 0.5
+        while time.perf_counter() < t_end:
+            call()
+            torch.cuda.synchronize()
+        ts = []
+        for _ in range(20):
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record(stream)
+            call()
+            e1.record(stream)
+            torch.cuda.synchronize()
+            ts.append(e0.elapsed_time(e1))
+        us = _stats_us(ts)["median_us"]
+        nbytes = (B * T * C + H * d * C + B * H * T * d) * 2
+        flops = 2 * B * T * C * H * d
+        r = {"workload": f"probe producer {B}x{T} tokens, C={C}, H={H}, d={d}, RoPE + gate",
+             "median_us": us, "gbps": round(nbytes / us / 1e3, 1),
+             "tflops": round(flops / us / 1e6, 2),
+             "bound": "hbm" if flops / nbytes < 312 else "mfma"}
+        r["frac"] = round(r["gbps"] / HBM_PEAK_GBPS if r["bound"] == "hbm"
+                          else r["tflops"] / BF16_PEAK_TFLOPS, 4)
+        rows.append(r)
+        print(json.dumps(r), flush=True)
+        del x, w, rho
+    if out_md:
+        with open(out_md, "w") as fh:
+            fh.write("| workload | median us | HBM GB/s | TFLOP/s | bound | roofline fraction |\n")
+            fh.write("|---|---|---|---|---|---|\n")
+            for r in rows:
+                peak = "8 TB/s" if r["bound"] == "hbm" else "2.5 PFLOP/s"
+                fh.write(f"| {r['workload']} | {r['median_us']} | {r['gbps']} | {r['tflops']} "
+                         f"| {r['bound']} | {100 * r['frac']:.1f}% of {peak} |\n")
+    return 0
+
+
 # ------------------------------------------------------------------------------ main
 
 def main():
@@ -388,6 +489,8 @@ def main():
     ap.add_argument("--summarize-counters", nargs=2, metavar=("FETCH_CSV_GLOB", "WRITE_CSV_GLOB"))
     ap.add_argument("--sweep", metavar="OUT_MD", nargs="?", const="",
                     help="time the long prefill and the decode grid instead of the step")
+    ap.add_argument("--probe-producer", metavar="OUT_MD", nargs="?", const="",
+                    help="time the probe producer instead of the step")
     ap.add_argument("--compare", metavar="OUT_MD", nargs="?", const="",
                     help="time Parallax against softmax-only attention (I/O- and "
                          "compute-matched) instead of the step")
@@ -407,6 +510,8 @@ def main():
         return sweep(args.sweep)
     if args.compare is not None:
         return compare(args.compare)
+    if args.probe_producer is not None:
+        return probe_producer(args.probe_producer)
 
     import torch
 
@@ -489,6 +594,7 @@ def main():
     dec_gbps = dbytes / dec_avg_s / 1e9
 
     traffic = committed_traffic()
+    read_gbps = streaming_read_gbps(torch, dev, stream)
     result = {
         "metric": "decode tokens/s & HBM GB/s frac; prefill TFLOP/s & MFMA util (B,H,T,d=128)",
         "value": round(tflops, 2),
@@ -521,6 +627,7 @@ def main():
                    "tokens_per_s": round(dcfg.B / dec_avg_s, 1),
                    "hbm_gbps": round(dec_gbps, 1),
                    "hbm_frac": round(dec_gbps / HBM_PEAK_GBPS, 4),
+                   "frac_of_measured_read": round(dec_gbps / read_gbps, 4),
                    "bytes": dbytes},
         "roofline": {"bound": "mfma", "achieved": round(tflops, 2), "peak": BF16_PEAK_TFLOPS,
                      "unit": "TFLOP/s", "frac": round(tflops / BF16_PEAK_TFLOPS, 4),
@@ -531,6 +638,11 @@ def main():
                             "frac": round(dec_gbps / HBM_PEAK_GBPS, 4), "traffic": None,
                             "work_per_launch": dbytes},
         "wall_s_timed": round(wall, 3),
+        "system": {"gpu": torch.cuda.get_device_name(dev), "hip": torch.version.hip,
+                   "torch": torch.__version__, "cus": torch.cuda.get_device_properties(dev)
+                   .multi_processor_count,
+                   "measured_hbm_read_gbps": round(read_gbps, 1),
+                   "source_sha256": source_hash(PREFILL_SOURCES + DECODE_SOURCES)},
     }
     if not args.no_cpu_baseline:
         result["cpu_baseline"] = cpu_baseline(px, dx)

@@ -133,6 +133,32 @@ plx_status_t plx_attn_decode(plx_dtype_t dtype, int32_t B, int32_t H, int32_t L_
                              int32_t num_splits, void* workspace, size_t workspace_bytes,
                              void* stream);
 
+/*
+ * The probe producer: rho = gate_h * RoPE(gamma (.) RMSNorm_head(x W_R^T)), written in the
+ * layout plx_attn_prefill / plx_attn_decode read (agihunt review, method paragraph: rho is one
+ * matrix product W_R x from the layer input, with its own RMSNorm and, optionally, RoPE; the
+ * mechanism-analysis paragraph of the same review mentions a learned gate on the probe).
+ *
+ *   x   : [B, T, C] tokens of the layer input (dtype)     w_r : [H*d, C] (dtype), row-major
+ *   rho : [B, H, T, d] (dtype), written
+ *   gamma     : device float[d] (16-byte aligned), the RMSNorm weight, or NULL for 1
+ *   gate      : device float[H], a per-head multiplier (e.g. a sigmoid gate's value), or NULL
+ *   positions : device int32[B], position of token 0 of sequence b (token t has position
+ *               positions[b] + t; for one decode token, seqlens[b] - 1), or NULL for 0
+ *   eps       : RMSNorm epsilon (>= 0): y / sqrt(mean over the head's d dims of y^2 + eps)
+ *   rope_base : 0 for no rotation; else > 1, the rotate-half RoPE: dims (i, i + d/2) of each
+ *               head turned by position * rope_base^(-2i/d), i < d/2
+ * Order: y = x W_R^T; per (token, head): RMSNorm, times gamma, RoPE, times gate.
+ * Arithmetic: bf16 products with fp32 accumulation on the matrix cores; normalisation and
+ * rotation in fp32; output rounded to bf16 (RNE).
+ * Built combination: (PLX_BF16, d = 128) with C a multiple of 8. Limits: B*T*C*2 < 2^31.
+ * Errors as for the other entry points; nothing is enqueued on a validation failure.
+ */
+plx_status_t plx_attn_probe(plx_dtype_t dtype, int32_t B, int32_t T, int32_t C, int32_t H,
+                            int32_t d, const void* x, const void* w_r, const float* gamma,
+                            const float* gate, const int32_t* positions, float eps,
+                            float rope_base, void* rho, void* stream);
+
 /* Static, NUL-terminated description of a status code. */
 const char* plx_status_string(plx_status_t s);
 

@@ -19,7 +19,8 @@ module builds it with gcc and marshals numpy arrays. Three forms are exposed:
                      that are merged [paper.rainbus.top summary, method steps 5-6 and
                      the streaming sentences; agihunt review, hardware paragraph].
 
-Pins for every form are in ``tests/test_oracle_pins.py``.
+Pins for every form are in ``tests/test_oracle_pins.py``. The probe producer
+(``probe``: rho = gate * RoPE(RMSNorm(x W_R^T)), plain numpy fp64) is in ``probe.py``.
 """
 from __future__ import annotations
 
@@ -134,4 +135,6 @@ def threads() -> int:
     return int(_load().plx_oracle_threads())
 
 
-__all__ = ["build", "prefill", "decode", "threads"]
+from .probe import probe  # noqa: E402
+
+__all__ = ["build", "prefill", "decode", "threads", "probe"]

@@ -19,7 +19,8 @@ def lib():
 def test_exports_every_declared_symbol(lib):
     declared = plx.header_functions()
     assert set(declared) == {"plx_attn_prefill", "plx_attn_decode", "plx_attn_decode_num_splits",
-                             "plx_attn_decode_workspace_size", "plx_status_string"}
+                             "plx_attn_decode_workspace_size", "plx_attn_probe",
+                             "plx_status_string"}
     out = subprocess.run(["nm", "-D", "--defined-only", plx.LIB_PATH], capture_output=True,
                          text=True, check=True).stdout
     exported = {line.split()[-1] for line in out.splitlines() if " T " in line}
@@ -108,3 +109,27 @@ def test_wave_range_plan_explicit(lib):
     assert plx.decode_workspace_size(8, 4, 300, 128, -16) == 0         # 32 (b, h) >= 2 * 16
     assert plx.decode_workspace_size(8, 4, 300, 128, -20) == 20 * 2 * 260 * 4
     assert plx.decode_workspace_size(1, 1, 40, 128, -4096) == 4096 * 2 * 260 * 4
+
+
+def _probe(lib, dtype=1, B=2, T=3, C=32, H=2, d=128, x=A, w=A, gamma=0, gate=0, pos=0, eps=1e-6,
+           base=0.0, rho=A):
+    return lib.plx_attn_probe(dtype, B, T, C, H, d, x, w, gamma, gate, pos, ctypes.c_float(eps),
+                              ctypes.c_float(base), rho, None)
+
+
+def test_probe_validation(lib):
+    assert _probe(lib, x=0) == 1
+    assert _probe(lib, rho=0) == 1
+    assert _probe(lib, T=0) == 2
+    assert _probe(lib, C=-8) == 2
+    assert _probe(lib, B=1 << 16, T=1 << 12, C=64) == 2       # B*T*C*2 >= 2^31
+    assert _probe(lib, eps=-1.0) == 3
+    assert _probe(lib, eps=float("nan")) == 3
+    assert _probe(lib, base=0.5) == 3                         # RoPE base must exceed 1
+    assert _probe(lib, dtype=5) == 3
+    assert _probe(lib, d=64) == 4
+    assert _probe(lib, C=36) == 4                             # C a multiple of 8
+    assert _probe(lib, dtype=0) == 4
+    assert _probe(lib, x=A + 8) == 5
+    assert _probe(lib, gate=A + 2) == 5
+    assert _probe(lib, gamma=A + 4) == 5

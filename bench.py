@@ -29,8 +29,9 @@ Extra modes:
 Used to produce the committed rocprofv3 summaries:
   --calibrate-copy        also run a reference kernel of known traffic (1 GiB read + 1 GiB
                           written), which scales the counters
-  --summarize-counters F W  fold rocprofv3 --pmc CSVs (FETCH_SIZE run F, WRITE_SIZE run W)
-                            into profiles/prefill_bf16_d128_counters.json
+  --summarize-counters F W [M]  fold rocprofv3 --pmc CSVs (FETCH_SIZE run F, WRITE_SIZE run W,
+                            MFMA run M: SQ_INSTS_VALU_MFMA_MOPS_BF16 SQ_VALU_MFMA_BUSY_CYCLES
+                            GRBM_GUI_ACTIVE) into profiles/prefill_bf16_d128_counters.json
 """
 from __future__ import annotations
 
@@ -96,9 +97,21 @@ def _pmc_rows(path_glob, counter):
     return out
 
 
-def summarize_counters(fetch_glob, write_glob, out_path=COUNTERS_JSON):
+def _agent_gpu_info(path_glob):
+    """(XCDs, SIMDs) of the GPU agent from rocprofv3's agent_info CSV, if present."""
+    for path in glob.glob(path_glob, recursive=True):
+        with open(path, newline="") as fh:
+            for row in csv.DictReader(fh):
+                if row.get("Agent_Type") == "GPU":
+                    return int(row["Num_Xcc"]), int(row["Simd_Count"])
+    return None
+
+
+def summarize_counters(fetch_glob, write_glob, mfma_glob=None, out_path=COUNTERS_JSON):
     """Per-dispatch FETCH_SIZE / WRITE_SIZE (KiB) of the prefill kernel, calibrated by a
-    plain copy of known size run in the same process."""
+    plain copy of known size run in the same process; with mfma_glob, also the matrix-core
+    counters of the same kernel (SQ_INSTS_VALU_MFMA_MOPS_BF16: units of 512 FLOP;
+    SQ_VALU_MFMA_BUSY_CYCLES summed over SIMDs; GRBM_GUI_ACTIVE summed over the XCDs)."""
     fetch = _pmc_rows(fetch_glob, "FETCH_SIZE")
     write = _pmc_rows(write_glob, "WRITE_SIZE")
 
@@ -126,13 +139,28 @@ def summarize_counters(fetch_glob, write_glob, out_path=COUNTERS_JSON):
         "hbm_bytes_per_dispatch": (f_k * fetch_scale + w_k * write_scale) * 1024.0,
         "source_sha256": source_hash(),
     }
+    if mfma_glob:
+        mops = pick(_pmc_rows(mfma_glob, "SQ_INSTS_VALU_MFMA_MOPS_BF16"), is_prefill)
+        busy = pick(_pmc_rows(mfma_glob, "SQ_VALU_MFMA_BUSY_CYCLES"), is_prefill)
+        gui = pick(_pmc_rows(mfma_glob, "GRBM_GUI_ACTIVE"), is_prefill)
+        info = _agent_gpu_info(os.path.join(os.path.dirname(mfma_glob.split("*")[0]) or ".",
+                                            "**", "*agent_info.csv"))
+        if None in (mops, busy, gui) or info is None:
+            raise SystemExit(f"missing MFMA counters: {mops} {busy} {gui} {info}")
+        xcc, simds = info
+        rec["mfma_flops_per_dispatch"] = mops * 512.0
+        rec["mfma_busy_cycles_per_dispatch"] = busy
+        rec["gui_active_cycles_per_dispatch_per_xcd"] = gui / xcc
+        rec["simds"] = simds
+        rec["mfma_busy_frac_profiled"] = busy / (gui / xcc * simds)
     with open(out_path, "w") as fh:
         json.dump(rec, fh, indent=1)
         fh.write("\n")
     print(json.dumps(rec))
 
 
-def committed_traffic():
+def committed_counters():
+    """The committed counter record of the prefill kernel, or None once its code changed."""
     try:
         with open(COUNTERS_JSON) as fh:
             rec = json.load(fh)
@@ -140,7 +168,26 @@ def committed_traffic():
         return None
     if rec.get("source_sha256") != source_hash():
         return None
-    return rec.get("hbm_bytes_per_dispatch")
+    return rec
+
+
+def counter_summary(flops, seconds):
+    """Matrix-core counters of the prefill kernel from the committed record: executed MFMA
+    FLOPs per launch (they include the masked parts of diagonal tiles) and the MFMA-busy
+    fraction, both under the profiler and against this run's own launch time."""
+    rec = committed_counters()
+    if rec is None or "mfma_flops_per_dispatch" not in rec:
+        return None
+    per_simd_busy_s = rec["mfma_busy_cycles_per_dispatch"] / rec["simds"] / 2.4e9
+    return {"mfma_flops_per_launch": rec["mfma_flops_per_dispatch"],
+            "mfma_flops_over_algorithmic": round(rec["mfma_flops_per_dispatch"] / flops, 4),
+            "mfma_busy_frac_profiled": round(rec["mfma_busy_frac_profiled"], 4),
+            "mfma_busy_frac_at_2p4ghz": round(per_simd_busy_s / seconds, 4)}
+
+
+def committed_traffic():
+    rec = committed_counters()
+    return None if rec is None else rec.get("hbm_bytes_per_dispatch")
 
 
 # ------------------------------------------------------------------------------ CPU baseline
@@ -182,17 +229,19 @@ def _cpu_model() -> str:
 
 
 def streaming_read_gbps(torch, dev, stream) -> float:
-    """Measured HBM read rate of this board: a sum over 1 GiB of fp32 (read once, a few KB
-    written), median of 10 calls after a short warm-up, HIP events on the launch stream."""
+    """A measured HBM read rate of this board for reference: torch row sums over 1 GiB of
+    fp32 (8192 rows; read once, 32 KB written), median of 10 calls after a short warm-up, HIP
+    events on the launch stream. (The fastest torch read on MI355X; a dedicated streaming
+    kernel reads somewhat faster.)"""
     x = torch.ones(1024 * 1024 * 1024 // 4, dtype=torch.float32, device=dev)
-    sink = torch.empty(1, dtype=torch.float32, device=dev)
+    sink = torch.empty(8192, dtype=torch.float32, device=dev)
     for _ in range(5):
-        torch.sum(x, dim=0, keepdim=True, out=sink)
+        torch.sum(x.view(8192, -1), dim=1, out=sink)
     ts = []
     for _ in range(10):
         e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
         e0.record(stream)
-        torch.sum(x, dim=0, keepdim=True, out=sink)
+        torch.sum(x.view(8192, -1), dim=1, out=sink)
         e1.record(stream)
         torch.cuda.synchronize()
         ts.append(e0.elapsed_time(e1))
@@ -486,7 +535,8 @@ def main():
     ap.add_argument("--copies", type=int, default=4, help="decode cache copies to rotate")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--calibrate-copy", action="store_true")
-    ap.add_argument("--summarize-counters", nargs=2, metavar=("FETCH_CSV_GLOB", "WRITE_CSV_GLOB"))
+    ap.add_argument("--summarize-counters", nargs="+",
+                    metavar="CSV_GLOB", help="FETCH_SIZE run, WRITE_SIZE run[, MFMA run]")
     ap.add_argument("--sweep", metavar="OUT_MD", nargs="?", const="",
                     help="time the long prefill and the decode grid instead of the step")
     ap.add_argument("--probe-producer", metavar="OUT_MD", nargs="?", const="",
@@ -627,21 +677,23 @@ def main():
                    "tokens_per_s": round(dcfg.B / dec_avg_s, 1),
                    "hbm_gbps": round(dec_gbps, 1),
                    "hbm_frac": round(dec_gbps / HBM_PEAK_GBPS, 4),
-                   "frac_of_measured_read": round(dec_gbps / read_gbps, 4),
+                   "frac_of_torch_rowsum_read": round(dec_gbps / read_gbps, 4),
                    "bytes": dbytes},
         "roofline": {"bound": "mfma", "achieved": round(tflops, 2), "peak": BF16_PEAK_TFLOPS,
                      "unit": "TFLOP/s", "frac": round(tflops / BF16_PEAK_TFLOPS, 4),
                      "traffic": traffic, "kernel": PREFILL_KERNEL,
-                     "work_per_launch": flops},
+                     "work_per_launch": flops, "counters": counter_summary(flops, pre_avg_s)},
         "roofline_decode": {"bound": "hbm", "achieved": round(dec_gbps, 1),
                             "peak": HBM_PEAK_GBPS, "unit": "GB/s",
                             "frac": round(dec_gbps / HBM_PEAK_GBPS, 4), "traffic": None,
                             "work_per_launch": dbytes},
         "wall_s_timed": round(wall, 3),
-        "system": {"gpu": torch.cuda.get_device_name(dev), "hip": torch.version.hip,
+        "system": {"gpu": torch.cuda.get_device_name(dev),
+                   "arch": getattr(torch.cuda.get_device_properties(dev), "gcnArchName", None),
+                   "hip": torch.version.hip,
                    "torch": torch.__version__, "cus": torch.cuda.get_device_properties(dev)
                    .multi_processor_count,
-                   "measured_hbm_read_gbps": round(read_gbps, 1),
+                   "measured_hbm_read_gbps_torch_rowsum": round(read_gbps, 1),
                    "source_sha256": source_hash(PREFILL_SOURCES + DECODE_SOURCES)},
     }
     if not args.no_cpu_baseline:

@@ -6,6 +6,7 @@ Python entry points over the C ABI of ``libplx_attn.so`` (include/plx_attn.h):
 * ``decode(q, rho, k_cache, v_cache, seqlens, scale=None, num_splits=0)`` -- one decode
   step over a contiguous per-sequence KV cache;
 * ``decode_num_splits`` / ``decode_workspace_size`` -- the split plan of a decode call;
+* ``decode_gqa`` / ``decode_gqa_plan`` -- decode with grouped query heads (H_q = G H_kv);
 * ``probe(x, w_r, H, ...)`` -- the probe producer rho = gate * RoPE(RMSNorm(x W_R^T)).
 
 All arithmetic runs in the HIP kernels; torch only supplies device memory and streams.
@@ -14,6 +15,8 @@ from ._lib import (  # noqa: F401
     LIB_PATH,
     PlxError,
     decode,
+    decode_gqa,
+    decode_gqa_plan,
     decode_num_splits,
     decode_workspace_size,
     header_functions,

@@ -51,6 +51,12 @@ def load() -> ctypes.CDLL:
     lib.plx_attn_decode.argtypes = ([ctypes.c_int] + [i32] * 5 + [vp] * 6 +
                                     [f32, i32, vp, ctypes.c_size_t, vp])
     lib.plx_attn_decode.restype = ctypes.c_int
+    lib.plx_attn_decode_gqa_plan.argtypes = [i32] * 6 + [ctypes.POINTER(i32),
+                                                         ctypes.POINTER(ctypes.c_size_t)]
+    lib.plx_attn_decode_gqa_plan.restype = ctypes.c_int
+    lib.plx_attn_decode_gqa.argtypes = ([ctypes.c_int] + [i32] * 6 + [vp] * 6 +
+                                        [f32, i32, vp, ctypes.c_size_t, vp])
+    lib.plx_attn_decode_gqa.restype = ctypes.c_int
     lib.plx_attn_probe.argtypes = [ctypes.c_int] + [i32] * 5 + [vp] * 5 + [f32, f32, vp, vp]
     lib.plx_attn_probe.restype = ctypes.c_int
     lib.plx_status_string.argtypes = [ctypes.c_int]
@@ -211,4 +217,56 @@ def probe(x: torch.Tensor, w_r: torch.Tensor, H: int, gamma: Optional[torch.Tens
                             _stream_handle(stream, x.device))
     if rc != 0:
         raise PlxError(rc, "plx_attn_probe")
+    return out
+
+
+def decode_gqa_plan(B: int, H_q: int, H_kv: int, L_max: int, d_v: int = 128,
+                    num_splits: int = 0) -> tuple:
+    """(split count, workspace bytes) of a grouped-query decode call."""
+    lib = load()
+    sp, nb = ctypes.c_int32(0), ctypes.c_size_t(0)
+    rc = lib.plx_attn_decode_gqa_plan(B, H_q, H_kv, L_max, d_v, num_splits, ctypes.byref(sp),
+                                      ctypes.byref(nb))
+    if rc != 0:
+        raise PlxError(rc, "plx_attn_decode_gqa_plan")
+    return sp.value, nb.value
+
+
+def decode_gqa(q: torch.Tensor, rho: Optional[torch.Tensor], k_cache: torch.Tensor,
+               v_cache: torch.Tensor, seqlens: torch.Tensor, scale: Optional[float] = None,
+               num_splits: int = 0, out: Optional[torch.Tensor] = None,
+               workspace: Optional[torch.Tensor] = None,
+               stream: Optional[torch.cuda.Stream] = None) -> torch.Tensor:
+    """Decode with grouped query heads: q, rho [B,H_q,d]; caches [B,H_kv,L_max,d] with
+    H_q / H_kv in {1, 2, 4, 8}; query head h reads cache head h // (H_q / H_kv)."""
+    lib = load()
+    if q.dim() != 3 or k_cache.dim() != 4:
+        raise ValueError("q must be [B, H_q, d], the caches [B, H_kv, L_max, d]")
+    B, Hq, dqk = q.shape
+    Hkv, L_max, dv = k_cache.shape[1], k_cache.shape[2], v_cache.shape[3]
+    _check(q, "q", None, None)
+    if rho is not None:
+        _check(rho, "rho", q.dtype, q.device, (B, Hq, dqk))
+    _check(k_cache, "k_cache", q.dtype, q.device, (B, Hkv, L_max, dqk))
+    _check(v_cache, "v_cache", q.dtype, q.device, (B, Hkv, L_max, dv))
+    _check(seqlens, "seqlens", torch.int32, q.device, (B,))
+    if out is None:
+        out = torch.empty((B, Hq, dv), dtype=q.dtype, device=q.device)
+    _check(out, "out", q.dtype, q.device, (B, Hq, dv))
+    _, need = decode_gqa_plan(B, Hq, Hkv, L_max, dv, num_splits)
+    if workspace is None and need > 0:
+        workspace = torch.empty(need // 4, dtype=torch.float32, device=q.device)
+    ws_ptr, ws_bytes = 0, 0
+    if workspace is not None:
+        _check(workspace, "workspace", None, q.device)
+        ws_ptr, ws_bytes = workspace.data_ptr(), workspace.numel() * workspace.element_size()
+    if scale is None:
+        scale = dqk ** -0.5
+    rc = lib.plx_attn_decode_gqa(_dtype_code(q), B, Hq, Hkv, L_max, dqk, dv, q.data_ptr(),
+                                 0 if rho is None else rho.data_ptr(), k_cache.data_ptr(),
+                                 v_cache.data_ptr(), seqlens.data_ptr(), out.data_ptr(),
+                                 float(scale), int(num_splits), ws_ptr, ws_bytes,
+                                 _stream_handle(stream, q.device))
+    if rc != 0:
+        raise PlxError(rc, "plx_attn_decode_gqa")
     return out

@@ -507,4 +507,10 @@ hipError_t launch_decode_bf16_d128(const DecodeArgs& a, hipStream_t stream) {
     return a.rho ? launch_decode<true>(a, stream) : launch_decode<false>(a, stream);
 }
 
+hipError_t launch_decode_combine(const DecodeArgs& a, hipStream_t stream) {
+    hipLaunchKernelGGL(decode_combine_kernel, dim3(a.B * a.H), dim3(NT), 0, stream,
+                       (const float*)a.ws, (__bf16*)a.o, a.splits);
+    return hipGetLastError();
+}
+
 }  // namespace plx

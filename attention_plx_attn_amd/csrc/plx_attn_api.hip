@@ -231,6 +231,72 @@ plx_status_t plx_attn_decode(plx_dtype_t dtype, int32_t B, int32_t H, int32_t L_
     return e == hipSuccess ? PLX_OK : PLX_ERR_HIP;
 }
 
+plx_status_t plx_attn_decode_gqa_plan(int32_t B, int32_t H_q, int32_t H_kv, int32_t L_max,
+                                     int32_t d_v, int32_t num_splits, int32_t* splits_out,
+                                     size_t* workspace_bytes_out) {
+    if (!splits_out || !workspace_bytes_out) return PLX_ERR_NULL_POINTER;
+    plx_status_t st = check_decode_shape(B, H_q, L_max, d_v);
+    if (st != PLX_OK) return st;
+    if (H_kv < 1 || H_q % H_kv != 0) return PLX_ERR_INVALID_SHAPE;
+    const int G = H_q / H_kv;
+    if (G != 1 && G != 2 && G != 4 && G != 8) return PLX_ERR_UNSUPPORTED;
+    if (num_splits < 0) return PLX_ERR_INVALID_ARG;  // split mode only
+    DecodePlan p;
+    st = plan_decode(B, H_kv, L_max, d_v, num_splits == 0 ? 0 : num_splits, &p);
+    if (st != PLX_OK) return st;
+    if (p.waves > 0) {  // the automatic plan of the grouped kernel is always split mode
+        int cus = 0;
+        st = current_cu_count(&cus);
+        if (st != PLX_OK) return st;
+        const long long bh = (long long)B * H_kv;
+        long long s = (kDecodeWgPerCu * (long long)cus + bh - 1) / bh;
+        const long long smax = (L_max + kDecodeMinChunk - 1) / kDecodeMinChunk;
+        s = s > smax ? smax : (s < 1 ? 1 : s);
+        p = DecodePlan{};
+        chunk_plan(L_max, (int)s, &p.chunk, &p.splits);
+    }
+    *splits_out = p.splits;
+    *workspace_bytes_out = p.splits > 1 ? (size_t)B * H_q * p.splits *
+                                              (size_t)(2 * d_v + 4) * sizeof(float)
+                                        : 0;
+    return PLX_OK;
+}
+
+plx_status_t plx_attn_decode_gqa(plx_dtype_t dtype, int32_t B, int32_t H_q, int32_t H_kv,
+                                 int32_t L_max, int32_t d_qk, int32_t d_v, const void* q,
+                                 const void* rho, const void* k_cache, const void* v_cache,
+                                 const int32_t* seqlens, void* o, float softmax_scale,
+                                 int32_t num_splits, void* workspace, size_t workspace_bytes,
+                                 void* stream) {
+    if (dtype != PLX_F32 && dtype != PLX_BF16) return PLX_ERR_INVALID_ARG;
+    if (!q || !k_cache || !v_cache || !seqlens || !o) return PLX_ERR_NULL_POINTER;
+    plx_status_t st = check_decode_shape(B, H_q, L_max, d_v);
+    if (st != PLX_OK) return st;
+    if (d_qk < 1 || H_kv < 1 || H_q % H_kv != 0) return PLX_ERR_INVALID_SHAPE;
+    if (!std::isfinite(softmax_scale) || softmax_scale < 0.f) return PLX_ERR_INVALID_ARG;
+    if (num_splits < 0 || num_splits > kDecodeMaxSplits) return PLX_ERR_INVALID_ARG;
+    const int G = H_q / H_kv;
+    if (!(dtype == PLX_BF16 && d_qk == 128 && d_v == 128) ||
+        (G != 1 && G != 2 && G != 4 && G != 8))
+        return PLX_ERR_UNSUPPORTED;
+    if (!aligned16(q) || !aligned16(rho) || !aligned16(k_cache) || !aligned16(v_cache) ||
+        !aligned16(o) || (reinterpret_cast<uintptr_t>(seqlens) & 3u) != 0)
+        return PLX_ERR_MISALIGNED;
+    int splits = 0;
+    size_t need = 0;
+    st = plx_attn_decode_gqa_plan(B, H_q, H_kv, L_max, d_v, num_splits, &splits, &need);
+    if (st != PLX_OK) return st;
+    if (need > 0) {
+        if (!workspace) return PLX_ERR_NULL_POINTER;
+        if (workspace_bytes < need) return PLX_ERR_WORKSPACE_TOO_SMALL;
+        if (!aligned16(workspace)) return PLX_ERR_MISALIGNED;
+    }
+    plx::DecodeArgs a{B, H_q, L_max, d_qk, q, rho, k_cache, v_cache, seqlens, o, softmax_scale,
+                      splits, 0, static_cast<float*>(workspace), 0, 0};
+    const hipError_t e = plx::launch_decode_gqa_bf16_d128(a, H_kv, static_cast<hipStream_t>(stream));
+    return e == hipSuccess ? PLX_OK : PLX_ERR_HIP;
+}
+
 plx_status_t plx_attn_probe(plx_dtype_t dtype, int32_t B, int32_t T, int32_t C, int32_t H,
                             int32_t d, const void* x, const void* w_r, const float* gamma,
                             const float* gate, const int32_t* positions, float eps,

@@ -54,5 +54,10 @@ hipError_t launch_prefill_f32(const PrefillArgs& a, hipStream_t stream);
 hipError_t launch_prefill_bf16_d128(const PrefillArgs& a, hipStream_t stream);
 hipError_t launch_decode_bf16_d128(const DecodeArgs& a, hipStream_t stream);
 hipError_t launch_probe_bf16_d128(const ProbeArgs& a, hipStream_t stream);
+// Grouped query heads: a.H query heads over Hkv cache heads (a.H / Hkv in {1, 2, 4, 8}), split
+// mode with a.splits chunks; partials in the split decode's record layout per query head.
+hipError_t launch_decode_gqa_bf16_d128(const DecodeArgs& a, int Hkv, hipStream_t stream);
+// The split decode's combine: merges a.splits records per (b, query head) into o.
+hipError_t launch_decode_combine(const DecodeArgs& a, hipStream_t stream);
 
 }  // namespace plx

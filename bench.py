@@ -24,6 +24,8 @@ Extra modes:
                           (H16 d128, B x ctx) instead of the step; one JSON line each
   --compare [OUT_MD]      time Parallax against softmax-only attention (rho = NULL) with the
                           same inputs and with twice the heads (equal matrix FLOPs)
+  --gqa [OUT_MD]          time the grouped-query decode (G = 1, 2, 4, 8 query heads per cache
+                          head) on a 1x16x32768 cache
   --probe-producer [OUT_MD]  time the probe producer (x W_R^T, RMSNorm, RoPE, gate) on the
                           prefill step's tokens at C = 32 and C = 2048
 Used to produce the committed rocprofv3 summaries:
@@ -459,6 +461,74 @@ def compare(out_md):
     return 0
 
 
+def gqa(out_md):
+    """Decode with grouped query heads at a fixed cache (B=1, H_kv=16, 32768 rows, d=128):
+    G = 1, 2, 4, 8 query heads per cache head, against the multi-head decode of the same
+    cache (G = 1). Cold caches (a 1 GiB read before each call), HIP events, median of 20."""
+    import torch
+
+    import attention_plx_attn_amd as plx
+
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    stream = torch.cuda.current_stream(dev)
+    g = torch.Generator(device=dev)
+    g.manual_seed(17)
+    flush = torch.ones(1024 * 1024 * 1024 // 4, dtype=torch.float32, device=dev)
+    sink = torch.empty(8192, dtype=torch.float32, device=dev)
+    B, Hkv, L, d = 1, 16, 32768, 128
+    kc = torch.randn((B, Hkv, L, d), generator=g, device=dev).to(torch.bfloat16)
+    vc = torch.randn((B, Hkv, L, d), generator=g, device=dev).to(torch.bfloat16)
+    sl = torch.full((B,), L, dtype=torch.int32, device=dev)
+
+    def timed(call):
+        for _ in range(3):
+            call()
+        ts = []
+        for _ in range(20):
+            torch.sum(flush.view(8192, -1), dim=1, out=sink)
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record(stream)
+            call()
+            e1.record(stream)
+            torch.cuda.synchronize()
+            ts.append(e0.elapsed_time(e1))
+        return _stats_us(ts)["median_us"]
+
+    rows = []
+    q16 = torch.randn((B, Hkv, d), generator=g, device=dev).to(torch.bfloat16)
+    r16 = (0.1 * torch.randn((B, Hkv, d), generator=g, device=dev)).to(torch.bfloat16)
+    o16 = torch.empty_like(q16)
+    us = timed(lambda: plx.decode(q16, r16, kc, vc, sl, d ** -0.5, out=o16))
+    rows.append({"kernel": "multi-head decode (VALU value products)", "G": 1, "H_q": Hkv,
+                 "median_us": us})
+    for G in (1, 2, 4, 8):
+        Hq = Hkv * G
+        q = torch.randn((B, Hq, d), generator=g, device=dev).to(torch.bfloat16)
+        r = (0.1 * torch.randn((B, Hq, d), generator=g, device=dev)).to(torch.bfloat16)
+        o = torch.empty_like(q)
+        _, need = plx.decode_gqa_plan(B, Hq, Hkv, L, d)
+        ws = torch.empty(max(need // 4, 1), dtype=torch.float32, device=dev)
+        us = timed(lambda: plx.decode_gqa(q, r, kc, vc, sl, d ** -0.5, out=o, workspace=ws))
+        rows.append({"kernel": "grouped-query decode (MFMA value products)", "G": G,
+                     "H_q": Hq, "median_us": us})
+    for r_ in rows:
+        nbytes = B * Hkv * L * 2 * d * 2 + B * r_["H_q"] * 3 * d * 2
+        r_["hbm_gbps"] = round(nbytes / r_["median_us"] / 1e3, 1)
+        r_["hbm_frac"] = round(r_["hbm_gbps"] / HBM_PEAK_GBPS, 4)
+        r_["query_heads_per_s"] = round(r_["H_q"] / (r_["median_us"] * 1e-6), 0)
+        print(json.dumps(r_), flush=True)
+    if out_md:
+        with open(out_md, "w") as fh:
+            fh.write("| kernel | G | H_q | median us | HBM GB/s | fraction of 8 TB/s | "
+                     "query-head rows / s |\n|---|---|---|---|---|---|---|\n")
+            for r_ in rows:
+                fh.write(f"| {r_['kernel']} | {r_['G']} | {r_['H_q']} | {r_['median_us']} | "
+                         f"{r_['hbm_gbps']} | {100 * r_['hbm_frac']:.1f}% | "
+                         f"{r_['query_heads_per_s']:,.0f} |\n")
+    return 0
+
+
 def probe_producer(out_md):
     """Times the probe producer rho = gate * RoPE(gamma * RMSNorm_head(x W_R^T)) on the prefill
     step's tokens (4 x 2048, H = 16, d = 128) at the configs' input width C = 32 (bound by
@@ -539,6 +609,8 @@ def main():
                     metavar="CSV_GLOB", help="FETCH_SIZE run, WRITE_SIZE run[, MFMA run]")
     ap.add_argument("--sweep", metavar="OUT_MD", nargs="?", const="",
                     help="time the long prefill and the decode grid instead of the step")
+    ap.add_argument("--gqa", metavar="OUT_MD", nargs="?", const="",
+                    help="time the grouped-query decode instead of the step")
     ap.add_argument("--probe-producer", metavar="OUT_MD", nargs="?", const="",
                     help="time the probe producer instead of the step")
     ap.add_argument("--compare", metavar="OUT_MD", nargs="?", const="",
@@ -562,6 +634,8 @@ def main():
         return compare(args.compare)
     if args.probe_producer is not None:
         return probe_producer(args.probe_producer)
+    if args.gqa is not None:
+        return gqa(args.gqa)
 
     import torch
 

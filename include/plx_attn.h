@@ -134,6 +134,29 @@ plx_status_t plx_attn_decode(plx_dtype_t dtype, int32_t B, int32_t H, int32_t L_
                              void* stream);
 
 /*
+ * Decode with grouped query heads: H_q query heads over H_kv cache heads, G = H_q / H_kv in {1, 2, 4, 8}; query head h reads cache head
+ * h / G. Same conventions as plx_attn_decode, with
+ *   q, rho  : [B, H_q, d_qk]      k_cache : [B, H_kv, L_max, d_qk]
+ *   v_cache : [B, H_kv, L_max, d_v]   o : [B, H_q, d_v]
+ * One matrix instruction per 16 cache rows yields the scores and probe products of all G
+ * heads (columns q_0, rho_0, ..., q_{G-1}, rho_{G-1}; agihunt review, hardware paragraph: the
+ * idle rows of a decode step's matrix instructions carry extra work), and the value products
+ * run on the matrix cores as well. Split mode only: num_splits 0 (heuristic) or > 0 chunks per
+ * (b, h_kv); rho may be NULL (rho = 0).
+ * plx_attn_decode_gqa_plan writes the split count and the workspace bytes a call with the
+ * same arguments needs (B*H_q*S*(2*d_v + 4)*4 for S > 1, else 0).
+ */
+plx_status_t plx_attn_decode_gqa_plan(int32_t B, int32_t H_q, int32_t H_kv, int32_t L_max,
+                                     int32_t d_v, int32_t num_splits, int32_t* splits_out,
+                                     size_t* workspace_bytes_out);
+plx_status_t plx_attn_decode_gqa(plx_dtype_t dtype, int32_t B, int32_t H_q, int32_t H_kv,
+                                 int32_t L_max, int32_t d_qk, int32_t d_v, const void* q,
+                                 const void* rho, const void* k_cache, const void* v_cache,
+                                 const int32_t* seqlens, void* o, float softmax_scale,
+                                 int32_t num_splits, void* workspace, size_t workspace_bytes,
+                                 void* stream);
+
+/*
  * The probe producer: rho = gate_h * RoPE(gamma (.) RMSNorm_head(x W_R^T)), written in the
  * layout plx_attn_prefill / plx_attn_decode read (agihunt review, method paragraph: rho is one
  * matrix product W_R x from the layer input, with its own RMSNorm and, optionally, RoPE; the

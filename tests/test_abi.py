@@ -20,6 +20,7 @@ def test_exports_every_declared_symbol(lib):
     declared = plx.header_functions()
     assert set(declared) == {"plx_attn_prefill", "plx_attn_decode", "plx_attn_decode_num_splits",
                              "plx_attn_decode_workspace_size", "plx_attn_probe",
+                             "plx_attn_decode_gqa", "plx_attn_decode_gqa_plan",
                              "plx_status_string"}
     out = subprocess.run(["nm", "-D", "--defined-only", plx.LIB_PATH], capture_output=True,
                          text=True, check=True).stdout
@@ -133,3 +134,26 @@ def test_probe_validation(lib):
     assert _probe(lib, x=A + 8) == 5
     assert _probe(lib, gate=A + 2) == 5
     assert _probe(lib, gamma=A + 4) == 5
+
+
+def _gqa(lib, dtype=1, B=2, Hq=8, Hkv=2, L=64, dqk=128, dv=128, q=A, rho=A, kc=A, vc=A, sl=A,
+         o=A, scale=0.1, splits=1, ws=0, wsb=0):
+    return lib.plx_attn_decode_gqa(dtype, B, Hq, Hkv, L, dqk, dv, q, rho, kc, vc, sl, o,
+                                   ctypes.c_float(scale), splits, ws, wsb, None)
+
+
+def test_decode_gqa_validation(lib):
+    assert _gqa(lib, q=0) == 1
+    assert _gqa(lib, rho=0, L=0) == 2                      # rho may be NULL
+    assert _gqa(lib, Hkv=3) == 2                           # H_q not a multiple of H_kv
+    assert _gqa(lib, Hkv=0) == 2
+    assert _gqa(lib, Hq=6, Hkv=2) == 4                     # G = 3 not built
+    assert _gqa(lib, Hq=32, Hkv=2) == 4                    # G = 16 > 8
+    assert _gqa(lib, splits=-4) == 3                       # split mode only
+    assert _gqa(lib, dqk=64, dv=64) == 4
+    assert _gqa(lib, kc=A + 8) == 5
+    assert _gqa(lib, L=1024, splits=4) == 1                # workspace required
+    need = 2 * 8 * 4 * (2 * 128 + 4) * 4
+    assert _gqa(lib, L=1024, splits=4, ws=A, wsb=need - 4) == 6
+    assert plx.decode_gqa_plan(2, 8, 2, 1024, 128, 4) == (4, need)
+    assert plx.decode_gqa_plan(2, 8, 2, 1024, 128, 1) == (1, 0)

@@ -7,6 +7,7 @@ Python entry points over the C ABI of ``libplx_attn.so`` (include/plx_attn.h):
   step over a contiguous per-sequence KV cache;
 * ``decode_num_splits`` / ``decode_workspace_size`` -- the split plan of a decode call;
 * ``decode_gqa`` / ``decode_gqa_plan`` -- decode with grouped query heads (H_q = G H_kv);
+* ``decode_paged`` -- decode over a paged KV cache (block pool + block table);
 * ``probe(x, w_r, H, ...)`` -- the probe producer rho = gate * RoPE(RMSNorm(x W_R^T)).
 
 All arithmetic runs in the HIP kernels; torch only supplies device memory and streams.
@@ -18,6 +19,7 @@ from ._lib import (  # noqa: F401
     decode_gqa,
     decode_gqa_plan,
     decode_num_splits,
+    decode_paged,
     decode_workspace_size,
     header_functions,
     load,

@@ -57,6 +57,9 @@ def load() -> ctypes.CDLL:
     lib.plx_attn_decode_gqa.argtypes = ([ctypes.c_int] + [i32] * 6 + [vp] * 6 +
                                         [f32, i32, vp, ctypes.c_size_t, vp])
     lib.plx_attn_decode_gqa.restype = ctypes.c_int
+    lib.plx_attn_decode_paged.argtypes = ([ctypes.c_int] + [i32] * 7 + [vp] * 7 +
+                                          [f32, i32, vp, ctypes.c_size_t, vp])
+    lib.plx_attn_decode_paged.restype = ctypes.c_int
     lib.plx_attn_probe.argtypes = [ctypes.c_int] + [i32] * 5 + [vp] * 5 + [f32, f32, vp, vp]
     lib.plx_attn_probe.restype = ctypes.c_int
     lib.plx_status_string.argtypes = [ctypes.c_int]
@@ -269,4 +272,46 @@ def decode_gqa(q: torch.Tensor, rho: Optional[torch.Tensor], k_cache: torch.Tens
                                  _stream_handle(stream, q.device))
     if rc != 0:
         raise PlxError(rc, "plx_attn_decode_gqa")
+    return out
+
+
+def decode_paged(q: torch.Tensor, rho: Optional[torch.Tensor], k_pool: torch.Tensor,
+                 v_pool: torch.Tensor, block_table: torch.Tensor, seqlens: torch.Tensor,
+                 scale: Optional[float] = None, num_splits: int = 0,
+                 out: Optional[torch.Tensor] = None, workspace: Optional[torch.Tensor] = None,
+                 stream: Optional[torch.cuda.Stream] = None) -> torch.Tensor:
+    """Decode over a paged cache: q, rho [B,H,d]; pools [num_blocks,H,block_size,d];
+    block_table int32 [B, max_blocks] (rows i*block_size.. of sequence b live in block
+    block_table[b, i]); seqlens int32 [B]."""
+    lib = load()
+    B, H, dqk = q.shape
+    nblk, _, bs, dv = v_pool.shape
+    max_blocks = block_table.shape[1]
+    _check(q, "q", None, None)
+    if rho is not None:
+        _check(rho, "rho", q.dtype, q.device, (B, H, dqk))
+    _check(k_pool, "k_pool", q.dtype, q.device, (nblk, H, bs, dqk))
+    _check(v_pool, "v_pool", q.dtype, q.device, (nblk, H, bs, dv))
+    _check(block_table, "block_table", torch.int32, q.device, (B, max_blocks))
+    _check(seqlens, "seqlens", torch.int32, q.device, (B,))
+    if out is None:
+        out = torch.empty((B, H, dv), dtype=q.dtype, device=q.device)
+    _check(out, "out", q.dtype, q.device, (B, H, dv))
+    _, need = decode_gqa_plan(B, H, H, max_blocks * bs, dv, num_splits)
+    if workspace is None and need > 0:
+        workspace = torch.empty(need // 4, dtype=torch.float32, device=q.device)
+    ws_ptr, ws_bytes = 0, 0
+    if workspace is not None:
+        _check(workspace, "workspace", None, q.device)
+        ws_ptr, ws_bytes = workspace.data_ptr(), workspace.numel() * workspace.element_size()
+    if scale is None:
+        scale = dqk ** -0.5
+    rc = lib.plx_attn_decode_paged(_dtype_code(q), B, H, bs, max_blocks, nblk, dqk, dv,
+                                   q.data_ptr(), 0 if rho is None else rho.data_ptr(),
+                                   k_pool.data_ptr(), v_pool.data_ptr(), block_table.data_ptr(),
+                                   seqlens.data_ptr(), out.data_ptr(), float(scale),
+                                   int(num_splits), ws_ptr, ws_bytes,
+                                   _stream_handle(stream, q.device))
+    if rc != 0:
+        raise PlxError(rc, "plx_attn_decode_paged")
     return out

@@ -110,16 +110,24 @@ __device__ __forceinline__ void store_merged(const Merge& st, __bf16* o_bh, int 
 
 // ------------------------------------------------------------------------------ split mode
 // PROBE = false (rho == NULL at the boundary): the softmax-only specialisation, see consume().
-template <bool PROBE>
+// PAGED: the cache is a pool of blocks [num_blocks, H, 2^bs_log2, d] and block_table[b][i]
+// names the block of rows i 2^bs_log2 .. of sequence b (blocks of at least 32 rows, so a step
+// never crosses a block). Only blocks holding rows below the chunk end are looked up; an entry
+// outside [0, num_blocks) is read as an empty block.
+template <bool PROBE, bool PAGED>
 __global__ __launch_bounds__(NT, 2) void decode_split_bf16_d128_kernel(
     const __bf16* __restrict__ q, const __bf16* __restrict__ rho, const __bf16* __restrict__ kc,
     const __bf16* __restrict__ vc, const int32_t* __restrict__ seqlens, __bf16* __restrict__ o,
-    float* __restrict__ ws, int H, int L_max, int S, float c) {
+    float* __restrict__ ws, int H, int L_max, int S, float c, const int32_t* __restrict__ table,
+    int max_blocks, int bs_log2, int num_blocks) {
     __shared__ __attribute__((aligned(16))) float ush[NW][2][KB];  // rounded w and w t per key
     __shared__ __attribute__((aligned(16))) float red[NW][2 * D + 4];
 
     const int s = blockIdx.x, h = blockIdx.y, b = blockIdx.z;
-    const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+    const int tid = threadIdx.x, lane = tid & 63;
+    // The paged instance needs the wave index (and with it each step's block) wave-uniform,
+    // so that the block's buffer resource lives in scalar registers.
+    const int w = PAGED ? __builtin_amdgcn_readfirstlane(tid >> 6) : tid >> 6;
     const int col = lane & 15;  // column of the score tile (0: q, 1: rho); V: dims 8 col ..
     const int g = lane >> 4;    // row group of the score tile; V: key sub-range
 
@@ -131,8 +139,36 @@ __global__ __launch_bounds__(NT, 2) void decode_split_bf16_d128_kernel(
     const int j1 = min(j0 + chunk, nb_keys);
     const size_t bh = (size_t)b * H + h;
     const uint32_t range = j1 > 0 ? (uint32_t)j1 * 256u : 0u;
-    const auto rk = make_rsrc(kc + bh * (size_t)L_max * D, range);
+    const auto rk = make_rsrc(kc + bh * (size_t)L_max * D, range);  // contiguous cache
     const auto rv = make_rsrc(vc + bh * (size_t)L_max * D, range);
+    // Block of the step at row kb0 (paged cache; looked up a step before its loads are
+    // issued, so that the table read is not on the way to them).
+    auto lookup = [&](int kb0) -> int {
+        if constexpr (!PAGED) return 0;
+        return kb0 < j1 ? __builtin_amdgcn_readfirstlane(
+                              table[(size_t)b * max_blocks + (kb0 >> bs_log2)])
+                        : -1;
+    };
+    // Loads of the step at row kb0: the contiguous cache, or the block that holds it.
+    auto load_at = [&](int kb0, int phys, Frag& f) {
+        if constexpr (!PAGED) {
+            decode::load_step(rk, rv, kb0, col, g, f);
+        } else {
+            int rel = 0;
+            uint32_t bytes = 0;
+            size_t base = 0;
+            if (kb0 < j1) {
+                const int blk = kb0 >> bs_log2, r0 = blk << bs_log2;
+                if (phys >= 0 && phys < num_blocks) {
+                    base = (((size_t)phys * H + h) << bs_log2) * D;
+                    bytes = (uint32_t)min(1 << bs_log2, j1 - r0) * 256u;
+                }
+                rel = kb0 - r0;
+            }
+            decode::load_step(make_rsrc(kc + base, bytes), make_rsrc(vc + base, bytes), rel, col,
+                              g, f);
+        }
+    };
 
     bf16x8 bqr[4];
     decode::load_qr(make_rsrc(q + bh * D, 256u), make_rsrc(PROBE ? rho + bh * D : q, PROBE ? 256u : 0u),
@@ -147,13 +183,27 @@ __global__ __launch_bounds__(NT, 2) void decode_split_bf16_d128_kernel(
     constexpr int STEP = KB * NW;
     Frag fa, fb;
     int kb0 = j0 + KB * w;
-    if (kb0 < j1) decode::load_step(rk, rv, kb0, col, g, fa);
-    for (; kb0 < j1; kb0 += 2 * STEP) {
-        decode::load_step(rk, rv, kb0 + STEP, col, g, fb);
-        decode::consume<PROBE>(acc, fa, bqr, kb0, j1, c, ush[w], col, g);
-        if (kb0 + STEP >= j1) break;
-        decode::load_step(rk, rv, kb0 + 2 * STEP, col, g, fa);
-        decode::consume<PROBE>(acc, fb, bqr, kb0 + STEP, j1, c, ush[w], col, g);
+    if constexpr (PAGED) {
+        if (kb0 < j1) load_at(kb0, lookup(kb0), fa);
+        int ph1 = lookup(kb0 + STEP);
+        for (; kb0 < j1; kb0 += 2 * STEP) {
+            load_at(kb0 + STEP, ph1, fb);
+            const int ph2 = lookup(kb0 + 2 * STEP);
+            decode::consume<PROBE>(acc, fa, bqr, kb0, j1, c, ush[w], col, g);
+            if (kb0 + STEP >= j1) break;
+            load_at(kb0 + 2 * STEP, ph2, fa);
+            ph1 = lookup(kb0 + 3 * STEP);
+            decode::consume<PROBE>(acc, fb, bqr, kb0 + STEP, j1, c, ush[w], col, g);
+        }
+    } else {
+        if (kb0 < j1) decode::load_step(rk, rv, kb0, col, g, fa);
+        for (; kb0 < j1; kb0 += 2 * STEP) {
+            decode::load_step(rk, rv, kb0 + STEP, col, g, fb);
+            decode::consume<PROBE>(acc, fa, bqr, kb0, j1, c, ush[w], col, g);
+            if (kb0 + STEP >= j1) break;
+            decode::load_step(rk, rv, kb0 + 2 * STEP, col, g, fa);
+            decode::consume<PROBE>(acc, fb, bqr, kb0 + STEP, j1, c, ush[w], col, g);
+        }
     }
 
     decode::wave_totals<PROBE>(acc);
@@ -491,9 +541,16 @@ hipError_t launch_decode(const DecodeArgs& a, hipStream_t stream) {
     }
     const int BH = a.B * a.H;
     dim3 grid(a.splits, a.H, a.B);
-    hipLaunchKernelGGL(decode_split_bf16_d128_kernel<PROBE>, grid, dim3(NT), 0, stream,
-                       (const __bf16*)a.q, rho, (const __bf16*)a.k, (const __bf16*)a.v,
-                       a.seqlens, (__bf16*)a.o, a.ws, a.H, a.L_max, a.splits, c);
+    if (a.table)
+        hipLaunchKernelGGL((decode_split_bf16_d128_kernel<PROBE, true>), grid, dim3(NT), 0,
+                           stream, (const __bf16*)a.q, rho, (const __bf16*)a.k,
+                           (const __bf16*)a.v, a.seqlens, (__bf16*)a.o, a.ws, a.H, a.L_max,
+                           a.splits, c, a.table, a.max_blocks, a.block_log2, a.num_blocks);
+    else
+        hipLaunchKernelGGL((decode_split_bf16_d128_kernel<PROBE, false>), grid, dim3(NT), 0,
+                           stream, (const __bf16*)a.q, rho, (const __bf16*)a.k,
+                           (const __bf16*)a.v, a.seqlens, (__bf16*)a.o, a.ws, a.H, a.L_max,
+                           a.splits, c, nullptr, 0, 0, 0);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess || a.splits == 1) return e;
     hipLaunchKernelGGL(decode_combine_kernel, dim3(BH), dim3(NT), 0, stream, (const float*)a.ws,

@@ -297,6 +297,48 @@ plx_status_t plx_attn_decode_gqa(plx_dtype_t dtype, int32_t B, int32_t H_q, int3
     return e == hipSuccess ? PLX_OK : PLX_ERR_HIP;
 }
 
+plx_status_t plx_attn_decode_paged(plx_dtype_t dtype, int32_t B, int32_t H, int32_t block_size,
+                                   int32_t max_blocks, int32_t num_blocks, int32_t d_qk,
+                                   int32_t d_v, const void* q, const void* rho,
+                                   const void* k_pool, const void* v_pool,
+                                   const int32_t* block_table, const int32_t* seqlens, void* o,
+                                   float softmax_scale, int32_t num_splits, void* workspace,
+                                   size_t workspace_bytes, void* stream) {
+    if (dtype != PLX_F32 && dtype != PLX_BF16) return PLX_ERR_INVALID_ARG;
+    if (!q || !k_pool || !v_pool || !block_table || !seqlens || !o) return PLX_ERR_NULL_POINTER;
+    if (block_size < 32 || (block_size & (block_size - 1)) != 0 || max_blocks < 1 ||
+        num_blocks < 1)
+        return PLX_ERR_INVALID_SHAPE;
+    if ((long long)max_blocks * block_size > INT_MAX) return PLX_ERR_INVALID_SHAPE;
+    const int L_max = max_blocks * block_size;
+    plx_status_t st = check_decode_shape(B, H, L_max, d_v);
+    if (st != PLX_OK) return st;
+    if (d_qk < 1) return PLX_ERR_INVALID_SHAPE;
+    if (!std::isfinite(softmax_scale) || softmax_scale < 0.f) return PLX_ERR_INVALID_ARG;
+    if (num_splits < 0 || num_splits > kDecodeMaxSplits) return PLX_ERR_INVALID_ARG;
+    if (!(dtype == PLX_BF16 && d_qk == 128 && d_v == 128)) return PLX_ERR_UNSUPPORTED;
+    if (!aligned16(q) || !aligned16(rho) || !aligned16(k_pool) || !aligned16(v_pool) ||
+        !aligned16(o) || (reinterpret_cast<uintptr_t>(seqlens) & 3u) != 0 ||
+        (reinterpret_cast<uintptr_t>(block_table) & 3u) != 0)
+        return PLX_ERR_MISALIGNED;
+    int splits = 0;
+    size_t need = 0;
+    st = plx_attn_decode_gqa_plan(B, H, H, L_max, d_v, num_splits, &splits, &need);
+    if (st != PLX_OK) return st;
+    if (need > 0) {
+        if (!workspace) return PLX_ERR_NULL_POINTER;
+        if (workspace_bytes < need) return PLX_ERR_WORKSPACE_TOO_SMALL;
+        if (!aligned16(workspace)) return PLX_ERR_MISALIGNED;
+    }
+    int log2 = 0;
+    while ((1 << log2) < block_size) ++log2;
+    plx::DecodeArgs a{B, H, L_max, d_qk, q, rho, k_pool, v_pool, seqlens, o, softmax_scale,
+                      splits, 0, static_cast<float*>(workspace), 0, 0,
+                      block_table, max_blocks, log2, num_blocks};
+    const hipError_t e = plx::launch_decode_bf16_d128(a, static_cast<hipStream_t>(stream));
+    return e == hipSuccess ? PLX_OK : PLX_ERR_HIP;
+}
+
 plx_status_t plx_attn_probe(plx_dtype_t dtype, int32_t B, int32_t T, int32_t C, int32_t H,
                             int32_t d, const void* x, const void* w_r, const float* gamma,
                             const float* gate, const int32_t* positions, float eps,

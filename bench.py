@@ -26,6 +26,7 @@ Extra modes:
                           same inputs and with twice the heads (equal matrix FLOPs)
   --gqa [OUT_MD]          time the grouped-query decode (G = 1, 2, 4, 8 query heads per cache
                           head) on a 1x16x32768 cache
+  --paged [OUT_MD]        time the paged-cache decode against the contiguous cache
   --probe-producer [OUT_MD]  time the probe producer (x W_R^T, RMSNorm, RoPE, gate) on the
                           prefill step's tokens at C = 32 and C = 2048
 Used to produce the committed rocprofv3 summaries:
@@ -529,6 +530,85 @@ def gqa(out_md):
     return 0
 
 
+def paged(out_md):
+    """Decode over a paged cache against the contiguous cache, same split plan: B=1, H=16,
+    32768 rows and B=16, H=16, 4096 rows (full lengths), blocks of 32, 64 and 256 rows in a
+    random order in the pool, and 64-row blocks in pool order. Cold caches (a 1 GiB read before each call), HIP events,
+    median of 20."""
+    import torch
+
+    import attention_plx_attn_amd as plx
+
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    stream = torch.cuda.current_stream(dev)
+    g = torch.Generator(device=dev)
+    g.manual_seed(19)
+    flush = torch.ones(1024 * 1024 * 1024 // 4, dtype=torch.float32, device=dev)
+    sink = torch.empty(8192, dtype=torch.float32, device=dev)
+
+    def timed(call):
+        for _ in range(3):
+            call()
+        ts = []
+        for _ in range(20):
+            torch.sum(flush.view(8192, -1), dim=1, out=sink)
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record(stream)
+            call()
+            e1.record(stream)
+            torch.cuda.synchronize()
+            ts.append(e0.elapsed_time(e1))
+        return _stats_us(ts)["median_us"]
+
+    rows = []
+    d = 128
+    for B, H, L in ((1, 16, 32768), (16, 16, 4096)):
+        q = torch.randn((B, H, d), generator=g, device=dev).to(torch.bfloat16)
+        r = (0.1 * torch.randn((B, H, d), generator=g, device=dev)).to(torch.bfloat16)
+        kc = torch.randn((B, H, L, d), generator=g, device=dev).to(torch.bfloat16)
+        vc = torch.randn((B, H, L, d), generator=g, device=dev).to(torch.bfloat16)
+        sl = torch.full((B,), L, dtype=torch.int32, device=dev)
+        o = torch.empty_like(q)
+        S, need = plx.decode_gqa_plan(B, H, H, L, d)
+        ws = torch.empty(max(need // 4, 1), dtype=torch.float32, device=dev)
+        nbytes = B * H * L * 2 * d * 2 + B * H * 3 * d * 2
+        us = timed(lambda: plx.decode(q, r, kc, vc, sl, d ** -0.5, num_splits=S, out=o,
+                                      workspace=ws))
+        rows.append({"workload": f"decode B{B} H{H} ctx{L}", "cache": "contiguous",
+                     "splits": S, "median_us": us})
+        for bs, shuffled in ((32, True), (64, True), (256, True), (64, False)):
+            mb = L // bs
+            perm = (torch.randperm(B * mb, generator=torch.Generator().manual_seed(bs))
+                    if shuffled else torch.arange(B * mb))
+            table = perm.view(B, mb).to(torch.int32).to(dev)
+            kp = torch.empty((B * mb, H, bs, d), dtype=torch.bfloat16, device=dev)
+            vp = torch.empty_like(kp)
+            kp[perm] = kc.view(B, H, mb, bs, d).permute(0, 2, 1, 3, 4).reshape(B * mb, H, bs, d)
+            vp[perm] = vc.view(B, H, mb, bs, d).permute(0, 2, 1, 3, 4).reshape(B * mb, H, bs, d)
+            us = timed(lambda: plx.decode_paged(q, r, kp, vp, table, sl, d ** -0.5,
+                                                num_splits=S, out=o, workspace=ws))
+            order = "shuffled" if shuffled else "in pool order"
+            rows.append({"workload": f"decode B{B} H{H} ctx{L}",
+                         "cache": f"paged, {bs}-row blocks, {order}", "splits": S,
+                         "median_us": us})
+            del kp, vp
+        for r_ in rows[-5:]:
+            r_["hbm_gbps"] = round(nbytes / r_["median_us"] / 1e3, 1)
+            r_["hbm_frac"] = round(r_["hbm_gbps"] / HBM_PEAK_GBPS, 4)
+            print(json.dumps(r_), flush=True)
+        del q, r, kc, vc, o, ws
+        torch.cuda.empty_cache()
+    if out_md:
+        with open(out_md, "w") as fh:
+            fh.write("| workload | cache | splits | median us | HBM GB/s | fraction of 8 TB/s |\n"
+                     "|---|---|---|---|---|---|\n")
+            for r_ in rows:
+                fh.write(f"| {r_['workload']} | {r_['cache']} | {r_['splits']} | "
+                         f"{r_['median_us']} | {r_['hbm_gbps']} | {100 * r_['hbm_frac']:.1f}% |\n")
+    return 0
+
+
 def probe_producer(out_md):
     """Times the probe producer rho = gate * RoPE(gamma * RMSNorm_head(x W_R^T)) on the prefill
     step's tokens (4 x 2048, H = 16, d = 128) at the configs' input width C = 32 (bound by
@@ -609,6 +689,8 @@ def main():
                     metavar="CSV_GLOB", help="FETCH_SIZE run, WRITE_SIZE run[, MFMA run]")
     ap.add_argument("--sweep", metavar="OUT_MD", nargs="?", const="",
                     help="time the long prefill and the decode grid instead of the step")
+    ap.add_argument("--paged", metavar="OUT_MD", nargs="?", const="",
+                    help="time the paged-cache decode instead of the step")
     ap.add_argument("--gqa", metavar="OUT_MD", nargs="?", const="",
                     help="time the grouped-query decode instead of the step")
     ap.add_argument("--probe-producer", metavar="OUT_MD", nargs="?", const="",
@@ -636,6 +718,8 @@ def main():
         return probe_producer(args.probe_producer)
     if args.gqa is not None:
         return gqa(args.gqa)
+    if args.paged is not None:
+        return paged(args.paged)
 
     import torch
 

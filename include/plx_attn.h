@@ -157,6 +157,26 @@ plx_status_t plx_attn_decode_gqa(plx_dtype_t dtype, int32_t B, int32_t H_q, int3
                                  void* stream);
 
 /*
+ * One decode step over a paged KV cache: the cache is a pool of blocks and each sequence lists
+ * its blocks in a table. Same conventions and split plan as plx_attn_decode_gqa with
+ * H_q = H_kv = H and L_max = max_blocks * block_size, with
+ *   k_pool, v_pool : [num_blocks, H, block_size, d] (dtype)
+ *   block_table    : device int32 [B, max_blocks]; rows i*block_size .. (i+1)*block_size - 1
+ *                    of sequence b are block block_table[b][i] of the pool
+ *   block_size     : a power of two, at least 32
+ * Only the blocks that hold rows below n_b are read; a table entry outside [0, num_blocks) is
+ * read as a block of zero rows (its rows are skipped) rather than out of bounds.
+ * Built combination: (PLX_BF16, d_qk = d_v = 128); rho may be NULL (rho = 0).
+ */
+plx_status_t plx_attn_decode_paged(plx_dtype_t dtype, int32_t B, int32_t H, int32_t block_size,
+                                   int32_t max_blocks, int32_t num_blocks, int32_t d_qk,
+                                   int32_t d_v, const void* q, const void* rho,
+                                   const void* k_pool, const void* v_pool,
+                                   const int32_t* block_table, const int32_t* seqlens, void* o,
+                                   float softmax_scale, int32_t num_splits, void* workspace,
+                                   size_t workspace_bytes, void* stream);
+
+/*
  * The probe producer: rho = gate_h * RoPE(gamma (.) RMSNorm_head(x W_R^T)), written in the
  * layout plx_attn_prefill / plx_attn_decode read (agihunt review, method paragraph: rho is one
  * matrix product W_R x from the layer input, with its own RMSNorm and, optionally, RoPE; the

@@ -21,6 +21,7 @@ def test_exports_every_declared_symbol(lib):
     assert set(declared) == {"plx_attn_prefill", "plx_attn_decode", "plx_attn_decode_num_splits",
                              "plx_attn_decode_workspace_size", "plx_attn_probe",
                              "plx_attn_decode_gqa", "plx_attn_decode_gqa_plan",
+                             "plx_attn_decode_paged",
                              "plx_status_string"}
     out = subprocess.run(["nm", "-D", "--defined-only", plx.LIB_PATH], capture_output=True,
                          text=True, check=True).stdout
@@ -157,3 +158,22 @@ def test_decode_gqa_validation(lib):
     assert _gqa(lib, L=1024, splits=4, ws=A, wsb=need - 4) == 6
     assert plx.decode_gqa_plan(2, 8, 2, 1024, 128, 4) == (4, need)
     assert plx.decode_gqa_plan(2, 8, 2, 1024, 128, 1) == (1, 0)
+
+
+def _paged(lib, dtype=1, B=2, H=2, bs=64, mb=4, nb=8, dqk=128, dv=128, q=A, rho=A, kp=A, vp=A,
+           tab=A, sl=A, o=A, scale=0.1, splits=1, ws=0, wsb=0):
+    return lib.plx_attn_decode_paged(dtype, B, H, bs, mb, nb, dqk, dv, q, rho, kp, vp, tab, sl,
+                                     o, ctypes.c_float(scale), splits, ws, wsb, None)
+
+
+def test_decode_paged_validation(lib):
+    assert _paged(lib, tab=0) == 1
+    assert _paged(lib, rho=0, B=0) == 2                    # rho may be NULL
+    assert _paged(lib, bs=48) == 2                         # block size a power of two
+    assert _paged(lib, bs=16) == 2                         # at least 32 rows
+    assert _paged(lib, mb=0) == 2
+    assert _paged(lib, nb=0) == 2
+    assert _paged(lib, splits=-1) == 3
+    assert _paged(lib, dqk=64, dv=64) == 4
+    assert _paged(lib, tab=A + 2) == 5
+    assert _paged(lib, mb=16, splits=4) == 1               # workspace required

@@ -20,7 +20,8 @@ module builds it with gcc and marshals numpy arrays. Three forms are exposed:
                      the streaming sentences; agihunt review, hardware paragraph].
 
 Pins for every form are in ``tests/test_oracle_pins.py``. The probe producer
-(``probe``: rho = gate * RoPE(RMSNorm(x W_R^T)), plain numpy fp64) is in ``probe.py``.
+(``probe``: rho = gate * RoPE(RMSNorm(x W_R^T)), plain numpy fp64) is in ``probe.py``; the
+backward of the causal prefill (``prefill_backward``, numpy fp64) in ``backward.py``.
 """
 from __future__ import annotations
 
@@ -135,6 +136,7 @@ def threads() -> int:
     return int(_load().plx_oracle_threads())
 
 
+from .backward import prefill_backward  # noqa: E402
 from .probe import probe  # noqa: E402
 
-__all__ = ["build", "prefill", "decode", "threads", "probe"]
+__all__ = ["build", "prefill", "decode", "threads", "probe", "prefill_backward"]

@@ -8,6 +8,8 @@ Python entry points over the C ABI of ``libplx_attn.so`` (include/plx_attn.h):
 * ``decode_num_splits`` / ``decode_workspace_size`` -- the split plan of a decode call;
 * ``decode_gqa`` / ``decode_gqa_plan`` -- decode with grouped query heads (H_q = G H_kv);
 * ``decode_paged`` -- decode over a paged KV cache (block pool + block table);
+* ``prefill_fwd`` / ``prefill_bwd`` -- the prefill with saved statistics and its backward
+  (gradients of q, k, v and rho);
 * ``probe(x, w_r, H, ...)`` -- the probe producer rho = gate * RoPE(RMSNorm(x W_R^T)).
 
 All arithmetic runs in the HIP kernels; torch only supplies device memory and streams.
@@ -24,5 +26,8 @@ from ._lib import (  # noqa: F401
     header_functions,
     load,
     prefill,
+    prefill_bwd,
+    prefill_bwd_workspace_size,
+    prefill_fwd,
     probe,
 )

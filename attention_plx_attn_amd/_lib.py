@@ -62,6 +62,13 @@ def load() -> ctypes.CDLL:
     lib.plx_attn_decode_paged.restype = ctypes.c_int
     lib.plx_attn_probe.argtypes = [ctypes.c_int] + [i32] * 5 + [vp] * 5 + [f32, f32, vp, vp]
     lib.plx_attn_probe.restype = ctypes.c_int
+    lib.plx_attn_prefill_fwd.argtypes = [ctypes.c_int] + [i32] * 5 + [vp] * 7 + [f32, vp]
+    lib.plx_attn_prefill_fwd.restype = ctypes.c_int
+    lib.plx_attn_prefill_bwd_workspace_size.argtypes = [i32] * 3 + [ctypes.POINTER(ctypes.c_size_t)]
+    lib.plx_attn_prefill_bwd_workspace_size.restype = ctypes.c_int
+    lib.plx_attn_prefill_bwd.argtypes = ([ctypes.c_int] + [i32] * 5 + [vp] * 13 +
+                                         [ctypes.c_size_t, f32, vp])
+    lib.plx_attn_prefill_bwd.restype = ctypes.c_int
     lib.plx_status_string.argtypes = [ctypes.c_int]
     lib.plx_status_string.restype = ctypes.c_char_p
     _lib = lib
@@ -129,6 +136,74 @@ def prefill(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, rho: Optional[tor
     if rc != 0:
         raise PlxError(rc, "plx_attn_prefill")
     return out
+
+
+def prefill_fwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, rho: Optional[torch.Tensor],
+                scale: Optional[float] = None, stream: Optional[torch.cuda.Stream] = None):
+    """Causal prefill that also saves what the backward needs (bf16, d = 128).
+
+    Returns (o, vbar, stats): o as prefill(); vbar [B,H,T,d] = O1 / l (bf16); stats
+    [B,H,T,2] float32 = (lse, tbar) per query row."""
+    lib = load()
+    if q.dim() != 4:
+        raise ValueError("q must be [B, H, T, d]")
+    B, H, T, d = q.shape
+    _check(q, "q", None, None)
+    for name, t in (("k", k), ("v", v)) + ((("rho", rho),) if rho is not None else ()):
+        _check(t, name, q.dtype, q.device, (B, H, T, d))
+    o = torch.empty_like(q)
+    vbar = torch.empty_like(q)
+    stats = torch.empty((B, H, T, 2), dtype=torch.float32, device=q.device)
+    if scale is None:
+        scale = d ** -0.5
+    rc = lib.plx_attn_prefill_fwd(_dtype_code(q), B, H, T, d, d, q.data_ptr(), k.data_ptr(),
+                                  v.data_ptr(), 0 if rho is None else rho.data_ptr(),
+                                  o.data_ptr(), vbar.data_ptr(), stats.data_ptr(), float(scale),
+                                  _stream_handle(stream, q.device))
+    if rc != 0:
+        raise PlxError(rc, "plx_attn_prefill_fwd")
+    return o, vbar, stats
+
+
+def prefill_bwd_workspace_size(B: int, H: int, T: int) -> int:
+    lib = load()
+    n = ctypes.c_size_t(0)
+    rc = lib.plx_attn_prefill_bwd_workspace_size(B, H, T, ctypes.byref(n))
+    if rc != 0:
+        raise PlxError(rc, "plx_attn_prefill_bwd_workspace_size")
+    return n.value
+
+
+def prefill_bwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, rho: torch.Tensor,
+                o: torch.Tensor, vbar: torch.Tensor, stats: torch.Tensor, d_o: torch.Tensor,
+                scale: Optional[float] = None, workspace: Optional[torch.Tensor] = None,
+                stream: Optional[torch.cuda.Stream] = None):
+    """Backward of the causal prefill (bf16, d = 128): gradients (dq, dk, dv, drho) of
+    sum(d_o * o), given the forward's o, vbar and stats from prefill_fwd()."""
+    lib = load()
+    if q.dim() != 4:
+        raise ValueError("q must be [B, H, T, d]")
+    B, H, T, d = q.shape
+    _check(q, "q", None, None)
+    for name, t in (("k", k), ("v", v), ("rho", rho), ("o", o), ("vbar", vbar), ("d_o", d_o)):
+        _check(t, name, q.dtype, q.device, (B, H, T, d))
+    _check(stats, "stats", torch.float32, q.device, (B, H, T, 2))
+    grads = [torch.empty_like(q) for _ in range(4)]
+    need = prefill_bwd_workspace_size(B, H, T)
+    if workspace is None:
+        workspace = torch.empty(need // 4, dtype=torch.float32, device=q.device)
+    _check(workspace, "workspace", None, q.device)
+    if scale is None:
+        scale = d ** -0.5
+    rc = lib.plx_attn_prefill_bwd(_dtype_code(q), B, H, T, d, d, q.data_ptr(), k.data_ptr(),
+                                  v.data_ptr(), rho.data_ptr(), o.data_ptr(), vbar.data_ptr(),
+                                  stats.data_ptr(), d_o.data_ptr(),
+                                  *(g.data_ptr() for g in grads), workspace.data_ptr(),
+                                  workspace.numel() * workspace.element_size(), float(scale),
+                                  _stream_handle(stream, q.device))
+    if rc != 0:
+        raise PlxError(rc, "plx_attn_prefill_bwd")
+    return tuple(grads)
 
 
 def decode_num_splits(B: int, H: int, L_max: int, num_splits: int = 0) -> int:

@@ -122,6 +122,17 @@ plx_status_t check_decode_shape(int B, int H, int L_max, int d_v) {
     return PLX_OK;
 }
 
+// Shapes of the forward-with-statistics and the backward: bf16, d_qk = d_v = 128 only.
+plx_status_t check_bwd_shape(plx_dtype_t dtype, int B, int H, int T, int d_qk, int d_v,
+                             float scale) {
+    if (B < 1 || H < 1 || T < 1 || d_qk < 1 || d_v < 1) return PLX_ERR_INVALID_SHAPE;
+    if (!std::isfinite(scale) || scale < 0.f) return PLX_ERR_INVALID_ARG;
+    if (dtype != PLX_BF16 || d_qk != 128 || d_v != 128) return PLX_ERR_UNSUPPORTED;
+    if ((long long)T * 256 >= (1LL << 31)) return PLX_ERR_INVALID_SHAPE;
+    if ((long long)B * H * ((T + 127) / 128) > INT_MAX) return PLX_ERR_INVALID_SHAPE;
+    return PLX_OK;
+}
+
 }  // namespace
 
 extern "C" {
@@ -169,6 +180,59 @@ plx_status_t plx_attn_prefill(plx_dtype_t dtype, int32_t B, int32_t H, int32_t T
     const hipStream_t st = static_cast<hipStream_t>(stream);
     const hipError_t e = dtype == PLX_BF16 ? plx::launch_prefill_bf16_d128(a, st)
                                            : plx::launch_prefill_f32(a, st);
+    return e == hipSuccess ? PLX_OK : PLX_ERR_HIP;
+}
+
+plx_status_t plx_attn_prefill_fwd(plx_dtype_t dtype, int32_t B, int32_t H, int32_t T,
+                                  int32_t d_qk, int32_t d_v, const void* q, const void* k,
+                                  const void* v, const void* rho, void* o, void* vbar,
+                                  float* stats, float softmax_scale, void* stream) {
+    if (dtype != PLX_F32 && dtype != PLX_BF16) return PLX_ERR_INVALID_ARG;
+    if (!q || !k || !v || !o || !vbar || !stats) return PLX_ERR_NULL_POINTER;
+    const plx_status_t s = check_bwd_shape(dtype, B, H, T, d_qk, d_v, softmax_scale);
+    if (s != PLX_OK) return s;
+    if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(rho) || !aligned16(o) ||
+        !aligned16(vbar) || !aligned16(stats))
+        return PLX_ERR_MISALIGNED;
+    int cus = 1;
+    const plx_status_t sc = current_cu_count(&cus);
+    if (sc != PLX_OK) return sc;
+    plx::PrefillArgs a{B, H, T, d_qk, q, k, v, rho, o, softmax_scale, cus};
+    a.vbar = vbar;
+    a.stats = stats;
+    const hipError_t e = plx::launch_prefill_bf16_d128(a, static_cast<hipStream_t>(stream));
+    return e == hipSuccess ? PLX_OK : PLX_ERR_HIP;
+}
+
+plx_status_t plx_attn_prefill_bwd_workspace_size(int32_t B, int32_t H, int32_t T,
+                                                 size_t* bytes_out) {
+    if (!bytes_out) return PLX_ERR_NULL_POINTER;
+    if (B < 1 || H < 1 || T < 1) return PLX_ERR_INVALID_SHAPE;
+    *bytes_out = (size_t)B * H * T * 4 * sizeof(float);
+    return PLX_OK;
+}
+
+plx_status_t plx_attn_prefill_bwd(plx_dtype_t dtype, int32_t B, int32_t H, int32_t T,
+                                  int32_t d_qk, int32_t d_v, const void* q, const void* k,
+                                  const void* v, const void* rho, const void* o,
+                                  const void* vbar, const float* stats, const void* d_o,
+                                  void* dq, void* dk, void* dv, void* drho, void* workspace,
+                                  size_t workspace_bytes, float softmax_scale, void* stream) {
+    if (dtype != PLX_F32 && dtype != PLX_BF16) return PLX_ERR_INVALID_ARG;
+    if (!q || !k || !v || !rho || !o || !vbar || !stats || !d_o || !dq || !dk || !dv ||
+        !drho || !workspace)
+        return PLX_ERR_NULL_POINTER;
+    const plx_status_t s = check_bwd_shape(dtype, B, H, T, d_qk, d_v, softmax_scale);
+    if (s != PLX_OK) return s;
+    const void* ptrs[] = {q, k, v, rho, o, vbar, stats, d_o, dq, dk, dv, drho, workspace};
+    for (const void* p : ptrs)
+        if (!aligned16(p)) return PLX_ERR_MISALIGNED;
+    size_t need = 0;
+    plx_attn_prefill_bwd_workspace_size(B, H, T, &need);
+    if (workspace_bytes < need) return PLX_ERR_WORKSPACE_TOO_SMALL;
+    plx::PrefillBwdArgs a{B, H, T, q, k, v, rho, o, vbar, stats, d_o, dq, dk, dv, drho,
+                          static_cast<float*>(workspace), softmax_scale};
+    const hipError_t e = plx::launch_prefill_bwd_bf16_d128(a, static_cast<hipStream_t>(stream));
     return e == hipSuccess ? PLX_OK : PLX_ERR_HIP;
 }
 

@@ -15,6 +15,21 @@ struct PrefillArgs {
     void* o;
     float scale;
     int workers;  // resident workgroups of a persistent launch (the device's compute units)
+    void* vbar = nullptr;    // bf16 d = 128 only: O1 / l per row [B, H, T, d], or nullptr
+    float* stats = nullptr;  // with vbar: (lse, tbar) per row [B, H, T, 2]
+};
+
+// Backward of the causal prefill (bf16, d = 128). All tensors [B, H, T, d] except stats
+// [B, H, T, 2] (lse, tbar from the forward) and ws [B, H, T] x 4 floats (per-row records the
+// dq kernel writes for the dk kernel).
+struct PrefillBwdArgs {
+    int B, H, T;
+    const void *q, *k, *v, *rho, *o, *vbar;
+    const float* stats;
+    const void* dout;
+    void *dq, *dk, *dv, *drho;
+    float* ws;
+    float scale;
 };
 
 struct DecodeArgs {
@@ -56,6 +71,7 @@ struct ProbeArgs {
 bool prefill_f32_supported(int d);
 hipError_t launch_prefill_f32(const PrefillArgs& a, hipStream_t stream);
 hipError_t launch_prefill_bf16_d128(const PrefillArgs& a, hipStream_t stream);
+hipError_t launch_prefill_bwd_bf16_d128(const PrefillBwdArgs& a, hipStream_t stream);
 hipError_t launch_decode_bf16_d128(const DecodeArgs& a, hipStream_t stream);
 hipError_t launch_probe_bf16_d128(const ProbeArgs& a, hipStream_t stream);
 // Grouped query heads: a.H query heads over Hkv cache heads (a.H / Hkv in {1, 2, 4, 8}), split

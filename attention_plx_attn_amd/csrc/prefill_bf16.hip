@@ -96,11 +96,18 @@ __device__ __forceinline__ float max_across_row_groups(float x) {
 // PROBE = false: the softmax-only specialisation (rho = 0 exactly): no R K^T products, no P2,
 // no O2 and no beta, so o = O1 / l. With rho = 0 the full kernel computes the same values in
 // the same order (P2 = 0, beta = 0, o = O1 (1 + 0) / l - 0), so both give identical bits.
-template <bool PROBE>
+//
+// STATS = true also writes, per query row, vbar = O1 / l (the softmax-weighted mean of the
+// values, rounded to bf16) and (lse, tbar) in fp32, with lse the natural log of the softmax
+// normaliser of scale * q.k; the backward pass starts from these. lse and tbar come from
+// extra fp32 sums of the unrounded weights and weight * probe products, so that they agree
+// with the weights and probe products the backward recomputes (with a large probe, |t| ~ 10,
+// the bf16-rounded beta / l would differ from them by ~2^-9 |t|).
+template <bool PROBE, bool STATS>
 __global__ __launch_bounds__(NT, 1) void prefill_bf16_d128_kernel(
     const __bf16* __restrict__ q, const __bf16* __restrict__ k, const __bf16* __restrict__ v,
-    const __bf16* __restrict__ rho, __bf16* __restrict__ o, int BH, int T, int nqb, float c,
-    int ncls) {
+    const __bf16* __restrict__ rho, __bf16* __restrict__ o, __bf16* __restrict__ vbar,
+    float* __restrict__ stats, int BH, int T, int nqb, float c, int ncls) {
     __shared__ __attribute__((aligned(16))) unsigned char lds[LDS_BYTES];
 
     const int tid = threadIdx.x;
@@ -136,6 +143,7 @@ __global__ __launch_bounds__(NT, 1) void prefill_bf16_d128_kernel(
 
     f32x4 a1[8], a2[8];  // O1^T, O2^T: dim block db (16 dims), lane: dims 16 db + 4 gq + i
     float lsum = 0.f, bsum = 0.f;
+    float lsx = 0.f, bsx = 0.f;  // STATS: the same sums of the unrounded weights and products
     float m_run = -INFINITY;
 
     // ---- staging: waves 0-3 load and store the K tile, waves 4-7 the V tile.
@@ -252,6 +260,10 @@ __global__ __launch_bounds__(NT, 1) void prefill_bf16_d128_kernel(
             }
             lsum *= alpha;
             if constexpr (PROBE) bsum *= alpha;
+            if constexpr (STATS) {
+                lsx *= alpha;
+                bsx *= alpha;
+            }
             m_run = mn;
         }
 #pragma unroll
@@ -268,6 +280,10 @@ __global__ __launch_bounds__(NT, 1) void prefill_bf16_d128_kernel(
                 }
                 p1[e] = pack_bf16x2(w0, w1);
                 lsum = add_bf16x2(p1[e], lsum);
+                if constexpr (STATS) {
+                    lsx += w0 + w1;
+                    if constexpr (PROBE) bsx = fmaf(w1, Tp[kb][i0 + 1], fmaf(w0, Tp[kb][i0], bsx));
+                }
                 if constexpr (PROBE) {
                     p2[e] = pack_bf16x2(w0 * Tp[kb][i0], w1 * Tp[kb][i0 + 1]);
                     bsum = add_bf16x2(p2[e], bsum);
@@ -339,6 +355,7 @@ __global__ __launch_bounds__(NT, 1) void prefill_bf16_d128_kernel(
 #pragma unroll
         for (int db = 0; db < 8; ++db) a1[db] = a2[db] = f32x4{};  // a2 stays 0 without PROBE
         lsum = bsum = 0.f;
+        lsx = bsx = 0.f;
         m_run = -INFINITY;
         const int qi = cur.q0 + 16 * w + col;
         f32x4 S[4], Tp[4];
@@ -397,6 +414,25 @@ __global__ __launch_bounds__(NT, 1) void prefill_bf16_d128_kernel(
                 *(u32x2*)(orow + 16 * db + 4 * gq) =
                     u32x2{pack_bf16x2(y[0], y[1]), pack_bf16x2(y[2], y[3])};
             }
+            if constexpr (STATS) {
+                __bf16* vrow = vbar + slice_of(cur.bh) + (size_t)qi * D;
+#pragma unroll
+                for (int db = 0; db < 8; ++db)
+                    *(u32x2*)(vrow + 16 * db + 4 * gq) =
+                        u32x2{pack_bf16x2(inv * a1[db][0], inv * a1[db][1]),
+                              pack_bf16x2(inv * a1[db][2], inv * a1[db][3])};
+                // lse and tbar from the unrounded weights: sum_j exp2(c s_ij) = lsx 2^m_run, so
+                // lse = (m_run + log2 lsx) ln 2, and tbar = bsx / lsx
+                lsx += shfl_xor(lsx, 16);
+                lsx += shfl_xor(lsx, 32);
+                bsx += shfl_xor(bsx, 16);
+                bsx += shfl_xor(bsx, 32);
+                if (gq == 0) {
+                    const float lse = (m_run + __builtin_log2f(lsx)) * 0.6931471805599453f;
+                    *(float2*)(stats + 2 * ((size_t)cur.bh * T + qi)) =
+                        float2{lse, PROBE ? bsx / lsx : 0.f};
+                }
+            }
         }
         if (!has_next) break;
         t0 += nt;
@@ -419,16 +455,20 @@ hipError_t launch_prefill_bf16_d128(const PrefillArgs& a, hipStream_t stream) {
         grid -= grid % 8;
     }
     if (grid < 1 || grid > 0x7fffffffLL) return hipErrorInvalidConfiguration;
-    if (a.rho)
-        hipLaunchKernelGGL(prefill_bf16_d128_kernel<true>, dim3((unsigned)grid), dim3(NT), 0,
-                           stream, (const __bf16*)a.q, (const __bf16*)a.k, (const __bf16*)a.v,
-                           (const __bf16*)a.rho, (__bf16*)a.o, BH, a.T, nqb, a.scale * kLog2e,
-                           ncls);
-    else
-        hipLaunchKernelGGL(prefill_bf16_d128_kernel<false>, dim3((unsigned)grid), dim3(NT), 0,
-                           stream, (const __bf16*)a.q, (const __bf16*)a.k, (const __bf16*)a.v,
-                           (const __bf16*)a.q, (__bf16*)a.o, BH, a.T, nqb, a.scale * kLog2e,
-                           ncls);
+    const __bf16* qp = (const __bf16*)a.q;
+    const __bf16* rp = a.rho ? (const __bf16*)a.rho : qp;  // unread without the probe branch
+    auto go = [&](auto kernel) {
+        hipLaunchKernelGGL(kernel, dim3((unsigned)grid), dim3(NT), 0, stream, qp,
+                           (const __bf16*)a.k, (const __bf16*)a.v, rp, (__bf16*)a.o,
+                           (__bf16*)a.vbar, a.stats, BH, a.T, nqb, a.scale * kLog2e, ncls);
+    };
+    if (a.stats) {
+        if (a.rho) go(prefill_bf16_d128_kernel<true, true>);
+        else go(prefill_bf16_d128_kernel<false, true>);
+    } else {
+        if (a.rho) go(prefill_bf16_d128_kernel<true, false>);
+        else go(prefill_bf16_d128_kernel<false, false>);
+    }
     return hipGetLastError();
 }
 

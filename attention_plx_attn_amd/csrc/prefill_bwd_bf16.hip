@@ -1,0 +1,444 @@
+// prefill_bwd_bf16.hip -- backward of the causal Parallax prefill, bf16 in/out, d = 128, gfx950.
+//
+// The forward computes o_i = sum_j s_ij v_j with s_ij = p_ij (1 - (t_ij - tbar_i)),
+// p_ij = softmax_j(scale <q_i, k_j>), t_ij = <rho_i, k_j>, tbar_i = sum_j p_ij t_ij
+// [Parallax (paper.rainbus.top summary), method steps 2-6; agihunt review, method paragraph].
+// The pages give no backward; the chain rule of that forward, per visible pair (i, j), is
+//
+//   g_ij = <dO_i, v_j>,  G_i = sum_j p_ij g_ij = <dO_i, vbar_i>,  D_i = <dO_i, o_i> + tbar_i G_i
+//   dt_ij = p_ij (G_i - g_ij)
+//   da_ij = p_ij ((1 - t_ij + tbar_i) g_ij + t_ij G_i - D_i)
+//   dV_j = sum_i s_ij dO_i                dK_j = scale sum_i da_ij q_i + sum_i dt_ij rho_i
+//   dQ_i = scale sum_j da_ij k_j          dR_i = sum_j dt_ij k_j
+//
+// with p_ij = exp(scale <q_i, k_j> - lse_i) recomputed from the forward's log-sum-exp, and
+// tbar_i, vbar_i = sum_j p_ij v_j saved by the forward. Two kernels, both on
+// v_mfma_f32_16x16x32_bf16 with fp32 accumulation and the pair quantities rounded to bf16
+// before they enter a product:
+//
+//   * dq kernel: a work item is 128 query rows of one (b, h); 8 waves of 16 rows. It first
+//     forms G_i and D_i for its rows (and hands them, with lse_i and tbar_i, to the dk kernel
+//     through a per-row record), then streams the visible key tiles (64 keys): the products
+//     S^T = K Q^T, T^T = K R^T, g^T = V dO^T take K and V rows from LDS as the A operand and
+//     the wave's Q, R, dO fragments from registers as the B operand; the weight blocks da^T,
+//     dt^T then feed dQ^T += K^T da^T and dR^T += K^T dt^T with K^T read from a transposed
+//     LDS copy of the tile. K and V rows sit in LDS in the forward kernel's key order, so each
+//     lane's product registers already hold the 8 consecutive keys its next operand wants.
+//   * dk kernel: a work item is 128 keys of one (b, h); 8 waves of 16 keys. It streams the
+//     query tiles (32 queries) at or after the item's first key: S = Q K^T, T = R K^T,
+//     g = dO V^T with Q, R, dO rows from LDS (A) and the wave's K, V fragments in registers
+//     (B), then dV^T += dO^T s, dK^T += Q^T (scale da) + R^T dt with transposed LDS copies of
+//     Q, R and dO as the A operand.
+// Both kernels double-buffer their tiles in LDS: tile n + 1 is loaded into registers while
+// tile n is processed and written to the other buffer afterwards; one barrier per tile.
+// Work items are dispatched longest first; with B*H a multiple of 8, item n (dispatched to
+// XCD n % 8) serves head n % (B*H), so all items of a head share one XCD's L2.
+#include "plx_device.hpp"
+#include "plx_kernels.hpp"
+
+namespace plx {
+namespace {
+
+constexpr int D = 128;
+constexpr int NT = 512;   // 8 waves
+constexpr int RS = D + 8;  // LDS row stride of a row-major tile (bf16): 272 bytes
+
+__device__ __forceinline__ f32x4 mfma16(bf16x8 a, bf16x8 b, f32x4 c) {
+    return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
+}
+
+// LDS row of element k (0..63) of a tile: inside each 32-element group, element
+// 8 q + 4 b + i goes to row 16 b + 4 q + i. A product whose A operand is read from these rows
+// leaves, in lane (column, g) of its row blocks 2 G and 2 G + 1, the elements
+// 32 G + 8 g .. 32 G + 8 g + 7: the k-slots of the lane in the next product.
+__device__ __forceinline__ int prow(int k) {
+    return (k & 32) | (((k >> 2) & 1) << 4) | (((k >> 3) & 3) << 2) | (k & 3);
+}
+
+// Transpose four rows (consecutive elements e .. e + 3) of one 8-dim chunk: out[2 p] holds dim
+// 2 p of the four rows, out[2 p + 1] dim 2 p + 1, each as two packed pairs.
+__device__ __forceinline__ void transpose4(const u32x4 (&r)[4], u32x2 (&out)[8]) {
+#pragma unroll
+    for (int p = 0; p < 4; ++p) {
+        out[2 * p] = u32x2{__builtin_amdgcn_perm(r[1][p], r[0][p], 0x05040100u),
+                           __builtin_amdgcn_perm(r[3][p], r[2][p], 0x05040100u)};
+        out[2 * p + 1] = u32x2{__builtin_amdgcn_perm(r[1][p], r[0][p], 0x07060302u),
+                               __builtin_amdgcn_perm(r[3][p], r[2][p], 0x07060302u)};
+    }
+}
+
+__device__ __forceinline__ bf16x8 pack8(const float (&x)[8]) {
+    return __builtin_bit_cast(bf16x8, u32x4{pack_bf16x2(x[0], x[1]), pack_bf16x2(x[2], x[3]),
+                                            pack_bf16x2(x[4], x[5]), pack_bf16x2(x[6], x[7])});
+}
+
+__device__ __forceinline__ float dot8(u32x4 a, u32x4 b, float acc) {
+    const bf16x8 x = as_bf16x8(a), y = as_bf16x8(b);
+#pragma unroll
+    for (int e = 0; e < 8; ++e) acc = fmaf((float)x[e], (float)y[e], acc);
+    return acc;
+}
+
+// Item n of a launch of BH * nblk items, longest first: block index and (b, h).
+__device__ __forceinline__ void item_of(int n, int BH, int nblk, bool longest_last_block,
+                                        int* bh, int* blk) {
+    *bh = n % BH;
+    const int r = n / BH;
+    *blk = longest_last_block ? nblk - 1 - r : r;
+}
+
+// ============================================================================ dq kernel
+constexpr int QBR = 128;                 // query rows per item
+constexpr int KBC = 64;                  // keys per tile
+constexpr int KTS = KBC + 8;             // row stride of the transposed K tile (bf16)
+constexpr int Q_KR = KBC * RS * 2;       // bytes of a row-major K (or V) tile
+constexpr int Q_KT = D * KTS * 2;        // bytes of the transposed K tile
+constexpr int Q_BUF = 2 * Q_KR + Q_KT;
+constexpr int Q_LDS = 2 * Q_BUF;
+static_assert(Q_LDS <= 160 * 1024, "LDS budget");
+
+__global__ __launch_bounds__(NT, 1) void prefill_bwd_dq_kernel(
+    const __bf16* __restrict__ q, const __bf16* __restrict__ k, const __bf16* __restrict__ v,
+    const __bf16* __restrict__ rho, const __bf16* __restrict__ o,
+    const __bf16* __restrict__ vbar, const float* __restrict__ stats,
+    const __bf16* __restrict__ dout, __bf16* __restrict__ dq, __bf16* __restrict__ dr,
+    f32x4* __restrict__ rec, int BH, int T, int nqb, float c, float scale) {
+    __shared__ __attribute__((aligned(16))) unsigned char lds[Q_LDS];
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int col = lane & 15, gq = lane >> 4;
+    int bh, qb;
+    item_of(blockIdx.x, BH, nqb, true, &bh, &qb);
+    const int q0 = qb * QBR;
+    const size_t slice = (size_t)bh * T * D;
+    const uint32_t slice_bytes = (uint32_t)T * D * 2u;
+    const int qi = q0 + 16 * w + col;
+
+    // ---- the wave's fragments (B operand): lane holds dims 32 s + 8 gq .. +7 of query qi
+    bf16x8 xq[4], xr[4], xdo[4];
+    float G, Dd, L2, tbar;
+    {
+        const auto rq = make_rsrc(q + slice, slice_bytes);
+        const auto rr = make_rsrc(rho + slice, slice_bytes);
+        const auto rd = make_rsrc(dout + slice, slice_bytes);
+        const auto ro = make_rsrc(o + slice, slice_bytes);
+        const auto rv = make_rsrc(vbar + slice, slice_bytes);
+        const auto rs = make_rsrc(stats + 2 * (size_t)bh * T, (uint32_t)T * 8u);
+        const uint32_t off = (uint32_t)qi * 256u + 16u * gq;
+        u32x4 vo[4], vv[4], vd[4];
+#pragma unroll
+        for (int s = 0; s < 4; ++s) {
+            xq[s] = as_bf16x8(load16(rq, off + 64u * s));
+            xr[s] = as_bf16x8(load16(rr, off + 64u * s));
+            vd[s] = load16(rd, off + 64u * s);
+            vo[s] = load16(ro, off + 64u * s);
+            vv[s] = load16(rv, off + 64u * s);
+            xdo[s] = as_bf16x8(vd[s]);
+        }
+        const float lse = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(
+                                                        rs, (uint32_t)qi * 8u, 0, 0));
+        tbar = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(
+                                             rs, (uint32_t)qi * 8u + 4u, 0, 0));
+        float pg = 0.f, pd = 0.f;
+#pragma unroll
+        for (int s = 0; s < 4; ++s) {
+            pg = dot8(vd[s], vv[s], pg);
+            pd = dot8(vd[s], vo[s], pd);
+        }
+        pg += shfl_xor(pg, 16);
+        pg += shfl_xor(pg, 32);
+        pd += shfl_xor(pd, 16);
+        pd += shfl_xor(pd, 32);
+        G = pg;
+        Dd = pd + tbar * pg;
+        L2 = lse * kLog2e;
+        if (gq == 0 && qi < T) rec[(size_t)bh * T + qi] = f32x4{L2, tbar, G, Dd};
+    }
+
+    f32x4 aq[8], ar[8];  // dQ^T, dR^T: dim block db, lane: dims 16 db + 4 gq + i of query qi
+#pragma unroll
+    for (int db = 0; db < 8; ++db) aq[db] = ar[db] = f32x4{};
+
+    // ---- staging: waves 0-3 K (row-major and transposed), waves 4-7 V (row-major). Thread st
+    // loads keys 4 (st >> 4) .. +3, dims 8 (st & 15) .. +7.
+    const bool kst = w < 4;
+    const int st = tid & 255, sdc = st & 15, skg = st >> 4;
+    const uint32_t soff = (uint32_t)(4 * skg) * 256u + 16u * sdc;
+    u32x4 stg[4];
+    const int kend = min(q0 + QBR, T);
+    const int ntiles = (kend + KBC - 1) / KBC;
+    const int nfull = min(ntiles, q0 / KBC);
+    auto gload = [&](int kt) {
+        const uint32_t rem = slice_bytes - (uint32_t)kt * KBC * 256u;
+        const auto r = make_rsrc((kst ? k : v) + slice + (size_t)kt * KBC * D, rem);
+#pragma unroll
+        for (int j = 0; j < 4; ++j) stg[j] = load16(r, soff + 256u * j);
+    };
+    auto lstore = [&](int buf) {
+        unsigned char* base = lds + buf * Q_BUF + (kst ? 0 : Q_KR);
+#pragma unroll
+        for (int j = 0; j < 4; ++j)
+            *(u32x4*)(base + prow(4 * skg + j) * RS * 2 + 16 * sdc) = stg[j];
+        if (kst) {
+            __bf16* Kt = (__bf16*)(lds + buf * Q_BUF + 2 * Q_KR);
+            u32x2 tr[8];
+            transpose4(stg, tr);
+            // 16-byte key chunks of a dim row are XOR-swizzled with bits 1..3 of its dim chunk
+            const int cs = 8 * ((skg >> 1) ^ ((sdc >> 1) & 7)) + 4 * (skg & 1);
+#pragma unroll
+            for (int r = 0; r < 8; ++r) *(u32x2*)(Kt + (8 * sdc + r) * KTS + cs) = tr[r];
+        }
+    };
+    // transposed reads: dim row 16 db + col, keys 32 G + 8 gq .. +7 at chunk (4 G + gq) ^ swz
+    int tlane[4];
+#pragma unroll
+    for (int x = 0; x < 4; ++x) tlane[x] = col * KTS * 2 + 16 * (gq ^ x);
+
+    auto tile = [&](int kt, int buf, bool diag) {
+        const unsigned char* Kr = lds + buf * Q_BUF + col * RS * 2 + 16 * gq;
+        const unsigned char* Vr = Kr + Q_KR;
+        const unsigned char* Kt = lds + buf * Q_BUF + 2 * Q_KR;
+        f32x4 S[4], Tp[4], Gm[4];
+#pragma unroll
+        for (int kb = 0; kb < 4; ++kb) {
+            S[kb] = Tp[kb] = Gm[kb] = f32x4{};
+#pragma unroll
+            for (int s = 0; s < 4; ++s) {
+                const bf16x8 kf = *(const bf16x8*)(Kr + 16 * kb * RS * 2 + 64 * s);
+                const bf16x8 vf = *(const bf16x8*)(Vr + 16 * kb * RS * 2 + 64 * s);
+                S[kb] = mfma16(kf, xq[s], S[kb]);
+                Tp[kb] = mfma16(kf, xr[s], Tp[kb]);
+                Gm[kb] = mfma16(vf, xdo[s], Gm[kb]);
+            }
+        }
+        // register i of block kb: key kt * 64 + 32 (kb >> 1) + 8 gq + 4 (kb & 1) + i
+        const int lim = qi - kt * KBC - 8 * gq;
+#pragma unroll
+        for (int G2 = 0; G2 < 2; ++G2) {
+            float fa[8], ft[8];
+#pragma unroll
+            for (int b = 0; b < 2; ++b)
+#pragma unroll
+                for (int i = 0; i < 4; ++i) {
+                    const int kb = 2 * G2 + b;
+                    float p = exp2_fast(fmaf(S[kb][i], c, -L2));
+                    if (diag && 32 * G2 + 4 * b + i > lim) p = 0.f;
+                    const float t = Tp[kb][i], g = Gm[kb][i];
+                    ft[4 * b + i] = p * (G - g);
+                    fa[4 * b + i] = p * (fmaf(1.f - t + tbar, g, t * G) - Dd);
+                }
+            const bf16x8 da = pack8(fa), dt = pack8(ft);
+#pragma unroll
+            for (int db = 0; db < 8; ++db) {
+                const bf16x8 kf = *(const bf16x8*)(Kt + tlane[db & 3] + 16 * db * KTS * 2 +
+                                                   64 * (G2 ^ (db >> 2)));
+                aq[db] = mfma16(kf, da, aq[db]);
+                ar[db] = mfma16(kf, dt, ar[db]);
+            }
+        }
+    };
+
+    gload(0);
+    lstore(0);
+    __syncthreads();
+    for (int kt = 0; kt < ntiles; ++kt) {
+        const int buf = kt & 1;
+        const bool more = kt + 1 < ntiles;
+        if (more) gload(kt + 1);
+        // a wave whose rows all precede the tile's first key has nothing to add
+        if (kt * KBC <= q0 + 16 * w + 15) tile(kt, buf, kt >= nfull);
+        if (more) lstore(buf ^ 1);
+        __syncthreads();
+    }
+
+    if (qi < T) {
+        __bf16* qrow = dq + slice + (size_t)qi * D;
+        __bf16* rrow = dr + slice + (size_t)qi * D;
+#pragma unroll
+        for (int db = 0; db < 8; ++db) {
+            *(u32x2*)(qrow + 16 * db + 4 * gq) =
+                u32x2{pack_bf16x2(scale * aq[db][0], scale * aq[db][1]),
+                      pack_bf16x2(scale * aq[db][2], scale * aq[db][3])};
+            *(u32x2*)(rrow + 16 * db + 4 * gq) = u32x2{pack_bf16x2(ar[db][0], ar[db][1]),
+                                                       pack_bf16x2(ar[db][2], ar[db][3])};
+        }
+    }
+}
+
+// ============================================================================ dk kernel
+constexpr int KBR = 128;                // keys per item
+constexpr int QBC = 32;                 // queries per tile
+constexpr int QTS = QBC + 8;            // row stride of a transposed tile (bf16): 80 bytes
+constexpr int K_R = QBC * RS * 2;       // bytes of one row-major tile (Q, R or dO)
+constexpr int K_T = D * QTS * 2;        // bytes of one transposed tile
+constexpr int K_REC = QBC * 16;         // per-row records (L2, tbar, G, D)
+constexpr int K_BUF = 3 * K_R + 3 * K_T + K_REC;
+constexpr int K_LDS = 2 * K_BUF;
+static_assert(K_LDS <= 160 * 1024, "LDS budget");
+
+__global__ __launch_bounds__(NT, 1) void prefill_bwd_dk_kernel(
+    const __bf16* __restrict__ q, const __bf16* __restrict__ k, const __bf16* __restrict__ v,
+    const __bf16* __restrict__ rho, const __bf16* __restrict__ dout,
+    const f32x4* __restrict__ rec, __bf16* __restrict__ dk, __bf16* __restrict__ dv, int BH,
+    int T, int nkb, float c, float scale) {
+    __shared__ __attribute__((aligned(16))) unsigned char lds[K_LDS];
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int col = lane & 15, gq = lane >> 4;
+    int bh, kbi;
+    item_of(blockIdx.x, BH, nkb, false, &bh, &kbi);
+    const int k0 = kbi * KBR;
+    const size_t slice = (size_t)bh * T * D;
+    const uint32_t slice_bytes = (uint32_t)T * D * 2u;
+    const int kj = k0 + 16 * w + col;  // the lane's key (score column)
+
+    bf16x8 xk[4], xv[4];
+    {
+        const auto rk = make_rsrc(k + slice, slice_bytes);
+        const auto rv = make_rsrc(v + slice, slice_bytes);
+        const uint32_t off = (uint32_t)kj * 256u + 16u * gq;
+#pragma unroll
+        for (int s = 0; s < 4; ++s) {
+            xk[s] = as_bf16x8(load16(rk, off + 64u * s));
+            xv[s] = as_bf16x8(load16(rv, off + 64u * s));
+        }
+    }
+    f32x4 ak[8], av[8];  // dK^T, dV^T: dim block db, lane: dims 16 db + 4 gq + i of key kj
+#pragma unroll
+    for (int db = 0; db < 8; ++db) ak[db] = av[db] = f32x4{};
+
+    // ---- staging: waves 0-1 Q, 2-3 R, 4-5 dO (rows 4 (u >> 4) .. +3, dims 8 (u & 15) .. +7),
+    // row-major and transposed; wave 6 the 32 per-row records.
+    const int which = w >> 1;  // 0 Q, 1 R, 2 dO, 3 records / idle
+    const int u = tid & 127, sdc = u & 15, sqg = u >> 4;
+    const __bf16* src = which == 0 ? q : which == 1 ? rho : dout;
+    u32x4 stg[4];
+    const int qt0 = k0 / QBC;                       // first query tile of the item
+    const int ntiles = (T + QBC - 1) / QBC - qt0;
+    auto gload = [&](int n) {
+        const int r0 = (qt0 + n) * QBC;
+        if (which < 3) {
+            const auto r = make_rsrc(src + slice + (size_t)r0 * D,
+                                     slice_bytes - (uint32_t)r0 * 256u);
+            const uint32_t off = (uint32_t)(4 * sqg) * 256u + 16u * sdc;
+#pragma unroll
+            for (int j = 0; j < 4; ++j) stg[j] = load16(r, off + 256u * j);
+        } else if (w == 6 && lane < QBC) {
+            const auto r = make_rsrc(rec + (size_t)bh * T + r0, (uint32_t)(T - r0) * 16u);
+            stg[0] = load16(r, 16u * lane);
+        }
+    };
+    auto lstore = [&](int buf) {
+        unsigned char* base = lds + buf * K_BUF;
+        if (which < 3) {
+            unsigned char* R = base + which * K_R;
+#pragma unroll
+            for (int j = 0; j < 4; ++j)
+                *(u32x4*)(R + prow(4 * sqg + j) * RS * 2 + 16 * sdc) = stg[j];
+            __bf16* Tt = (__bf16*)(base + 3 * K_R + which * K_T);
+            u32x2 tr[8];
+            transpose4(stg, tr);
+#pragma unroll
+            for (int r = 0; r < 8; ++r) *(u32x2*)(Tt + (8 * sdc + r) * QTS + 4 * sqg) = tr[r];
+        } else if (w == 6 && lane < QBC) {
+            *(u32x4*)(base + 3 * K_R + 3 * K_T + 16 * lane) = stg[0];
+        }
+    };
+
+    auto tile = [&](int n, int buf, bool mask) {
+        const unsigned char* base = lds + buf * K_BUF;
+        const unsigned char* Qr = base + col * RS * 2 + 16 * gq;
+        const unsigned char* Rr = Qr + K_R;
+        const unsigned char* Dr = Qr + 2 * K_R;
+        f32x4 S[2], Tp[2], Gm[2];
+#pragma unroll
+        for (int b = 0; b < 2; ++b) {
+            S[b] = Tp[b] = Gm[b] = f32x4{};
+#pragma unroll
+            for (int s = 0; s < 4; ++s) {
+                const int o = 16 * b * RS * 2 + 64 * s;
+                S[b] = mfma16(*(const bf16x8*)(Qr + o), xk[s], S[b]);
+                Tp[b] = mfma16(*(const bf16x8*)(Rr + o), xk[s], Tp[b]);
+                Gm[b] = mfma16(*(const bf16x8*)(Dr + o), xv[s], Gm[b]);
+            }
+        }
+        // register i of block b: query (qt0 + n) * 32 + 8 gq + 4 b + i
+        const f32x4* recs = (const f32x4*)(base + 3 * K_R + 3 * K_T) + 8 * gq;
+        const int qbase = (qt0 + n) * QBC + 8 * gq;
+        float fs[8], fa[8], ft[8];
+#pragma unroll
+        for (int b = 0; b < 2; ++b)
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                const f32x4 rw = recs[4 * b + i];  // L2, tbar, G, D
+                float p = exp2_fast(fmaf(S[b][i], c, -rw[0]));
+                const int qi = qbase + 4 * b + i;
+                if (mask && (qi < kj || qi >= T)) p = 0.f;
+                const float t = Tp[b][i], g = Gm[b][i];
+                const float one = 1.f - t + rw[1];
+                fs[4 * b + i] = p * one;
+                ft[4 * b + i] = p * (rw[2] - g);
+                fa[4 * b + i] = scale * p * (fmaf(one, g, t * rw[2]) - rw[3]);
+            }
+        const bf16x8 ps = pack8(fs), pa = pack8(fa), pt = pack8(ft);
+        const unsigned char* Tq = base + 3 * K_R + col * QTS * 2 + 16 * gq;
+#pragma unroll
+        for (int db = 0; db < 8; ++db) {
+            const int o = 16 * db * QTS * 2;
+            av[db] = mfma16(*(const bf16x8*)(Tq + 2 * K_T + o), ps, av[db]);
+            ak[db] = mfma16(*(const bf16x8*)(Tq + o), pa, ak[db]);
+            ak[db] = mfma16(*(const bf16x8*)(Tq + K_T + o), pt, ak[db]);
+        }
+    };
+
+    const int tail = (T - 1) / QBC - qt0;  // local index of the tile holding row T - 1
+    gload(0);
+    lstore(0);
+    __syncthreads();
+    for (int n = 0; n < ntiles; ++n) {
+        const int buf = n & 1;
+        const bool more = n + 1 < ntiles;
+        if (more) gload(n + 1);
+        const int r0 = (qt0 + n) * QBC;
+        // rows r0 .. r0 + 31 all precede the wave's first key: nothing to add
+        if (r0 + QBC - 1 >= k0 + 16 * w) tile(n, buf, r0 < k0 + KBR || n == tail);
+        if (more) lstore(buf ^ 1);
+        __syncthreads();
+    }
+
+    if (kj < T) {
+        __bf16* krow = dk + slice + (size_t)kj * D;
+        __bf16* vrow = dv + slice + (size_t)kj * D;
+#pragma unroll
+        for (int db = 0; db < 8; ++db) {
+            *(u32x2*)(krow + 16 * db + 4 * gq) = u32x2{pack_bf16x2(ak[db][0], ak[db][1]),
+                                                       pack_bf16x2(ak[db][2], ak[db][3])};
+            *(u32x2*)(vrow + 16 * db + 4 * gq) = u32x2{pack_bf16x2(av[db][0], av[db][1]),
+                                                       pack_bf16x2(av[db][2], av[db][3])};
+        }
+    }
+}
+
+}  // namespace
+
+hipError_t launch_prefill_bwd_bf16_d128(const PrefillBwdArgs& a, hipStream_t stream) {
+    const int BH = a.B * a.H;
+    const int nblk = (a.T + 127) / 128;
+    const long long items = (long long)BH * nblk;
+    if (items < 1 || items > 0x7fffffffLL) return hipErrorInvalidConfiguration;
+    const float c = a.scale * kLog2e;
+    hipLaunchKernelGGL(prefill_bwd_dq_kernel, dim3((unsigned)items), dim3(NT), 0, stream,
+                       (const __bf16*)a.q, (const __bf16*)a.k, (const __bf16*)a.v,
+                       (const __bf16*)a.rho, (const __bf16*)a.o, (const __bf16*)a.vbar,
+                       a.stats, (const __bf16*)a.dout, (__bf16*)a.dq, (__bf16*)a.drho,
+                       (f32x4*)a.ws, BH, a.T, nblk, c, a.scale);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    hipLaunchKernelGGL(prefill_bwd_dk_kernel, dim3((unsigned)items), dim3(NT), 0, stream,
+                       (const __bf16*)a.q, (const __bf16*)a.k, (const __bf16*)a.v,
+                       (const __bf16*)a.rho, (const __bf16*)a.dout, (const f32x4*)a.ws,
+                       (__bf16*)a.dk, (__bf16*)a.dv, BH, a.T, nblk, c, a.scale);
+    return hipGetLastError();
+}
+
+}  // namespace plx

@@ -202,6 +202,48 @@ plx_status_t plx_attn_probe(plx_dtype_t dtype, int32_t B, int32_t T, int32_t C, 
                             const float* gate, const int32_t* positions, float eps,
                             float rope_base, void* rho, void* stream);
 
+/*
+ * Training support: the causal prefill with saved statistics, and its backward.
+ *
+ * The layer is trained from scratch (0.6B and 1.7B language models pretrained with it:
+ * Parallax (paper.rainbus.top summary), sections "实验结果" and "复现评估"), but the pages give
+ * no backward; the gradients below are the chain rule of the forward (1) in its
+ * corrected-weight form. For each visible pair (i, j), with s_ij = p_ij (1 - t_ij +
+ * tbar_i), g_ij = <dO_i, v_j>, G_i = <dO_i, vbar_i>, D_i = <dO_i, o_i> + tbar_i G_i:
+ *     dt_ij = p_ij (G_i - g_ij)        da_ij = p_ij ((1 - t_ij + tbar_i) g_ij + t_ij G_i - D_i)
+ *     dv_j = sum_i s_ij dO_i           dk_j = scale sum_i da_ij q_i + sum_i dt_ij rho_i
+ *     dq_i = scale sum_j da_ij k_j     drho_i = sum_j dt_ij k_j
+ *
+ * plx_attn_prefill_fwd: as plx_attn_prefill (same o, bit for bit), and also writes
+ *   vbar  : [B, H, T, d] (dtype) the softmax-weighted mean of the values, O1 / l, per row
+ *   stats : [B, H, T, 2] float, per row (lse, tbar): lse = ln sum_j exp(scale <q_i, k_j>)
+ *           over the visible keys, tbar = sum_j p_ij t_ij (0 when rho == NULL)
+ *
+ * plx_attn_prefill_bwd: gradients of sum(d_o * o) with respect to q, k, v and rho, given the
+ *   forward's inputs, its o, vbar and stats, and d_o [B, H, T, d]. rho must not be NULL (pass
+ *   zeros for plain softmax attention; drho is still the gradient at rho = 0).
+ *   dq, dk, dv, drho : [B, H, T, d] (dtype), written; none may alias an input
+ *   workspace        : device buffer of plx_attn_prefill_bwd_workspace_size() bytes (per-row
+ *                      records passed between the two kernels of the call)
+ * Arithmetic: products on the matrix cores (bf16 operands, fp32 accumulation); the pair
+ * quantities s, scale * da and dt are rounded to bf16 before the accumulating products; p is
+ * recomputed as exp(scale <q_i, k_j> - lse_i). Output rounded to bf16 (RNE).
+ * Built combination (both calls): (PLX_BF16, d_qk = d_v = 128). Limits: T * 256 < 2^31.
+ * Errors as for the other entry points; PLX_ERR_WORKSPACE_TOO_SMALL for a short workspace.
+ */
+plx_status_t plx_attn_prefill_fwd(plx_dtype_t dtype, int32_t B, int32_t H, int32_t T,
+                                  int32_t d_qk, int32_t d_v, const void* q, const void* k,
+                                  const void* v, const void* rho, void* o, void* vbar,
+                                  float* stats, float softmax_scale, void* stream);
+plx_status_t plx_attn_prefill_bwd_workspace_size(int32_t B, int32_t H, int32_t T,
+                                                 size_t* bytes_out);
+plx_status_t plx_attn_prefill_bwd(plx_dtype_t dtype, int32_t B, int32_t H, int32_t T,
+                                  int32_t d_qk, int32_t d_v, const void* q, const void* k,
+                                  const void* v, const void* rho, const void* o,
+                                  const void* vbar, const float* stats, const void* d_o,
+                                  void* dq, void* dk, void* dv, void* drho, void* workspace,
+                                  size_t workspace_bytes, float softmax_scale, void* stream);
+
 /* Static, NUL-terminated description of a status code. */
 const char* plx_status_string(plx_status_t s);
 

@@ -136,7 +136,8 @@ def threads() -> int:
     return int(_load().plx_oracle_threads())
 
 
-from .backward import prefill_backward  # noqa: E402
+from .backward import prefill_backward, prefill_stats  # noqa: E402
 from .probe import probe  # noqa: E402
 
-__all__ = ["build", "prefill", "decode", "threads", "probe", "prefill_backward"]
+__all__ = ["build", "prefill", "decode", "threads", "probe", "prefill_backward",
+           "prefill_stats"]

@@ -15,13 +15,39 @@ give no backward formulas; these are the chain rule of that forward, written out
   dQ_i  = scale sum_j da_ij k_j           dK_j = scale sum_i da_ij q_i + sum_i dt_ij rho_i
   dR_i  = sum_j dt_ij k_j
 
+``prefill_stats`` gives the per-row quantities a forward pass saves for the backward
+(lse, tbar, vbar).
+
 Pins: tests/test_oracle_backward_pins.py (finite differences of the pinned forward oracle;
 torch float64 autograd of softmax attention at rho = 0; dR = -Sigma_KV^T dO, since the
-correction is linear in rho).
+correction is linear in rho; the saved statistics against scipy's logsumexp, the pinned forward
+at rho = 0, and that forward with the keys as values).
 """
 from __future__ import annotations
 
 import numpy as np
+
+
+def prefill_stats(q, k, v, rho, scale: float):
+    """What a forward pass saves for the backward, per query row of the causal prefill:
+    lse_i = ln sum_{j<=i} exp(scale <q_i, k_j>), tbar_i = sum_j p_ij <rho_i, k_j> and
+    vbar_i = sum_j p_ij v_j (the softmax-attention output). Returns ([B,H,T], [B,H,T], [B,H,T,d])."""
+    q, k, v, rho = (np.asarray(a, dtype=np.float64) for a in (q, k, v, rho))
+    B, H, T, _ = q.shape
+    lse = np.zeros((B, H, T))
+    tbar = np.zeros((B, H, T))
+    vbar = np.zeros(v.shape)
+    visible = np.tril(np.ones((T, T), dtype=bool))
+    for b in range(B):
+        for h in range(H):
+            a = np.where(visible, scale * (q[b, h] @ k[b, h].T), -np.inf)
+            m = a.max(axis=1, keepdims=True)
+            e = np.exp(a - m)
+            lse[b, h] = (m + np.log(e.sum(axis=1, keepdims=True)))[:, 0]
+            p = e / e.sum(axis=1, keepdims=True)
+            tbar[b, h] = (p * (rho[b, h] @ k[b, h].T)).sum(axis=1)
+            vbar[b, h] = p @ v[b, h]
+    return lse, tbar, vbar
 
 
 def prefill_backward(q, k, v, rho, scale: float, do):
@@ -51,4 +77,4 @@ def prefill_backward(q, k, v, rho, scale: float, do):
     return dq, dk, dv, dr
 
 
-__all__ = ["prefill_backward"]
+__all__ = ["prefill_backward", "prefill_stats"]

@@ -12,5 +12,6 @@ from .inputs import (  # noqa: F401
     decode_inputs,
     decode_grid_cells,
     prefill_inputs,
+    prefill_upstream_grad,
     to_dtype,
 )

@@ -28,7 +28,7 @@ import numpy as np
 import torch
 
 # tensor ids inside the key
-T_Q, T_K, T_V, T_X, T_WR, T_SEQ, T_RHO = 0, 1, 2, 3, 4, 5, 6
+T_Q, T_K, T_V, T_X, T_WR, T_SEQ, T_RHO, T_DO = 0, 1, 2, 3, 4, 5, 6, 7
 
 RMS_EPS = 1e-6
 
@@ -159,6 +159,12 @@ def prefill_inputs(cfg: PrefillConfig, seed: int = 0, device: Optional[str] = No
         out = {k_: t.to(device) for k_, t in out.items()}
     out["scale"] = cfg.scale
     return out
+
+
+def prefill_upstream_grad(cfg: PrefillConfig, seed: int = 0) -> torch.Tensor:
+    """The gradient arriving at the prefill output for a backward pass: N(0, 1), [B, H, T, d]."""
+    return to_dtype(_per_head((cfg.B, cfg.H, cfg.T, cfg.d), seed, cfg.cfg_id, T_DO, cfg.H),
+                    cfg.dtype)
 
 
 def small_prefill(B, H, T, d, dtype="bf16", rho="scaled", seed=0, cfg_id=100):

@@ -21,7 +21,8 @@ def test_exports_every_declared_symbol(lib):
     assert set(declared) == {"plx_attn_prefill", "plx_attn_decode", "plx_attn_decode_num_splits",
                              "plx_attn_decode_workspace_size", "plx_attn_probe",
                              "plx_attn_decode_gqa", "plx_attn_decode_gqa_plan",
-                             "plx_attn_decode_paged",
+                             "plx_attn_decode_paged", "plx_attn_prefill_fwd",
+                             "plx_attn_prefill_bwd", "plx_attn_prefill_bwd_workspace_size",
                              "plx_status_string"}
     out = subprocess.run(["nm", "-D", "--defined-only", plx.LIB_PATH], capture_output=True,
                          text=True, check=True).stdout
@@ -177,3 +178,49 @@ def test_decode_paged_validation(lib):
     assert _paged(lib, dqk=64, dv=64) == 4
     assert _paged(lib, tab=A + 2) == 5
     assert _paged(lib, mb=16, splits=4) == 1               # workspace required
+
+
+def _fwd(lib, dtype=1, B=1, H=2, T=64, dqk=128, dv=128, q=A, k=A, v=A, rho=A, o=A, vbar=A,
+         stats=A, scale=0.1):
+    return lib.plx_attn_prefill_fwd(dtype, B, H, T, dqk, dv, q, k, v, rho, o, vbar, stats,
+                                    scale, None)
+
+
+def _bwd(lib, dtype=1, B=1, H=2, T=64, dqk=128, dv=128, ptrs=None, ws_bytes=None, scale=0.1):
+    p = dict.fromkeys(("q", "k", "v", "rho", "o", "vbar", "stats", "d_o", "dq", "dk", "dv",
+                       "drho", "ws"), A)
+    p.update(ptrs or {})
+    if ws_bytes is None:
+        ws_bytes = B * H * T * 16
+    return lib.plx_attn_prefill_bwd(dtype, B, H, T, dqk, dv, *p.values(), ws_bytes, scale, None)
+
+
+def test_prefill_fwd_validation(lib):
+    assert _fwd(lib, vbar=0) == 1
+    assert _fwd(lib, stats=0) == 1
+    assert _fwd(lib, o=0) == 1
+    assert _fwd(lib, T=0) == 2
+    assert _fwd(lib, T=1 << 23) == 2                          # T * 256 >= 2^31
+    assert _fwd(lib, scale=-1.0) == 3
+    assert _fwd(lib, dtype=7) == 3
+    assert _fwd(lib, dtype=0) == 4                            # fp32 not built
+    assert _fwd(lib, dqk=64, dv=64) == 4
+    assert _fwd(lib, stats=A + 4) == 5
+    assert _fwd(lib, vbar=A + 2) == 5
+
+
+def test_prefill_bwd_validation(lib):
+    n = ctypes.c_size_t(0)
+    assert lib.plx_attn_prefill_bwd_workspace_size(2, 3, 100, ctypes.byref(n)) == 0
+    assert n.value == 2 * 3 * 100 * 16
+    assert lib.plx_attn_prefill_bwd_workspace_size(2, 0, 100, ctypes.byref(n)) == 2
+    assert lib.plx_attn_prefill_bwd_workspace_size(2, 3, 100, None) == 1
+    for name in ("q", "k", "v", "rho", "o", "vbar", "stats", "d_o", "dq", "dk", "dv", "drho",
+                 "ws"):
+        assert _bwd(lib, ptrs={name: 0}) == 1, name
+        assert _bwd(lib, ptrs={name: A + 8}) == 5, name
+    assert _bwd(lib, T=-1) == 2
+    assert _bwd(lib, scale=float("inf")) == 3
+    assert _bwd(lib, dtype=0) == 4
+    assert _bwd(lib, dqk=128, dv=64) == 4
+    assert _bwd(lib, ws_bytes=1 * 2 * 64 * 16 - 1) == 6

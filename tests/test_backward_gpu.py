@@ -1,0 +1,136 @@
+"""GPU parity of the prefill backward (plx_attn_prefill_fwd + plx_attn_prefill_bwd) against
+the fp64 oracle (oracle.prefill_stats, oracle.prefill_backward) on the same bf16 inputs.
+
+Tolerances. vbar uses the bf16 bar of the forward (parity.check_bf16: elementwise 1e-2 beyond
+half an output ulp, rel-L2 <= 5e-3). Gradients use the same two numbers with the elementwise
+one taken relative to the tensor's scale: |g - r| <= ulp(r)/2 + 1e-2 max(1, max |r|) and
+rel-L2 <= 5e-3. The forward's bar is for outputs of unit scale; gradients reach ~40 (drho sums
+dt_ij k_j with g_ij ~ N(0, d)), and every error source of the backward is relative: the pair
+quantities s, scale * da and dt are rounded to bf16 (2^-9) before their products, and G and D
+are formed from the forward's bf16 vbar and o (each element within 2^-9). Emulating those
+roundings in fp64 gives rel-L2 ~3e-3 and elementwise errors ~1e-3 of the tensor's largest
+value. A gradient that is exactly zero (dq, dk and drho with a single key) must be within 1e-2
+absolute. lse and tbar come from fp32 sums of the unrounded weights in the forward: within
+1e-3 absolute (fp32 sums over <= 2^15 terms and the hardware exp2, ~1e-5 in practice).
+"""
+import numpy as np
+import pytest
+import torch
+
+import attention_plx_attn_amd as plx
+import oracle
+from parity import BF16_ABS, BF16_REL_L2, check_bf16, metrics, to_f64
+from plx_synth import CONFIGS, prefill_inputs, prefill_upstream_grad
+from plx_synth.inputs import PrefillConfig
+
+pytestmark = pytest.mark.gpu
+DEV = "cuda:0"
+LSE_ABS, TBAR_ABS = 1e-3, 1e-3
+
+
+def _say(*a):
+    print(*a, flush=True)
+
+
+def _inputs(cfg, seed):
+    x = prefill_inputs(cfg, seed=seed)
+    x["d_o"] = prefill_upstream_grad(cfg, seed=seed)
+    return x
+
+
+def _gpu(x, rho=True):
+    d = {k: x[k].to(DEV) for k in ("q", "k", "v", "rho", "d_o")}
+    o, vbar, stats = plx.prefill_fwd(d["q"], d["k"], d["v"], d["rho"] if rho else None,
+                                     x["scale"])
+    grads = plx.prefill_bwd(d["q"], d["k"], d["v"], d["rho"], o, vbar, stats, d["d_o"],
+                            x["scale"])
+    torch.cuda.synchronize()
+    return d, o, vbar, stats, grads
+
+
+def check_grad(got, ref, what):
+    m = metrics(got, ref)
+    assert m["finite"], f"{what}: non-finite output"
+    assert m["excess_over_half_ulp"] <= BF16_ABS * max(1.0, float(np.abs(ref).max())), \
+        f"{what}: {m}"
+    assert m["rel_l2"] <= BF16_REL_L2, f"{what}: {m}"
+    return m
+
+
+def _check_grads(grads, x, what, sel=(slice(None), slice(None))):
+    ref = oracle.prefill_backward(*(to_f64(x[n])[sel] for n in ("q", "k", "v", "rho")),
+                                  x["scale"], to_f64(x["d_o"])[sel])
+    out = {}
+    for name, g, r in zip(("dq", "dk", "dv", "drho"), grads, ref):
+        if not np.any(r):  # an exactly-zero gradient (one key: dq = dk = drho = 0)
+            assert np.abs(to_f64(g[sel])).max() <= BF16_ABS, f"{what} {name}"
+            continue
+        out[name] = check_grad(g[sel], r, f"{what} {name}")
+    _say(what, {k: (round(m["max_abs"], 5), round(m["rel_l2"], 6)) for k, m in out.items()})
+
+
+@pytest.mark.parametrize("B,H,T,rho", [(1, 2, 1, "scaled"), (1, 2, 64, "scaled"),
+                                       (1, 2, 100, "proj32"), (2, 3, 333, "scaled"),
+                                       (1, 2, 1024, "proj32")])
+def test_forward_statistics(B, H, T, rho):
+    cfg = PrefillConfig("bwd", 41, B, H, T, 128, "bf16", rho)
+    x = _inputs(cfg, seed=T)
+    _say("fwd stats", B, H, T)
+    d, o, vbar, stats, _ = _gpu(x)
+    plain = plx.prefill(d["q"], d["k"], d["v"], d["rho"], x["scale"])
+    torch.cuda.synchronize()
+    assert torch.equal(o, plain)
+    lse, tbar, vb = oracle.prefill_stats(*(to_f64(x[n]) for n in ("q", "k", "v", "rho")),
+                                         x["scale"])
+    check_bf16(vbar, vb, "vbar")
+    s = to_f64(stats)
+    e_lse, e_tbar = np.abs(s[..., 0] - lse).max(), np.abs(s[..., 1] - tbar).max()
+    _say("lse err", e_lse, "tbar err", e_tbar)
+    assert e_lse <= LSE_ABS and e_tbar <= TBAR_ABS
+
+
+def test_forward_statistics_softmax_only():
+    cfg = PrefillConfig("bwd", 42, 1, 2, 200, 128, "bf16", "scaled")
+    x = _inputs(cfg, seed=0)
+    d, o, vbar, stats, _ = _gpu(x, rho=False)
+    assert torch.equal(o, plx.prefill(d["q"], d["k"], d["v"], None, x["scale"]))
+    assert torch.count_nonzero(stats[..., 1]).item() == 0
+
+
+@pytest.mark.parametrize("B,H,T", [(1, 1, 1), (1, 2, 31), (1, 2, 64), (1, 2, 100),
+                                   (2, 3, 333), (1, 2, 1024), (2, 1, 700)])
+@pytest.mark.parametrize("rho", ["scaled", "proj32"])
+def test_backward_parity(B, H, T, rho):
+    cfg = PrefillConfig("bwd", 43, B, H, T, 128, "bf16", rho)
+    x = _inputs(cfg, seed=T + 1)
+    _say("bwd", B, H, T, rho)
+    _, _, _, _, grads = _gpu(x)
+    _check_grads(grads, x, f"bwd B={B} H={H} T={T} rho={rho}")
+
+
+def test_backward_rho_zero_is_softmax_attention():
+    cfg = PrefillConfig("bwd", 44, 1, 2, 300, 128, "bf16", "zero")
+    x = _inputs(cfg, seed=5)
+    _say("bwd rho=0")
+    _, _, _, _, grads = _gpu(x)
+    _check_grads(grads, x, "bwd rho=0")
+
+
+def test_backward_deterministic():
+    cfg = PrefillConfig("bwd", 45, 2, 2, 500, 128, "bf16", "scaled")
+    x = _inputs(cfg, seed=2)
+    d, o, vbar, stats, g1 = _gpu(x)
+    g2 = plx.prefill_bwd(d["q"], d["k"], d["v"], d["rho"], o, vbar, stats, d["d_o"], x["scale"])
+    torch.cuda.synchronize()
+    for a, b in zip(g1, g2):
+        assert torch.equal(a, b)
+
+
+def test_backward_full_size_sampled_heads():
+    """B=4, H=16, T=2048 (the prefill workload), every row of three sampled (b, h)."""
+    cfg = CONFIGS["prefill_bf16"]
+    x = _inputs(cfg, seed=0)
+    _say("bwd full size", cfg)
+    _, _, _, _, grads = _gpu(x)
+    for b, h in ((0, 0), (1, 7), (3, 15)):
+        _check_grads(grads, x, f"bwd full b={b} h={h}", (slice(b, b + 1), slice(h, h + 1)))

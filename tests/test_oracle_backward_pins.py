@@ -7,8 +7,12 @@
   attention (the layer is then softmax attention; agihunt review, method paragraph);
 * dR_i = -(Sigma_KV^(i))^T dO_i: the correction is Sigma_KV rho with Sigma_KV independent of
   rho [gist.science summary (Spanish), central equation], checked with numpy.cov weights;
-* planted mistakes in copies (a sign, the tbar path, the softmax term) fail the pins.
+* planted mistakes in copies (a sign, the tbar path, the softmax term) fail the pins;
+* the saved statistics (oracle.prefill_stats): lse against scipy.special.logsumexp of the
+  visible scores, vbar against the pinned forward at rho = 0 (softmax attention), and tbar as
+  <rho_i, kbar_i> with kbar the same forward run with the keys as values.
 """
+import scipy.special
 import numpy as np
 import pytest
 import torch
@@ -112,3 +116,20 @@ def _mutant(kind):
 def test_pins_catch_planted_mistakes(kind):
     assert _fd_ok(_mutant("none"), 0)
     assert not _fd_ok(_mutant(kind), 0)
+
+
+@pytest.mark.parametrize("seed", range(3))
+def test_saved_statistics(seed):
+    q, k, v, rho, _ = _draw(seed, B=2, H=2, T=10, d=6)
+    scale = 0.8
+    lse, tbar, vbar = oracle.prefill_stats(q, k, v, rho, scale)
+    for b in range(2):
+        for h in range(2):
+            for i in range(10):
+                s = scale * (k[b, h, : i + 1] @ q[b, h, i])
+                assert np.isclose(lse[b, h, i], scipy.special.logsumexp(s), rtol=1e-13)
+    zero = np.zeros_like(rho)
+    assert np.allclose(vbar, oracle.prefill(q, k, v, zero, scale, form="cov"), rtol=1e-12,
+                       atol=1e-13)
+    kbar = oracle.prefill(q, k, k, zero, scale, form="cov")
+    assert np.allclose(tbar, np.einsum("bhtd,bhtd->bht", rho, kbar), rtol=1e-12, atol=1e-13)

@@ -307,10 +307,12 @@ __global__ __launch_bounds__(NT, 1) void prefill_bwd_dk_kernel(
 #pragma unroll
     for (int db = 0; db < 8; ++db) ak[db] = av[db] = f32x4{};
 
-    // ---- staging: waves 0-1 Q, 2-3 R, 4-5 dO (rows 4 (u >> 4) .. +3, dims 8 (u & 15) .. +7),
-    // row-major and transposed; wave 6 the 32 per-row records.
+    // ---- staging: waves 0-1 Q, 2-3 R, 4-5 dO (rows 4 (u & 7) .. +3, dims 8 (u >> 3) .. +7),
+    // row-major and transposed; wave 6 the 32 per-row records. The row group varies fastest
+    // across lanes: the 8-byte stores of the transposed copy then fall on distinct banks in
+    // pairs (with the dim chunk fastest, 8 lanes would share a bank).
     const int which = w >> 1;  // 0 Q, 1 R, 2 dO, 3 records / idle
-    const int u = tid & 127, sdc = u & 15, sqg = u >> 4;
+    const int u = tid & 127, sqg = u & 7, sdc = u >> 3;
     const __bf16* src = which == 0 ? q : which == 1 ? rho : dout;
     u32x4 stg[4];
     const int qt0 = k0 / QBC;                       // first query tile of the item

@@ -29,6 +29,8 @@ Extra modes:
   --paged [OUT_MD]        time the paged-cache decode against the contiguous cache
   --probe-producer [OUT_MD]  time the probe producer (x W_R^T, RMSNorm, RoPE, gate) on the
                           prefill step's tokens at C = 32 and C = 2048
+  --backward [OUT_MD]     time the training pair on the prefill workload: the forward with
+                          saved statistics and the backward (dq, dk, dv, drho)
 Used to produce the committed rocprofv3 summaries:
   --calibrate-copy        also run a reference kernel of known traffic (1 GiB read + 1 GiB
                           written), which scales the counters
@@ -670,6 +672,68 @@ def probe_producer(out_md):
     return 0
 
 
+def backward(out_md):
+    """Times the prefill forward with saved statistics and the backward on the prefill
+    workload (B=4, H=16, T=2048, d=128, bf16, probe 0.1 * RMSNorm(N(0,1)), upstream gradient
+    N(0,1)); HIP events on the launch stream, median of 20 calls after 0.5 s of untimed
+    calls. Algorithmic FLOPs per visible causal pair: 8 d for the forward (Q K^T, R K^T, P V,
+    (P*T) V) and 16 d for the backward (the three pair products Q K^T, R K^T, dO V^T, and the
+    five accumulating products for dV, dK (two), dQ and dR)."""
+    import torch
+
+    import attention_plx_attn_amd as plx
+    from plx_synth import CONFIGS, prefill_inputs, prefill_upstream_grad
+
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    stream = torch.cuda.current_stream(dev)
+    cfg = CONFIGS["prefill_bf16"]
+    x = prefill_inputs(cfg, seed=0, device=dev)
+    do = prefill_upstream_grad(cfg, seed=0).to(dev)
+    o, vbar, stats = plx.prefill_fwd(x["q"], x["k"], x["v"], x["rho"], cfg.scale)
+    ws = torch.empty(plx.prefill_bwd_workspace_size(cfg.B, cfg.H, cfg.T) // 4,
+                     dtype=torch.float32, device=dev)
+    pairs = cfg.B * cfg.H * cfg.T * (cfg.T + 1) // 2
+    calls = {
+        "forward (plx_attn_prefill)": (
+            lambda: plx.prefill(x["q"], x["k"], x["v"], x["rho"], cfg.scale), 8 * cfg.d * pairs),
+        "forward with saved statistics (plx_attn_prefill_fwd)": (
+            lambda: plx.prefill_fwd(x["q"], x["k"], x["v"], x["rho"], cfg.scale),
+            8 * cfg.d * pairs),
+        "backward (plx_attn_prefill_bwd: dq/drho and dk/dv kernels)": (
+            lambda: plx.prefill_bwd(x["q"], x["k"], x["v"], x["rho"], o, vbar, stats, do,
+                                    cfg.scale, workspace=ws), 16 * cfg.d * pairs),
+    }
+    rows = []
+    for name, (call, flops) in calls.items():
+        t_end = time.perf_counter() + 0.5
+        while time.perf_counter() < t_end:
+            call()
+            torch.cuda.synchronize()
+        ts = []
+        for _ in range(20):
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record(stream)
+            call()
+            e1.record(stream)
+            torch.cuda.synchronize()
+            ts.append(e0.elapsed_time(e1))
+        us = _stats_us(ts)["median_us"]
+        r = {"workload": f"{name}, B{cfg.B} H{cfg.H} T{cfg.T} d{cfg.d}", "median_us": us,
+             "tflops": round(flops / us / 1e6, 1),
+             "frac": round(flops / us / 1e6 / BF16_PEAK_TFLOPS, 4)}
+        rows.append(r)
+        print(json.dumps(r), flush=True)
+    if out_md:
+        with open(out_md, "w") as fh:
+            fh.write("| call | median us | algorithmic TFLOP/s | fraction of 2.5 PFLOP/s |\n")
+            fh.write("|---|---|---|---|\n")
+            for r in rows:
+                fh.write(f"| {r['workload']} | {r['median_us']} | {r['tflops']} | "
+                         f"{100 * r['frac']:.1f}% |\n")
+    return 0
+
+
 # ------------------------------------------------------------------------------ main
 
 def main():
@@ -695,6 +759,9 @@ def main():
                     help="time the grouped-query decode instead of the step")
     ap.add_argument("--probe-producer", metavar="OUT_MD", nargs="?", const="",
                     help="time the probe producer instead of the step")
+    ap.add_argument("--backward", metavar="OUT_MD", nargs="?", const="",
+                    help="time the prefill forward with statistics and its backward instead "
+                         "of the step")
     ap.add_argument("--compare", metavar="OUT_MD", nargs="?", const="",
                     help="time Parallax against softmax-only attention (I/O- and "
                          "compute-matched) instead of the step")
@@ -720,6 +787,8 @@ def main():
         return gqa(args.gqa)
     if args.paged is not None:
         return paged(args.paged)
+    if args.backward is not None:
+        return backward(args.backward)
 
     import torch
 

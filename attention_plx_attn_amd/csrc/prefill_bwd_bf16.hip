@@ -25,10 +25,11 @@
 //     LDS copy of the tile. K and V rows sit in LDS in the forward kernel's key order, so each
 //     lane's product registers already hold the 8 consecutive keys its next operand wants.
 //   * dk kernel: a work item is 128 keys of one (b, h); 8 waves of 16 keys. It streams the
-//     query tiles (32 queries) at or after the item's first key: S = Q K^T, T = R K^T,
+//     query tiles (64 queries) at or after the item's first key: S = Q K^T, T = R K^T,
 //     g = dO V^T with Q, R, dO rows from LDS (A) and the wave's K, V fragments in registers
-//     (B), then dV^T += dO^T s, dK^T += Q^T (scale da) + R^T dt with transposed LDS copies of
-//     Q, R and dO as the A operand.
+//     (B), then dV^T += dO^T s, dK^T += Q^T (scale da) + R^T dt, whose A operands (8 queries
+//     of one dim per lane) come from the same row-major tiles through gfx950's transposing
+//     LDS read, so the tiles are stored once.
 // Both kernels double-buffer their tiles in LDS: tile n + 1 is loaded into registers while
 // tile n is processed and written to the other buffer afterwards; one barrier per tile.
 // Work items are dispatched longest first; with B*H a multiple of 8, item n (dispatched to
@@ -267,14 +268,22 @@ __global__ __launch_bounds__(NT, 1) void prefill_bwd_dq_kernel(
 
 // ============================================================================ dk kernel
 constexpr int KBR = 128;                // keys per item
-constexpr int QBC = 32;                 // queries per tile
-constexpr int QTS = QBC + 8;            // row stride of a transposed tile (bf16): 80 bytes
+constexpr int QBC = 64;                 // queries per tile
 constexpr int K_R = QBC * RS * 2;       // bytes of one row-major tile (Q, R or dO)
-constexpr int K_T = D * QTS * 2;        // bytes of one transposed tile
 constexpr int K_REC = QBC * 16;         // per-row records (L2, tbar, G, D)
-constexpr int K_BUF = 3 * K_R + 3 * K_T + K_REC;
+constexpr int K_BUF = 3 * K_R + K_REC;
 constexpr int K_LDS = 2 * K_BUF;
 static_assert(K_LDS <= 160 * 1024, "LDS budget");
+
+typedef short i16x4 __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) i16x4 lds_i16x4;
+
+// Transposing LDS read (ds_read_b64_tr_b16): within each 16-lane group, lane 4 a + b receives
+// element b of the 4 consecutive 16-bit elements that lanes 4 j + a (j = 0..3) address.
+__device__ __forceinline__ i16x4 read_tr(const unsigned char* p) {
+    return __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+        (lds_i16x4*)(__attribute__((address_space(3))) unsigned char*)p);
+}
 
 __global__ __launch_bounds__(NT, 1) void prefill_bwd_dk_kernel(
     const __bf16* __restrict__ q, const __bf16* __restrict__ k, const __bf16* __restrict__ v,
@@ -303,97 +312,103 @@ __global__ __launch_bounds__(NT, 1) void prefill_bwd_dk_kernel(
             xv[s] = as_bf16x8(load16(rv, off + 64u * s));
         }
     }
-    f32x4 ak[8], av[8];  // dK^T, dV^T: dim block db, lane: dims 16 db + 4 gq + i of key kj
+    f32x4 ak[8], av[8];
 #pragma unroll
     for (int db = 0; db < 8; ++db) ak[db] = av[db] = f32x4{};
 
-    // ---- staging: waves 0-1 Q, 2-3 R, 4-5 dO (rows 4 (u & 7) .. +3, dims 8 (u >> 3) .. +7),
-    // row-major and transposed; wave 6 the 32 per-row records. The row group varies fastest
-    // across lanes: the 8-byte stores of the transposed copy then fall on distinct banks in
-    // pairs (with the dim chunk fastest, 8 lanes would share a bank).
-    const int which = w >> 1;  // 0 Q, 1 R, 2 dO, 3 records / idle
-    const int u = tid & 127, sqg = u & 7, sdc = u >> 3;
-    const __bf16* src = which == 0 ? q : which == 1 ? rho : dout;
-    u32x4 stg[4];
-    const int qt0 = k0 / QBC;                       // first query tile of the item
+    // ---- staging: chunk m (0..5) of thread t is tensor m / 2 (Q, R, dO), row
+    // (t >> 4) + 32 (m & 1), dims 8 (t & 15) .. +7; threads 0..63 also stage the row records.
+    u32x4 stg[6];
+    u32x4 srec = u32x4{};
+    const int qt0 = k0 / QBC;
     const int ntiles = (T + QBC - 1) / QBC - qt0;
+    const int srow = tid >> 4, sc = tid & 15;
     auto gload = [&](int n) {
         const int r0 = (qt0 + n) * QBC;
-        if (which < 3) {
-            const auto r = make_rsrc(src + slice + (size_t)r0 * D,
-                                     slice_bytes - (uint32_t)r0 * 256u);
-            const uint32_t off = (uint32_t)(4 * sqg) * 256u + 16u * sdc;
+        const uint32_t rem = slice_bytes - (uint32_t)r0 * 256u;
+        const auto r_q = make_rsrc(q + slice + (size_t)r0 * D, rem);
+        const auto r_r = make_rsrc(rho + slice + (size_t)r0 * D, rem);
+        const auto r_d = make_rsrc(dout + slice + (size_t)r0 * D, rem);
 #pragma unroll
-            for (int j = 0; j < 4; ++j) stg[j] = load16(r, off + 256u * j);
-        } else if (w == 6 && lane < QBC) {
+        for (int h = 0; h < 2; ++h) {
+            const uint32_t off = (uint32_t)(srow + 32 * h) * 256u + 16u * sc;
+            stg[h] = load16(r_q, off);
+            stg[2 + h] = load16(r_r, off);
+            stg[4 + h] = load16(r_d, off);
+        }
+        if (w == 0) {
             const auto r = make_rsrc(rec + (size_t)bh * T + r0, (uint32_t)(T - r0) * 16u);
-            stg[0] = load16(r, 16u * lane);
+            srec = load16(r, 16u * lane);
         }
     };
     auto lstore = [&](int buf) {
         unsigned char* base = lds + buf * K_BUF;
-        if (which < 3) {
-            unsigned char* R = base + which * K_R;
 #pragma unroll
-            for (int j = 0; j < 4; ++j)
-                *(u32x4*)(R + prow(4 * sqg + j) * RS * 2 + 16 * sdc) = stg[j];
-            __bf16* Tt = (__bf16*)(base + 3 * K_R + which * K_T);
-            u32x2 tr[8];
-            transpose4(stg, tr);
-#pragma unroll
-            for (int r = 0; r < 8; ++r) *(u32x2*)(Tt + (8 * sdc + r) * QTS + 4 * sqg) = tr[r];
-        } else if (w == 6 && lane < QBC) {
-            *(u32x4*)(base + 3 * K_R + 3 * K_T + 16 * lane) = stg[0];
-        }
+        for (int m = 0; m < 6; ++m)
+            *(u32x4*)(base + (m >> 1) * K_R + prow(srow + 32 * (m & 1)) * RS * 2 + 16 * sc) =
+                stg[m];
+        if (w == 0) *(u32x4*)(base + 3 * K_R + 16 * lane) = srec;
     };
+
+    // transposed-read lane base: source lane (4 j + a) of group gq addresses tile row
+    // 4 gq + j (+ 32 G + 16 h), dims 4 a .. +3 (+ 16 db)
+    const int trl = (4 * gq + (col >> 2)) * RS * 2 + 8 * (col & 3);
 
     auto tile = [&](int n, int buf, bool mask) {
         const unsigned char* base = lds + buf * K_BUF;
         const unsigned char* Qr = base + col * RS * 2 + 16 * gq;
-        const unsigned char* Rr = Qr + K_R;
-        const unsigned char* Dr = Qr + 2 * K_R;
-        f32x4 S[2], Tp[2], Gm[2];
+        f32x4 S[4], Tp[4], Gm[4];
 #pragma unroll
-        for (int b = 0; b < 2; ++b) {
+        for (int b = 0; b < 4; ++b) {
             S[b] = Tp[b] = Gm[b] = f32x4{};
 #pragma unroll
             for (int s = 0; s < 4; ++s) {
                 const int o = 16 * b * RS * 2 + 64 * s;
                 S[b] = mfma16(*(const bf16x8*)(Qr + o), xk[s], S[b]);
-                Tp[b] = mfma16(*(const bf16x8*)(Rr + o), xk[s], Tp[b]);
-                Gm[b] = mfma16(*(const bf16x8*)(Dr + o), xv[s], Gm[b]);
+                Tp[b] = mfma16(*(const bf16x8*)(Qr + K_R + o), xk[s], Tp[b]);
+                Gm[b] = mfma16(*(const bf16x8*)(Qr + 2 * K_R + o), xv[s], Gm[b]);
             }
         }
-        // register i of block b: query (qt0 + n) * 32 + 8 gq + 4 b + i
-        const f32x4* recs = (const f32x4*)(base + 3 * K_R + 3 * K_T) + 8 * gq;
-        const int qbase = (qt0 + n) * QBC + 8 * gq;
-        float fs[8], fa[8], ft[8];
+        // register i of block b: query (qt0 + n) * 64 + 32 (b >> 1) + 8 gq + 4 (b & 1) + i
+        const f32x4* recs = (const f32x4*)(base + 3 * K_R);
+        const int qbase = (qt0 + n) * QBC;
 #pragma unroll
-        for (int b = 0; b < 2; ++b)
+        for (int G2 = 0; G2 < 2; ++G2) {
+            float fs[8], fa[8], ft[8];
 #pragma unroll
-            for (int i = 0; i < 4; ++i) {
-                const f32x4 rw = recs[4 * b + i];  // L2, tbar, G, D
-                float p = exp2_fast(fmaf(S[b][i], c, -rw[0]));
-                const int qi = qbase + 4 * b + i;
-                if (mask && (qi < kj || qi >= T)) p = 0.f;
-                const float t = Tp[b][i], g = Gm[b][i];
-                const float one = 1.f - t + rw[1];
-                fs[4 * b + i] = p * one;
-                ft[4 * b + i] = p * (rw[2] - g);
-                fa[4 * b + i] = scale * p * (fmaf(one, g, t * rw[2]) - rw[3]);
+            for (int bb = 0; bb < 2; ++bb)
+#pragma unroll
+                for (int i = 0; i < 4; ++i) {
+                    const int b = 2 * G2 + bb;
+                    const int ql = 32 * G2 + 8 * gq + 4 * bb + i;
+                    const f32x4 rw = recs[ql];  // L2, tbar, G, D
+                    float p = exp2_fast(fmaf(S[b][i], c, -rw[0]));
+                    if (mask && (qbase + ql < kj || qbase + ql >= T)) p = 0.f;
+                    const float t = Tp[b][i], g = Gm[b][i];
+                    const float one = 1.f - t + rw[1];
+                    fs[4 * bb + i] = p * one;
+                    ft[4 * bb + i] = p * (rw[2] - g);
+                    fa[4 * bb + i] = scale * p * (fmaf(one, g, t * rw[2]) - rw[3]);
+                }
+            const bf16x8 ps = pack8(fs), pa = pack8(fa), pt = pack8(ft);
+            const unsigned char* Tr = base + trl + 32 * G2 * RS * 2;
+#pragma unroll
+            for (int db = 0; db < 8; ++db) {
+                const int o = 32 * db;
+                auto op = [&](int tensor) {
+                    const unsigned char* p0 = Tr + tensor * K_R + o;
+                    const i16x4 lo = read_tr(p0), hi = read_tr(p0 + 16 * RS * 2);
+                    return __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3,
+                                                                              4, 5, 6, 7));
+                };
+                av[db] = mfma16(op(2), ps, av[db]);
+                ak[db] = mfma16(op(0), pa, ak[db]);
+                ak[db] = mfma16(op(1), pt, ak[db]);
             }
-        const bf16x8 ps = pack8(fs), pa = pack8(fa), pt = pack8(ft);
-        const unsigned char* Tq = base + 3 * K_R + col * QTS * 2 + 16 * gq;
-#pragma unroll
-        for (int db = 0; db < 8; ++db) {
-            const int o = 16 * db * QTS * 2;
-            av[db] = mfma16(*(const bf16x8*)(Tq + 2 * K_T + o), ps, av[db]);
-            ak[db] = mfma16(*(const bf16x8*)(Tq + o), pa, ak[db]);
-            ak[db] = mfma16(*(const bf16x8*)(Tq + K_T + o), pt, ak[db]);
         }
     };
 
-    const int tail = (T - 1) / QBC - qt0;  // local index of the tile holding row T - 1
+    const int tail = (T - 1) / QBC - qt0;
     gload(0);
     lstore(0);
     __syncthreads();
@@ -402,7 +417,6 @@ __global__ __launch_bounds__(NT, 1) void prefill_bwd_dk_kernel(
         const bool more = n + 1 < ntiles;
         if (more) gload(n + 1);
         const int r0 = (qt0 + n) * QBC;
-        // rows r0 .. r0 + 31 all precede the wave's first key: nothing to add
         if (r0 + QBC - 1 >= k0 + 16 * w) tile(n, buf, r0 < k0 + KBR || n == tail);
         if (more) lstore(buf ^ 1);
         __syncthreads();

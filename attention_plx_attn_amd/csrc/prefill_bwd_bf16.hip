@@ -21,9 +21,10 @@
 //     through a per-row record), then streams the visible key tiles (64 keys): the products
 //     S^T = K Q^T, T^T = K R^T, g^T = V dO^T take K and V rows from LDS as the A operand and
 //     the wave's Q, R, dO fragments from registers as the B operand; the weight blocks da^T,
-//     dt^T then feed dQ^T += K^T da^T and dR^T += K^T dt^T with K^T read from a transposed
-//     LDS copy of the tile. K and V rows sit in LDS in the forward kernel's key order, so each
-//     lane's product registers already hold the 8 consecutive keys its next operand wants.
+//     dt^T then feed dQ^T += K^T da^T and dR^T += K^T dt^T with K^T read from the same K tile
+//     through gfx950's transposing LDS read. K and V rows sit in LDS in the forward kernel's key
+//     order, so each lane's product registers already hold the 8 consecutive keys its next
+//     operand wants.
 //   * dk kernel: a work item is 128 keys of one (b, h); 8 waves of 16 keys. It streams the
 //     query tiles (64 queries) at or after the item's first key: S = Q K^T, T = R K^T,
 //     g = dO V^T with Q, R, dO rows from LDS (A) and the wave's K, V fragments in registers
@@ -56,18 +57,6 @@ __device__ __forceinline__ int prow(int k) {
     return (k & 32) | (((k >> 2) & 1) << 4) | (((k >> 3) & 3) << 2) | (k & 3);
 }
 
-// Transpose four rows (consecutive elements e .. e + 3) of one 8-dim chunk: out[2 p] holds dim
-// 2 p of the four rows, out[2 p + 1] dim 2 p + 1, each as two packed pairs.
-__device__ __forceinline__ void transpose4(const u32x4 (&r)[4], u32x2 (&out)[8]) {
-#pragma unroll
-    for (int p = 0; p < 4; ++p) {
-        out[2 * p] = u32x2{__builtin_amdgcn_perm(r[1][p], r[0][p], 0x05040100u),
-                           __builtin_amdgcn_perm(r[3][p], r[2][p], 0x05040100u)};
-        out[2 * p + 1] = u32x2{__builtin_amdgcn_perm(r[1][p], r[0][p], 0x07060302u),
-                               __builtin_amdgcn_perm(r[3][p], r[2][p], 0x07060302u)};
-    }
-}
-
 __device__ __forceinline__ bf16x8 pack8(const float (&x)[8]) {
     return __builtin_bit_cast(bf16x8, u32x4{pack_bf16x2(x[0], x[1]), pack_bf16x2(x[2], x[3]),
                                             pack_bf16x2(x[4], x[5]), pack_bf16x2(x[6], x[7])});
@@ -78,6 +67,25 @@ __device__ __forceinline__ float dot8(u32x4 a, u32x4 b, float acc) {
 #pragma unroll
     for (int e = 0; e < 8; ++e) acc = fmaf((float)x[e], (float)y[e], acc);
     return acc;
+}
+
+typedef short i16x4 __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) i16x4 lds_i16x4;
+
+// Transposing LDS read (ds_read_b64_tr_b16): within each 16-lane group, lane 4 a + b receives
+// element b of the 4 consecutive 16-bit elements that lanes 4 j + a (j = 0..3) address.
+__device__ __forceinline__ i16x4 read_tr(const unsigned char* p) {
+    return __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+        (lds_i16x4*)(__attribute__((address_space(3))) unsigned char*)p);
+}
+
+// A operand of 16 rows x 32 k-slots whose k runs down the rows of a row-major LDS tile: tile
+// rows (in prow order) 32 G + 8 g + 0..7 for lane group g, 16 consecutive columns from the
+// lane base. `p` is the lane's base (row 4 g + j, columns 4 a .. +3 for source lane 4 j + a)
+// plus the step's offset; the second half of the slots lies 16 tile rows further down.
+__device__ __forceinline__ bf16x8 read_tr_operand(const unsigned char* p, int row_bytes) {
+    const i16x4 lo = read_tr(p), hi = read_tr(p + 16 * row_bytes);
+    return __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
 }
 
 // Item n of a launch of BH * nblk items, longest first: block index and (b, h).
@@ -91,10 +99,8 @@ __device__ __forceinline__ void item_of(int n, int BH, int nblk, bool longest_la
 // ============================================================================ dq kernel
 constexpr int QBR = 128;                 // query rows per item
 constexpr int KBC = 64;                  // keys per tile
-constexpr int KTS = KBC + 8;             // row stride of the transposed K tile (bf16)
 constexpr int Q_KR = KBC * RS * 2;       // bytes of a row-major K (or V) tile
-constexpr int Q_KT = D * KTS * 2;        // bytes of the transposed K tile
-constexpr int Q_BUF = 2 * Q_KR + Q_KT;
+constexpr int Q_BUF = 2 * Q_KR;
 constexpr int Q_LDS = 2 * Q_BUF;
 static_assert(Q_LDS <= 160 * 1024, "LDS budget");
 
@@ -160,8 +166,8 @@ __global__ __launch_bounds__(NT, 1) void prefill_bwd_dq_kernel(
 #pragma unroll
     for (int db = 0; db < 8; ++db) aq[db] = ar[db] = f32x4{};
 
-    // ---- staging: waves 0-3 K (row-major and transposed), waves 4-7 V (row-major). Thread st
-    // loads keys 4 (st >> 4) .. +3, dims 8 (st & 15) .. +7.
+    // ---- staging: waves 0-3 K, waves 4-7 V (row-major, rows in prow order). Thread st loads
+    // keys 4 (st >> 4) .. +3, dims 8 (st & 15) .. +7.
     const bool kst = w < 4;
     const int st = tid & 255, sdc = st & 15, skg = st >> 4;
     const uint32_t soff = (uint32_t)(4 * skg) * 256u + 16u * sdc;
@@ -180,25 +186,15 @@ __global__ __launch_bounds__(NT, 1) void prefill_bwd_dq_kernel(
 #pragma unroll
         for (int j = 0; j < 4; ++j)
             *(u32x4*)(base + prow(4 * skg + j) * RS * 2 + 16 * sdc) = stg[j];
-        if (kst) {
-            __bf16* Kt = (__bf16*)(lds + buf * Q_BUF + 2 * Q_KR);
-            u32x2 tr[8];
-            transpose4(stg, tr);
-            // 16-byte key chunks of a dim row are XOR-swizzled with bits 1..3 of its dim chunk
-            const int cs = 8 * ((skg >> 1) ^ ((sdc >> 1) & 7)) + 4 * (skg & 1);
-#pragma unroll
-            for (int r = 0; r < 8; ++r) *(u32x2*)(Kt + (8 * sdc + r) * KTS + cs) = tr[r];
-        }
     };
-    // transposed reads: dim row 16 db + col, keys 32 G + 8 gq .. +7 at chunk (4 G + gq) ^ swz
-    int tlane[4];
-#pragma unroll
-    for (int x = 0; x < 4; ++x) tlane[x] = col * KTS * 2 + 16 * (gq ^ x);
+    // K^T operands through the transposing read: source lane (4 j + a) of group gq addresses
+    // K tile row 4 gq + j (+ 32 G + 16 h), dims 4 a .. +3 (+ 16 db)
+    const int trl = (4 * gq + (col >> 2)) * RS * 2 + 8 * (col & 3);
 
     auto tile = [&](int kt, int buf, bool diag) {
         const unsigned char* Kr = lds + buf * Q_BUF + col * RS * 2 + 16 * gq;
         const unsigned char* Vr = Kr + Q_KR;
-        const unsigned char* Kt = lds + buf * Q_BUF + 2 * Q_KR;
+        const unsigned char* Kt = lds + buf * Q_BUF + trl;
         f32x4 S[4], Tp[4], Gm[4];
 #pragma unroll
         for (int kb = 0; kb < 4; ++kb) {
@@ -231,8 +227,7 @@ __global__ __launch_bounds__(NT, 1) void prefill_bwd_dq_kernel(
             const bf16x8 da = pack8(fa), dt = pack8(ft);
 #pragma unroll
             for (int db = 0; db < 8; ++db) {
-                const bf16x8 kf = *(const bf16x8*)(Kt + tlane[db & 3] + 16 * db * KTS * 2 +
-                                                   64 * (G2 ^ (db >> 2)));
+                const bf16x8 kf = read_tr_operand(Kt + 32 * G2 * RS * 2 + 32 * db, RS * 2);
                 aq[db] = mfma16(kf, da, aq[db]);
                 ar[db] = mfma16(kf, dt, ar[db]);
             }
@@ -274,16 +269,6 @@ constexpr int K_REC = QBC * 16;         // per-row records (L2, tbar, G, D)
 constexpr int K_BUF = 3 * K_R + K_REC;
 constexpr int K_LDS = 2 * K_BUF;
 static_assert(K_LDS <= 160 * 1024, "LDS budget");
-
-typedef short i16x4 __attribute__((ext_vector_type(4)));
-typedef __attribute__((address_space(3))) i16x4 lds_i16x4;
-
-// Transposing LDS read (ds_read_b64_tr_b16): within each 16-lane group, lane 4 a + b receives
-// element b of the 4 consecutive 16-bit elements that lanes 4 j + a (j = 0..3) address.
-__device__ __forceinline__ i16x4 read_tr(const unsigned char* p) {
-    return __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-        (lds_i16x4*)(__attribute__((address_space(3))) unsigned char*)p);
-}
 
 __global__ __launch_bounds__(NT, 1) void prefill_bwd_dk_kernel(
     const __bf16* __restrict__ q, const __bf16* __restrict__ k, const __bf16* __restrict__ v,
@@ -395,12 +380,7 @@ __global__ __launch_bounds__(NT, 1) void prefill_bwd_dk_kernel(
 #pragma unroll
             for (int db = 0; db < 8; ++db) {
                 const int o = 32 * db;
-                auto op = [&](int tensor) {
-                    const unsigned char* p0 = Tr + tensor * K_R + o;
-                    const i16x4 lo = read_tr(p0), hi = read_tr(p0 + 16 * RS * 2);
-                    return __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3,
-                                                                              4, 5, 6, 7));
-                };
+                auto op = [&](int tensor) { return read_tr_operand(Tr + tensor * K_R + o, RS * 2); };
                 av[db] = mfma16(op(2), ps, av[db]);
                 ak[db] = mfma16(op(0), pa, ak[db]);
                 ak[db] = mfma16(op(1), pt, ak[db]);

@@ -48,6 +48,18 @@ def check_bf16(got, ref, what: str = "") -> dict:
     return m
 
 
+def check_grad(got, ref, what: str = "") -> dict:
+    """Gradients of the bf16 backward: rel-L2 <= 5e-3 and |g - r| <= ulp(r)/2 + 1e-2 max(1,
+    max |r|) (the forward's elementwise bar taken relative to the tensor's scale: every error
+    source of the backward is relative, and gradients reach ~40)."""
+    m = metrics(got, ref)
+    assert m["finite"], f"{what}: non-finite output"
+    scale = max(1.0, float(np.abs(to_f64(ref)).max())) if to_f64(ref).size else 1.0
+    assert m["excess_over_half_ulp"] <= BF16_ABS * scale, f"{what}: {m}"
+    assert m["rel_l2"] <= BF16_REL_L2, f"{what}: {m}"
+    return m
+
+
 def check_f32(got, ref, what: str = "") -> dict:
     m = metrics(got, ref)
     assert m["finite"], f"{what}: non-finite output"

@@ -19,7 +19,7 @@ import torch
 
 import attention_plx_attn_amd as plx
 import oracle
-from parity import BF16_ABS, BF16_REL_L2, check_bf16, metrics, to_f64
+from parity import BF16_ABS, check_bf16, check_grad, to_f64
 from plx_synth import CONFIGS, prefill_inputs, prefill_upstream_grad
 from plx_synth.inputs import PrefillConfig
 
@@ -46,15 +46,6 @@ def _gpu(x, rho=True):
                             x["scale"])
     torch.cuda.synchronize()
     return d, o, vbar, stats, grads
-
-
-def check_grad(got, ref, what):
-    m = metrics(got, ref)
-    assert m["finite"], f"{what}: non-finite output"
-    assert m["excess_over_half_ulp"] <= BF16_ABS * max(1.0, float(np.abs(ref).max())), \
-        f"{what}: {m}"
-    assert m["rel_l2"] <= BF16_REL_L2, f"{what}: {m}"
-    return m
 
 
 def _check_grads(grads, x, what, sel=(slice(None), slice(None))):

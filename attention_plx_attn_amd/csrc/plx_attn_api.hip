@@ -164,7 +164,7 @@ plx_status_t plx_attn_prefill(plx_dtype_t dtype, int32_t B, int32_t H, int32_t T
         return PLX_ERR_INVALID_SHAPE;
     if ((long long)B * H > INT_MAX / 2) return PLX_ERR_INVALID_SHAPE;
     if (d_qk != d_v) return PLX_ERR_UNSUPPORTED;
-    const bool ok = (dtype == PLX_BF16 && d_qk == 128) ||
+    const bool ok = (dtype == PLX_BF16 && (d_qk == 128 || d_qk == 64)) ||
                     (dtype == PLX_F32 && plx::prefill_f32_supported(d_qk));
     if (!ok) return PLX_ERR_UNSUPPORTED;
     if (dtype == PLX_F32 && (B > 65535 || H > 65535)) return PLX_ERR_INVALID_SHAPE;
@@ -178,7 +178,7 @@ plx_status_t plx_attn_prefill(plx_dtype_t dtype, int32_t B, int32_t H, int32_t T
     }
     plx::PrefillArgs a{B, H, T, d_qk, q, k, v, rho, o, softmax_scale, cus};
     const hipStream_t st = static_cast<hipStream_t>(stream);
-    const hipError_t e = dtype == PLX_BF16 ? plx::launch_prefill_bf16_d128(a, st)
+    const hipError_t e = dtype == PLX_BF16 ? plx::launch_prefill_bf16(a, st)
                                            : plx::launch_prefill_f32(a, st);
     return e == hipSuccess ? PLX_OK : PLX_ERR_HIP;
 }
@@ -200,7 +200,7 @@ plx_status_t plx_attn_prefill_fwd(plx_dtype_t dtype, int32_t B, int32_t H, int32
     plx::PrefillArgs a{B, H, T, d_qk, q, k, v, rho, o, softmax_scale, cus};
     a.vbar = vbar;
     a.stats = stats;
-    const hipError_t e = plx::launch_prefill_bf16_d128(a, static_cast<hipStream_t>(stream));
+    const hipError_t e = plx::launch_prefill_bf16(a, static_cast<hipStream_t>(stream));
     return e == hipSuccess ? PLX_OK : PLX_ERR_HIP;
 }
 

@@ -70,7 +70,7 @@ struct ProbeArgs {
 
 bool prefill_f32_supported(int d);
 hipError_t launch_prefill_f32(const PrefillArgs& a, hipStream_t stream);
-hipError_t launch_prefill_bf16_d128(const PrefillArgs& a, hipStream_t stream);
+hipError_t launch_prefill_bf16(const PrefillArgs& a, hipStream_t stream);
 hipError_t launch_prefill_bwd_bf16_d128(const PrefillBwdArgs& a, hipStream_t stream);
 hipError_t launch_decode_bf16_d128(const DecodeArgs& a, hipStream_t stream);
 hipError_t launch_probe_bf16_d128(const ProbeArgs& a, hipStream_t stream);

@@ -1,4 +1,4 @@
-// prefill_bf16.hip -- causal Parallax prefill, bf16 in/out, d_qk = d_v = 128, gfx950.
+// prefill_bf16.hip -- causal Parallax prefill, bf16 in/out, d_qk = d_v = 128 or 64, gfx950.
 //
 // Method [Parallax (paper.rainbus.top summary), "方法步骤详情": per KV block compute the
 // scores S1 = Q K^T and the probe products S2 = R K^T, then P1 = exp(S1 - m) and
@@ -43,18 +43,29 @@
 namespace plx {
 namespace {
 
-constexpr int D = 128;
 constexpr int BR = 128;  // query rows per work item
 constexpr int BC = 64;   // keys per LDS tile
 constexpr int NT = 512;  // threads per workgroup (8 waves x 16 query rows)
-constexpr int KS = D + 8;         // LDS row stride of a K tile (bf16 elements)
 constexpr int VS = BC + 8;        // LDS row stride of a transposed V tile
-constexpr int K_ELEMS = BC * KS;  // 8704 bf16
-constexpr int V_ELEMS = D * VS;   // 9216 bf16
 constexpr int NBUF = 4;  // stream tiles s + 2 is staged while s is processed
-constexpr int OFF_V = NBUF * K_ELEMS * 2;
-constexpr int LDS_BYTES = OFF_V + NBUF * V_ELEMS * 2;
-static_assert(LDS_BYTES <= 160 * 1024, "LDS budget");
+
+// Sizes that follow from the head dim D (d_qk = d_v = D, a multiple of 32, at most 128).
+template <int D>
+struct Geo {
+    static constexpr int KS = D + 8;         // LDS row stride of a K tile (bf16 elements)
+    static constexpr int K_ELEMS = BC * KS;  // 8704 bf16 at D = 128
+    static constexpr int V_ELEMS = D * VS;   // 9216 bf16 at D = 128
+    static constexpr int OFF_V = NBUF * K_ELEMS * 2;
+    static constexpr int LDS_BYTES = OFF_V + NBUF * V_ELEMS * 2;
+    static constexpr int NS = D / 32;    // 32-dim steps of a q.k product
+    static constexpr int NDB = D / 16;   // 16-dim blocks of a value product
+    static constexpr int CPR = D / 8;    // 16-byte chunks per row
+    static constexpr int CPR_LOG = D == 128 ? 4 : 3;
+    static constexpr int KCH = BC * CPR / 256;  // chunks per K stager thread
+    static constexpr uint32_t ROWB = 2 * D;     // bytes per row
+    static_assert(D == 64 || D == 128, "head dim");
+    static_assert(LDS_BYTES <= 160 * 1024, "LDS budget");
+};
 constexpr float kLazyTau = 8.0f;  // log2 headroom before the running max moves
 
 // K row of key k (0..63) of a tile: inside each 32-key group, key 8 q + 4 b + i goes to row
@@ -103,12 +114,17 @@ __device__ __forceinline__ float max_across_row_groups(float x) {
 // extra fp32 sums of the unrounded weights and weight * probe products, so that they agree
 // with the weights and probe products the backward recomputes (with a large probe, |t| ~ 10,
 // the bf16-rounded beta / l would differ from them by ~2^-9 |t|).
-template <bool PROBE, bool STATS>
-__global__ __launch_bounds__(NT, 1) void prefill_bf16_d128_kernel(
+template <int D, bool PROBE, bool STATS>
+__global__ __launch_bounds__(NT, 1) void prefill_bf16_kernel(
     const __bf16* __restrict__ q, const __bf16* __restrict__ k, const __bf16* __restrict__ v,
     const __bf16* __restrict__ rho, __bf16* __restrict__ o, __bf16* __restrict__ vbar,
     float* __restrict__ stats, int BH, int T, int nqb, float c, int ncls) {
-    __shared__ __attribute__((aligned(16))) unsigned char lds[LDS_BYTES];
+    using G_ = Geo<D>;
+    constexpr int KS = G_::KS, K_ELEMS = G_::K_ELEMS, V_ELEMS = G_::V_ELEMS, OFF_V = G_::OFF_V;
+    constexpr int NS = G_::NS, NDB = G_::NDB, CPR = G_::CPR, CPR_LOG = G_::CPR_LOG;
+    constexpr int KCH = G_::KCH;
+    constexpr uint32_t ROWB = G_::ROWB;
+    __shared__ __attribute__((aligned(16))) unsigned char lds[G_::LDS_BYTES];
 
     const int tid = threadIdx.x;
     const int lane = tid & 63;
@@ -129,54 +145,59 @@ __global__ __launch_bounds__(NT, 1) void prefill_bf16_d128_kernel(
 
     // Q and R fragments (B operand of S^T = K Q^T): lane holds dims 32 st + 8 gq .. +7 of
     // query `col`.
-    bf16x8 xq[4], xr[4];
+    bf16x8 xq[NS], xr[NS];
     auto load_x = [&](const Item& it) {
         const auto rq = make_rsrc(q + slice_of(it.bh), slice_bytes);
         const auto rr = make_rsrc(rho + slice_of(it.bh), slice_bytes);
-        const uint32_t qoff = (uint32_t)(it.q0 + 16 * w + col) * 256u + 16u * gq;
+        const uint32_t qoff = (uint32_t)(it.q0 + 16 * w + col) * ROWB + 16u * gq;
 #pragma unroll
-        for (int st = 0; st < 4; ++st) {
+        for (int st = 0; st < NS; ++st) {
             xq[st] = as_bf16x8(load16(rq, qoff + 64u * st));
             if constexpr (PROBE) xr[st] = as_bf16x8(load16(rr, qoff + 64u * st));
         }
     };
 
-    f32x4 a1[8], a2[8];  // O1^T, O2^T: dim block db (16 dims), lane: dims 16 db + 4 gq + i
+    f32x4 a1[NDB], a2[NDB];  // O1^T, O2^T: dim block db (16 dims), lane: dims 16 db + 4 gq + i
     float lsum = 0.f, bsum = 0.f;
     float lsx = 0.f, bsx = 0.f;  // STATS: the same sums of the unrounded weights and products
     float m_run = -INFINITY;
 
-    // ---- staging: waves 0-3 load and store the K tile, waves 4-7 the V tile.
+    // ---- staging: waves 0-3 load and store the K tile, waves 4-7 the V tile. K stager st
+    // moves chunks st + 256 j (key chunk / CPR, dims 8 (chunk % CPR) ..); V stager st moves
+    // keys 4 (st / CPR) .. +3 of dim chunk st % CPR (all of waves 4-7 at D = 128, the first
+    // 2 D of them otherwise). CPR (16-byte chunks per row) is a power of two.
     const bool kstager = w < 4;
     const int st = tid & 255;
-    const uint32_t koff = (uint32_t)(st >> 4) * 256u + 16u * (st & 15);        // + 4096 j
-    const uint32_t voff = (uint32_t)(4 * (st >> 4)) * 256u + 16u * (st & 15);  // + 256 j
+    const bool vactive = 2 * D >= 256 || st < 2 * D;
+    const uint32_t koff = (uint32_t)(st >> CPR_LOG) * ROWB + 16u * (st & (CPR - 1));  // + 4096 j
+    const uint32_t voff =
+        (uint32_t)(4 * (st >> CPR_LOG)) * ROWB + 16u * (st & (CPR - 1));  // + ROWB j
     u32x4 stg[4];
     auto gload = [&](int bh, int kt) {
         const size_t base = slice_of(bh) + (size_t)kt * BC * D;
-        const uint32_t bytes = slice_bytes - (uint32_t)kt * BC * 256u;  // kt * BC < T
+        const uint32_t bytes = slice_bytes - (uint32_t)kt * BC * ROWB;  // kt * BC < T
         if (kstager) {
             const auto rk = make_rsrc(k + base, bytes);
 #pragma unroll
-            for (int j = 0; j < 4; ++j) stg[j] = load16(rk, koff + 4096u * j);
-        } else {
+            for (int j = 0; j < KCH; ++j) stg[j] = load16(rk, koff + 4096u * j);
+        } else if (vactive) {
             const auto rv = make_rsrc(v + base, bytes);
 #pragma unroll
-            for (int j = 0; j < 4; ++j) stg[j] = load16(rv, voff + 256u * j);
+            for (int j = 0; j < 4; ++j) stg[j] = load16(rv, voff + ROWB * j);
         }
     };
     auto lstore = [&](int t) {
         if (kstager) {
             unsigned char* Kl = kbuf(t);
 #pragma unroll
-            for (int j = 0; j < 4; ++j) {
+            for (int j = 0; j < KCH; ++j) {
                 const int chunk = st + 256 * j;
-                const int key = chunk >> 4, cc = chunk & 15;
+                const int key = chunk >> CPR_LOG, cc = chunk & (CPR - 1);
                 *(u32x4*)(Kl + krow(key) * KS * 2 + cc * 16) = stg[j];
             }
-        } else {
+        } else if (vactive) {
             __bf16* Vl = (__bf16*)vbuf(t);
-            const int vdc = st & 15, vkg = st >> 4;
+            const int vdc = st & (CPR - 1), vkg = st >> CPR_LOG;
 #pragma unroll
             for (int p = 0; p < 4; ++p) {
                 const uint32_t lo01 = __builtin_amdgcn_perm(stg[1][p], stg[0][p], 0x05040100u);
@@ -201,7 +222,7 @@ __global__ __launch_bounds__(NT, 1) void prefill_bf16_d128_kernel(
             S[kb] = f32x4{};
             Tp[kb] = f32x4{};
 #pragma unroll
-            for (int s = 0; s < 4; ++s) {
+            for (int s = 0; s < NS; ++s) {
                 const bf16x8 kf = *(const bf16x8*)(Kl + 16 * kb * KS * 2 + 64 * s);
                 S[kb] = mfma16(kf, xq[s], S[kb]);
                 if constexpr (PROBE) Tp[kb] = mfma16(kf, xr[s], Tp[kb]);
@@ -217,7 +238,7 @@ __global__ __launch_bounds__(NT, 1) void prefill_bf16_d128_kernel(
     auto values = [&](int t, int G, bf16x8 p1, bf16x8 p2) {
         const unsigned char* Vl = vbuf(t);
 #pragma unroll
-        for (int db = 0; db < 8; ++db) {
+        for (int db = 0; db < NDB; ++db) {
             const bf16x8 vf = *(const bf16x8*)(Vl + vlane[db & 3] + 16 * db * VS * 2 +
                                                64 * (G ^ (db >> 2)));
             a1[db] = mfma16(vf, p1, a1[db]);
@@ -254,7 +275,7 @@ __global__ __launch_bounds__(NT, 1) void prefill_bf16_d128_kernel(
             const float mn = need ? ms : m_run;
             const float alpha = exp2_fast(m_run - mn);
 #pragma unroll
-            for (int db = 0; db < 8; ++db) {
+            for (int db = 0; db < NDB; ++db) {
                 a1[db] *= alpha;
                 if constexpr (PROBE) a2[db] *= alpha;
             }
@@ -353,7 +374,7 @@ __global__ __launch_bounds__(NT, 1) void prefill_bf16_d128_kernel(
             if ((t0 + kt) & 1) __syncthreads();
         };
 #pragma unroll
-        for (int db = 0; db < 8; ++db) a1[db] = a2[db] = f32x4{};  // a2 stays 0 without PROBE
+        for (int db = 0; db < NDB; ++db) a1[db] = a2[db] = f32x4{};  // a2 stays 0 without PROBE
         lsum = bsum = 0.f;
         lsx = bsx = 0.f;
         m_run = -INFINITY;
@@ -406,7 +427,7 @@ __global__ __launch_bounds__(NT, 1) void prefill_bf16_d128_kernel(
             const float one_tb = 1.f + bsum * inv;
             __bf16* orow = o + slice_of(cur.bh) + (size_t)qi * D;
 #pragma unroll
-            for (int db = 0; db < 8; ++db) {
+            for (int db = 0; db < NDB; ++db) {
                 float y[4];
 #pragma unroll
                 for (int i = 0; i < 4; ++i)
@@ -417,7 +438,7 @@ __global__ __launch_bounds__(NT, 1) void prefill_bf16_d128_kernel(
             if constexpr (STATS) {
                 __bf16* vrow = vbar + slice_of(cur.bh) + (size_t)qi * D;
 #pragma unroll
-                for (int db = 0; db < 8; ++db)
+                for (int db = 0; db < NDB; ++db)
                     *(u32x2*)(vrow + 16 * db + 4 * gq) =
                         u32x2{pack_bf16x2(inv * a1[db][0], inv * a1[db][1]),
                               pack_bf16x2(inv * a1[db][2], inv * a1[db][3])};
@@ -444,7 +465,7 @@ __global__ __launch_bounds__(NT, 1) void prefill_bf16_d128_kernel(
 
 }  // namespace
 
-hipError_t launch_prefill_bf16_d128(const PrefillArgs& a, hipStream_t stream) {
+hipError_t launch_prefill_bf16(const PrefillArgs& a, hipStream_t stream) {
     const int BH = a.B * a.H;
     const int nqb = (a.T + BR - 1) / BR;
     const long long nitems = (long long)BH * nqb;
@@ -462,12 +483,20 @@ hipError_t launch_prefill_bf16_d128(const PrefillArgs& a, hipStream_t stream) {
                            (const __bf16*)a.k, (const __bf16*)a.v, rp, (__bf16*)a.o,
                            (__bf16*)a.vbar, a.stats, BH, a.T, nqb, a.scale * kLog2e, ncls);
     };
-    if (a.stats) {
-        if (a.rho) go(prefill_bf16_d128_kernel<true, true>);
-        else go(prefill_bf16_d128_kernel<false, true>);
+    if (a.d == 64) {
+        if (a.stats) return hipErrorInvalidValue;  // statistics (for the backward): d = 128
+        if (a.rho) go(prefill_bf16_kernel<64, true, false>);
+        else go(prefill_bf16_kernel<64, false, false>);
+    } else if (a.d == 128) {
+        if (a.stats) {
+            if (a.rho) go(prefill_bf16_kernel<128, true, true>);
+            else go(prefill_bf16_kernel<128, false, true>);
+        } else {
+            if (a.rho) go(prefill_bf16_kernel<128, true, false>);
+            else go(prefill_bf16_kernel<128, false, false>);
+        }
     } else {
-        if (a.rho) go(prefill_bf16_d128_kernel<true, false>);
-        else go(prefill_bf16_d128_kernel<false, false>);
+        return hipErrorInvalidValue;
     }
     return hipGetLastError();
 }

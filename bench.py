@@ -56,7 +56,12 @@ sys.path.insert(0, ROOT)
 HBM_PEAK_GBPS = 8000.0
 BF16_PEAK_TFLOPS = 2500.0
 COUNTERS_JSON = os.path.join(ROOT, "profiles", "prefill_bf16_d128_counters.json")
-PREFILL_KERNEL = "prefill_bf16_d128_kernel"
+PREFILL_KERNEL = "prefill_bf16_kernel<128>"
+
+
+def is_prefill_d128(name: str) -> bool:
+    """The d = 128 instances of the prefill kernel, by demangled or mangled name."""
+    return "prefill_bf16_kernel" in name and ("<128" in name or "ILi128E" in name)
 COPY_BYTES = 1 << 30
 PREFILL_SOURCES = ("attention_plx_attn_amd/csrc/prefill_bf16.hip",
                    "attention_plx_attn_amd/csrc/plx_device.hpp")
@@ -124,7 +129,7 @@ def summarize_counters(fetch_glob, write_glob, mfma_glob=None, out_path=COUNTERS
         vals = [v for k, vs in d.items() if key(k) for v in vs]
         return sum(vals) / len(vals) if vals else None
 
-    is_prefill = lambda k: PREFILL_KERNEL in k  # noqa: E731
+    is_prefill = is_prefill_d128
     is_ref = lambda k: "neg" in k.lower()  # the --calibrate-copy reference kernel  # noqa: E731
     f_k, w_k = pick(fetch, is_prefill), pick(write, is_prefill)
     f_c, w_c = pick(fetch, is_ref), pick(write, is_ref)

@@ -55,7 +55,8 @@ def test_prefill_validation(lib):
     assert _prefill(lib, scale=float("inf")) == 3
     assert _prefill(lib, scale=-1.0) == 3
     assert _prefill(lib, dtype=7) == 3
-    assert _prefill(lib, dqk=64, dv=64) == 4              # bf16 only at d = 128
+    assert _prefill(lib, dqk=32, dv=32) == 4              # bf16 only at d in {64, 128}
+    assert _prefill(lib, dqk=96, dv=96) == 4
     assert _prefill(lib, dqk=128, dv=64) == 4
     assert _prefill(lib, dtype=0, dqk=128, dv=128) == 4   # f32 only at d in {16, 32, 64}
     assert _prefill(lib, dtype=0, dqk=48, dv=48) == 4

@@ -81,9 +81,10 @@ plx_status_t plan_decode(int B, int H, int L_max, int d_v, int num_splits, Decod
     *p = DecodePlan{};
     const long long bh = (long long)B * H;
     const size_t rec_bytes = (size_t)(2 * d_v + 4) * sizeof(float);
+    const bool range_built = d_v == 128;  // wave-range mode exists at d = 128 only
     int waves = 0, splits = num_splits;
     if (num_splits < 0) {
-        if (!range_mode_fits(B, H, L_max)) return PLX_ERR_UNSUPPORTED;
+        if (!range_built || !range_mode_fits(B, H, L_max)) return PLX_ERR_UNSUPPORTED;
         waves = ceil_div(-(long long)num_splits, 4) * 4;
     } else if (num_splits == 0) {
         int cus = 0;
@@ -91,7 +92,7 @@ plx_status_t plan_decode(int B, int H, int L_max, int d_v, int num_splits, Decod
         if (st != PLX_OK) return st;
         long long wg = bh / (4LL * kRangeWholeBhPerWave);
         if (wg > (long long)kRangeWgPerCu * cus) wg = (long long)kRangeWgPerCu * cus;
-        if (range_mode_fits(B, H, L_max) && L_max <= kRangeMaxAutoLmax &&
+        if (range_built && range_mode_fits(B, H, L_max) && L_max <= kRangeMaxAutoLmax &&
             wg >= (long long)kRangeMinWgPerCu * cus)
             waves = (int)(4 * wg);
         if (!waves) {  // split mode: fill the chip once with (b, h, chunk) workgroups
@@ -275,7 +276,8 @@ plx_status_t plx_attn_decode(plx_dtype_t dtype, int32_t B, int32_t H, int32_t L_
     if (!std::isfinite(softmax_scale) || softmax_scale < 0.f) return PLX_ERR_INVALID_ARG;
     if (num_splits > kDecodeMaxSplits || num_splits < -plx::kDecodeRangeMaxWaves)
         return PLX_ERR_INVALID_ARG;
-    if (!(dtype == PLX_BF16 && d_qk == 128 && d_v == 128)) return PLX_ERR_UNSUPPORTED;
+    if (!(dtype == PLX_BF16 && d_qk == d_v && (d_qk == 128 || d_qk == 64)))
+        return PLX_ERR_UNSUPPORTED;
     if (!aligned16(q) || !aligned16(rho) || !aligned16(k_cache) || !aligned16(v_cache) ||
         !aligned16(o) || (reinterpret_cast<uintptr_t>(seqlens) & 3u) != 0)
         return PLX_ERR_MISALIGNED;
@@ -291,7 +293,9 @@ plx_status_t plx_attn_decode(plx_dtype_t dtype, int32_t B, int32_t H, int32_t L_
     plx::DecodeArgs a{B, H, L_max, d_qk, q, rho, k_cache, v_cache, seqlens, o, softmax_scale,
                       p.splits, p.chunk, static_cast<float*>(workspace), p.waves,
                       p.whole ? 1 : 0};
-    const hipError_t e = plx::launch_decode_bf16_d128(a, static_cast<hipStream_t>(stream));
+    const hipError_t e = d_qk == 64
+                             ? plx::launch_decode_bf16_d64(a, static_cast<hipStream_t>(stream))
+                             : plx::launch_decode_bf16_d128(a, static_cast<hipStream_t>(stream));
     return e == hipSuccess ? PLX_OK : PLX_ERR_HIP;
 }
 

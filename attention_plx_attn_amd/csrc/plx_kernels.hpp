@@ -73,6 +73,9 @@ hipError_t launch_prefill_f32(const PrefillArgs& a, hipStream_t stream);
 hipError_t launch_prefill_bf16(const PrefillArgs& a, hipStream_t stream);
 hipError_t launch_prefill_bwd_bf16_d128(const PrefillBwdArgs& a, hipStream_t stream);
 hipError_t launch_decode_bf16_d128(const DecodeArgs& a, hipStream_t stream);
+// Head dim 64: split mode over a contiguous cache (a.waves == 0, a.table == nullptr), with its
+// own combine when a.splits > 1 (records of 2 * 64 + 4 floats).
+hipError_t launch_decode_bf16_d64(const DecodeArgs& a, hipStream_t stream);
 hipError_t launch_probe_bf16_d128(const ProbeArgs& a, hipStream_t stream);
 // Grouped query heads: a.H query heads over Hkv cache heads (a.H / Hkv in {1, 2, 4, 8}), split
 // mode with a.splits chunks; partials in the split decode's record layout per query head.

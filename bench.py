@@ -429,14 +429,17 @@ def compare(out_md):
 
     rows = []
     B, T, d = 4, 2048, 128
-    for name, H, probe in (("Parallax", 16, True), ("softmax only, I/O-matched", 16, False),
-                           ("softmax only, compute-matched (2x heads)", 32, False)):
-        q, k, v = bf((B, H, T, d)), bf((B, H, T, d)), bf((B, H, T, d))
-        rho = bf((B, H, T, d), 0.1) if probe else None
+    for name, H, dh, probe in (
+            ("Parallax", 16, d, True), ("softmax only, I/O-matched", 16, d, False),
+            ("softmax only, compute-matched (2x heads)", 32, d, False),
+            ("Parallax, compute-matched (head dim halved, same FLOPs as softmax at d 128)",
+             16, d // 2, True)):
+        q, k, v = bf((B, H, T, dh)), bf((B, H, T, dh)), bf((B, H, T, dh))
+        rho = bf((B, H, T, dh), 0.1) if probe else None
         o = torch.empty_like(q)
-        us = timed(lambda: plx.prefill(q, k, v, rho, d ** -0.5, out=o), cold=False)
-        fl = (8 if probe else 4) * d * B * H * T * (T + 1) // 2
-        rows.append({"kernel": "prefill", "variant": name, "shape": f"{B}x{H}x{T} d{d}",
+        us = timed(lambda: plx.prefill(q, k, v, rho, dh ** -0.5, out=o), cold=False)
+        fl = (8 if probe else 4) * dh * B * H * T * (T + 1) // 2
+        rows.append({"kernel": "prefill", "variant": name, "shape": f"{B}x{H}x{T} d{dh}",
                      "median_us": us, "tflops": round(fl / us / 1e6, 1)})
         print(json.dumps(rows[-1]), flush=True)
         del q, k, v, rho, o

@@ -83,7 +83,9 @@ def test_decode_validation(lib):
     assert _decode(lib, B=64, H=64, L=1 << 20, splits=-8) == 4  # flat rows must fit in int32
     assert _decode(lib, splits=5000) == 3
     assert _decode(lib, dtype=0) == 4
-    assert _decode(lib, dqk=64, dv=64) == 4
+    assert _decode(lib, dqk=32, dv=32) == 4               # bf16 at d in {64, 128}
+    assert _decode(lib, dqk=64, dv=128) == 4
+    assert _decode(lib, dqk=64, dv=64, splits=-8) == 4    # wave-range mode: d = 128 only
     assert _decode(lib, vc=A + 2) == 5
     assert _decode(lib, sl=A + 2) == 5
     # split run: the workspace is required and must be large enough

@@ -1,6 +1,7 @@
-// decode_d64_bf16.hip -- one Parallax decode step at head dim 64 (the compute-matched head dim:
-// halving d makes the layer's four products per cached row cost what softmax attention's two
-// cost at d = 128), bf16 in/out, gfx950. Split-KV partials plus a combine, as at d = 128.
+// decode_d64_bf16.hip -- one Parallax decode step at head dim 64 (the compute-matched head dim
+// of the agihunt review's pretraining table: halving d makes the four products per cached row
+// cost what softmax attention's two cost at d = 128), bf16 in/out, gfx950. Split-KV
+// partials plus a combine, as at d = 128.
 //
 // The per-wave step follows the d = 128 decode [agihunt review, hardware paragraph: the probe
 // products ride in accumulator rows a single query row leaves idle]:
@@ -12,7 +13,9 @@
 //    steps 2-6];
 //  * values: a 64-dim row is 8 lanes of 16 bytes, so the 64 lanes take 8 row groups: lane
 //    (col, g) accumulates A1 = sum w v and A2 = sum w t v for dims 8 (col & 7) .. +7 over the
-//    4 rows 4 (2 g + (col >> 3)) .. +3 of each 32-row step.
+//    8 rows 8 (2 g + (col >> 3)) .. +7 of each 64-row step.
+// A step covers 64 rows, so that a wave has as many bytes in flight per step as the d = 128
+// decode's 32-row steps.
 // Loads use raw buffer resources: rows at or beyond the resource's range read as zero.
 #include "plx_device.hpp"
 #include "plx_kernels.hpp"
@@ -21,9 +24,9 @@ namespace plx {
 namespace {
 
 constexpr int D = 64;
-constexpr int KB = 32;       // keys per wave step
+constexpr int KB = 64;       // keys per wave step (16 KB of K and V, as a d = 128 step)
 constexpr int KT = KB / 16;  // score tiles per step
-constexpr int VR = 4;        // value rows per lane per step
+constexpr int VR = KB / 8;   // value rows per lane per step (8 row groups)
 constexpr int NW = 4;        // waves per workgroup
 constexpr int NT = 64 * NW;
 constexpr int REC = 2 * D + 4;  // record: A1[D], A2[D], m, l, beta, pad
@@ -46,7 +49,7 @@ __device__ __forceinline__ float combine_out(float a1, float a2, float l, float 
 
 struct Frag {
     u32x4 k[KT][2];  // K rows 16 t + col, dims 32 st + 8 g .. +7
-    u32x4 v[VR];     // V rows 4 (2 g + (col >> 3)) + r, dims 8 (col & 7) .. +7
+    u32x4 v[VR];     // V rows VR (2 g + (col >> 3)) + r, dims 8 (col & 7) .. +7
 };
 
 struct Acc {
@@ -126,19 +129,22 @@ __device__ __forceinline__ void consume(Acc& s, const Frag& f, const bf16x8 (&bq
     __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
 
     const int vg = 2 * g + (col >> 3);
-    const f32x4 u0 = *(const f32x4*)&ush[0][VR * vg];
-    const f32x4 u1 = PROBE ? *(const f32x4*)&ush[1][VR * vg] : f32x4{};
 #pragma unroll
-    for (int rr = 0; rr < VR; ++rr) {
-        const u32x4 x = f.v[rr];
+    for (int r4 = 0; r4 < VR / 4; ++r4) {
+        const f32x4 u0 = *(const f32x4*)&ush[0][VR * vg + 4 * r4];
+        const f32x4 u1 = PROBE ? *(const f32x4*)&ush[1][VR * vg + 4 * r4] : f32x4{};
 #pragma unroll
-        for (int p = 0; p < 4; ++p) {
-            const float vlo = bf16_lo(x[p]), vhi = bf16_hi(x[p]);
-            s.a1[2 * p] = fmaf(u0[rr], vlo, s.a1[2 * p]);
-            s.a1[2 * p + 1] = fmaf(u0[rr], vhi, s.a1[2 * p + 1]);
-            if constexpr (PROBE) {
-                s.a2[2 * p] = fmaf(u1[rr], vlo, s.a2[2 * p]);
-                s.a2[2 * p + 1] = fmaf(u1[rr], vhi, s.a2[2 * p + 1]);
+        for (int rr = 0; rr < 4; ++rr) {
+            const u32x4 x = f.v[4 * r4 + rr];
+#pragma unroll
+            for (int p = 0; p < 4; ++p) {
+                const float vlo = bf16_lo(x[p]), vhi = bf16_hi(x[p]);
+                s.a1[2 * p] = fmaf(u0[rr], vlo, s.a1[2 * p]);
+                s.a1[2 * p + 1] = fmaf(u0[rr], vhi, s.a1[2 * p + 1]);
+                if constexpr (PROBE) {
+                    s.a2[2 * p] = fmaf(u1[rr], vlo, s.a2[2 * p]);
+                    s.a2[2 * p + 1] = fmaf(u1[rr], vhi, s.a2[2 * p + 1]);
+                }
             }
         }
     }
@@ -148,7 +154,7 @@ __device__ __forceinline__ void consume(Acc& s, const Frag& f, const bf16x8 (&bq
 }
 
 // Split mode: workgroup (s, h, b) takes chunk s of sequence b's rows for head h; its 4 waves
-// stride through the chunk in 32-row steps (loads of the next step issued before the current
+// stride through the chunk in 64-row steps (loads of the next step issued before the current
 // one is consumed) and merge their states through LDS. S == 1 writes o, else a record.
 template <bool PROBE>
 __global__ __launch_bounds__(NT, 2) void decode_split_bf16_d64_kernel(
@@ -259,28 +265,72 @@ __global__ __launch_bounds__(NT, 2) void decode_split_bf16_d64_kernel(
     }
 }
 
-// One wave per (b, h): lane owns dim lane and folds the S records (an empty one has m = -inf)
-// with one rescale per record whose m raises the running maximum.
-__global__ __launch_bounds__(64) void decode_combine_d64_kernel(const float* __restrict__ ws,
+// Online merge state of one wave; lane owns dim lane.
+struct Merge {
+    float m = -INFINITY, l = 0.f, beta = 0.f, a1 = 0.f, a2 = 0.f;
+};
+
+// Fold records rec_at(0 .. n-1) into st, issuing the loads of a batch of 8 records before using
+// any of them (one memory round trip per batch). An empty record has m = -inf.
+template <class RecAt>
+__device__ __forceinline__ void fold_records(Merge& st, int n, RecAt rec_at, int lane) {
+    constexpr int BATCH = 8;
+    for (int u0 = 0; u0 < n; u0 += BATCH) {
+        float ms[BATCH], ls[BATCH], bs[BATCH], x1[BATCH], x2[BATCH];
+#pragma unroll
+        for (int u = 0; u < BATCH; ++u) {
+            const float* rec = rec_at(min(u0 + u, n - 1));
+            ms[u] = u0 + u < n ? rec[2 * D] : -INFINITY;
+            ls[u] = rec[2 * D + 1];
+            bs[u] = rec[2 * D + 2];
+            x1[u] = rec[lane];
+            x2[u] = rec[D + lane];
+        }
+        float mb = st.m;
+#pragma unroll
+        for (int u = 0; u < BATCH; ++u) mb = fmaxf(mb, ms[u]);
+        if (mb == -INFINITY) continue;  // nothing non-empty yet (wave-uniform)
+        const float fo = st.m > -INFINITY ? exp2_fast(st.m - mb) : 0.f;
+        st.l *= fo;
+        st.beta *= fo;
+        st.a1 *= fo;
+        st.a2 *= fo;
+#pragma unroll
+        for (int u = 0; u < BATCH; ++u) {
+            const float f = ms[u] > -INFINITY ? exp2_fast(ms[u] - mb) : 0.f;
+            st.l = fmaf(f, ls[u], st.l);
+            st.beta = fmaf(f, bs[u], st.beta);
+            st.a1 = fmaf(f, x1[u], st.a1);
+            st.a2 = fmaf(f, x2[u], st.a2);
+        }
+        st.m = mb;
+    }
+}
+
+// One workgroup per (b, h): wave w folds the records s = w, w + 4, ..., then the four wave
+// states are merged through LDS.
+__global__ __launch_bounds__(NT) void decode_combine_d64_kernel(const float* __restrict__ ws,
                                                                __bf16* __restrict__ o, int S) {
-    const int lane = threadIdx.x;
+    __shared__ __attribute__((aligned(16))) float reds[NW][REC];
+    const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
     const size_t bh = blockIdx.x;
     const float* base = ws + bh * (size_t)S * REC;
-    float m = -INFINITY, l = 0.f, beta = 0.f, a1 = 0.f, a2 = 0.f;
-    for (int s = 0; s < S; ++s) {
-        const float* rec = base + (size_t)s * REC;
-        const float ms = rec[2 * D];
-        if (ms == -INFINITY) continue;  // empty chunk (wave-uniform)
-        const float mn = fmaxf(m, ms);
-        const float fo = m > -INFINITY ? exp2_fast(m - mn) : 0.f;
-        const float fs = exp2_fast(ms - mn);
-        l = fmaf(fs, rec[2 * D + 1], l * fo);
-        beta = fmaf(fs, rec[2 * D + 2], beta * fo);
-        a1 = fmaf(fs, rec[lane], a1 * fo);
-        a2 = fmaf(fs, rec[D + lane], a2 * fo);
-        m = mn;
+    Merge st;
+    const int n = w < S ? (S - w + NW - 1) / NW : 0;
+    fold_records(st, n, [&](int u) { return base + (size_t)(w + NW * u) * REC; }, lane);
+    reds[w][lane] = st.a1;
+    reds[w][D + lane] = st.a2;
+    if (lane == 0) {
+        reds[w][2 * D] = st.m;
+        reds[w][2 * D + 1] = st.l;
+        reds[w][2 * D + 2] = st.beta;
     }
-    o[bh * D + lane] = (__bf16)combine_out(a1, a2, l, beta);
+    __syncthreads();
+    if (w == 0) {
+        Merge all;
+        fold_records(all, NW, [&](int i) { return &reds[i][0]; }, lane);
+        o[bh * D + lane] = (__bf16)combine_out(all.a1, all.a2, all.l, all.beta);
+    }
 }
 
 }  // namespace
@@ -301,7 +351,7 @@ hipError_t launch_decode_bf16_d64(const DecodeArgs& a, hipStream_t stream) {
                            a.splits, c);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess || a.splits == 1) return e;
-    hipLaunchKernelGGL(decode_combine_d64_kernel, dim3(a.B * a.H), dim3(64), 0, stream,
+    hipLaunchKernelGGL(decode_combine_d64_kernel, dim3(a.B * a.H), dim3(NT), 0, stream,
                        (const float*)a.ws, (__bf16*)a.o, a.splits);
     return hipGetLastError();
 }

@@ -444,18 +444,21 @@ def compare(out_md):
         print(json.dumps(rows[-1]), flush=True)
         del q, k, v, rho, o
     L = 32768
-    for name, H, probe in (("Parallax", 16, True), ("softmax only, I/O-matched", 16, False),
-                           ("softmax only, compute-matched (2x heads)", 32, False)):
-        q, kc, vc = bf((1, H, d)), bf((1, H, L, d)), bf((1, H, L, d))
-        rho = bf((1, H, d)) if probe else None
+    for name, H, dh, probe in (
+            ("Parallax", 16, d, True), ("softmax only, I/O-matched", 16, d, False),
+            ("softmax only, compute-matched (2x heads)", 32, d, False),
+            ("Parallax, compute-matched (head dim halved: half the cache bytes)", 16, d // 2,
+             True)):
+        q, kc, vc = bf((1, H, dh)), bf((1, H, L, dh)), bf((1, H, L, dh))
+        rho = bf((1, H, dh)) if probe else None
         sl = torch.full((1,), L, dtype=torch.int32, device=dev)
         o = torch.empty_like(q)
-        ws = torch.empty(max(plx.decode_workspace_size(1, H, L, d) // 4, 1),
+        ws = torch.empty(max(plx.decode_workspace_size(1, H, L, dh) // 4, 1),
                          dtype=torch.float32, device=dev)
-        us = timed(lambda: plx.decode(q, rho, kc, vc, sl, d ** -0.5, out=o, workspace=ws),
+        us = timed(lambda: plx.decode(q, rho, kc, vc, sl, dh ** -0.5, out=o, workspace=ws),
                    cold=True)
-        nbytes = decode_bytes([L], H, d) - (0 if probe else H * d * 2)
-        rows.append({"kernel": "decode", "variant": name, "shape": f"1x{H}x{L} d{d}",
+        nbytes = decode_bytes([L], H, dh) - (0 if probe else H * dh * 2)
+        rows.append({"kernel": "decode", "variant": name, "shape": f"1x{H}x{L} d{dh}",
                      "median_us": us, "hbm_gbps": round(nbytes / us / 1e3, 1)})
         print(json.dumps(rows[-1]), flush=True)
         del q, kc, vc, rho, o, ws

@@ -72,8 +72,11 @@ typedef enum { PLX_F32 = 0, PLX_BF16 = 1 } plx_dtype_t;
  *   rho == NULL means rho = 0 exactly: plain softmax attention, computed by a specialisation
  *   without the probe branch; its output is bit-identical to a call with an all-zero rho.
  *
- * Built combinations: (PLX_BF16, d_qk = d_v = 128) on the matrix cores;
- * (PLX_F32, d_qk = d_v in {16, 32, 64}) on the vector ALUs.
+ * Built combinations: (PLX_BF16, d_qk = d_v in {64, 128}) on the matrix cores (d = 64 is
+ * the compute-matched head dim of the pages' control: a Parallax layer with the head dim
+ * halved does the FLOPs of softmax attention at the full head dim [agihunt review,
+ * pretraining table and the paragraph after it; gist.science summary (Spanish), results
+ * section, controls item]); (PLX_F32, d_qk = d_v in {16, 32, 64}) on the vector ALUs.
  * Limits: B*H <= 2^31-1 and T * d * sizeof(dtype) < 2^31 (one (b,h) slice per buffer).
  */
 plx_status_t plx_attn_prefill(plx_dtype_t dtype, int32_t B, int32_t H, int32_t T,
@@ -82,11 +85,12 @@ plx_status_t plx_attn_prefill(plx_dtype_t dtype, int32_t B, int32_t H, int32_t T
                               void* stream);
 
 /*
- * The plan a decode call with these arguments will use, written to *splits_out in the
- * encoding of num_splits: S > 0 for split mode with S chunks per (b, h), or -G for
+ * The plan a decode call with these arguments will use at d = 128, written to *splits_out in
+ * the encoding of num_splits: S > 0 for split mode with S chunks per (b, h), or -G for
  * wave-range mode with G waves. num_splits > 0 and < 0 are taken as given (a negative count
  * is rounded up to a multiple of 4); 0 picks from B*H, L_max and the current device's
- * compute-unit count.
+ * compute-unit count. At d = 64 only split mode exists: 0 then picks the split count the
+ * split heuristic gives (plx_attn_decode_workspace_size, which takes d_v, sizes it).
  */
 plx_status_t plx_attn_decode_num_splits(int32_t B, int32_t H, int32_t L_max,
                                         int32_t num_splits, int32_t* splits_out);
@@ -123,7 +127,8 @@ plx_status_t plx_attn_decode_workspace_size(int32_t B, int32_t H, int32_t L_max,
  *   workspace  : device buffer of at least plx_attn_decode_workspace_size() bytes
  *              (may be NULL when that size is 0).
  *
- * Built combination: (PLX_BF16, d_qk = d_v = 128).
+ * Built combinations: (PLX_BF16, d_qk = d_v = 128), both modes; (PLX_BF16, d_qk = d_v = 64),
+ * split mode (num_splits >= 0; a negative count returns PLX_ERR_UNSUPPORTED).
  * Limits: L_max * d * 2 < 2^31; -65536 <= num_splits <= 4096.
  */
 plx_status_t plx_attn_decode(plx_dtype_t dtype, int32_t B, int32_t H, int32_t L_max,

@@ -44,14 +44,19 @@ namespace plx {
 namespace {
 
 constexpr int BR = 128;  // query rows per work item
-constexpr int BC = 64;   // keys per LDS tile
 constexpr int NT = 512;  // threads per workgroup (8 waves x 16 query rows)
-constexpr int VS = BC + 8;        // LDS row stride of a transposed V tile
 constexpr int NBUF = 4;  // stream tiles s + 2 is staged while s is processed
 
 // Sizes that follow from the head dim D (d_qk = d_v = D, a multiple of 32, at most 128).
 template <int D>
 struct Geo {
+    // Keys per LDS tile: 64 at d = 128; 128 at d = 64, so that a tile holds the same bytes,
+    // the stagers move the same number of chunks and the per-tile softmax and barrier cost
+    // is spread over as much matrix work as possible.
+    static constexpr int BC = D == 64 ? 128 : 64;
+    static constexpr int NKB = BC / 16;      // 16-key score blocks per tile
+    static constexpr int NG = BC / 32;       // 32-key value steps per tile
+    static constexpr int VS = BC + 8;        // LDS row stride of a transposed V tile
     static constexpr int KS = D + 8;         // LDS row stride of a K tile (bf16 elements)
     static constexpr int K_ELEMS = BC * KS;  // 8704 bf16 at D = 128
     static constexpr int V_ELEMS = D * VS;   // 9216 bf16 at D = 128
@@ -62,17 +67,18 @@ struct Geo {
     static constexpr int CPR = D / 8;    // 16-byte chunks per row
     static constexpr int CPR_LOG = D == 128 ? 4 : 3;
     static constexpr int KCH = BC * CPR / 256;  // chunks per K stager thread
+    static constexpr int VST = BC / 4 * CPR;    // V stager threads (4 keys x one chunk each)
     static constexpr uint32_t ROWB = 2 * D;     // bytes per row
     static_assert(D == 64 || D == 128, "head dim");
     static_assert(LDS_BYTES <= 160 * 1024, "LDS budget");
 };
 constexpr float kLazyTau = 8.0f;  // log2 headroom before the running max moves
 
-// K row of key k (0..63) of a tile: inside each 32-key group, key 8 q + 4 b + i goes to row
+// K row of key k of a tile: inside each 32-key group, key 8 q + 4 b + i goes to row
 // 16 b + 4 q + i, so that the score blocks b = 0, 1 give each lane the 8 consecutive keys
 // 8 q .. 8 q + 7 that the value product's operand wants.
 __device__ __forceinline__ int krow(int k) {
-    return (k & 32) | (((k >> 2) & 1) << 4) | (((k >> 3) & 3) << 2) | (k & 3);
+    return (k & ~31) | (((k >> 2) & 1) << 4) | (((k >> 3) & 3) << 2) | (k & 3);
 }
 
 __device__ __forceinline__ f32x4 mfma16(bf16x8 a, bf16x8 b, f32x4 c) {
@@ -87,6 +93,7 @@ struct Item {
     int bh, q0, ntiles, nfull;
 };
 
+template <int BC>
 __device__ __forceinline__ Item item_at(int pos, int cls, int ncls, int nbh_c, int nqb, int T) {
     Item it;
     const int qb = nqb - 1 - pos / nbh_c;
@@ -121,6 +128,7 @@ __global__ __launch_bounds__(NT, 1) void prefill_bf16_kernel(
     float* __restrict__ stats, int BH, int T, int nqb, float c, int ncls) {
     using G_ = Geo<D>;
     constexpr int KS = G_::KS, K_ELEMS = G_::K_ELEMS, V_ELEMS = G_::V_ELEMS, OFF_V = G_::OFF_V;
+    constexpr int BC = G_::BC, NKB = G_::NKB, NG = G_::NG, VS = G_::VS;
     constexpr int NS = G_::NS, NDB = G_::NDB, CPR = G_::CPR, CPR_LOG = G_::CPR_LOG;
     constexpr int KCH = G_::KCH;
     constexpr uint32_t ROWB = G_::ROWB;
@@ -168,7 +176,7 @@ __global__ __launch_bounds__(NT, 1) void prefill_bf16_kernel(
     // 2 D of them otherwise). CPR (16-byte chunks per row) is a power of two.
     const bool kstager = w < 4;
     const int st = tid & 255;
-    const bool vactive = 2 * D >= 256 || st < 2 * D;
+    const bool vactive = G_::VST >= 256 || st < G_::VST;
     const uint32_t koff = (uint32_t)(st >> CPR_LOG) * ROWB + 16u * (st & (CPR - 1));  // + 4096 j
     const uint32_t voff =
         (uint32_t)(4 * (st >> CPR_LOG)) * ROWB + 16u * (st & (CPR - 1));  // + ROWB j
@@ -215,10 +223,10 @@ __global__ __launch_bounds__(NT, 1) void prefill_bf16_kernel(
     // Scores and probe products of K tile t: block kb covers LDS rows 16 kb .. +15.
     // Lane (col, gq) register i of block kb holds key 32 (kb >> 1) + 8 gq + 4 (kb & 1) + i.
     const int klane = col * KS * 2 + 16 * gq;
-    auto products = [&](int t, f32x4 (&S)[4], f32x4 (&Tp)[4]) {
+    auto products = [&](int t, f32x4 (&S)[NKB], f32x4 (&Tp)[NKB]) {
         const unsigned char* Kl = kbuf(t) + klane;
 #pragma unroll
-        for (int kb = 0; kb < 4; ++kb) {
+        for (int kb = 0; kb < NKB; ++kb) {
             S[kb] = f32x4{};
             Tp[kb] = f32x4{};
 #pragma unroll
@@ -248,14 +256,15 @@ __global__ __launch_bounds__(NT, 1) void prefill_bf16_kernel(
     };
 
     // Weights and value products of tile t (local index kt) from its products S, Tp.
-    auto finish = [&](int t, int kt, int qi, auto diag_tag, f32x4 (&S)[4], const f32x4 (&Tp)[4]) {
+    auto finish = [&](int t, int kt, int qi, auto diag_tag, f32x4 (&S)[NKB],
+                      const f32x4 (&Tp)[NKB]) {
         constexpr bool DIAG = decltype(diag_tag)::value;
         if constexpr (DIAG) {
             // key kt * BC + 8 gq + (32 (kb >> 1) + 4 (kb & 1) + i) is visible iff the constant
             // part is at most lim
             const int lim = qi - kt * BC - 8 * gq;
 #pragma unroll
-            for (int kb = 0; kb < 4; ++kb)
+            for (int kb = 0; kb < NKB; ++kb)
 #pragma unroll
                 for (int i = 0; i < 4; ++i)
                     if (32 * (kb >> 1) + 4 * (kb & 1) + i > lim) S[kb][i] = -INFINITY;
@@ -268,6 +277,13 @@ __global__ __launch_bounds__(NT, 1) void prefill_bf16_kernel(
         mt = max3(mt, S[2][3], S[3][0]);
         mt = max3(mt, S[3][1], S[3][2]);
         mt = max3(mt, S[3][3], S[3][3]);
+#pragma unroll
+        for (int kb = 4; kb < NKB; kb += 2) {
+            mt = max3(mt, S[kb][0], S[kb][1]);
+            mt = max3(mt, S[kb][2], S[kb][3]);
+            mt = max3(mt, S[kb + 1][0], S[kb + 1][1]);
+            mt = max3(mt, S[kb + 1][2], S[kb + 1][3]);
+        }
         mt = max_across_row_groups(mt);
         const float ms = mt > -INFINITY ? mt * c : -INFINITY;
         const bool need = ms > m_run + kLazyTau;
@@ -288,7 +304,7 @@ __global__ __launch_bounds__(NT, 1) void prefill_bf16_kernel(
             m_run = mn;
         }
 #pragma unroll
-        for (int G = 0; G < 2; ++G) {
+        for (int G = 0; G < NG; ++G) {
             uint32_t p1[4], p2[4];
 #pragma unroll
             for (int e = 0; e < 4; ++e) {
@@ -325,7 +341,7 @@ __global__ __launch_bounds__(NT, 1) void prefill_bf16_kernel(
     int kk = 0;
     int pos = item_position(0, jw, Wc);
     if (pos >= nit_c) return;
-    Item cur = item_at(pos, cls, ncls, nbh_c, nqb, T);
+    Item cur = item_at<BC>(pos, cls, ncls, nbh_c, nqb, T);
     // Source of the tile `ahead` tiles after local tile kt of item a, given the next two items.
     auto source = [&](const Item& a, int kt, int ahead, bool h1, const Item& n1, bool h2,
                       const Item& n2, int* bh, int* tile) {
@@ -343,8 +359,8 @@ __global__ __launch_bounds__(NT, 1) void prefill_bf16_kernel(
     {
         const int p1 = item_position(1, jw, Wc), p2 = item_position(2, jw, Wc);
         const bool h1 = p1 < nit_c, h2 = p2 < nit_c;
-        const Item n1 = item_at(h1 ? p1 : pos, cls, ncls, nbh_c, nqb, T);
-        const Item n2 = item_at(h2 ? p2 : pos, cls, ncls, nbh_c, nqb, T);
+        const Item n1 = item_at<BC>(h1 ? p1 : pos, cls, ncls, nbh_c, nqb, T);
+        const Item n2 = item_at<BC>(h2 ? p2 : pos, cls, ncls, nbh_c, nqb, T);
         gload(cur.bh, 0);
         lstore(0);
         int sbh = 0, stile = 0;
@@ -359,10 +375,10 @@ __global__ __launch_bounds__(NT, 1) void prefill_bf16_kernel(
     for (;;) {
         const int pos_n = item_position(kk + 1, jw, Wc);
         const bool has_next = pos_n < nit_c;
-        const Item nx = item_at(has_next ? pos_n : pos, cls, ncls, nbh_c, nqb, T);
+        const Item nx = item_at<BC>(has_next ? pos_n : pos, cls, ncls, nbh_c, nqb, T);
         const int pos_n2 = item_position(kk + 2, jw, Wc);
         const bool has_next2 = has_next && pos_n2 < nit_c;
-        const Item nx2 = item_at(has_next2 ? pos_n2 : pos, cls, ncls, nbh_c, nqb, T);
+        const Item nx2 = item_at<BC>(has_next2 ? pos_n2 : pos, cls, ncls, nbh_c, nqb, T);
         const int nt = cur.ntiles;
         auto stage = [&](int kt) {
             int sbh = 0, stile = 0;
@@ -379,7 +395,7 @@ __global__ __launch_bounds__(NT, 1) void prefill_bf16_kernel(
         lsx = bsx = 0.f;
         m_run = -INFINITY;
         const int qi = cur.q0 + 16 * w + col;
-        f32x4 S[4], Tp[4];
+        f32x4 S[NKB], Tp[NKB];
         for (int kt = 0; kt < cur.nfull; ++kt) {
             const bool staged = stage(kt);
             products(t0 + kt, S, Tp);

@@ -15,7 +15,7 @@ struct PrefillArgs {
     void* o;
     float scale;
     int workers;  // resident workgroups of a persistent launch (the device's compute units)
-    void* vbar = nullptr;    // bf16 d = 128 only: O1 / l per row [B, H, T, d], or nullptr
+    void* vbar = nullptr;    // d = 128 only: O1 / l per row [B, H, T, d] (bf16), or nullptr
     float* stats = nullptr;  // with vbar: (lse, tbar) per row [B, H, T, 2]
 };
 
@@ -70,6 +70,7 @@ struct ProbeArgs {
 
 bool prefill_f32_supported(int d);
 hipError_t launch_prefill_f32(const PrefillArgs& a, hipStream_t stream);
+// bf16 prefill, d = 64 or 128 (statistics for the backward at d = 128).
 hipError_t launch_prefill_bf16(const PrefillArgs& a, hipStream_t stream);
 hipError_t launch_prefill_bwd_bf16_d128(const PrefillBwdArgs& a, hipStream_t stream);
 hipError_t launch_decode_bf16_d128(const DecodeArgs& a, hipStream_t stream);

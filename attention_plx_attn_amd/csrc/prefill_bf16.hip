@@ -16,7 +16,7 @@
 //   * K rows are stored in LDS in an order (key 8 q + 4 b + i of each 32-key group at row
 //     16 b + 4 q + i) that makes each lane's accumulator registers of two score blocks hold
 //     the 8 consecutive keys of its value-product operand: no cross-lane traffic;
-//   * V is stored transposed (d rows x 64 keys, 16-byte key chunks XOR-swizzled with bits
+//   * V is stored transposed (d rows x BC keys, 16-byte key chunks XOR-swizzled with bits
 //     4..6 of d), so a value operand is one 16-byte LDS read whose address is a per-lane base
 //     plus a constant;
 //   * P1 and P2 are rounded to bf16 and l = sum P1, beta = sum P2 are taken from the rounded
@@ -24,6 +24,7 @@
 //     from the unrounded P1;
 //   * the running max is updated lazily (only when a row's tile max exceeds it by more than
 //     2^8); the result is the same exact expression, with far fewer rescales.
+// A tile holds BC = 64 keys at d = 128 and BC = 128 keys at d = 64 (the same bytes).
 // Waves 0-3 stage the K tiles and waves 4-7 the V tiles (with the transpose); the V stagers
 // issue at a higher priority, which balances the two waves of a SIMD (the hardware otherwise
 // favours the older wave for the matrix pipe, and the V stagers have the longer slot).

@@ -149,6 +149,19 @@ def summarize_counters(fetch_glob, write_glob, mfma_glob=None, out_path=COUNTERS
         "hbm_bytes_per_dispatch": (f_k * fetch_scale + w_k * write_scale) * 1024.0,
         "source_sha256": source_hash(),
     }
+    # The decode call of the same step (split kernel + combine), scaled the same way.
+    is_split = lambda k: "decode_split" in k  # noqa: E731
+    is_comb = lambda k: "decode_combine" in k  # noqa: E731
+    f_s, w_s = pick(fetch, is_split), pick(write, is_split)
+    f_m, w_m = pick(fetch, is_comb), pick(write, is_comb)
+    if None not in (f_s, w_s, f_m, w_m):
+        rec["decode"] = {
+            "workload": "decode B1 H16 L32768 d128 bf16 (split kernel + combine)",
+            "hbm_bytes_per_call": (f_s * fetch_scale + w_s * write_scale +
+                                   f_m * fetch_scale + w_m * write_scale) * 1024.0,
+            "split_hbm_bytes_per_dispatch": (f_s * fetch_scale + w_s * write_scale) * 1024.0,
+            "source_sha256": source_hash(DECODE_SOURCES),
+        }
     if mfma_glob:
         mops = pick(_pmc_rows(mfma_glob, "SQ_INSTS_VALU_MFMA_MOPS_BF16"), is_prefill)
         busy = pick(_pmc_rows(mfma_glob, "SQ_VALU_MFMA_BUSY_CYCLES"), is_prefill)
@@ -198,6 +211,19 @@ def counter_summary(flops, seconds):
 def committed_traffic():
     rec = committed_counters()
     return None if rec is None else rec.get("hbm_bytes_per_dispatch")
+
+
+def committed_decode_traffic():
+    """HBM bytes per decode call from the committed counters, or None once the decode code
+    changed since they were taken."""
+    try:
+        with open(COUNTERS_JSON) as fh:
+            dec = json.load(fh).get("decode")
+    except (OSError, ValueError):
+        return None
+    if not dec or dec.get("source_sha256") != source_hash(DECODE_SOURCES):
+        return None
+    return dec.get("hbm_bytes_per_call")
 
 
 # ------------------------------------------------------------------------------ CPU baseline
@@ -923,7 +949,8 @@ def main():
                      "work_per_launch": flops, "counters": counter_summary(flops, pre_avg_s)},
         "roofline_decode": {"bound": "hbm", "achieved": round(dec_gbps, 1),
                             "peak": HBM_PEAK_GBPS, "unit": "GB/s",
-                            "frac": round(dec_gbps / HBM_PEAK_GBPS, 4), "traffic": None,
+                            "frac": round(dec_gbps / HBM_PEAK_GBPS, 4),
+                            "traffic": committed_decode_traffic(),
                             "work_per_launch": dbytes},
         "wall_s_timed": round(wall, 3),
         "system": {"gpu": torch.cuda.get_device_name(dev),

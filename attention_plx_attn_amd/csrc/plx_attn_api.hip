@@ -123,13 +123,14 @@ plx_status_t check_decode_shape(int B, int H, int L_max, int d_v) {
     return PLX_OK;
 }
 
-// Shapes of the forward-with-statistics and the backward: bf16, d_qk = d_v = 128 only.
+// Shapes of the forward-with-statistics and the backward: bf16, d_qk = d_v in {64, 128}.
 plx_status_t check_bwd_shape(plx_dtype_t dtype, int B, int H, int T, int d_qk, int d_v,
                              float scale) {
     if (B < 1 || H < 1 || T < 1 || d_qk < 1 || d_v < 1) return PLX_ERR_INVALID_SHAPE;
     if (!std::isfinite(scale) || scale < 0.f) return PLX_ERR_INVALID_ARG;
-    if (dtype != PLX_BF16 || d_qk != 128 || d_v != 128) return PLX_ERR_UNSUPPORTED;
-    if ((long long)T * 256 >= (1LL << 31)) return PLX_ERR_INVALID_SHAPE;
+    if (dtype != PLX_BF16 || d_qk != d_v || (d_qk != 128 && d_qk != 64))
+        return PLX_ERR_UNSUPPORTED;
+    if ((long long)T * d_qk * 2 >= (1LL << 31)) return PLX_ERR_INVALID_SHAPE;
     if ((long long)B * H * ((T + 127) / 128) > INT_MAX) return PLX_ERR_INVALID_SHAPE;
     return PLX_OK;
 }
@@ -231,9 +232,9 @@ plx_status_t plx_attn_prefill_bwd(plx_dtype_t dtype, int32_t B, int32_t H, int32
     size_t need = 0;
     plx_attn_prefill_bwd_workspace_size(B, H, T, &need);
     if (workspace_bytes < need) return PLX_ERR_WORKSPACE_TOO_SMALL;
-    plx::PrefillBwdArgs a{B, H, T, q, k, v, rho, o, vbar, stats, d_o, dq, dk, dv, drho,
+    plx::PrefillBwdArgs a{B, H, T, d_qk, q, k, v, rho, o, vbar, stats, d_o, dq, dk, dv, drho,
                           static_cast<float*>(workspace), softmax_scale};
-    const hipError_t e = plx::launch_prefill_bwd_bf16_d128(a, static_cast<hipStream_t>(stream));
+    const hipError_t e = plx::launch_prefill_bwd_bf16(a, static_cast<hipStream_t>(stream));
     return e == hipSuccess ? PLX_OK : PLX_ERR_HIP;
 }
 

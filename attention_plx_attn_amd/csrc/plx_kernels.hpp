@@ -15,15 +15,15 @@ struct PrefillArgs {
     void* o;
     float scale;
     int workers;  // resident workgroups of a persistent launch (the device's compute units)
-    void* vbar = nullptr;    // d = 128 only: O1 / l per row [B, H, T, d] (bf16), or nullptr
+    void* vbar = nullptr;    // O1 / l per row [B, H, T, d] (bf16), or nullptr
     float* stats = nullptr;  // with vbar: (lse, tbar) per row [B, H, T, 2]
 };
 
-// Backward of the causal prefill (bf16, d = 128). All tensors [B, H, T, d] except stats
-// [B, H, T, 2] (lse, tbar from the forward) and ws [B, H, T] x 4 floats (per-row records the
-// dq kernel writes for the dk kernel).
+// Backward of the causal prefill (bf16, d = 64 or 128). All tensors [B, H, T, d] except
+// stats [B, H, T, 2] (lse, tbar from the forward) and ws [B, H, T] x 4 floats (per-row records
+// the dq kernel writes for the dk kernel).
 struct PrefillBwdArgs {
-    int B, H, T;
+    int B, H, T, d;
     const void *q, *k, *v, *rho, *o, *vbar;
     const float* stats;
     const void* dout;
@@ -70,9 +70,9 @@ struct ProbeArgs {
 
 bool prefill_f32_supported(int d);
 hipError_t launch_prefill_f32(const PrefillArgs& a, hipStream_t stream);
-// bf16 prefill, d = 64 or 128 (statistics for the backward at d = 128).
+// bf16 prefill, d = 64 or 128 (with vbar and stats: the statistics the backward starts from).
 hipError_t launch_prefill_bf16(const PrefillArgs& a, hipStream_t stream);
-hipError_t launch_prefill_bwd_bf16_d128(const PrefillBwdArgs& a, hipStream_t stream);
+hipError_t launch_prefill_bwd_bf16(const PrefillBwdArgs& a, hipStream_t stream);
 hipError_t launch_decode_bf16_d128(const DecodeArgs& a, hipStream_t stream);
 // Head dim 64: split mode over a contiguous cache (a.waves == 0, a.table == nullptr), with its
 // own combine when a.splits > 1 (records of 2 * 64 + 4 floats).

@@ -501,9 +501,13 @@ hipError_t launch_prefill_bf16(const PrefillArgs& a, hipStream_t stream) {
                            (__bf16*)a.vbar, a.stats, BH, a.T, nqb, a.scale * kLog2e, ncls);
     };
     if (a.d == 64) {
-        if (a.stats) return hipErrorInvalidValue;  // statistics (for the backward): d = 128
-        if (a.rho) go(prefill_bf16_kernel<64, true, false>);
-        else go(prefill_bf16_kernel<64, false, false>);
+        if (a.stats) {
+            if (a.rho) go(prefill_bf16_kernel<64, true, true>);
+            else go(prefill_bf16_kernel<64, false, true>);
+        } else {
+            if (a.rho) go(prefill_bf16_kernel<64, true, false>);
+            else go(prefill_bf16_kernel<64, false, false>);
+        }
     } else if (a.d == 128) {
         if (a.stats) {
             if (a.rho) go(prefill_bf16_kernel<128, true, true>);

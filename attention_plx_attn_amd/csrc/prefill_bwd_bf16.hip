@@ -41,9 +41,19 @@
 namespace plx {
 namespace {
 
-constexpr int D = 128;
 constexpr int NT = 512;   // 8 waves
-constexpr int RS = D + 8;  // LDS row stride of a row-major tile (bf16): 272 bytes
+
+// Sizes that follow from the head dim D (64 or 128).
+template <int D>
+struct BG {
+    static constexpr int RS = D + 8;     // LDS row stride of a row-major tile (bf16)
+    static constexpr int NS = D / 32;    // 32-dim steps of a product over d
+    static constexpr int NDB = D / 16;   // 16-dim blocks of an accumulator
+    static constexpr int CPR = D / 8;    // 16-byte chunks per row
+    static constexpr int CPR_LOG = D == 128 ? 4 : 3;
+    static constexpr uint32_t ROWB = 2 * D;
+    static_assert(D == 64 || D == 128, "head dim");
+};
 
 __device__ __forceinline__ f32x4 mfma16(bf16x8 a, bf16x8 b, f32x4 c) {
     return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
@@ -99,18 +109,21 @@ __device__ __forceinline__ void item_of(int n, int BH, int nblk, bool longest_la
 // ============================================================================ dq kernel
 constexpr int QBR = 128;                 // query rows per item
 constexpr int KBC = 64;                  // keys per tile
-constexpr int Q_KR = KBC * RS * 2;       // bytes of a row-major K (or V) tile
-constexpr int Q_BUF = 2 * Q_KR;
-constexpr int Q_LDS = 2 * Q_BUF;
-static_assert(Q_LDS <= 160 * 1024, "LDS budget");
 
+template <int D>
 __global__ __launch_bounds__(NT, 1) void prefill_bwd_dq_kernel(
     const __bf16* __restrict__ q, const __bf16* __restrict__ k, const __bf16* __restrict__ v,
     const __bf16* __restrict__ rho, const __bf16* __restrict__ o,
     const __bf16* __restrict__ vbar, const float* __restrict__ stats,
     const __bf16* __restrict__ dout, __bf16* __restrict__ dq, __bf16* __restrict__ dr,
     f32x4* __restrict__ rec, int BH, int T, int nqb, float c, float scale) {
-    __shared__ __attribute__((aligned(16))) unsigned char lds[Q_LDS];
+    using G_ = BG<D>;
+    constexpr int RS = G_::RS, NS = G_::NS, NDB = G_::NDB, CPR = G_::CPR, CPR_LOG = G_::CPR_LOG;
+    constexpr uint32_t ROWB = G_::ROWB;
+    constexpr int Q_KR = KBC * RS * 2;  // bytes of a row-major K (or V) tile
+    constexpr int Q_BUF = 2 * Q_KR;
+    static_assert(2 * Q_BUF <= 160 * 1024, "LDS budget");
+    __shared__ __attribute__((aligned(16))) unsigned char lds[2 * Q_BUF];
     const int tid = threadIdx.x, lane = tid & 63;
     const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int col = lane & 15, gq = lane >> 4;
@@ -122,7 +135,7 @@ __global__ __launch_bounds__(NT, 1) void prefill_bwd_dq_kernel(
     const int qi = q0 + 16 * w + col;
 
     // ---- the wave's fragments (B operand): lane holds dims 32 s + 8 gq .. +7 of query qi
-    bf16x8 xq[4], xr[4], xdo[4];
+    bf16x8 xq[NS], xr[NS], xdo[NS];
     float G, Dd, L2, tbar;
     {
         const auto rq = make_rsrc(q + slice, slice_bytes);
@@ -131,10 +144,10 @@ __global__ __launch_bounds__(NT, 1) void prefill_bwd_dq_kernel(
         const auto ro = make_rsrc(o + slice, slice_bytes);
         const auto rv = make_rsrc(vbar + slice, slice_bytes);
         const auto rs = make_rsrc(stats + 2 * (size_t)bh * T, (uint32_t)T * 8u);
-        const uint32_t off = (uint32_t)qi * 256u + 16u * gq;
-        u32x4 vo[4], vv[4], vd[4];
+        const uint32_t off = (uint32_t)qi * ROWB + 16u * gq;
+        u32x4 vo[NS], vv[NS], vd[NS];
 #pragma unroll
-        for (int s = 0; s < 4; ++s) {
+        for (int s = 0; s < NS; ++s) {
             xq[s] = as_bf16x8(load16(rq, off + 64u * s));
             xr[s] = as_bf16x8(load16(rr, off + 64u * s));
             vd[s] = load16(rd, off + 64u * s);
@@ -148,7 +161,7 @@ __global__ __launch_bounds__(NT, 1) void prefill_bwd_dq_kernel(
                                              rs, (uint32_t)qi * 8u + 4u, 0, 0));
         float pg = 0.f, pd = 0.f;
 #pragma unroll
-        for (int s = 0; s < 4; ++s) {
+        for (int s = 0; s < NS; ++s) {
             pg = dot8(vd[s], vv[s], pg);
             pd = dot8(vd[s], vo[s], pd);
         }
@@ -162,30 +175,31 @@ __global__ __launch_bounds__(NT, 1) void prefill_bwd_dq_kernel(
         if (gq == 0 && qi < T) rec[(size_t)bh * T + qi] = f32x4{L2, tbar, G, Dd};
     }
 
-    f32x4 aq[8], ar[8];  // dQ^T, dR^T: dim block db, lane: dims 16 db + 4 gq + i of query qi
+    f32x4 aq[NDB], ar[NDB];  // dQ^T, dR^T: dim block db, lane: dims 16 db + 4 gq + i of qi
 #pragma unroll
-    for (int db = 0; db < 8; ++db) aq[db] = ar[db] = f32x4{};
+    for (int db = 0; db < NDB; ++db) aq[db] = ar[db] = f32x4{};
 
     // ---- staging: waves 0-3 K, waves 4-7 V (row-major, rows in prow order). Thread st loads
-    // keys 4 (st >> 4) .. +3, dims 8 (st & 15) .. +7.
+    // keys KPT (st / CPR) .. + KPT - 1, dims 8 (st % CPR) .. +7 (KPT = 4 at d = 128, 2 at 64).
+    constexpr int KPT = CPR / 4;
     const bool kst = w < 4;
-    const int st = tid & 255, sdc = st & 15, skg = st >> 4;
-    const uint32_t soff = (uint32_t)(4 * skg) * 256u + 16u * sdc;
-    u32x4 stg[4];
+    const int st = tid & 255, sdc = st & (CPR - 1), skg = st >> CPR_LOG;
+    const uint32_t soff = (uint32_t)(KPT * skg) * ROWB + 16u * sdc;
+    u32x4 stg[KPT];
     const int kend = min(q0 + QBR, T);
     const int ntiles = (kend + KBC - 1) / KBC;
     const int nfull = min(ntiles, q0 / KBC);
     auto gload = [&](int kt) {
-        const uint32_t rem = slice_bytes - (uint32_t)kt * KBC * 256u;
+        const uint32_t rem = slice_bytes - (uint32_t)kt * KBC * ROWB;
         const auto r = make_rsrc((kst ? k : v) + slice + (size_t)kt * KBC * D, rem);
 #pragma unroll
-        for (int j = 0; j < 4; ++j) stg[j] = load16(r, soff + 256u * j);
+        for (int j = 0; j < KPT; ++j) stg[j] = load16(r, soff + ROWB * j);
     };
     auto lstore = [&](int buf) {
         unsigned char* base = lds + buf * Q_BUF + (kst ? 0 : Q_KR);
 #pragma unroll
-        for (int j = 0; j < 4; ++j)
-            *(u32x4*)(base + prow(4 * skg + j) * RS * 2 + 16 * sdc) = stg[j];
+        for (int j = 0; j < KPT; ++j)
+            *(u32x4*)(base + prow(KPT * skg + j) * RS * 2 + 16 * sdc) = stg[j];
     };
     // K^T operands through the transposing read: source lane (4 j + a) of group gq addresses
     // K tile row 4 gq + j (+ 32 G + 16 h), dims 4 a .. +3 (+ 16 db)
@@ -200,7 +214,7 @@ __global__ __launch_bounds__(NT, 1) void prefill_bwd_dq_kernel(
         for (int kb = 0; kb < 4; ++kb) {
             S[kb] = Tp[kb] = Gm[kb] = f32x4{};
 #pragma unroll
-            for (int s = 0; s < 4; ++s) {
+            for (int s = 0; s < NS; ++s) {
                 const bf16x8 kf = *(const bf16x8*)(Kr + 16 * kb * RS * 2 + 64 * s);
                 const bf16x8 vf = *(const bf16x8*)(Vr + 16 * kb * RS * 2 + 64 * s);
                 S[kb] = mfma16(kf, xq[s], S[kb]);
@@ -226,7 +240,7 @@ __global__ __launch_bounds__(NT, 1) void prefill_bwd_dq_kernel(
                 }
             const bf16x8 da = pack8(fa), dt = pack8(ft);
 #pragma unroll
-            for (int db = 0; db < 8; ++db) {
+            for (int db = 0; db < NDB; ++db) {
                 const bf16x8 kf = read_tr_operand(Kt + 32 * G2 * RS * 2 + 32 * db, RS * 2);
                 aq[db] = mfma16(kf, da, aq[db]);
                 ar[db] = mfma16(kf, dt, ar[db]);
@@ -251,7 +265,7 @@ __global__ __launch_bounds__(NT, 1) void prefill_bwd_dq_kernel(
         __bf16* qrow = dq + slice + (size_t)qi * D;
         __bf16* rrow = dr + slice + (size_t)qi * D;
 #pragma unroll
-        for (int db = 0; db < 8; ++db) {
+        for (int db = 0; db < NDB; ++db) {
             *(u32x2*)(qrow + 16 * db + 4 * gq) =
                 u32x2{pack_bf16x2(scale * aq[db][0], scale * aq[db][1]),
                       pack_bf16x2(scale * aq[db][2], scale * aq[db][3])};
@@ -264,18 +278,21 @@ __global__ __launch_bounds__(NT, 1) void prefill_bwd_dq_kernel(
 // ============================================================================ dk kernel
 constexpr int KBR = 128;                // keys per item
 constexpr int QBC = 64;                 // queries per tile
-constexpr int K_R = QBC * RS * 2;       // bytes of one row-major tile (Q, R or dO)
 constexpr int K_REC = QBC * 16;         // per-row records (L2, tbar, G, D)
-constexpr int K_BUF = 3 * K_R + K_REC;
-constexpr int K_LDS = 2 * K_BUF;
-static_assert(K_LDS <= 160 * 1024, "LDS budget");
 
+template <int D>
 __global__ __launch_bounds__(NT, 1) void prefill_bwd_dk_kernel(
     const __bf16* __restrict__ q, const __bf16* __restrict__ k, const __bf16* __restrict__ v,
     const __bf16* __restrict__ rho, const __bf16* __restrict__ dout,
     const f32x4* __restrict__ rec, __bf16* __restrict__ dk, __bf16* __restrict__ dv, int BH,
     int T, int nkb, float c, float scale) {
-    __shared__ __attribute__((aligned(16))) unsigned char lds[K_LDS];
+    using G_ = BG<D>;
+    constexpr int RS = G_::RS, NS = G_::NS, NDB = G_::NDB, CPR = G_::CPR, CPR_LOG = G_::CPR_LOG;
+    constexpr uint32_t ROWB = G_::ROWB;
+    constexpr int K_R = QBC * RS * 2;  // bytes of one row-major tile (Q, R or dO)
+    constexpr int K_BUF = 3 * K_R + K_REC;
+    static_assert(2 * K_BUF <= 160 * 1024, "LDS budget");
+    __shared__ __attribute__((aligned(16))) unsigned char lds[2 * K_BUF];
     const int tid = threadIdx.x, lane = tid & 63;
     const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int col = lane & 15, gq = lane >> 4;
@@ -286,40 +303,42 @@ __global__ __launch_bounds__(NT, 1) void prefill_bwd_dk_kernel(
     const uint32_t slice_bytes = (uint32_t)T * D * 2u;
     const int kj = k0 + 16 * w + col;  // the lane's key (score column)
 
-    bf16x8 xk[4], xv[4];
+    bf16x8 xk[NS], xv[NS];
     {
         const auto rk = make_rsrc(k + slice, slice_bytes);
         const auto rv = make_rsrc(v + slice, slice_bytes);
-        const uint32_t off = (uint32_t)kj * 256u + 16u * gq;
+        const uint32_t off = (uint32_t)kj * ROWB + 16u * gq;
 #pragma unroll
-        for (int s = 0; s < 4; ++s) {
+        for (int s = 0; s < NS; ++s) {
             xk[s] = as_bf16x8(load16(rk, off + 64u * s));
             xv[s] = as_bf16x8(load16(rv, off + 64u * s));
         }
     }
-    f32x4 ak[8], av[8];
+    f32x4 ak[NDB], av[NDB];
 #pragma unroll
-    for (int db = 0; db < 8; ++db) ak[db] = av[db] = f32x4{};
+    for (int db = 0; db < NDB; ++db) ak[db] = av[db] = f32x4{};
 
-    // ---- staging: chunk m (0..5) of thread t is tensor m / 2 (Q, R, dO), row
-    // (t >> 4) + 32 (m & 1), dims 8 (t & 15) .. +7; threads 0..63 also stage the row records.
-    u32x4 stg[6];
+    // ---- staging: chunk m (0 .. 3 NP - 1) of thread t is tensor m / NP (Q, R, dO), row
+    // t / CPR + RPP (m % NP), dims 8 (t % CPR) .. +7, with RPP = 512 / CPR rows per pass and
+    // NP = 64 / RPP passes (2 at d = 128, 1 at 64); threads 0..63 also stage the row records.
+    constexpr int RPP = 512 / CPR, NP = QBC / RPP;
+    u32x4 stg[3 * NP];
     u32x4 srec = u32x4{};
     const int qt0 = k0 / QBC;
     const int ntiles = (T + QBC - 1) / QBC - qt0;
-    const int srow = tid >> 4, sc = tid & 15;
+    const int srow = tid >> CPR_LOG, sc = tid & (CPR - 1);
     auto gload = [&](int n) {
         const int r0 = (qt0 + n) * QBC;
-        const uint32_t rem = slice_bytes - (uint32_t)r0 * 256u;
+        const uint32_t rem = slice_bytes - (uint32_t)r0 * ROWB;
         const auto r_q = make_rsrc(q + slice + (size_t)r0 * D, rem);
         const auto r_r = make_rsrc(rho + slice + (size_t)r0 * D, rem);
         const auto r_d = make_rsrc(dout + slice + (size_t)r0 * D, rem);
 #pragma unroll
-        for (int h = 0; h < 2; ++h) {
-            const uint32_t off = (uint32_t)(srow + 32 * h) * 256u + 16u * sc;
+        for (int h = 0; h < NP; ++h) {
+            const uint32_t off = (uint32_t)(srow + RPP * h) * ROWB + 16u * sc;
             stg[h] = load16(r_q, off);
-            stg[2 + h] = load16(r_r, off);
-            stg[4 + h] = load16(r_d, off);
+            stg[NP + h] = load16(r_r, off);
+            stg[2 * NP + h] = load16(r_d, off);
         }
         if (w == 0) {
             const auto r = make_rsrc(rec + (size_t)bh * T + r0, (uint32_t)(T - r0) * 16u);
@@ -329,8 +348,8 @@ __global__ __launch_bounds__(NT, 1) void prefill_bwd_dk_kernel(
     auto lstore = [&](int buf) {
         unsigned char* base = lds + buf * K_BUF;
 #pragma unroll
-        for (int m = 0; m < 6; ++m)
-            *(u32x4*)(base + (m >> 1) * K_R + prow(srow + 32 * (m & 1)) * RS * 2 + 16 * sc) =
+        for (int m = 0; m < 3 * NP; ++m)
+            *(u32x4*)(base + (m / NP) * K_R + prow(srow + RPP * (m % NP)) * RS * 2 + 16 * sc) =
                 stg[m];
         if (w == 0) *(u32x4*)(base + 3 * K_R + 16 * lane) = srec;
     };
@@ -347,7 +366,7 @@ __global__ __launch_bounds__(NT, 1) void prefill_bwd_dk_kernel(
         for (int b = 0; b < 4; ++b) {
             S[b] = Tp[b] = Gm[b] = f32x4{};
 #pragma unroll
-            for (int s = 0; s < 4; ++s) {
+            for (int s = 0; s < NS; ++s) {
                 const int o = 16 * b * RS * 2 + 64 * s;
                 S[b] = mfma16(*(const bf16x8*)(Qr + o), xk[s], S[b]);
                 Tp[b] = mfma16(*(const bf16x8*)(Qr + K_R + o), xk[s], Tp[b]);
@@ -378,7 +397,7 @@ __global__ __launch_bounds__(NT, 1) void prefill_bwd_dk_kernel(
             const bf16x8 ps = pack8(fs), pa = pack8(fa), pt = pack8(ft);
             const unsigned char* Tr = base + trl + 32 * G2 * RS * 2;
 #pragma unroll
-            for (int db = 0; db < 8; ++db) {
+            for (int db = 0; db < NDB; ++db) {
                 const int o = 32 * db;
                 auto op = [&](int tensor) { return read_tr_operand(Tr + tensor * K_R + o, RS * 2); };
                 av[db] = mfma16(op(2), ps, av[db]);
@@ -406,7 +425,7 @@ __global__ __launch_bounds__(NT, 1) void prefill_bwd_dk_kernel(
         __bf16* krow = dk + slice + (size_t)kj * D;
         __bf16* vrow = dv + slice + (size_t)kj * D;
 #pragma unroll
-        for (int db = 0; db < 8; ++db) {
+        for (int db = 0; db < NDB; ++db) {
             *(u32x2*)(krow + 16 * db + 4 * gq) = u32x2{pack_bf16x2(ak[db][0], ak[db][1]),
                                                        pack_bf16x2(ak[db][2], ak[db][3])};
             *(u32x2*)(vrow + 16 * db + 4 * gq) = u32x2{pack_bf16x2(av[db][0], av[db][1]),
@@ -417,24 +436,35 @@ __global__ __launch_bounds__(NT, 1) void prefill_bwd_dk_kernel(
 
 }  // namespace
 
-hipError_t launch_prefill_bwd_bf16_d128(const PrefillBwdArgs& a, hipStream_t stream) {
+namespace {
+
+template <int D>
+hipError_t launch_bwd(const PrefillBwdArgs& a, hipStream_t stream) {
     const int BH = a.B * a.H;
     const int nblk = (a.T + 127) / 128;
     const long long items = (long long)BH * nblk;
     if (items < 1 || items > 0x7fffffffLL) return hipErrorInvalidConfiguration;
     const float c = a.scale * kLog2e;
-    hipLaunchKernelGGL(prefill_bwd_dq_kernel, dim3((unsigned)items), dim3(NT), 0, stream,
+    hipLaunchKernelGGL(prefill_bwd_dq_kernel<D>, dim3((unsigned)items), dim3(NT), 0, stream,
                        (const __bf16*)a.q, (const __bf16*)a.k, (const __bf16*)a.v,
                        (const __bf16*)a.rho, (const __bf16*)a.o, (const __bf16*)a.vbar,
                        a.stats, (const __bf16*)a.dout, (__bf16*)a.dq, (__bf16*)a.drho,
                        (f32x4*)a.ws, BH, a.T, nblk, c, a.scale);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
-    hipLaunchKernelGGL(prefill_bwd_dk_kernel, dim3((unsigned)items), dim3(NT), 0, stream,
+    hipLaunchKernelGGL(prefill_bwd_dk_kernel<D>, dim3((unsigned)items), dim3(NT), 0, stream,
                        (const __bf16*)a.q, (const __bf16*)a.k, (const __bf16*)a.v,
                        (const __bf16*)a.rho, (const __bf16*)a.dout, (const f32x4*)a.ws,
                        (__bf16*)a.dk, (__bf16*)a.dv, BH, a.T, nblk, c, a.scale);
     return hipGetLastError();
+}
+
+}  // namespace
+
+hipError_t launch_prefill_bwd_bf16(const PrefillBwdArgs& a, hipStream_t stream) {
+    if (a.d == 128) return launch_bwd<128>(a, stream);
+    if (a.d == 64) return launch_bwd<64>(a, stream);
+    return hipErrorInvalidValue;
 }
 
 }  // namespace plx

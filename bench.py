@@ -731,6 +731,11 @@ def backward(out_md):
     ws = torch.empty(plx.prefill_bwd_workspace_size(cfg.B, cfg.H, cfg.T) // 4,
                      dtype=torch.float32, device=dev)
     pairs = cfg.B * cfg.H * cfg.T * (cfg.T + 1) // 2
+    # the same workload at head dim 64 (the compute-matched head dim)
+    x64 = {n: t[..., : cfg.d // 2].contiguous() for n, t in x.items() if n != "scale"}
+    do64 = do[..., : cfg.d // 2].contiguous()
+    s64 = (cfg.d // 2) ** -0.5
+    o64, vbar64, stats64 = plx.prefill_fwd(x64["q"], x64["k"], x64["v"], x64["rho"], s64)
     calls = {
         "forward (plx_attn_prefill)": (
             lambda: plx.prefill(x["q"], x["k"], x["v"], x["rho"], cfg.scale), 8 * cfg.d * pairs),
@@ -740,6 +745,12 @@ def backward(out_md):
         "backward (plx_attn_prefill_bwd: dq/drho and dk/dv kernels)": (
             lambda: plx.prefill_bwd(x["q"], x["k"], x["v"], x["rho"], o, vbar, stats, do,
                                     cfg.scale, workspace=ws), 16 * cfg.d * pairs),
+        "forward with saved statistics, d = 64": (
+            lambda: plx.prefill_fwd(x64["q"], x64["k"], x64["v"], x64["rho"], s64),
+            8 * (cfg.d // 2) * pairs),
+        "backward, d = 64": (
+            lambda: plx.prefill_bwd(x64["q"], x64["k"], x64["v"], x64["rho"], o64, vbar64,
+                                    stats64, do64, s64, workspace=ws), 16 * (cfg.d // 2) * pairs),
     }
     rows = []
     for name, (call, flops) in calls.items():
@@ -756,7 +767,7 @@ def backward(out_md):
             torch.cuda.synchronize()
             ts.append(e0.elapsed_time(e1))
         us = _stats_us(ts)["median_us"]
-        r = {"workload": f"{name}, B{cfg.B} H{cfg.H} T{cfg.T} d{cfg.d}", "median_us": us,
+        r = {"workload": f"{name}, B{cfg.B} H{cfg.H} T{cfg.T}", "median_us": us,
              "tflops": round(flops / us / 1e6, 1),
              "frac": round(flops / us / 1e6 / BF16_PEAK_TFLOPS, 4)}
         rows.append(r)

@@ -207,7 +207,8 @@ def test_prefill_fwd_validation(lib):
     assert _fwd(lib, scale=-1.0) == 3
     assert _fwd(lib, dtype=7) == 3
     assert _fwd(lib, dtype=0) == 4                            # fp32 not built
-    assert _fwd(lib, dqk=64, dv=64) == 4
+    assert _fwd(lib, dqk=32, dv=32) == 4
+    assert _fwd(lib, dqk=64, dv=128) == 4
     assert _fwd(lib, stats=A + 4) == 5
     assert _fwd(lib, vbar=A + 2) == 5
 

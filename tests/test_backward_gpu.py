@@ -99,6 +99,23 @@ def test_backward_parity(B, H, T, rho):
     _check_grads(grads, x, f"bwd B={B} H={H} T={T} rho={rho}")
 
 
+@pytest.mark.parametrize("B,H,T", [(1, 1, 1), (1, 2, 100), (2, 3, 333), (1, 2, 1024)])
+def test_backward_parity_d64(B, H, T):
+    """Head dim 64 (the compute-matched head dim): forward statistics and gradients."""
+    cfg = PrefillConfig("bwd64", 46, B, H, T, 64, "bf16", "scaled")
+    x = _inputs(cfg, seed=T + 3)
+    _say("bwd d64", B, H, T)
+    d, o, vbar, stats, grads = _gpu(x)
+    assert torch.equal(o, plx.prefill(d["q"], d["k"], d["v"], d["rho"], x["scale"]))
+    lse, tbar, vb = oracle.prefill_stats(*(to_f64(x[n]) for n in ("q", "k", "v", "rho")),
+                                         x["scale"])
+    check_bf16(vbar, vb, "vbar d64")
+    st = to_f64(stats)
+    assert np.abs(st[..., 0] - lse).max() <= LSE_ABS
+    assert np.abs(st[..., 1] - tbar).max() <= TBAR_ABS
+    _check_grads(grads, x, f"bwd d64 B={B} H={H} T={T}")
+
+
 def test_backward_rho_zero_is_softmax_attention():
     cfg = PrefillConfig("bwd", 44, 1, 2, 300, 128, "bf16", "zero")
     x = _inputs(cfg, seed=5)

@@ -233,7 +233,8 @@ plx_status_t plx_attn_probe(plx_dtype_t dtype, int32_t B, int32_t T, int32_t C, 
  * Arithmetic: products on the matrix cores (bf16 operands, fp32 accumulation); the pair
  * quantities s, scale * da and dt are rounded to bf16 before the accumulating products; p is
  * recomputed as exp(scale <q_i, k_j> - lse_i). Output rounded to bf16 (RNE).
- * Built combination (both calls): (PLX_BF16, d_qk = d_v = 128). Limits: T * 256 < 2^31.
+ * Built combinations (both calls): (PLX_BF16, d_qk = d_v in {64, 128}). Limits:
+ * T * d * 2 < 2^31.
  * Errors as for the other entry points; PLX_ERR_WORKSPACE_TOO_SMALL for a short workspace.
  */
 plx_status_t plx_attn_prefill_fwd(plx_dtype_t dtype, int32_t B, int32_t H, int32_t T,

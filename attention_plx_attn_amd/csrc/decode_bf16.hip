@@ -63,9 +63,8 @@ struct Merge {
 
 // Fold records rec_at(0 .. n-1) into st, issuing the loads of a batch of 8 records before
 // using any of them (one memory round trip per batch). An empty record has m = -inf.
-template <class RecAt>
+template <int BATCH = 8, class RecAt>
 __device__ __forceinline__ void fold_records(Merge& st, int n, RecAt rec_at, int lane) {
-    constexpr int BATCH = 8;
     for (int u0 = 0; u0 < n; u0 += BATCH) {
         float ms[BATCH], ls[BATCH], bs[BATCH];
         float2 x1[BATCH], x2[BATCH];
@@ -254,31 +253,16 @@ __global__ __launch_bounds__(NT, 2) void decode_split_bf16_d128_kernel(
     }
 }
 
-// One workgroup per (b, h): wave w folds the partials s = w, w + 4, ..., then the four wave
-// states are merged through LDS with one rescale each.
-__global__ __launch_bounds__(NT) void decode_combine_kernel(const float* __restrict__ ws,
+// One wave per (b, h): lane owns dims 2 lane, 2 lane + 1 and folds the S records in batches of
+// 16 (all loads of a batch in flight together; one batch for up to 16 splits).
+__global__ __launch_bounds__(64) void decode_combine_kernel(const float* __restrict__ ws,
                                                             __bf16* __restrict__ o, int S) {
-    __shared__ __attribute__((aligned(16))) float reds[NW][2 * D + 4];
-    const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+    const int lane = threadIdx.x;
     const size_t bh = blockIdx.x;
     const float* base = ws + bh * (size_t)S * REC;
-
     Merge st;
-    const int n = w < S ? (S - w + NW - 1) / NW : 0;
-    fold_records(st, n, [&](int u) { return base + (size_t)(w + NW * u) * REC; }, lane);
-    *(float2*)&reds[w][2 * lane] = float2{st.a1x, st.a1y};
-    *(float2*)&reds[w][D + 2 * lane] = float2{st.a2x, st.a2y};
-    if (lane == 0) {
-        reds[w][2 * D] = st.m;
-        reds[w][2 * D + 1] = st.l;
-        reds[w][2 * D + 2] = st.beta;
-    }
-    __syncthreads();
-    if (w == 0) {
-        Merge all;
-        fold_records(all, NW, [&](int i) { return &reds[i][0]; }, lane);
-        store_merged(all, o + bh * D, lane);
-    }
+    fold_records<16>(st, S, [&](int u) { return base + (size_t)u * REC; }, lane);
+    store_merged(st, o + bh * D, lane);
 }
 
 // ------------------------------------------------------------------------ wave-range mode
@@ -553,7 +537,7 @@ hipError_t launch_decode(const DecodeArgs& a, hipStream_t stream) {
                            a.splits, c, nullptr, 0, 0, 0);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess || a.splits == 1) return e;
-    hipLaunchKernelGGL(decode_combine_kernel, dim3(BH), dim3(NT), 0, stream, (const float*)a.ws,
+    hipLaunchKernelGGL(decode_combine_kernel, dim3(BH), dim3(64), 0, stream, (const float*)a.ws,
                        (__bf16*)a.o, a.splits);
     return hipGetLastError();
 }
@@ -565,7 +549,7 @@ hipError_t launch_decode_bf16_d128(const DecodeArgs& a, hipStream_t stream) {
 }
 
 hipError_t launch_decode_combine(const DecodeArgs& a, hipStream_t stream) {
-    hipLaunchKernelGGL(decode_combine_kernel, dim3(a.B * a.H), dim3(NT), 0, stream,
+    hipLaunchKernelGGL(decode_combine_kernel, dim3(a.B * a.H), dim3(64), 0, stream,
                        (const float*)a.ws, (__bf16*)a.o, a.splits);
     return hipGetLastError();
 }

@@ -237,7 +237,7 @@ __global__ __launch_bounds__(NT, 1) void prefill_bf16_kernel(
                 if constexpr (PROBE) Tp[kb] = mfma16(kf, xr[s], Tp[kb]);
             }
         }
-        __builtin_amdgcn_iglp_opt(0);
+        __builtin_amdgcn_iglp_opt(1);
     };
     // Value products of 32-key step G of V tile t: lane (col, gq) of dim block db reads dim
     // row 16 db + col, keys 32 G + 8 gq .. +7, stored at chunk (4 G + gq) ^ db.
@@ -253,7 +253,7 @@ __global__ __launch_bounds__(NT, 1) void prefill_bf16_kernel(
             a1[db] = mfma16(vf, p1, a1[db]);
             if constexpr (PROBE) a2[db] = mfma16(vf, p2, a2[db]);
         }
-        __builtin_amdgcn_iglp_opt(0);
+        __builtin_amdgcn_iglp_opt(1);
     };
 
     // Weights and value products of tile t (local index kt) from its products S, Tp.
@@ -334,7 +334,7 @@ __global__ __launch_bounds__(NT, 1) void prefill_bf16_kernel(
         }
     };
 
-    if (w >= 4) __builtin_amdgcn_s_setprio(1);  // the V stagers carry the longer slot
+    if (w >= 4) __builtin_amdgcn_s_setprio(2);  // the V stagers carry the longer slot
     // Stream tile s + 2 is staged while tile s is processed (four buffers), so a barrier is
     // needed only after every second tile: between the step that last reads a buffer (s - 2)
     // and the one that refills it (s) lies a barrier, and so does between that refill and the

@@ -222,7 +222,8 @@ __global__ __launch_bounds__(NT, 1) void prefill_bwd_dq_kernel(
                 Gm[kb] = mfma16(vf, xdo[s], Gm[kb]);
             }
         }
-        __builtin_amdgcn_iglp_opt(1);  // measured: faster here (207 -> 199 us), slower in dk
+        // measured at d = 128: faster here (207 -> 199 us), slower in dk
+        if constexpr (D == 128) __builtin_amdgcn_iglp_opt(1);
         // register i of block kb: key kt * 64 + 32 (kb >> 1) + 8 gq + 4 (kb & 1) + i
         const int lim = qi - kt * KBC - 8 * gq;
 #pragma unroll
@@ -246,7 +247,7 @@ __global__ __launch_bounds__(NT, 1) void prefill_bwd_dq_kernel(
                 aq[db] = mfma16(kf, da, aq[db]);
                 ar[db] = mfma16(kf, dt, ar[db]);
             }
-            __builtin_amdgcn_iglp_opt(1);
+            if constexpr (D == 128) __builtin_amdgcn_iglp_opt(1);
         }
     };
 

@@ -270,11 +270,10 @@ struct Merge {
     float m = -INFINITY, l = 0.f, beta = 0.f, a1 = 0.f, a2 = 0.f;
 };
 
-// Fold records rec_at(0 .. n-1) into st, issuing the loads of a batch of 8 records before using
-// any of them (one memory round trip per batch). An empty record has m = -inf.
-template <class RecAt>
+// Fold records rec_at(0 .. n-1) into st, issuing the loads of a batch of BATCH records before
+// using any of them (one memory round trip per batch). An empty record has m = -inf.
+template <int BATCH, class RecAt>
 __device__ __forceinline__ void fold_records(Merge& st, int n, RecAt rec_at, int lane) {
-    constexpr int BATCH = 8;
     for (int u0 = 0; u0 < n; u0 += BATCH) {
         float ms[BATCH], ls[BATCH], bs[BATCH], x1[BATCH], x2[BATCH];
 #pragma unroll
@@ -307,30 +306,16 @@ __device__ __forceinline__ void fold_records(Merge& st, int n, RecAt rec_at, int
     }
 }
 
-// One workgroup per (b, h): wave w folds the records s = w, w + 4, ..., then the four wave
-// states are merged through LDS.
-__global__ __launch_bounds__(NT) void decode_combine_d64_kernel(const float* __restrict__ ws,
+// One wave per (b, h): lane owns dim lane and folds the S records in batches of 16 (all loads
+// of a batch in flight together; one batch for up to 16 splits).
+__global__ __launch_bounds__(64) void decode_combine_d64_kernel(const float* __restrict__ ws,
                                                                __bf16* __restrict__ o, int S) {
-    __shared__ __attribute__((aligned(16))) float reds[NW][REC];
-    const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+    const int lane = threadIdx.x;
     const size_t bh = blockIdx.x;
     const float* base = ws + bh * (size_t)S * REC;
     Merge st;
-    const int n = w < S ? (S - w + NW - 1) / NW : 0;
-    fold_records(st, n, [&](int u) { return base + (size_t)(w + NW * u) * REC; }, lane);
-    reds[w][lane] = st.a1;
-    reds[w][D + lane] = st.a2;
-    if (lane == 0) {
-        reds[w][2 * D] = st.m;
-        reds[w][2 * D + 1] = st.l;
-        reds[w][2 * D + 2] = st.beta;
-    }
-    __syncthreads();
-    if (w == 0) {
-        Merge all;
-        fold_records(all, NW, [&](int i) { return &reds[i][0]; }, lane);
-        o[bh * D + lane] = (__bf16)combine_out(all.a1, all.a2, all.l, all.beta);
-    }
+    fold_records<16>(st, S, [&](int u) { return base + (size_t)u * REC; }, lane);
+    o[bh * D + lane] = (__bf16)combine_out(st.a1, st.a2, st.l, st.beta);
 }
 
 }  // namespace
@@ -351,7 +336,7 @@ hipError_t launch_decode_bf16_d64(const DecodeArgs& a, hipStream_t stream) {
                            a.splits, c);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess || a.splits == 1) return e;
-    hipLaunchKernelGGL(decode_combine_d64_kernel, dim3(a.B * a.H), dim3(NT), 0, stream,
+    hipLaunchKernelGGL(decode_combine_d64_kernel, dim3(a.B * a.H), dim3(64), 0, stream,
                        (const float*)a.ws, (__bf16*)a.o, a.splits);
     return hipGetLastError();
 }

@@ -49,8 +49,8 @@ struct DecodeArgs {
     int whole;   // wave-range mode: slices end at (b, h) boundaries, no partials
     // Paged cache (split mode only): k, v are pools [num_blocks, H, 2^block_log2, d] and
     // table [B][max_blocks] names each sequence's blocks; L_max = max_blocks 2^block_log2.
-    const int32_t* table;
-    int max_blocks, block_log2, num_blocks;
+    const int32_t* table = nullptr;
+    int max_blocks = 0, block_log2 = 0, num_blocks = 0;
 };
 
 constexpr int kDecodeRecord = 2 * 128 + 4;  // A1[128], A2[128], m, l, beta, pad

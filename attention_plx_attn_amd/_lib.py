@@ -108,6 +108,19 @@ def _stream_handle(stream: Optional[torch.cuda.Stream], device) -> int:
     return ctypes.c_void_p(s.cuda_stream).value or 0
 
 
+def _bind(stream: Optional[torch.cuda.Stream], *tensors) -> None:
+    """Tensors allocated here (outputs, workspaces) are written by kernels on `stream`. The
+    caching allocator tracks a block only on the stream that was current at allocation, so
+    when the kernels run on another stream it must also wait for that one before it reuses
+    the memory (a freed workspace could otherwise be handed out while the kernels still use
+    it)."""
+    if stream is None:
+        return
+    for t in tensors:
+        if t is not None and stream != torch.cuda.current_stream(t.device):
+            t.record_stream(stream)
+
+
 def prefill(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, rho: Optional[torch.Tensor],
             scale: Optional[float] = None, out: Optional[torch.Tensor] = None,
             stream: Optional[torch.cuda.Stream] = None) -> torch.Tensor:
@@ -126,6 +139,7 @@ def prefill(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, rho: Optional[tor
     _check(v, "v", q.dtype, q.device, (B, H, T, dv))
     if out is None:
         out = torch.empty((B, H, T, dv), dtype=q.dtype, device=q.device)
+        _bind(stream, out)
     _check(out, "out", q.dtype, q.device, (B, H, T, dv))
     if scale is None:
         scale = dqk ** -0.5
@@ -154,6 +168,7 @@ def prefill_fwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, rho: Optional
     o = torch.empty_like(q)
     vbar = torch.empty_like(q)
     stats = torch.empty((B, H, T, 2), dtype=torch.float32, device=q.device)
+    _bind(stream, o, vbar, stats)
     if scale is None:
         scale = d ** -0.5
     rc = lib.plx_attn_prefill_fwd(_dtype_code(q), B, H, T, d, d, q.data_ptr(), k.data_ptr(),
@@ -189,9 +204,11 @@ def prefill_bwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, rho: torch.Te
         _check(t, name, q.dtype, q.device, (B, H, T, d))
     _check(stats, "stats", torch.float32, q.device, (B, H, T, 2))
     grads = [torch.empty_like(q) for _ in range(4)]
+    _bind(stream, *grads)
     need = prefill_bwd_workspace_size(B, H, T)
     if workspace is None:
         workspace = torch.empty(need // 4, dtype=torch.float32, device=q.device)
+        _bind(stream, workspace)
     _check(workspace, "workspace", None, q.device)
     if scale is None:
         scale = d ** -0.5
@@ -244,10 +261,12 @@ def decode(q: torch.Tensor, rho: Optional[torch.Tensor], k_cache: torch.Tensor, 
     _check(seqlens, "seqlens", torch.int32, q.device, (B,))
     if out is None:
         out = torch.empty((B, H, dv), dtype=q.dtype, device=q.device)
+        _bind(stream, out)
     _check(out, "out", q.dtype, q.device, (B, H, dv))
     need = decode_workspace_size(B, H, L_max, dv, num_splits)
     if workspace is None and need > 0:
         workspace = torch.empty(need // 4, dtype=torch.float32, device=q.device)
+        _bind(stream, workspace)
     ws_ptr, ws_bytes = 0, 0
     if workspace is not None:
         _check(workspace, "workspace", None, q.device)
@@ -289,6 +308,7 @@ def probe(x: torch.Tensor, w_r: torch.Tensor, H: int, gamma: Optional[torch.Tens
         ptrs.append(0 if t is None else t.data_ptr())
     if out is None:
         out = torch.empty((B, H, T, d), dtype=x.dtype, device=x.device)
+        _bind(stream, out)
     _check(out, "out", x.dtype, x.device, (B, H, T, d))
     rc = lib.plx_attn_probe(_dtype_code(x), B, T, C, H, d, x.data_ptr(), w_r.data_ptr(), *ptrs,
                             float(eps), float(rope_base), out.data_ptr(),
@@ -330,10 +350,12 @@ def decode_gqa(q: torch.Tensor, rho: Optional[torch.Tensor], k_cache: torch.Tens
     _check(seqlens, "seqlens", torch.int32, q.device, (B,))
     if out is None:
         out = torch.empty((B, Hq, dv), dtype=q.dtype, device=q.device)
+        _bind(stream, out)
     _check(out, "out", q.dtype, q.device, (B, Hq, dv))
     _, need = decode_gqa_plan(B, Hq, Hkv, L_max, dv, num_splits)
     if workspace is None and need > 0:
         workspace = torch.empty(need // 4, dtype=torch.float32, device=q.device)
+        _bind(stream, workspace)
     ws_ptr, ws_bytes = 0, 0
     if workspace is not None:
         _check(workspace, "workspace", None, q.device)
@@ -371,10 +393,12 @@ def decode_paged(q: torch.Tensor, rho: Optional[torch.Tensor], k_pool: torch.Ten
     _check(seqlens, "seqlens", torch.int32, q.device, (B,))
     if out is None:
         out = torch.empty((B, H, dv), dtype=q.dtype, device=q.device)
+        _bind(stream, out)
     _check(out, "out", q.dtype, q.device, (B, H, dv))
     _, need = decode_gqa_plan(B, H, H, max_blocks * bs, dv, num_splits)
     if workspace is None and need > 0:
         workspace = torch.empty(need // 4, dtype=torch.float32, device=q.device)
+        _bind(stream, workspace)
     ws_ptr, ws_bytes = 0, 0
     if workspace is not None:
         _check(workspace, "workspace", None, q.device)

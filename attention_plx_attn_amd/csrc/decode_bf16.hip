@@ -112,14 +112,14 @@ __device__ __forceinline__ void store_merged(const Merge& st, __bf16* o_bh, int 
 // PAGED: the cache is a pool of blocks [num_blocks, H, 2^bs_log2, d] and block_table[b][i]
 // names the block of rows i 2^bs_log2 .. of sequence b (blocks of at least 32 rows, so a step
 // never crosses a block). Only blocks holding rows below the chunk end are looked up; an entry
-// outside [0, num_blocks) is read as an empty block.
+// outside [0, num_blocks) is never dereferenced and its rows get no weight (skipped).
 template <bool PROBE, bool PAGED>
 __global__ __launch_bounds__(NT, 2) void decode_split_bf16_d128_kernel(
     const __bf16* __restrict__ q, const __bf16* __restrict__ rho, const __bf16* __restrict__ kc,
     const __bf16* __restrict__ vc, const int32_t* __restrict__ seqlens, __bf16* __restrict__ o,
     float* __restrict__ ws, int H, int L_max, int S, float c, const int32_t* __restrict__ table,
     int max_blocks, int bs_log2, int num_blocks) {
-    __shared__ __attribute__((aligned(16))) float ush[NW][2][KB];  // rounded w and w t per key
+    __shared__ __attribute__((aligned(16))) float ush[NW][2][KB];  // fp32 w and w t per key
     __shared__ __attribute__((aligned(16))) float red[NW][2 * D + 4];
 
     const int s = blockIdx.x, h = blockIdx.y, b = blockIdx.z;
@@ -183,16 +183,25 @@ __global__ __launch_bounds__(NT, 2) void decode_split_bf16_d128_kernel(
     Frag fa, fb;
     int kb0 = j0 + KB * w;
     if constexpr (PAGED) {
-        if (kb0 < j1) load_at(kb0, lookup(kb0), fa);
+        // A step whose table entry lies outside [0, num_blocks) has no rows: its loads read
+        // zeros and its row limit is its own first row, so none of its rows gets a weight.
+        auto limit = [&](int phys, int at) {
+            return (unsigned)phys < (unsigned)num_blocks ? j1 : at;
+        };
+        int pha = lookup(kb0);
+        if (kb0 < j1) load_at(kb0, pha, fa);
         int ph1 = lookup(kb0 + STEP);
         for (; kb0 < j1; kb0 += 2 * STEP) {
             load_at(kb0 + STEP, ph1, fb);
+            const int phb = ph1;
             const int ph2 = lookup(kb0 + 2 * STEP);
-            decode::consume<PROBE>(acc, fa, bqr, kb0, j1, c, ush[w], col, g);
+            decode::consume<PROBE>(acc, fa, bqr, kb0, limit(pha, kb0), c, ush[w], col, g);
             if (kb0 + STEP >= j1) break;
             load_at(kb0 + 2 * STEP, ph2, fa);
+            pha = ph2;
             ph1 = lookup(kb0 + 3 * STEP);
-            decode::consume<PROBE>(acc, fb, bqr, kb0 + STEP, j1, c, ush[w], col, g);
+            decode::consume<PROBE>(acc, fb, bqr, kb0 + STEP, limit(phb, kb0 + STEP), c, ush[w],
+                                   col, g);
         }
     } else {
         if (kb0 < j1) decode::load_step(rk, rv, kb0, col, g, fa);

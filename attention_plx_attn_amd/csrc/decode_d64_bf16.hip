@@ -8,9 +8,9 @@
 //  * scores: each 16-row key tile is one v_mfma_f32_16x16x32_bf16 per 32 dims (two here) with
 //    the keys as rows and the columns [q, rho, 0 ... 0], so column 0 holds q.k and column 1
 //    the probe products t = rho.k;
-//  * online softmax with a wave-uniform running max; the weights w and w*t are rounded to bf16
-//    and l, beta summed from the rounded values [Parallax (paper.rainbus.top summary), method
-//    steps 2-6];
+//  * online softmax with a wave-uniform running max; the weights w and w*t stay fp32 (the
+//    value products run on the VALU) and l, beta are summed from them [Parallax
+//    (paper.rainbus.top summary), method steps 2-6];
 //  * values: a 64-dim row is 8 lanes of 16 bytes, so the 64 lanes take 8 row groups: lane
 //    (col, g) accumulates A1 = sum w v and A2 = sum w t v for dims 8 (col & 7) .. +7 over the
 //    8 rows 8 (2 g + (col >> 3)) .. +7 of each 64-row step.
@@ -117,12 +117,10 @@ __device__ __forceinline__ void consume(Acc& s, const Frag& f, const bf16x8 (&bq
             const float wgt = valid ? exp2_fast(fmaf(score, c, -s.m_run)) : 0.f;
             u[i] = col == 0 ? wgt : (col == 1 ? wgt * own : 0.f);
         }
-        const uint32_t p01 = pack_bf16x2(u[0], u[1]);
-        const uint32_t p23 = pack_bf16x2(u[2], u[3]);
-        s.rsum = add_bf16x2(p23, add_bf16x2(p01, s.rsum));
-        if (col < 2)
-            *(f32x4*)&ush[col][16 * t + 4 * g] =
-                f32x4{bf16_lo(p01), bf16_hi(p01), bf16_lo(p23), bf16_hi(p23)};
+        // The value products run on the VALU in fp32, so w and w t stay fp32 and l, beta
+        // are summed from exactly the weights that multiply the values.
+        s.rsum += (u[0] + u[1]) + (u[2] + u[3]);
+        if (col < 2) *(f32x4*)&ush[col][16 * t + 4 * g] = f32x4{u[0], u[1], u[2], u[3]};
     }
     __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
     __builtin_amdgcn_wave_barrier();

@@ -12,14 +12,14 @@
 // the 16 columns c as the MFMA rows. The k index of a matrix instruction is a sum index, so its
 // order is free: k-slot (g, e) of lane group g stands for key 4 g + e (e < 4) or 16 + 4 g + e - 4
 // (e >= 4) of the 32-key step, which is exactly what the score accumulators of lane (c, g)
-// hold. The weights therefore become the A operand in place (rounded to bf16), with no lane
-// exchange. V is loaded in the same key order (lane (c, g) loads the 8 keys of its k-slots, 8
+// hold. The weights therefore become the A operand in place, as two bf16 terms (hi and the
+// rounding remainder lo, one matrix instruction each), with no lane exchange. V is loaded in the same key order (lane (c, g) loads the 8 keys of its k-slots, 8
 // dims each), transposed in registers and stored in LDS as V^T[dim][slot], so each B operand
 // read is one 16-byte LDS load.
 //
 // Per (b, h_kv, chunk) a workgroup of 4 waves streams its keys in 32-key steps (next step's
-// loads in flight); each column keeps its own running max (lazy update by 2^8) and the sums
-// l = sum w, beta = sum w t from the rounded weights. The 4 wave states merge through LDS; with
+// loads in flight); each column keeps its own running max (lazy update by 2^8) and the fp32
+// sums l = sum w, beta = sum w t. The 4 wave states merge through LDS; with
 // one chunk per (b, h_kv) the kernel writes o, otherwise per-query-head partials (the record
 // of the split decode) that the split decode's combine kernel merges.
 #include "plx_device.hpp"
@@ -152,8 +152,11 @@ __global__ __launch_bounds__(NT, 2) void decode_gqa_bf16_d128_kernel(
         // Weights: even columns w = exp2(s c - m), odd columns w t; 0 past the range and for
         // columns beyond the group. Packed in k-slot order: slots e < 4 are tile 0, e >= 4
         // tile 1.
+        // Each weight u enters the value products as two bf16 terms, hi = bf16(u) and
+        // lo = bf16(u - hi), so the products see u to about 2^-17 relative, and l, beta are
+        // the fp32 sums of u itself.
         const bool live_col = col < 2 * G;
-        uint32_t pk[4];
+        uint32_t pk[4], pl[4];
 #pragma unroll
         for (int t = 0; t < 2; ++t) {
             float u[4];
@@ -166,12 +169,15 @@ __global__ __launch_bounds__(NT, 2) void decode_gqa_bf16_d128_kernel(
                 const float wgt = valid ? exp2_fast(fmaf(score, c, -m_run)) : 0.f;
                 u[i] = (col & 1) ? wgt * own : wgt;
             }
+            rsum += (u[0] + u[1]) + (u[2] + u[3]);
             pk[2 * t] = pack_bf16x2(u[0], u[1]);
             pk[2 * t + 1] = pack_bf16x2(u[2], u[3]);
+            pl[2 * t] = pack_bf16x2(u[0] - bf16_lo(pk[2 * t]), u[1] - bf16_hi(pk[2 * t]));
+            pl[2 * t + 1] =
+                pack_bf16x2(u[2] - bf16_lo(pk[2 * t + 1]), u[3] - bf16_hi(pk[2 * t + 1]));
         }
-#pragma unroll
-        for (int e = 0; e < 4; ++e) rsum = add_bf16x2(pk[e], rsum);
         const bf16x8 pa = __builtin_bit_cast(bf16x8, u32x4{pk[0], pk[1], pk[2], pk[3]});
+        const bf16x8 pb = __builtin_bit_cast(bf16x8, u32x4{pl[0], pl[1], pl[2], pl[3]});
         __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
         __builtin_amdgcn_wave_barrier();
         __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
@@ -181,6 +187,7 @@ __global__ __launch_bounds__(NT, 2) void decode_gqa_bf16_d128_kernel(
         for (int blk = 0; blk < 8; ++blk) {
             const bf16x8 vb = *(const bf16x8*)(vtw + (16 * blk + col) * VTS + 8 * g);
             acc[blk] = mfma16(pa, vb, acc[blk]);
+            acc[blk] = mfma16(pb, vb, acc[blk]);
         }
         __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
         __builtin_amdgcn_wave_barrier();
@@ -199,7 +206,7 @@ __global__ __launch_bounds__(NT, 2) void decode_gqa_bf16_d128_kernel(
         consume(kb0 + STEP, fb);
     }
 
-    // Column totals of the rounded weights (over the 4 row groups).
+    // Column totals of the weights (over the 4 row groups).
     rsum += shfl_xor(rsum, 16);
     rsum += shfl_xor(rsum, 32);
     if (g == 0) {

@@ -8,8 +8,8 @@
 //    query row, so Parallax puts the probe products into accumulator rows that would
 //    otherwise sit idle];
 //  * online softmax with a wave-uniform running max (one rescale when it grows);
-//  * the weights w and w*t are rounded to bf16, summed into l and beta from the rounded
-//    values, and handed through LDS to the value layout, where each lane accumulates
+//  * the weights w and w*t stay fp32 (the value products run on the VALU), are summed into
+//    l and beta, and are handed through LDS to the value layout, where each lane accumulates
 //    A1 = sum w v and A2 = sum w t v for 8 dims over 8 of the step's rows.
 // Loads use raw buffer resources: rows at or beyond the resource's range read as zero
 // without touching memory, which masks sequence ends and empty prefetches.
@@ -40,7 +40,7 @@ struct Frag {
 // Running state of one wave over one piece of a (b, h) key range.
 struct Acc {
     float m_run;  // running max of the log2-domain scores
-    float rsum;   // sum of rounded weights: l in column-0 lanes, beta in column-1 lanes
+    float rsum;   // sum of the weights: l in column-0 lanes, beta in column-1 lanes
     float a1[8], a2[8];
 
     __device__ __forceinline__ void reset() {
@@ -78,7 +78,7 @@ __device__ __forceinline__ void load_qr(__amdgpu_buffer_rsrc_t rq, __amdgpu_buff
 }
 
 // Consume the step whose loads are in f: rows kb0 + ... count while below je.
-// ush: this wave's [2][KB] LDS exchange area (w and w t per row).
+// ush: this wave's [2][KB] LDS exchange area (fp32 w and w t per row).
 // PROBE = false is the softmax-only specialisation (rho = 0 exactly, column 1 of bqr zero):
 // A2 stays 0 and is not accumulated; every other value is computed as with PROBE and rho = 0.
 template <bool PROBE>
@@ -127,12 +127,10 @@ __device__ __forceinline__ void consume(Acc& s, const Frag& f, const bf16x8 (&bq
             const float wgt = valid ? exp2_fast(fmaf(score, c, -s.m_run)) : 0.f;
             u[i] = col == 0 ? wgt : (col == 1 ? wgt * own : 0.f);
         }
-        const uint32_t p01 = pack_bf16x2(u[0], u[1]);
-        const uint32_t p23 = pack_bf16x2(u[2], u[3]);
-        s.rsum = add_bf16x2(p23, add_bf16x2(p01, s.rsum));
-        if (col < 2)
-            *(f32x4*)&ush[col][16 * t + 4 * g] =
-                f32x4{bf16_lo(p01), bf16_hi(p01), bf16_lo(p23), bf16_hi(p23)};
+        // The value products run on the VALU in fp32, so w and w t stay fp32 and l, beta
+        // are summed from exactly the weights that multiply the values.
+        s.rsum += (u[0] + u[1]) + (u[2] + u[3]);
+        if (col < 2) *(f32x4*)&ush[col][16 * t + 4 * g] = f32x4{u[0], u[1], u[2], u[3]};
     }
     __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
     __builtin_amdgcn_wave_barrier();

@@ -169,8 +169,10 @@ plx_status_t plx_attn_decode_gqa(plx_dtype_t dtype, int32_t B, int32_t H_q, int3
  *   block_table    : device int32 [B, max_blocks]; rows i*block_size .. (i+1)*block_size - 1
  *                    of sequence b are block block_table[b][i] of the pool
  *   block_size     : a power of two, at least 32
- * Only the blocks that hold rows below n_b are read; a table entry outside [0, num_blocks) is
- * read as a block of zero rows (its rows are skipped) rather than out of bounds.
+ * Only the blocks that hold rows below n_b are read. A table entry outside [0, num_blocks) is
+ * never dereferenced: the rows it would hold are skipped (they get no softmax weight, as if
+ * they were not part of the sequence), so a sequence with such an entry below n_b attends to
+ * its other rows only.
  * Built combination: (PLX_BF16, d_qk = d_v = 128); rho may be NULL (rho = 0).
  */
 plx_status_t plx_attn_decode_paged(plx_dtype_t dtype, int32_t B, int32_t H, int32_t block_size,

@@ -26,21 +26,23 @@ def _run(x, num_splits=0, seqlens=None, rho=True):
     return o
 
 
+@pytest.mark.parametrize("rho", ["scaled", "proj32"])
 @pytest.mark.parametrize("splits", [0, 1, 3, 16])
 @pytest.mark.parametrize("L", [1, 40, 300, 1000])
-def test_d64_decode_with_poisoned_tail(L, splits):
-    cfg = DecodeConfig("d64", 61, 3, 4, L, 64, "bf16", "scaled", "uniform_half")
+def test_d64_decode_with_poisoned_tail(L, splits, rho):
+    cfg = DecodeConfig("d64", 61, 3, 4, L, 64, "bf16", rho, "uniform_half")
     x = decode_inputs(cfg, seed=L, poison=True)
-    _say("decode d64", L, splits, x["seqlens"].tolist())
+    _say("decode d64", L, splits, rho, x["seqlens"].tolist())
     o = _run(x, splits)
     k = torch.nan_to_num(x["k_cache"].float())  # rows >= seqlens are never read
     v = torch.nan_to_num(x["v_cache"].float())
     ref = oracle.decode(x["q"], x["rho"], k, v, x["seqlens"], x["scale"], form="cov")
-    check_bf16(o, ref, f"d64 L={L} splits={splits}")
+    check_bf16(o, ref, f"d64 L={L} splits={splits} rho={rho}")
 
 
-def test_d64_seqlens_edge_cases():
-    cfg = DecodeConfig("d64", 62, 5, 2, 200, 64, "bf16", "scaled", "full")
+@pytest.mark.parametrize("rho", ["scaled", "proj32"])
+def test_d64_seqlens_edge_cases(rho):
+    cfg = DecodeConfig("d64", 62, 5, 2, 200, 64, "bf16", rho, "full")
     x = decode_inputs(cfg, seed=1)
     sl = torch.tensor([0, -5, 1, 200, 100000], dtype=torch.int32)
     for splits in (1, 4):

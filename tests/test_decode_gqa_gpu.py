@@ -34,17 +34,19 @@ def _oracle(q, rho, kc, vc, sl, scale, G):
     return oracle.decode(q, r, k, v, sl, scale, form="cov")
 
 
+@pytest.mark.parametrize("probe", ["scaled", "proj32"])
 @pytest.mark.parametrize("G", [1, 2, 4, 8])
 @pytest.mark.parametrize("splits", [0, 1, 3])
-@pytest.mark.parametrize("L", [40, 700])
-def test_gqa_matches_oracle(G, splits, L):
+@pytest.mark.parametrize("L", [1, 40, 700])
+def test_gqa_matches_oracle(G, splits, L, probe):
     B, Hkv = 3, 2
-    q, rho, kc, vc, sl, scale = _inputs(B, Hkv * G, G, L, seed=G * 10 + L)
-    print("gqa", G, splits, L, sl.tolist(), flush=True)
+    q, rho, kc, vc, sl, scale = _inputs(B, Hkv * G, G, L, seed=G * 10 + L, rho=probe)
+    print("gqa", G, splits, L, probe, sl.tolist(), flush=True)
     o = plx.decode_gqa(q.to(DEV), rho.to(DEV), kc.to(DEV), vc.to(DEV), sl.to(DEV), scale,
                        num_splits=splits)
     torch.cuda.synchronize()
-    check_bf16(o, _oracle(q, rho, kc, vc, sl, scale, G), f"gqa G={G} splits={splits} L={L}")
+    check_bf16(o, _oracle(q, rho, kc, vc, sl, scale, G),
+               f"gqa G={G} splits={splits} L={L} rho={probe}")
 
 
 @pytest.mark.parametrize("G", [2, 8])

@@ -41,13 +41,14 @@ def _paged(x, bs, seed):
     return kp, vp, table
 
 
+@pytest.mark.parametrize("rho_kind", ["scaled", "proj32"])
 @pytest.mark.parametrize("bs", [32, 64, 256])
 @pytest.mark.parametrize("splits", [0, 1, 3])
-def test_paged_equals_contiguous_and_oracle(bs, splits):
-    cfg = DecodeConfig("d", 42, 4, 3, 1024, 128, "bf16", "scaled", "uniform_half")
+def test_paged_equals_contiguous_and_oracle(bs, splits, rho_kind):
+    cfg = DecodeConfig("d", 42, 4, 3, 1024, 128, "bf16", rho_kind, "uniform_half")
     x = decode_inputs(cfg, seed=bs + splits, poison=True)
     kp, vp, table = _paged(x, bs, seed=bs)
-    print("paged", bs, splits, x["seqlens"].tolist(), flush=True)
+    print("paged", bs, splits, rho_kind, x["seqlens"].tolist(), flush=True)
     q, rho, sl = (x[k].to(DEV) for k in ("q", "rho", "seqlens"))
     o = plx.decode_paged(q, rho, kp.to(DEV), vp.to(DEV), table.to(DEV), sl, x["scale"],
                          num_splits=splits)
@@ -59,7 +60,7 @@ def test_paged_equals_contiguous_and_oracle(bs, splits):
     k = torch.nan_to_num(x["k_cache"].float())
     v = torch.nan_to_num(x["v_cache"].float())
     ref = oracle.decode(x["q"], x["rho"], k, v, x["seqlens"], x["scale"], form="cov")
-    check_bf16(o, ref, f"paged bs={bs} splits={splits}")
+    check_bf16(o, ref, f"paged bs={bs} splits={splits} rho={rho_kind}")
 
 
 def test_paged_seqlens_edges_and_softmax_only():
@@ -78,3 +79,27 @@ def test_paged_seqlens_edges_and_softmax_only():
     assert torch.equal(o[2], x["v_cache"][2, :, 0])
     ref = oracle.decode(x["q"], x["rho"], x["k_cache"], x["v_cache"], sl, x["scale"])
     check_bf16(o[3:], ref[3:], "paged edges")
+
+
+@pytest.mark.parametrize("splits", [1, 3])
+def test_paged_invalid_entry_below_seqlens_is_skipped(splits):
+    """A table entry outside [0, num_blocks) inside a sequence's valid range: those rows get
+    no weight, so the output equals the oracle over the sequence without them."""
+    bs = 64
+    cfg = DecodeConfig("d", 44, 3, 2, 512, 128, "bf16", "proj32", "full")
+    x = decode_inputs(cfg, seed=6)
+    kp, vp, table = _paged(x, bs, seed=7)
+    bad = {0: (1, -1), 1: (3, 1 << 30), 2: (0, kp.shape[0])}  # b: (block index, entry)
+    keep = []
+    for b, (i, entry) in bad.items():
+        table[b, i] = entry
+        rows = np.r_[0:i * bs, (i + 1) * bs:512]
+        keep.append(rows)
+    d = [t.to(DEV) for t in (x["q"], x["rho"], kp, vp, table, x["seqlens"])]
+    o = plx.decode_paged(*d, x["scale"], num_splits=splits).cpu()
+    for b, rows in enumerate(keep):
+        k = x["k_cache"][b: b + 1, :, rows]
+        v = x["v_cache"][b: b + 1, :, rows]
+        ref = oracle.decode(x["q"][b: b + 1], x["rho"][b: b + 1], k, v,
+                            np.array([len(rows)], np.int32), x["scale"])
+        check_bf16(o[b: b + 1], ref, f"paged invalid entry b={b} splits={splits}")

@@ -117,3 +117,29 @@ def test_graph_replays_merge_every_time(d):
             _call(g, x, S, ws)
             torch.cuda.synchronize()
     check_bf16(eager[0], _oracle(xs[0]), f"graph d={d}")
+
+
+def test_side_stream_with_internal_workspace():
+    """Calls on a side stream whose output and workspace the binding allocates, while the
+    current stream allocates and overwrites memory of the same sizes right after each call:
+    every result has the bits of a call on the current stream, and matches the oracle."""
+    B, H, L, splits = 1, 16, 8192, 16
+    x = decode_inputs(DecodeConfig("m", 53, B, H, L, 128, "bf16", "proj32", "full"), seed=0)
+    g = _dev(x)
+    want = _call(g, x, splits, None)
+    torch.cuda.synchronize()
+    side = torch.cuda.Stream(device=DEV)
+    side.wait_stream(torch.cuda.current_stream())
+    n_ws = plx.decode_workspace_size(B, H, L, 128, splits) // 4
+    outs = []
+    for _ in range(8):
+        outs.append(plx.decode(g["q"], g["rho"], g["k_cache"], g["v_cache"], g["seqlens"],
+                               x["scale"], num_splits=splits, stream=side))
+        junk = torch.full((n_ws,), float("nan"), device=DEV)
+        junk_o = torch.full((B, H, 128), 7.0, dtype=torch.bfloat16, device=DEV)
+        del junk, junk_o
+    side.synchronize()
+    torch.cuda.synchronize()
+    for o in outs:
+        assert torch.equal(o, want)
+    _say("side stream", check_bf16(outs[0], _oracle(x), "side stream"))

@@ -18,6 +18,7 @@ LIB_PATH = os.path.join(_PKG, "libplx_attn.so")
 HEADER_PATH = os.path.join(os.path.dirname(_PKG), "include", "plx_attn.h")
 
 PLX_F32, PLX_BF16 = 0, 1
+PLX_PREFILL_SPLIT_WEIGHTS = 1
 _STATUS = {0: "PLX_OK", 1: "PLX_ERR_NULL_POINTER", 2: "PLX_ERR_INVALID_SHAPE",
            3: "PLX_ERR_INVALID_ARG", 4: "PLX_ERR_UNSUPPORTED", 5: "PLX_ERR_MISALIGNED",
            6: "PLX_ERR_WORKSPACE_TOO_SMALL", 7: "PLX_ERR_HIP"}
@@ -44,6 +45,9 @@ def load() -> ctypes.CDLL:
     i32, vp, f32 = ctypes.c_int32, ctypes.c_void_p, ctypes.c_float
     lib.plx_attn_prefill.argtypes = [ctypes.c_int] + [i32] * 5 + [vp] * 5 + [f32, vp]
     lib.plx_attn_prefill.restype = ctypes.c_int
+    lib.plx_attn_prefill_ex.argtypes = ([ctypes.c_int] + [i32] * 5 + [vp] * 5 +
+                                        [f32, ctypes.c_uint32, vp])
+    lib.plx_attn_prefill_ex.restype = ctypes.c_int
     lib.plx_attn_decode_num_splits.argtypes = [i32] * 4 + [ctypes.POINTER(i32)]
     lib.plx_attn_decode_num_splits.restype = ctypes.c_int
     lib.plx_attn_decode_workspace_size.argtypes = [i32] * 5 + [ctypes.POINTER(ctypes.c_size_t)]
@@ -123,10 +127,13 @@ def _bind(stream: Optional[torch.cuda.Stream], *tensors) -> None:
 
 def prefill(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, rho: Optional[torch.Tensor],
             scale: Optional[float] = None, out: Optional[torch.Tensor] = None,
-            stream: Optional[torch.cuda.Stream] = None) -> torch.Tensor:
+            stream: Optional[torch.cuda.Stream] = None,
+            split_weights: bool = False) -> torch.Tensor:
     """Causal Parallax prefill. q, k, rho [B,H,T,d_qk]; v [B,H,T,d_v] -> o [B,H,T,d_v].
 
-    rho=None means rho = 0 exactly (plain softmax attention, the specialised kernel)."""
+    rho=None means rho = 0 exactly (plain softmax attention, the specialised kernel).
+    split_weights=True passes the weights to the value products as hi + lo bf16 terms
+    (plx_attn_prefill_ex with PLX_PREFILL_SPLIT_WEIGHTS)."""
     lib = load()
     if q.dim() != 4:
         raise ValueError("q must be [B, H, T, d_qk]")
@@ -143,12 +150,15 @@ def prefill(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, rho: Optional[tor
     _check(out, "out", q.dtype, q.device, (B, H, T, dv))
     if scale is None:
         scale = dqk ** -0.5
-    rc = lib.plx_attn_prefill(_dtype_code(q), B, H, T, dqk, dv, q.data_ptr(), k.data_ptr(),
-                              v.data_ptr(), 0 if rho is None else rho.data_ptr(),
-                              out.data_ptr(), float(scale),
-                              _stream_handle(stream, q.device))
+    args = (_dtype_code(q), B, H, T, dqk, dv, q.data_ptr(), k.data_ptr(), v.data_ptr(),
+            0 if rho is None else rho.data_ptr(), out.data_ptr(), float(scale))
+    if split_weights:
+        rc = lib.plx_attn_prefill_ex(*args, PLX_PREFILL_SPLIT_WEIGHTS,
+                                     _stream_handle(stream, q.device))
+    else:
+        rc = lib.plx_attn_prefill(*args, _stream_handle(stream, q.device))
     if rc != 0:
-        raise PlxError(rc, "plx_attn_prefill")
+        raise PlxError(rc, "plx_attn_prefill_ex" if split_weights else "plx_attn_prefill")
     return out
 
 

@@ -157,7 +157,16 @@ plx_status_t plx_attn_prefill(plx_dtype_t dtype, int32_t B, int32_t H, int32_t T
                               int32_t d_qk, int32_t d_v, const void* q, const void* k,
                               const void* v, const void* rho, void* o, float softmax_scale,
                               void* stream) {
+    return plx_attn_prefill_ex(dtype, B, H, T, d_qk, d_v, q, k, v, rho, o, softmax_scale, 0u,
+                               stream);
+}
+
+plx_status_t plx_attn_prefill_ex(plx_dtype_t dtype, int32_t B, int32_t H, int32_t T,
+                                 int32_t d_qk, int32_t d_v, const void* q, const void* k,
+                                 const void* v, const void* rho, void* o, float softmax_scale,
+                                 uint32_t flags, void* stream) {
     if (dtype != PLX_F32 && dtype != PLX_BF16) return PLX_ERR_INVALID_ARG;
+    if (flags & ~(uint32_t)PLX_PREFILL_SPLIT_WEIGHTS) return PLX_ERR_INVALID_ARG;
     if (!q || !k || !v || !o) return PLX_ERR_NULL_POINTER;  // rho == NULL: softmax only
     if (B < 1 || H < 1 || T < 1 || d_qk < 1 || d_v < 1) return PLX_ERR_INVALID_SHAPE;
     if (!std::isfinite(softmax_scale) || softmax_scale < 0.f) return PLX_ERR_INVALID_ARG;
@@ -179,6 +188,7 @@ plx_status_t plx_attn_prefill(plx_dtype_t dtype, int32_t B, int32_t H, int32_t T
         if (s != PLX_OK) return s;
     }
     plx::PrefillArgs a{B, H, T, d_qk, q, k, v, rho, o, softmax_scale, cus};
+    a.split = (flags & PLX_PREFILL_SPLIT_WEIGHTS) != 0;  // no rounding to split on fp32
     const hipStream_t st = static_cast<hipStream_t>(stream);
     const hipError_t e = dtype == PLX_BF16 ? plx::launch_prefill_bf16(a, st)
                                            : plx::launch_prefill_f32(a, st);

@@ -17,6 +17,7 @@ struct PrefillArgs {
     int workers;  // resident workgroups of a persistent launch (the device's compute units)
     void* vbar = nullptr;    // O1 / l per row [B, H, T, d] (bf16), or nullptr
     float* stats = nullptr;  // with vbar: (lse, tbar) per row [B, H, T, 2]
+    bool split = false;      // weights as hi + lo bf16 terms (bf16 path, without stats)
 };
 
 // Backward of the causal prefill (bf16, d = 64 or 128). All tensors [B, H, T, d] except

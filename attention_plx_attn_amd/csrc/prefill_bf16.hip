@@ -3,8 +3,9 @@
 // Method [Parallax (paper.rainbus.top summary), "方法步骤详情": per KV block compute the
 // scores S1 = Q K^T and the probe products S2 = R K^T, then P1 = exp(S1 - m) and
 // P2 = P1 * S2, and accumulate O1 += P1 V and O2 += P2 V in parallel; agihunt review,
-// hardware paragraph: both branches share one KV stream, one running max and one rescale
-// factor]. Final combine o = (1 + tbar) O1 - O2 with tbar = sum P2 / sum P1 (step 6).
+// hardware paragraph: the softmax and correction branches read the keys and values once
+// between them and are rescaled together from a single row maximum]. Final combine
+// o = (1 + tbar) O1 - O2 with tbar = sum P2 / sum P1 (step 6).
 //
 // Work decomposition: a work item is 128 query rows of one (b, h); a workgroup has 8 waves
 // (two per SIMD) of 16 query rows each, and every wave runs both branches for its rows on
@@ -21,7 +22,8 @@
 //     plus a constant;
 //   * P1 and P2 are rounded to bf16 and l = sum P1, beta = sum P2 are taken from the rounded
 //     values, so the effective corrected weights sum to exactly one; P2 = P1 * T is formed
-//     from the unrounded P1;
+//     from the unrounded P1 (or, in the SPLIT instances, both go in as hi + lo bf16 terms
+//     and l, beta are fp32 sums of the unrounded weights);
 //   * the running max is updated lazily (only when a row's tile max exceeds it by more than
 //     2^8); the result is the same exact expression, with far fewer rescales.
 // A tile holds BC = 64 keys at d = 128 and BC = 128 keys at d = 64 (the same bytes).
@@ -122,11 +124,18 @@ __device__ __forceinline__ float max_across_row_groups(float x) {
 // extra fp32 sums of the unrounded weights and weight * probe products, so that they agree
 // with the weights and probe products the backward recomputes (with a large probe, |t| ~ 10,
 // the bf16-rounded beta / l would differ from them by ~2^-9 |t|).
-template <int D, bool PROBE, bool STATS>
+//
+// SPLIT = true passes each weight u (P1 and P2) to the value products as two bf16 terms,
+// hi = bf16(u) and lo = bf16(u - hi), one matrix instruction each, and sums l and beta from
+// the fp32 weights: the products then see the weights to about 2^-17 relative instead of
+// 2^-9. The output's sensitivity to the weights grows with |t - tbar| (the correction's
+// size), so a unit-RMS probe (|t| ~ 10) needs this to stay within 1e-2 of the exact result.
+template <int D, bool PROBE, bool STATS, bool SPLIT>
 __global__ __launch_bounds__(NT, 1) void prefill_bf16_kernel(
     const __bf16* __restrict__ q, const __bf16* __restrict__ k, const __bf16* __restrict__ v,
     const __bf16* __restrict__ rho, __bf16* __restrict__ o, __bf16* __restrict__ vbar,
     float* __restrict__ stats, int BH, int T, int nqb, float c, int ncls) {
+    static_assert(!(STATS && SPLIT), "the statistics instances keep single bf16 weights");
     using G_ = Geo<D>;
     constexpr int KS = G_::KS, K_ELEMS = G_::K_ELEMS, V_ELEMS = G_::V_ELEMS, OFF_V = G_::OFF_V;
     constexpr int BC = G_::BC, NKB = G_::NKB, NG = G_::NG, VS = G_::VS;
@@ -244,7 +253,8 @@ __global__ __launch_bounds__(NT, 1) void prefill_bf16_kernel(
     int vlane[4];
 #pragma unroll
     for (int x = 0; x < 4; ++x) vlane[x] = col * VS * 2 + 16 * (gq ^ x);
-    auto values = [&](int t, int G, bf16x8 p1, bf16x8 p2) {
+    // SPLIT: q1, q2 are the lo terms of p1, p2 (same V operand, two more products).
+    auto values = [&](int t, int G, bf16x8 p1, bf16x8 p2, bf16x8 q1, bf16x8 q2) {
         const unsigned char* Vl = vbuf(t);
 #pragma unroll
         for (int db = 0; db < NDB; ++db) {
@@ -252,6 +262,10 @@ __global__ __launch_bounds__(NT, 1) void prefill_bf16_kernel(
                                                64 * (G ^ (db >> 2)));
             a1[db] = mfma16(vf, p1, a1[db]);
             if constexpr (PROBE) a2[db] = mfma16(vf, p2, a2[db]);
+            if constexpr (SPLIT) {
+                a1[db] = mfma16(vf, q1, a1[db]);
+                if constexpr (PROBE) a2[db] = mfma16(vf, q2, a2[db]);
+            }
         }
         __builtin_amdgcn_iglp_opt(1);
     };
@@ -306,7 +320,7 @@ __global__ __launch_bounds__(NT, 1) void prefill_bf16_kernel(
         }
 #pragma unroll
         for (int G = 0; G < NG; ++G) {
-            uint32_t p1[4], p2[4];
+            uint32_t p1[4], p2[4], q1[4] = {}, q2[4] = {};
 #pragma unroll
             for (int e = 0; e < 4; ++e) {
                 const int kb = 2 * G + (e >> 1), i0 = 2 * (e & 1);
@@ -317,20 +331,33 @@ __global__ __launch_bounds__(NT, 1) void prefill_bf16_kernel(
                     w1 = S[kb][i0 + 1] == -INFINITY ? 0.f : w1;
                 }
                 p1[e] = pack_bf16x2(w0, w1);
-                lsum = add_bf16x2(p1[e], lsum);
+                if constexpr (SPLIT) {
+                    q1[e] = pack_bf16x2(w0 - bf16_lo(p1[e]), w1 - bf16_hi(p1[e]));
+                    lsum += w0 + w1;
+                } else {
+                    lsum = add_bf16x2(p1[e], lsum);
+                }
                 if constexpr (STATS) {
                     lsx += w0 + w1;
                     if constexpr (PROBE) bsx = fmaf(w1, Tp[kb][i0 + 1], fmaf(w0, Tp[kb][i0], bsx));
                 }
                 if constexpr (PROBE) {
-                    p2[e] = pack_bf16x2(w0 * Tp[kb][i0], w1 * Tp[kb][i0 + 1]);
-                    bsum = add_bf16x2(p2[e], bsum);
+                    const float u0 = w0 * Tp[kb][i0], u1 = w1 * Tp[kb][i0 + 1];
+                    p2[e] = pack_bf16x2(u0, u1);
+                    if constexpr (SPLIT) {
+                        q2[e] = pack_bf16x2(u0 - bf16_lo(p2[e]), u1 - bf16_hi(p2[e]));
+                        bsum += u0 + u1;
+                    } else {
+                        bsum = add_bf16x2(p2[e], bsum);
+                    }
                 } else {
                     p2[e] = 0u;
                 }
             }
             values(t, G, __builtin_bit_cast(bf16x8, u32x4{p1[0], p1[1], p1[2], p1[3]}),
-                   __builtin_bit_cast(bf16x8, u32x4{p2[0], p2[1], p2[2], p2[3]}));
+                   __builtin_bit_cast(bf16x8, u32x4{p2[0], p2[1], p2[2], p2[3]}),
+                   __builtin_bit_cast(bf16x8, u32x4{q1[0], q1[1], q1[2], q1[3]}),
+                   __builtin_bit_cast(bf16x8, u32x4{q2[0], q2[1], q2[2], q2[3]}));
         }
     };
 
@@ -500,22 +527,24 @@ hipError_t launch_prefill_bf16(const PrefillArgs& a, hipStream_t stream) {
                            (const __bf16*)a.k, (const __bf16*)a.v, rp, (__bf16*)a.o,
                            (__bf16*)a.vbar, a.stats, BH, a.T, nqb, a.scale * kLog2e, ncls);
     };
+    if (a.stats && a.split) return hipErrorInvalidValue;
+    auto pick = [&](auto d_tag) {
+        constexpr int D = decltype(d_tag)::value;
+        if (a.stats) {
+            if (a.rho) go(prefill_bf16_kernel<D, true, true, false>);
+            else go(prefill_bf16_kernel<D, false, true, false>);
+        } else if (a.split) {
+            if (a.rho) go(prefill_bf16_kernel<D, true, false, true>);
+            else go(prefill_bf16_kernel<D, false, false, true>);
+        } else {
+            if (a.rho) go(prefill_bf16_kernel<D, true, false, false>);
+            else go(prefill_bf16_kernel<D, false, false, false>);
+        }
+    };
     if (a.d == 64) {
-        if (a.stats) {
-            if (a.rho) go(prefill_bf16_kernel<64, true, true>);
-            else go(prefill_bf16_kernel<64, false, true>);
-        } else {
-            if (a.rho) go(prefill_bf16_kernel<64, true, false>);
-            else go(prefill_bf16_kernel<64, false, false>);
-        }
+        pick(std::integral_constant<int, 64>{});
     } else if (a.d == 128) {
-        if (a.stats) {
-            if (a.rho) go(prefill_bf16_kernel<128, true, true>);
-            else go(prefill_bf16_kernel<128, false, true>);
-        } else {
-            if (a.rho) go(prefill_bf16_kernel<128, true, false>);
-            else go(prefill_bf16_kernel<128, false, false>);
-        }
+        pick(std::integral_constant<int, 128>{});
     } else {
         return hipErrorInvalidValue;
     }

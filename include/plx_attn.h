@@ -34,10 +34,13 @@
  *   - Arguments are validated on the host first; an invalid call returns its status code
  *     without enqueuing anything. A launch failure returns PLX_ERR_HIP. No exception
  *     crosses the ABI and the library never aborts.
- *   - Arithmetic: bf16 inputs are multiplied on the matrix cores with fp32 accumulation;
- *     the softmax weights and the weight*probe products are rounded to bf16 (RNE) before
- *     the value products, and the row sums are taken from the same rounded values. Output
- *     is rounded to the input dtype (RNE). fp32 inputs use fp32 throughout.
+ *   - Arithmetic: bf16 inputs are multiplied on the matrix cores with fp32 accumulation.
+ *     Prefill rounds the softmax weights and the weight*probe products to bf16 (RNE) before
+ *     the value products and takes the row sums from the same rounded values, unless
+ *     plx_attn_prefill_ex is asked to split them (hi + lo bf16 terms, fp32 row sums). The
+ *     decode paths keep the weights in fp32 (vector-ALU value products) or split them (the
+ *     grouped-head decode's matrix-core value products). Output is rounded to the input
+ *     dtype (RNE). fp32 inputs use fp32 throughout.
  *   - softmax_scale multiplies q.k only (t is unscaled); it must be finite and >= 0
  *     (0 gives uniform weights).
  */
@@ -83,6 +86,29 @@ plx_status_t plx_attn_prefill(plx_dtype_t dtype, int32_t B, int32_t H, int32_t T
                               int32_t d_qk, int32_t d_v, const void* q, const void* k,
                               const void* v, const void* rho, void* o, float softmax_scale,
                               void* stream);
+
+/* Flags of plx_attn_prefill_ex. */
+#define PLX_PREFILL_SPLIT_WEIGHTS 1u
+
+/*
+ * plx_attn_prefill with a flags word (plx_attn_prefill is this call with flags = 0). Same
+ * arguments, layouts, ownership and errors; flags other than those defined here give
+ * PLX_ERR_INVALID_ARG.
+ *
+ * PLX_PREFILL_SPLIT_WEIGHTS (bf16 path): each softmax weight w and each weight*probe product
+ * w*t enters the value products as two bf16 terms, hi = bf16(u) and lo = bf16(u - hi), and
+ * the row sums l, beta are fp32 sums of the unrounded values. The corrected output
+ * o = sum_j p_j (1 - (t_j - tbar)) v_j [paper.rainbus.top summary, method steps 2-6] moves
+ * by about sum_j p_j |1 + tbar - t_j| |v_j - vbar| times the relative error of the weights,
+ * which bf16 weights (2^-9) keep under 1e-2 only while |t| stays small (probe RMS ~0.1 at
+ * d = 128); a unit-RMS probe (|t| ~ 10, a probe normalised as the method prescribes
+ * [agihunt review, method paragraph]) needs the split, whose weights reach ~2^-17. It costs
+ * two more matrix products per value operand. No effect on the fp32 path (fp32 weights).
+ */
+plx_status_t plx_attn_prefill_ex(plx_dtype_t dtype, int32_t B, int32_t H, int32_t T,
+                                 int32_t d_qk, int32_t d_v, const void* q, const void* k,
+                                 const void* v, const void* rho, void* o, float softmax_scale,
+                                 uint32_t flags, void* stream);
 
 /*
  * The plan a decode call with these arguments will use at d = 128, written to *splits_out in

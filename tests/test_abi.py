@@ -18,7 +18,8 @@ def lib():
 
 def test_exports_every_declared_symbol(lib):
     declared = plx.header_functions()
-    assert set(declared) == {"plx_attn_prefill", "plx_attn_decode", "plx_attn_decode_num_splits",
+    assert set(declared) == {"plx_attn_prefill", "plx_attn_prefill_ex", "plx_attn_decode",
+                             "plx_attn_decode_num_splits",
                              "plx_attn_decode_workspace_size", "plx_attn_probe",
                              "plx_attn_decode_gqa", "plx_attn_decode_gqa_plan",
                              "plx_attn_decode_paged", "plx_attn_prefill_fwd",
@@ -62,6 +63,23 @@ def test_prefill_validation(lib):
     assert _prefill(lib, dtype=0, dqk=48, dv=48) == 4
     assert _prefill(lib, ptrs=(A + 8, A, A, A, A)) == 5
     assert _prefill(lib, dtype=0, dqk=16, dv=16, ptrs=(A, A, A, A + 4, A)) == 5
+
+
+def _prefill_ex(lib, flags, dtype=1, T=8, ptrs=(A,) * 5):
+    return lib.plx_attn_prefill_ex(dtype, 1, 1, T, 128, 128, *ptrs, ctypes.c_float(0.1), flags,
+                                   None)
+
+
+def test_prefill_ex_validation(lib):
+    # the flags word: unknown bits are rejected before anything else is looked at
+    assert _prefill_ex(lib, 2) == 3
+    assert _prefill_ex(lib, 0x80000000) == 3
+    assert _prefill_ex(lib, 1 | 4) == 3
+    # the same checks as plx_attn_prefill with a valid flags word
+    assert _prefill_ex(lib, 1, ptrs=(0, A, A, A, A)) == 1
+    assert _prefill_ex(lib, 1, T=0) == 2
+    assert _prefill_ex(lib, 1, dtype=7) == 3
+    assert _prefill_ex(lib, 1, ptrs=(A + 8, A, A, A, A)) == 5
 
 
 def _decode(lib, dtype=1, B=2, H=2, L=64, dqk=128, dv=128, q=A, rho=A, kc=A, vc=A, sl=A, o=A,

@@ -19,9 +19,10 @@ def _say(*a):
     print(*a, flush=True)
 
 
-def _run(x, rho=True):
+def _run(x, rho=True, split=False):
     d = {k: x[k].to(DEV) for k in ("q", "k", "v", "rho")}
-    o = plx.prefill(d["q"], d["k"], d["v"], d["rho"] if rho else None, x["scale"])
+    o = plx.prefill(d["q"], d["k"], d["v"], d["rho"] if rho else None, x["scale"],
+                    split_weights=split)
     torch.cuda.synchronize()
     return o
 
@@ -37,17 +38,31 @@ def test_d64_parity(B, H, T):
     _say(check_bf16(o, ref, f"d64 B={B} H={H} T={T}"))
 
 
+@pytest.mark.parametrize("B,H,T", [(1, 2, 1), (2, 3, 31), (1, 4, 333), (2, 2, 1024)])
+def test_d64_split_parity(B, H, T):
+    cfg = PrefillConfig("d64", 51, B, H, T, 64, "bf16", "scaled")
+    x = prefill_inputs(cfg, seed=T)
+    o = _run(x, split=True)
+    ref = oracle.prefill(x["q"], x["k"], x["v"], x["rho"], x["scale"], form="cov")
+    _say(check_bf16(o, ref, f"d64 split B={B} H={H} T={T}"))
+
+
+@pytest.mark.parametrize("qs", [1, 3])
 @pytest.mark.parametrize("T", [31, 300])
-def test_d64_strong_probe_within_derived_rounding_bound(T):
-    # Unit-RMS probe (|t| ~ 8 at d = 64, ten times the workload probes): the bf16 rounding of
-    # w*t dominates, as at d = 128; rel-L2 at the bf16 bar, every element within half an
-    # output ulp + 1e-3 + the first-order weight-rounding bound.
+def test_d64_strong_probe(T, qs):
+    # Unit-RMS probe (|t| ~ 8 at d = 64, ten times the workload probes): split weights meet the
+    # plain bf16 bar; single bf16 weights keep rel-L2 at the bar and every element within half
+    # an output ulp + 1e-3 + the first-order weight-rounding bound.
     cfg = PrefillConfig("d64", 55, 2, 3, T, 64, "bf16", "proj32")
     x = prefill_inputs(cfg, seed=T)
-    o = _run(x)
+    x["q"] = (x["q"].float() * qs).to(torch.bfloat16)
     ref = oracle.prefill(x["q"], x["k"], x["v"], x["rho"], x["scale"], form="cov")
+    ms = check_bf16(_run(x, split=True), ref, f"d64 strong probe split T={T} q*{qs}")
+    o = _run(x)
     m = metrics(o, ref)
-    _say("d64 strong probe", T, m)
+    _say(f"STRESS d=64 T={T} rms=1(proj32) q*{qs}: default excess "
+         f"{m['excess_over_half_ulp']:.4f} rel {m['rel_l2']:.2e} | split excess "
+         f"{ms['excess_over_half_ulp']:.4f} rel {ms['rel_l2']:.2e}")
     assert m["finite"] and m["rel_l2"] <= 5e-3, m
     bound = weight_rounding_bound(x["q"], x["k"], x["v"], x["rho"], x["scale"])
     err = np.abs(to_f64(o) - ref)

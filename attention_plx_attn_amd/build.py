@@ -27,6 +27,25 @@ def sources():
     return sorted(glob.glob(os.path.join(CSRC, "*.hip")))
 
 
+BENCH_CSRC = os.path.join(PKG, "bench_csrc")
+BENCH_LIB = os.path.join(PKG, "libplx_bench.so")
+
+
+def build_bench(verbose: bool = False) -> str:
+    """The benchmark's own measuring kernels (not part of the attention library)."""
+    hipcc = os.environ.get("HIPCC", "hipcc")
+    tmp = BENCH_LIB + ".tmp"
+    cmd = [hipcc, *HIPCC_FLAGS, *sorted(glob.glob(os.path.join(BENCH_CSRC, "*.hip"))),
+           "-o", tmp]
+    if verbose:
+        print(" ".join(cmd), flush=True)
+    r = subprocess.run(cmd, capture_output=True, text=True)
+    if r.returncode != 0:
+        raise RuntimeError(f"hipcc failed ({r.returncode}):\n{r.stderr}")
+    os.replace(tmp, BENCH_LIB)
+    return BENCH_LIB
+
+
 def build(verbose: bool = False, extra_flags=()) -> str:
     hipcc = os.environ.get("HIPCC", "hipcc")
     tmp = LIB + ".tmp"
@@ -47,3 +66,4 @@ def build(verbose: bool = False, extra_flags=()) -> str:
 
 if __name__ == "__main__":
     print(build(verbose=True))
+    print(build_bench(verbose=True))

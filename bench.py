@@ -14,6 +14,11 @@ last-level cache.
 Prints ONE JSON line. `value` is the prefill's algorithmic throughput in TFLOP/s
 (8*d FLOPs per visible causal (query, key) pair: Q K^T, R K^T, P V and (P*T) V);
 the decode figures (tokens/s, algorithmic HBM GB/s) ride along in the same line.
+After the timed steps the line also carries, each with its own algorithmic work and roofline
+fraction: the same prefill with split weights (`prefill_split_weights`), the long prefill
+B1 H32 T32768 (`prefill_long`) and every decode grid cell that moves at least 100 MB
+(`decode_grid`, cold caches, each beside the time a plain streaming-read kernel takes for
+the same bytes in the same run).
 `roofline` describes the dominant kernel (the prefill), timed with HIP events on the
 stream it runs on; `traffic` comes from committed rocprofv3 counter summaries and is
 null when the kernel source changed since they were taken. `cpu_baseline` times the
@@ -240,6 +245,16 @@ def cpu_baseline(px, dx):
     oracle.decode(dx["q"], dx["rho"], dx["k_cache"], dx["v_cache"], dx["seqlens"], dx["scale"],
                   form="stream", block=64)
     t_dec = time.perf_counter() - t0
+    # The long prefill (B1 H32 T32768) takes minutes on the host: one of its heads with a
+    # probe (head 16) is timed instead, and its rate stands for the whole workload.
+    from plx_synth import CONFIGS, prefill_head_inputs
+
+    lcfg = CONFIGS["prefill_long"]
+    hx = prefill_head_inputs(lcfg, 0, lcfg.H // 2, seed=0)
+    t0 = time.perf_counter()
+    oracle.prefill(hx["q"], hx["k"], hx["v"], hx["rho"], hx["scale"], form="stream", block=64)
+    t_long = time.perf_counter() - t0
+    long_head_flops = prefill_flops(1, 1, lcfg.T, lcfg.d)
     return {
         "value": prefill_flops(B, H, T, d) / t_pre / 1e12,
         "unit": "TFLOP/s",
@@ -247,8 +262,13 @@ def cpu_baseline(px, dx):
         "kind": "oracle",
         "sample": (f"the full prefill workload B{B} H{H} T{T} d{d} in the oracle's fp64 "
                    f"streaming form ({t_pre:.2f} s); decode B1 H16 L32768 in the same form "
-                   f"({t_dec:.2f} s)"),
+                   f"({t_dec:.2f} s); one head (h = {lcfg.H // 2}, with probe) of the long "
+                   f"prefill B1 H{lcfg.H} T{lcfg.T} in the same form ({t_long:.2f} s)"),
         "decode_tokens_per_s": dx["q"].shape[0] / t_dec,
+        "prefill_long_head_subset": {
+            "heads": 1, "seconds": round(t_long, 3),
+            "tflops": round(long_head_flops / t_long / 1e12, 4),
+            "whole_workload_seconds_extrapolated": round(t_long * lcfg.B * lcfg.H, 1)},
         "cpu_model": _cpu_model(),
     }
 
@@ -288,6 +308,169 @@ def streaming_read_gbps(torch, dev, stream) -> float:
 
 def x_bytes_gbps(nbytes: int, ms: float) -> float:
     return nbytes / (ms * 1e-3) / 1e9
+
+
+# ------------------------------------------------------------------------------ sub-records
+
+def _bench_lib():
+    """The benchmark's own streaming-read kernel (attention_plx_attn_amd/bench_csrc)."""
+    import ctypes
+
+    path = os.path.join(ROOT, "attention_plx_attn_amd", "libplx_bench.so")
+    if not os.path.exists(path):
+        raise RuntimeError(f"{path} is missing: build it with "
+                           "`python -c 'import __graft_entry__ as g; g.build()'`")
+    lib = ctypes.CDLL(path)
+    lib.plx_bench_stream_read.argtypes = [ctypes.c_void_p, ctypes.c_size_t, ctypes.c_void_p,
+                                          ctypes.c_size_t, ctypes.c_void_p, ctypes.c_int,
+                                          ctypes.c_void_p]
+    lib.plx_bench_stream_read.restype = ctypes.c_int
+    return lib
+
+
+class ColdCaches:
+    """Reads 1 GiB before a timed call: evicts the L2s and the 256 MB last-level cache without
+    leaving dirty lines whose write-back would be charged to the call."""
+
+    def __init__(self, torch, dev):
+        self.torch = torch
+        self.flush = torch.ones(COPY_BYTES // 4, dtype=torch.float32, device=dev)
+        self.sink = torch.empty(1, dtype=torch.float32, device=dev)
+
+    def __call__(self):
+        self.torch.sum(self.flush, dim=0, keepdim=True, out=self.sink)
+
+
+def timed_calls(torch, stream, call, n, cold=None, settle_s=0.0):
+    """Median/p10/p90 of n calls bracketed by HIP events on `stream` (after `settle_s` seconds
+    of untimed calls and 3 warm-up calls; `cold` runs before each timed call)."""
+    t_end = time.perf_counter() + settle_s
+    while time.perf_counter() < t_end:
+        call()
+        torch.cuda.synchronize()
+    for _ in range(3):
+        call()
+    ts = []
+    for _ in range(n):
+        if cold is not None:
+            cold()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        call()
+        e1.record(stream)
+        torch.cuda.synchronize()
+        ts.append(e0.elapsed_time(e1))
+    return _stats_us(ts)
+
+
+def stream_floor(torch, blib, stream, a, b, nbytes, cold, n=10):
+    """Time of the streaming-read kernel over nbytes (half from each of the device tensors a
+    and b), cold caches, best median over five grid sizes: the floor for a call that must
+    read that many bytes."""
+    half = nbytes // 2 // 16 * 16
+    assert half <= a.numel() * a.element_size() and half <= b.numel() * b.element_size()
+    sink = torch.zeros(1024, dtype=torch.int32, device=a.device)
+    h = ctypes_stream(stream)
+    best = None
+    for grid in (512, 1024, 2048, 4096, 8192):
+        def call(grid=grid):
+            rc = blib.plx_bench_stream_read(a.data_ptr(), half, b.data_ptr(), half,
+                                            sink.data_ptr(), grid, h)
+            if rc != 0:
+                raise RuntimeError(f"plx_bench_stream_read: HIP error {rc}")
+        st = timed_calls(torch, stream, call, n, cold=cold)
+        if best is None or st["median_us"] < best["median_us"]:
+            best = dict(st, grid=grid, bytes=2 * half)
+    return best
+
+
+def ctypes_stream(stream) -> int:
+    import ctypes
+    return ctypes.c_void_p(stream.cuda_stream).value or 0
+
+
+def prefill_split_record(torch, plx, stream, pd, pcfg, default_us, n=20):
+    """The same prefill with split weights (hi + lo bf16 terms, PLX_PREFILL_SPLIT_WEIGHTS)."""
+    o = torch.empty_like(pd["q"])
+    st = timed_calls(torch, stream, lambda: plx.prefill(pd["q"], pd["k"], pd["v"], pd["rho"],
+                                                         pcfg.scale, out=o, split_weights=True),
+                     n, settle_s=0.3)
+    fl = prefill_flops(pcfg.B, pcfg.H, pcfg.T, pcfg.d)
+    tf = fl / (st["median_us"] * 1e-6) / 1e12
+    return {"workload": f"prefill B{pcfg.B} H{pcfg.H} T{pcfg.T} d{pcfg.d} bf16, split weights",
+            **st, "tflops": round(tf, 1), "mfma_frac": round(tf / BF16_PEAK_TFLOPS, 4),
+            "time_over_default": round(st["median_us"] / default_us, 4)}
+
+
+def prefill_long_record(torch, plx, dev, stream, n=5):
+    """The long prefill B1 H32 T32768 d128, inputs drawn on the device with the recipe's
+    distributions (q, k, v ~ N(0,1); rho zero on heads < 16, 0.1 RMSNorm(N(0,1)) on the rest)."""
+    from plx_synth import CONFIGS
+
+    cfg = CONFIGS["prefill_long"]
+    g = torch.Generator(device=dev)
+    g.manual_seed(5)
+    shp = (cfg.B, cfg.H, cfg.T, cfg.d)
+    d = {k: torch.randn(shp, generator=g, device=dev, dtype=torch.float32).to(torch.bfloat16)
+         for k in ("q", "k", "v")}
+    r = torch.randn(shp, generator=g, device=dev, dtype=torch.float32)
+    r = 0.1 * r * torch.rsqrt(r.pow(2).mean(-1, keepdim=True) + 1e-6)
+    r[:, : cfg.H // 2] = 0
+    d["rho"] = r.to(torch.bfloat16)
+    del r
+    o = torch.empty_like(d["q"])
+    st = timed_calls(torch, stream,
+                     lambda: plx.prefill(d["q"], d["k"], d["v"], d["rho"], cfg.scale, out=o), n,
+                     settle_s=0.3)
+    fl = prefill_flops(cfg.B, cfg.H, cfg.T, cfg.d)
+    tf = fl / (st["median_us"] * 1e-6) / 1e12
+    del d, o
+    torch.cuda.empty_cache()
+    return {"workload": f"prefill B{cfg.B} H{cfg.H} T{cfg.T} d{cfg.d} bf16 causal, half the "
+                        "heads rho = 0", **st, "flops": fl, "tflops": round(tf, 1),
+            "mfma_frac": round(tf / BF16_PEAK_TFLOPS, 4),
+            "tokens_per_s": round(cfg.B * cfg.T / (st["median_us"] * 1e-6), 0)}
+
+
+def decode_grid_records(torch, plx, dev, stream, min_bytes=100e6, n=10):
+    """Decode grid cells (H16 d128, B x ctx, seqlens ~ U[ctx/2, ctx]) that move at least
+    min_bytes, automatic plan, cold caches; each beside the streaming-read floor of its KV
+    bytes measured in the same run."""
+    from plx_synth import decode_grid_cells, decode_inputs
+    from plx_synth.inputs import draw_seqlens
+
+    blib = _bench_lib()
+    cold = ColdCaches(torch, dev)
+    recs = []
+    for cfg in decode_grid_cells():
+        nbytes = decode_bytes(draw_seqlens(cfg, 0).tolist(), cfg.H, cfg.d)
+        if nbytes < min_bytes:
+            continue
+        dx = decode_inputs(cfg, seed=0, device=str(dev), device_draw=True)
+        splits = plx.decode_num_splits(cfg.B, cfg.H, cfg.L_max, 0)
+        wsb = plx.decode_workspace_size(cfg.B, cfg.H, cfg.L_max, cfg.d, 0)
+        ws = torch.empty(max(wsb // 4, 1), dtype=torch.float32, device=dev)
+        od = torch.empty_like(dx["q"])
+        st = timed_calls(torch, stream,
+                         lambda: plx.decode(dx["q"], dx["rho"], dx["k_cache"], dx["v_cache"],
+                                            dx["seqlens"], cfg.scale, out=od, workspace=ws),
+                         n, cold=cold)
+        kv = nbytes - cfg.B * cfg.H * 3 * cfg.d * 2
+        fl = stream_floor(torch, blib, stream, dx["k_cache"], dx["v_cache"], kv, cold)
+        gbps = nbytes / (st["median_us"] * 1e-6) / 1e9
+        recs.append({"workload": f"decode B{cfg.B} H{cfg.H} ctx{cfg.L_max} d{cfg.d} bf16",
+                     **st, "plan": splits, "bytes": nbytes, "hbm_gbps": round(gbps, 1),
+                     "hbm_frac": round(gbps / HBM_PEAK_GBPS, 4),
+                     "tokens_per_s": round(cfg.B / (st["median_us"] * 1e-6), 1),
+                     "floor_us": fl["median_us"], "floor_bytes": fl["bytes"],
+                     "floor_gbps": round(fl["bytes"] / (fl["median_us"] * 1e-6) / 1e9, 1),
+                     "time_over_floor": round(st["median_us"] / fl["median_us"], 4)})
+        print(json.dumps(recs[-1]), file=sys.stderr, flush=True)
+        del dx, ws, od
+        torch.cuda.empty_cache()
+    del cold
+    torch.cuda.empty_cache()
+    return recs
 
 
 # ------------------------------------------------------------------------------ sweep
@@ -796,6 +979,8 @@ def main():
                          "under-reports the steady rate")
     ap.add_argument("--copies", type=int, default=4, help="decode cache copies to rotate")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-grid", action="store_true",
+                    help="leave the decode grid cells out of the line (profiling runs)")
     ap.add_argument("--calibrate-copy", action="store_true")
     ap.add_argument("--summarize-counters", nargs="+",
                     metavar="CSV_GLOB", help="FETCH_SIZE run, WRITE_SIZE run[, MFMA run]")
@@ -920,6 +1105,16 @@ def main():
 
     traffic = committed_traffic()
     read_gbps = streaming_read_gbps(torch, dev, stream)
+    # Sub-records after the timed steps: the split-weights prefill, the long prefill and the
+    # bandwidth-dominated decode grid cells (each beside its streaming-read floor).
+    split_rec = prefill_split_record(torch, plx, stream, pd, pcfg, avg(pre_ms) * 1e3)
+    print(json.dumps(split_rec), file=sys.stderr, flush=True)
+    n_copies = len(caches)
+    del caches
+    torch.cuda.empty_cache()
+    long_rec = prefill_long_record(torch, plx, dev, stream)
+    print(json.dumps(long_rec), file=sys.stderr, flush=True)
+    grid_recs = [] if args.no_grid else decode_grid_records(torch, plx, dev, stream)
     result = {
         "metric": "decode tokens/s & HBM GB/s frac; prefill TFLOP/s & MFMA util (B,H,T,d=128)",
         "value": round(tflops, 2),
@@ -939,7 +1134,7 @@ def main():
                                "decode B1 H16 L32768 d128",
                    "prefill": {"B": pcfg.B, "H": pcfg.H, "T": pcfg.T, "d": pcfg.d},
                    "decode": {"B": dcfg.B, "H": dcfg.H, "L": dcfg.L_max, "d": dcfg.d,
-                              "splits": splits, "cache_copies": len(caches)}},
+                              "splits": splits, "cache_copies": n_copies}},
         "prefill": {"us_avg": round(avg(pre_ms) * 1e3, 2),
                     "us_p10": round(pct(pre_ms, 0.1) * 1e3, 2),
                     "us_p90": round(pct(pre_ms, 0.9) * 1e3, 2),
@@ -963,6 +1158,12 @@ def main():
                             "frac": round(dec_gbps / HBM_PEAK_GBPS, 4),
                             "traffic": committed_decode_traffic(),
                             "work_per_launch": dbytes},
+        "prefill_split_weights": split_rec,
+        "prefill_long": dict(long_rec, roofline={
+            "bound": "mfma", "achieved": long_rec["tflops"], "peak": BF16_PEAK_TFLOPS,
+            "unit": "TFLOP/s", "frac": long_rec["mfma_frac"], "traffic": None,
+            "work_per_launch": long_rec["flops"]}),
+        "decode_grid": grid_recs,
         "wall_s_timed": round(wall, 3),
         "system": {"gpu": torch.cuda.get_device_name(dev),
                    "arch": getattr(torch.cuda.get_device_properties(dev), "gcnArchName", None),

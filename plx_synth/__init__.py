@@ -11,6 +11,7 @@ from .inputs import (  # noqa: F401
     PrefillConfig,
     decode_inputs,
     decode_grid_cells,
+    prefill_head_inputs,
     prefill_inputs,
     prefill_upstream_grad,
     to_dtype,

@@ -161,6 +161,24 @@ def prefill_inputs(cfg: PrefillConfig, seed: int = 0, device: Optional[str] = No
     return out
 
 
+def prefill_head_inputs(cfg: PrefillConfig, b: int, h: int, seed: int = 0):
+    """Slice (b, h) of prefill_inputs(cfg, seed) alone, as [1, 1, T, d] tensors: the same
+    keyed streams, so it equals the full draw's slice. Probe recipes drawn per (b, h):
+    "scaled", "half_zero_heads" and "zero"."""
+    if cfg.rho not in ("scaled", "half_zero_heads", "zero"):
+        raise ValueError(f"probe recipe {cfg.rho} is not drawn per head")
+    shp = (cfg.T, cfg.d)
+    chunk = b * cfg.H + h
+    out = {name: to_dtype(_normal_host(shp, seed, cfg.cfg_id, tid, chunk)[None, None], cfg.dtype)
+           for name, tid in (("q", T_Q), ("k", T_K), ("v", T_V))}
+    zero = cfg.rho == "zero" or (cfg.rho == "half_zero_heads" and h < cfg.H // 2)
+    r = np.zeros(shp) if zero else 0.1 * _rms_norm_lastdim(
+        _normal_host(shp, seed, cfg.cfg_id, T_RHO, chunk))
+    out["rho"] = to_dtype(r[None, None], cfg.dtype)
+    out["scale"] = cfg.scale
+    return out
+
+
 def prefill_upstream_grad(cfg: PrefillConfig, seed: int = 0) -> torch.Tensor:
     """The gradient arriving at the prefill output for a backward pass: N(0, 1), [B, H, T, d]."""
     return to_dtype(_per_head((cfg.B, cfg.H, cfg.T, cfg.d), seed, cfg.cfg_id, T_DO, cfg.H),
@@ -245,5 +263,6 @@ def small_decode(B, H, L_max, d, dtype="bf16", rho="scaled", seqlens="uniform_ha
 
 
 __all__ = ["PrefillConfig", "DecodeConfig", "CONFIGS", "decode_grid_cells", "prefill_inputs",
+           "prefill_head_inputs",
            "decode_inputs", "small_prefill", "small_decode", "to_dtype", "draw_seqlens",
            "host_draw_ok", "replace"]

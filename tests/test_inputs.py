@@ -59,3 +59,13 @@ def test_chunks_regenerate_independently():
         assert torch.isfinite(x["k_cache"][b]).all()
     y = decode_inputs(DecodeConfig("t", 7, 3, 2, 40, 8, "f32", "scaled", "full"), seed=9)
     assert torch.equal(x["v_cache"], y["v_cache"])
+
+
+def test_prefill_head_inputs_equal_the_full_draw_slice():
+    from plx_synth import prefill_head_inputs
+    cfg = PrefillConfig("t", 5, 2, 4, 40, 128, "bf16", "half_zero_heads")
+    full = prefill_inputs(cfg, seed=2)
+    for b, h in ((0, 0), (1, 1), (0, 2), (1, 3)):
+        one = prefill_head_inputs(cfg, b, h, seed=2)
+        for n in ("q", "k", "v", "rho"):
+            assert torch.equal(one[n], full[n][b: b + 1, h: h + 1]), (b, h, n)

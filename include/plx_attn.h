@@ -131,7 +131,13 @@ plx_status_t plx_attn_decode_workspace_size(int32_t B, int32_t H, int32_t L_max,
                                             size_t* bytes_out);
 
 /*
- * One decode step over a contiguous per-sequence KV cache.
+ * One decode step over a contiguous per-sequence KV cache: equation (1) for the one new query
+ * row of each (b, h) against its cached keys. The score and probe products of a cache row
+ * share one matrix instruction (the probe fills accumulator rows the single query leaves idle
+ * [agihunt review, hardware paragraph]), and the key loop is split across workgroups whose
+ * partial states are then reduced [Parallax (paper.rainbus.top summary), reproducibility
+ * section: the decode kernel is optimised by instruction sharing, splitting the KV loop and
+ * reducing the split partials].
  *
  *   q, rho   : [B, H, d_qk]            k_cache : [B, H, L_max, d_qk]
  *   v_cache  : [B, H, L_max, d_v]      o       : [B, H, d_v]

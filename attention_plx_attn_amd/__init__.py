@@ -6,6 +6,8 @@ Python entry points over the C ABI of ``libplx_attn.so`` (include/plx_attn.h):
 * ``decode(q, rho, k_cache, v_cache, seqlens, scale=None, num_splits=0)`` -- one decode
   step over a contiguous per-sequence KV cache;
 * ``decode_num_splits`` / ``decode_workspace_size`` -- the split plan of a decode call;
+* ``decode_noalloc(q, rho, k_cache, v_cache, seqlens, out, ...)`` -- the same step for
+  callers that cannot allocate (split records in the library's fixed per-GPU scratch);
 * ``decode_gqa`` / ``decode_gqa_plan`` -- decode with grouped query heads (H_q = G H_kv);
 * ``decode_paged`` -- decode over a paged KV cache (block pool + block table);
 * ``prefill_fwd`` / ``prefill_bwd`` -- the prefill with saved statistics and its backward
@@ -20,6 +22,7 @@ from ._lib import (  # noqa: F401
     decode,
     decode_gqa,
     decode_gqa_plan,
+    decode_noalloc,
     decode_num_splits,
     decode_paged,
     decode_workspace_size,

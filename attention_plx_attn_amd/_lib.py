@@ -55,6 +55,9 @@ def load() -> ctypes.CDLL:
     lib.plx_attn_decode.argtypes = ([ctypes.c_int] + [i32] * 5 + [vp] * 6 +
                                     [f32, i32, vp, ctypes.c_size_t, vp])
     lib.plx_attn_decode.restype = ctypes.c_int
+    lib.plx_attn_decode_noalloc.argtypes = ([ctypes.c_int] + [i32] * 5 + [vp] * 6 +
+                                            [f32, i32, vp])
+    lib.plx_attn_decode_noalloc.restype = ctypes.c_int
     lib.plx_attn_decode_gqa_plan.argtypes = [i32] * 6 + [ctypes.POINTER(i32),
                                                          ctypes.POINTER(ctypes.c_size_t)]
     lib.plx_attn_decode_gqa_plan.restype = ctypes.c_int
@@ -290,6 +293,37 @@ def decode(q: torch.Tensor, rho: Optional[torch.Tensor], k_cache: torch.Tensor, 
                              _stream_handle(stream, q.device))
     if rc != 0:
         raise PlxError(rc, "plx_attn_decode")
+    return out
+
+
+def decode_noalloc(q: torch.Tensor, rho: Optional[torch.Tensor], k_cache: torch.Tensor,
+                   v_cache: torch.Tensor, seqlens: torch.Tensor, out: torch.Tensor,
+                   scale: Optional[float] = None, num_splits: int = 0,
+                   stream: Optional[torch.cuda.Stream] = None) -> torch.Tensor:
+    """decode() through plx_attn_decode_noalloc: the split records live in the library's
+    fixed per-GPU scratch, and the caller passes the output, so the call allocates nothing.
+    Calls that overlap on one GPU race on that scratch."""
+    lib = load()
+    if q.dim() != 3:
+        raise ValueError("q must be [B, H, d_qk]")
+    B, H, dqk = q.shape
+    L_max, dv = v_cache.shape[2], v_cache.shape[3]
+    _check(q, "q", None, None)
+    if rho is not None:
+        _check(rho, "rho", q.dtype, q.device, (B, H, dqk))
+    _check(k_cache, "k_cache", q.dtype, q.device, (B, H, L_max, dqk))
+    _check(v_cache, "v_cache", q.dtype, q.device, (B, H, L_max, dv))
+    _check(seqlens, "seqlens", torch.int32, q.device, (B,))
+    _check(out, "out", q.dtype, q.device, (B, H, dv))
+    if scale is None:
+        scale = dqk ** -0.5
+    rc = lib.plx_attn_decode_noalloc(_dtype_code(q), B, H, L_max, dqk, dv, q.data_ptr(),
+                                     0 if rho is None else rho.data_ptr(), k_cache.data_ptr(),
+                                     v_cache.data_ptr(), seqlens.data_ptr(), out.data_ptr(),
+                                     float(scale), int(num_splits),
+                                     _stream_handle(stream, q.device))
+    if rc != 0:
+        raise PlxError(rc, "plx_attn_decode_noalloc")
     return out
 
 

@@ -6,6 +6,7 @@
 #include <atomic>
 #include <climits>
 #include <cmath>
+#include <mutex>
 
 #include "plx_attn.h"
 #include "plx_kernels.hpp"
@@ -134,6 +135,43 @@ plx_status_t check_bwd_shape(plx_dtype_t dtype, int B, int H, int T, int d_qk, i
     if ((long long)B * H * ((T + 127) / 128) > INT_MAX) return PLX_ERR_INVALID_SHAPE;
     return PLX_OK;
 }
+
+// ---------------------------------------------------------------- no-allocation decode
+// Scratch of plx_attn_decode_noalloc: the split partial records of a decode call, in a
+// file-scope device array (one copy per GPU, held until the process ends). Host code never
+// passes the array's name to a kernel (on the host it is only a stand-in for the symbol): the
+// device address of each GPU's copy is looked up once per device with hipGetSymbolAddress
+// and kept here.
+constexpr size_t kScratchBytes = PLX_DECODE_NOALLOC_SCRATCH_BYTES;
+__device__ __align__(256) float scratch[kScratchBytes / sizeof(float)];
+
+std::atomic<void*> g_scratch_ptr[kMaxDevices];
+std::mutex g_scratch_mutex;
+
+// Device address of the current device's `scratch`, looked up on the first call on a device
+// (with that device current) and cached.
+plx_status_t scratch_of_current_device(void** out) {
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return PLX_ERR_HIP;
+    void* ptr = g_scratch_ptr[dev].load(std::memory_order_acquire);
+    if (ptr == nullptr) {
+        std::lock_guard<std::mutex> lock(g_scratch_mutex);
+        ptr = g_scratch_ptr[dev].load(std::memory_order_relaxed);
+        if (ptr == nullptr) {
+            if (hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch)) != hipSuccess || ptr == nullptr)
+                return PLX_ERR_HIP;
+            g_scratch_ptr[dev].store(ptr, std::memory_order_release);
+        }
+    }
+    *out = ptr;
+    return PLX_OK;
+}
+
+plx_status_t decode_call(plx_dtype_t dtype, int32_t B, int32_t H, int32_t L_max, int32_t d_qk,
+                         int32_t d_v, const void* q, const void* rho, const void* k_cache,
+                         const void* v_cache, const int32_t* seqlens, void* o,
+                         float softmax_scale, int32_t num_splits, void* workspace,
+                         size_t workspace_bytes, void* stream, bool use_scratch);
 
 }  // namespace
 
@@ -279,6 +317,30 @@ plx_status_t plx_attn_decode(plx_dtype_t dtype, int32_t B, int32_t H, int32_t L_
                              const int32_t* seqlens, void* o, float softmax_scale,
                              int32_t num_splits, void* workspace, size_t workspace_bytes,
                              void* stream) {
+    return decode_call(dtype, B, H, L_max, d_qk, d_v, q, rho, k_cache, v_cache, seqlens, o,
+                       softmax_scale, num_splits, workspace, workspace_bytes, stream, false);
+}
+
+plx_status_t plx_attn_decode_noalloc(plx_dtype_t dtype, int32_t B, int32_t H, int32_t L_max,
+                                     int32_t d_qk, int32_t d_v, const void* q, const void* rho,
+                                     const void* k_cache, const void* v_cache,
+                                     const int32_t* seqlens, void* o, float softmax_scale,
+                                     int32_t num_splits, void* stream) {
+    return decode_call(dtype, B, H, L_max, d_qk, d_v, q, rho, k_cache, v_cache, seqlens, o,
+                       softmax_scale, num_splits, nullptr, kScratchBytes, stream, true);
+}
+
+}  // extern "C"
+
+namespace {
+
+// One decode step (the body of plx_attn_decode). With use_scratch, the split records go to
+// this GPU's copy of `scratch` (workspace is ignored, workspace_bytes is the array's size).
+plx_status_t decode_call(plx_dtype_t dtype, int32_t B, int32_t H, int32_t L_max, int32_t d_qk,
+                         int32_t d_v, const void* q, const void* rho, const void* k_cache,
+                         const void* v_cache, const int32_t* seqlens, void* o,
+                         float softmax_scale, int32_t num_splits, void* workspace,
+                         size_t workspace_bytes, void* stream, bool use_scratch) {
     if (dtype != PLX_F32 && dtype != PLX_BF16) return PLX_ERR_INVALID_ARG;
     if (!q || !k_cache || !v_cache || !seqlens || !o) return PLX_ERR_NULL_POINTER;
     plx_status_t st = check_decode_shape(B, H, L_max, d_v);
@@ -296,6 +358,11 @@ plx_status_t plx_attn_decode(plx_dtype_t dtype, int32_t B, int32_t H, int32_t L_
     DecodePlan p;
     st = plan_decode(B, H, L_max, d_v, num_splits, &p);
     if (st != PLX_OK) return st;
+    if (use_scratch) {
+        if (p.ws_bytes > kScratchBytes) return PLX_ERR_WORKSPACE_TOO_SMALL;
+        st = scratch_of_current_device(&workspace);
+        if (st != PLX_OK) return st;
+    }
     if (p.ws_bytes > 0) {
         if (!workspace) return PLX_ERR_NULL_POINTER;
         if (workspace_bytes < p.ws_bytes) return PLX_ERR_WORKSPACE_TOO_SMALL;
@@ -309,6 +376,10 @@ plx_status_t plx_attn_decode(plx_dtype_t dtype, int32_t B, int32_t H, int32_t L_
                              : plx::launch_decode_bf16_d128(a, static_cast<hipStream_t>(stream));
     return e == hipSuccess ? PLX_OK : PLX_ERR_HIP;
 }
+
+}  // namespace
+
+extern "C" {
 
 plx_status_t plx_attn_decode_gqa_plan(int32_t B, int32_t H_q, int32_t H_kv, int32_t L_max,
                                      int32_t d_v, int32_t num_splits, int32_t* splits_out,

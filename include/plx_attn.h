@@ -170,6 +170,31 @@ plx_status_t plx_attn_decode(plx_dtype_t dtype, int32_t B, int32_t H, int32_t L_
                              int32_t num_splits, void* workspace, size_t workspace_bytes,
                              void* stream);
 
+/* Bytes of the per-GPU scratch array of plx_attn_decode_noalloc. */
+#define PLX_DECODE_NOALLOC_SCRATCH_BYTES (16u << 20)
+
+/*
+ * plx_attn_decode for callers that cannot allocate device memory (code under HIP graph
+ * capture, tight serving loops, harnesses that forbid allocation): the same step with the
+ * same arguments, plan, kernels and results, except that the split partial records go to a
+ * fixed scratch array the library holds on each GPU it runs on (PLX_DECODE_NOALLOC_SCRATCH_BYTES,
+ * 16 MiB, kept until the process ends) instead of a caller workspace. The caller still passes
+ * the inputs and the output. The call allocates nothing: no hipMalloc, no hipFree, no
+ * allocating library routine. The scratch's device address is looked up on the first call on
+ * each device (with that device current) and cached.
+ *
+ * A plan whose workspace (plx_attn_decode_workspace_size) exceeds the scratch returns
+ * PLX_ERR_WORKSPACE_TOO_SMALL without enqueuing anything; pass a smaller num_splits.
+ * All calls on one GPU share its scratch: calls that overlap on one GPU (on different streams,
+ * or from several threads) race and must be serialised by the caller. Nothing in the scratch
+ * needs to start at zero (every record a call reads, that call has written).
+ */
+plx_status_t plx_attn_decode_noalloc(plx_dtype_t dtype, int32_t B, int32_t H, int32_t L_max,
+                                     int32_t d_qk, int32_t d_v, const void* q, const void* rho,
+                                     const void* k_cache, const void* v_cache,
+                                     const int32_t* seqlens, void* o, float softmax_scale,
+                                     int32_t num_splits, void* stream);
+
 /*
  * Decode with grouped query heads: H_q query heads over H_kv cache heads, G = H_q / H_kv in {1, 2, 4, 8}; query head h reads cache head
  * h / G. Same conventions as plx_attn_decode, with

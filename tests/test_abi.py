@@ -19,7 +19,7 @@ def lib():
 def test_exports_every_declared_symbol(lib):
     declared = plx.header_functions()
     assert set(declared) == {"plx_attn_prefill", "plx_attn_prefill_ex", "plx_attn_decode",
-                             "plx_attn_decode_num_splits",
+                             "plx_attn_decode_noalloc", "plx_attn_decode_num_splits",
                              "plx_attn_decode_workspace_size", "plx_attn_probe",
                              "plx_attn_decode_gqa", "plx_attn_decode_gqa_plan",
                              "plx_attn_decode_paged", "plx_attn_prefill_fwd",
@@ -246,3 +246,16 @@ def test_prefill_bwd_validation(lib):
     assert _bwd(lib, dtype=0) == 4
     assert _bwd(lib, dqk=128, dv=64) == 4
     assert _bwd(lib, ws_bytes=1 * 2 * 64 * 16 - 1) == 6
+
+
+def test_decode_noalloc_validation(lib):
+    # host-side checks run before the scratch is looked up (no GPU needed for these)
+    args = lambda **kw: [kw.get("dtype", 1), kw.get("B", 2), 2, 64, 128, 128, A, A, A, A,  # noqa: E731
+                         kw.get("sl", A), kw.get("o", A), ctypes.c_float(kw.get("scale", 0.1)),
+                         kw.get("splits", 1), None]
+    assert lib.plx_attn_decode_noalloc(*args(sl=0)) == 1
+    assert lib.plx_attn_decode_noalloc(*args(o=0)) == 1
+    assert lib.plx_attn_decode_noalloc(*args(B=0)) == 2
+    assert lib.plx_attn_decode_noalloc(*args(scale=-1.0)) == 3
+    assert lib.plx_attn_decode_noalloc(*args(dtype=0)) == 4
+    assert lib.plx_attn_decode_noalloc(*args(splits=5000)) == 3

@@ -42,6 +42,15 @@ constexpr int kDecodeWaveKeys = 64;      // chunk granularity (keys)
 constexpr int kDecodeMinChunk = 256;     // at least one step per wave of a 4-wave workgroup
 constexpr int kDecodeMaxSplits = 4096;
 constexpr int kDecodeWgPerCu = 1;        // one streaming workgroup per compute unit (measured best)
+// Ragged batches: with one chunk per (b, h) the longest sequences set the time. Long contexts
+// are therefore split further, up to kDecodeBalanceWgPerCu workgroups per compute unit in all
+// (enough for the dispatcher to even out the lengths as workgroups finish) and at most one
+// chunk per kDecodeBalanceRows rows of L_max (shorter chunks cost more in per-workgroup
+// overhead than they gain in balance). Measured on the decode grid (seqlens ~ U[ctx/2, ctx]):
+// 16 x 32768 555 -> 474 us at 16 chunks, 128 x 32768 4154 -> 3794 us at 2, 16 x 4096 76 -> 72
+// us at 2; contexts up to 2048 rows, and B H >= 32 CUs, keep one chunk.
+constexpr int kDecodeBalanceWgPerCu = 32;
+constexpr int kDecodeBalanceRows = 2048;
 // Wave-range mode: slices end at (b, h) starts once there are 2 (b, h) per wave. The automatic
 // plan uses it only in that form, for short contexts with enough (b, h) for at least 2 and at
 // most 4 (the register limit) 4-wave workgroups per compute unit. Measured on MI355X: ahead
@@ -98,6 +107,9 @@ plx_status_t plan_decode(int B, int H, int L_max, int d_v, int num_splits, Decod
             waves = (int)(4 * wg);
         if (!waves) {  // split mode: fill the chip once with (b, h, chunk) workgroups
             long long s = (kDecodeWgPerCu * (long long)cus + bh - 1) / bh;
+            long long s_bal = (kDecodeBalanceWgPerCu * (long long)cus + bh - 1) / bh;
+            if (s_bal > L_max / kDecodeBalanceRows) s_bal = L_max / kDecodeBalanceRows;
+            if (s < s_bal) s = s_bal;
             const long long smax = (L_max + kDecodeMinChunk - 1) / kDecodeMinChunk;
             if (s > smax) s = smax;
             if (s < 1) s = 1;

@@ -50,8 +50,9 @@ constexpr int BR = 128;  // query rows per work item
 constexpr int NT = 512;  // threads per workgroup (8 waves x 16 query rows)
 constexpr int NBUF = 4;  // stream tiles s + 2 is staged while s is processed
 
-// Sizes that follow from the head dim D (d_qk = d_v = D, a multiple of 32, at most 128).
-template <int D>
+// Sizes that follow from the head dim D (d_qk = d_v = D, a multiple of 32, at most 128) and
+// from how the K tiles are staged.
+template <int D, bool KDMA_>
 struct Geo {
     // Keys per LDS tile: 64 at d = 128; 128 at d = 64, so that a tile holds the same bytes,
     // the stagers move the same number of chunks and the per-tile softmax and barrier cost
@@ -60,8 +61,13 @@ struct Geo {
     static constexpr int NKB = BC / 16;      // 16-key score blocks per tile
     static constexpr int NG = BC / 32;       // 32-key value steps per tile
     static constexpr int VS = BC + 8;        // LDS row stride of a transposed V tile
-    static constexpr int KS = D + 8;         // LDS row stride of a K tile (bf16 elements)
-    static constexpr int K_ELEMS = BC * KS;  // 8704 bf16 at D = 128
+    // KDMA (d = 128): the K tiles are staged by direct-to-LDS loads into unpadded 256-byte
+    // rows whose 16-byte chunks are XOR-swizzled by the row (chunk c of row r at position
+    // c ^ (r & 15)), which keeps the operand reads conflict-free without padding. Otherwise
+    // the stagers store through registers into rows padded by 16 bytes.
+    static constexpr bool KDMA = KDMA_;
+    static constexpr int KS = KDMA ? D : D + 8;  // LDS row stride of a K tile (bf16 elements)
+    static constexpr int K_ELEMS = BC * KS;      // 8192 bf16 at D = 128
     static constexpr int V_ELEMS = D * VS;   // 9216 bf16 at D = 128
     static constexpr int OFF_V = NBUF * K_ELEMS * 2;
     static constexpr int LDS_BYTES = OFF_V + NBUF * V_ELEMS * 2;
@@ -82,6 +88,11 @@ constexpr float kLazyTau = 8.0f;  // log2 headroom before the running max moves
 // 8 q .. 8 q + 7 that the value product's operand wants.
 __device__ __forceinline__ int krow(int k) {
     return (k & ~31) | (((k >> 2) & 1) << 4) | (((k >> 3) & 3) << 2) | (k & 3);
+}
+
+// Key stored at LDS row r (the inverse of krow).
+__device__ __forceinline__ int krow_inv(int r) {
+    return (r & ~31) | (((r >> 2) & 3) << 3) | (((r >> 4) & 1) << 2) | (r & 3);
 }
 
 __device__ __forceinline__ f32x4 mfma16(bf16x8 a, bf16x8 b, f32x4 c) {
@@ -136,7 +147,10 @@ __global__ __launch_bounds__(NT, 1) void prefill_bf16_kernel(
     const __bf16* __restrict__ rho, __bf16* __restrict__ o, __bf16* __restrict__ vbar,
     float* __restrict__ stats, int BH, int T, int nqb, float c, int ncls) {
     static_assert(!(STATS && SPLIT), "the statistics instances keep single bf16 weights");
-    using G_ = Geo<D>;
+    // Direct-to-LDS K staging where it fits the register budget: at d = 128 without split
+    // weights (the split instances need the registers the role-specialised tile loops cost).
+    constexpr bool KDMA = D == 128 && !SPLIT;
+    using G_ = Geo<D, KDMA>;
     constexpr int KS = G_::KS, K_ELEMS = G_::K_ELEMS, V_ELEMS = G_::V_ELEMS, OFF_V = G_::OFF_V;
     constexpr int BC = G_::BC, NKB = G_::NKB, NG = G_::NG, VS = G_::VS;
     constexpr int NS = G_::NS, NDB = G_::NDB, CPR = G_::CPR, CPR_LOG = G_::CPR_LOG;
@@ -191,21 +205,49 @@ __global__ __launch_bounds__(NT, 1) void prefill_bf16_kernel(
     const uint32_t voff =
         (uint32_t)(4 * (st >> CPR_LOG)) * ROWB + 16u * (st & (CPR - 1));  // + ROWB j
     u32x4 stg[4];
-    auto gload = [&](int bh, int kt) {
+    // Loads of tile kt of head bh, bound for ring slot t: direct-to-LDS for K at d = 128 (the
+    // LDS destination must be known now), into registers otherwise (stored by lstore).
+    // The staging role is a template argument of the tile loop (wave-uniform), so that the
+    // K stagers' direct-to-LDS loads never meet the V stagers' register staging at a join:
+    // there the compiler would drain every outstanding load before the V path's copies.
+    // role: std::true_type / std::false_type (K / V stager) in the KDMA instances; elsewhere
+    // the runtime role `kstager` decides and the argument is ignored.
+    auto is_k = [&](auto role) {
+        if constexpr (KDMA) return decltype(role)::value;
+        else return kstager;
+    };
+    auto gload = [&](auto role, int bh, int kt, int t) {
         const size_t base = slice_of(bh) + (size_t)kt * BC * D;
         const uint32_t bytes = slice_bytes - (uint32_t)kt * BC * ROWB;  // kt * BC < T
-        if (kstager) {
+        if (is_k(role)) {
             const auto rk = make_rsrc(k + base, bytes);
+            if constexpr (KDMA) {
+                // Load j of K-stager wave w fills LDS rows 16 j + 4 w .. +3 (1 KB, 16 bytes per
+                // lane in lane order): lane (row r, position p) fetches chunk p ^ (r & 15) of
+                // key krow_inv(r). Rows past T read as zero.
+                unsigned char* Kl = kbuf(t);
+                const int p = lane & 15;
 #pragma unroll
-            for (int j = 0; j < KCH; ++j) stg[j] = load16(rk, koff + 4096u * j);
+                for (int j = 0; j < KCH; ++j) {
+                    const int r = 16 * j + 4 * w + (lane >> 4);
+                    const uint32_t src = (uint32_t)krow_inv(r) * ROWB + 16u * (p ^ (r & 15));
+                    __builtin_amdgcn_raw_ptr_buffer_load_lds(
+                        rk, (__attribute__((address_space(3))) void*)(Kl + (16 * j + 4 * w) * ROWB),
+                        16, src, 0, 0, 0);
+                }
+            } else {
+#pragma unroll
+                for (int j = 0; j < KCH; ++j) stg[j] = load16(rk, koff + 4096u * j);
+            }
         } else if (vactive) {
             const auto rv = make_rsrc(v + base, bytes);
 #pragma unroll
             for (int j = 0; j < 4; ++j) stg[j] = load16(rv, voff + ROWB * j);
         }
     };
-    auto lstore = [&](int t) {
-        if (kstager) {
+    auto lstore = [&](auto role, int t) {
+        if (is_k(role)) {
+            if constexpr (KDMA) return;  // already in LDS
             unsigned char* Kl = kbuf(t);
 #pragma unroll
             for (int j = 0; j < KCH; ++j) {
@@ -232,16 +274,24 @@ __global__ __launch_bounds__(NT, 1) void prefill_bf16_kernel(
 
     // Scores and probe products of K tile t: block kb covers LDS rows 16 kb .. +15.
     // Lane (col, gq) register i of block kb holds key 32 (kb >> 1) + 8 gq + 4 (kb & 1) + i.
-    const int klane = col * KS * 2 + 16 * gq;
+    // The operand of lane (col, gq) for dim step s is chunk 4 s + gq of row 16 kb + col; in the
+    // swizzled d = 128 layout it sits at position (4 s + gq) ^ col = 4 (s ^ (col >> 2)) +
+    // (gq ^ (col & 3)), one lane offset per s.
+    int klane[NS];
+#pragma unroll
+    for (int s = 0; s < NS; ++s)
+        klane[s] = KDMA ? col * KS * 2 + 16 * (gq ^ (col & 3)) + 64 * (s ^ (col >> 2))
+                        : col * KS * 2 + 16 * gq;  // + 64 s as an immediate offset below
     auto products = [&](int t, f32x4 (&S)[NKB], f32x4 (&Tp)[NKB]) {
-        const unsigned char* Kl = kbuf(t) + klane;
+        const unsigned char* Kl = kbuf(t);
 #pragma unroll
         for (int kb = 0; kb < NKB; ++kb) {
             S[kb] = f32x4{};
             Tp[kb] = f32x4{};
 #pragma unroll
             for (int s = 0; s < NS; ++s) {
-                const bf16x8 kf = *(const bf16x8*)(Kl + 16 * kb * KS * 2 + 64 * s);
+                const bf16x8 kf = *(const bf16x8*)(Kl + (KDMA ? klane[s] : klane[0] + 64 * s) +
+                                                   16 * kb * KS * 2);
                 S[kb] = mfma16(kf, xq[s], S[kb]);
                 if constexpr (PROBE) Tp[kb] = mfma16(kf, xr[s], Tp[kb]);
             }
@@ -389,17 +439,26 @@ __global__ __launch_bounds__(NT, 1) void prefill_bf16_kernel(
         const bool h1 = p1 < nit_c, h2 = p2 < nit_c;
         const Item n1 = item_at<BC>(h1 ? p1 : pos, cls, ncls, nbh_c, nqb, T);
         const Item n2 = item_at<BC>(h2 ? p2 : pos, cls, ncls, nbh_c, nqb, T);
-        gload(cur.bh, 0);
-        lstore(0);
-        int sbh = 0, stile = 0;
-        if (source(cur, 0, 1, h1, n1, h2, n2, &sbh, &stile)) {
-            gload(sbh, stile);
-            lstore(1);
+        auto first_two = [&](auto role) {
+            gload(role, cur.bh, 0, 0);
+            lstore(role, 0);
+            int sbh = 0, stile = 0;
+            if (source(cur, 0, 1, h1, n1, h2, n2, &sbh, &stile)) {
+                gload(role, sbh, stile, 1);
+                lstore(role, 1);
+            }
+        };
+        if constexpr (KDMA) {
+            if (kstager) first_two(std::true_type{});
+            else first_two(std::false_type{});
+        } else {
+            first_two(std::false_type{});
         }
     }
     __syncthreads();
     __builtin_amdgcn_s_waitcnt(0x0F70);  // the fragments have arrived (see the epilogue)
     int t0 = 0;
+    auto tile_loop = [&](auto role) {
     for (;;) {
         const int pos_n = item_position(kk + 1, jw, Wc);
         const bool has_next = pos_n < nit_c;
@@ -411,7 +470,7 @@ __global__ __launch_bounds__(NT, 1) void prefill_bf16_kernel(
         auto stage = [&](int kt) {
             int sbh = 0, stile = 0;
             if (!source(cur, kt, 2, has_next, nx, has_next2, nx2, &sbh, &stile)) return false;
-            gload(sbh, stile);
+            gload(role, sbh, stile, t0 + kt + 2);
             return true;
         };
         auto slot_end = [&](int kt) {
@@ -428,14 +487,14 @@ __global__ __launch_bounds__(NT, 1) void prefill_bf16_kernel(
             const bool staged = stage(kt);
             products(t0 + kt, S, Tp);
             finish(t0 + kt, kt, qi, std::false_type{}, S, Tp);
-            if (staged) lstore(t0 + kt + 2);
+            if (staged) lstore(role, t0 + kt + 2);
             slot_end(kt);
         }
         for (int kt = cur.nfull; kt < nt - 1; ++kt) {
             const bool staged = stage(kt);
             products(t0 + kt, S, Tp);
             finish(t0 + kt, kt, qi, std::true_type{}, S, Tp);
-            if (staged) lstore(t0 + kt + 2);
+            if (staged) lstore(role, t0 + kt + 2);
             slot_end(kt);
         }
         {
@@ -448,7 +507,7 @@ __global__ __launch_bounds__(NT, 1) void prefill_bf16_kernel(
             if (!skip) products(t0 + kt, S, Tp);
             if (has_next) load_x(nx);
             if (!skip) finish(t0 + kt, kt, qi, std::true_type{}, S, Tp);
-            if (staged) lstore(t0 + kt + 2);
+            if (staged) lstore(role, t0 + kt + 2);
             slot_end(kt);
         }
         __builtin_amdgcn_s_waitcnt(0x0F70);
@@ -504,6 +563,13 @@ __global__ __launch_bounds__(NT, 1) void prefill_bf16_kernel(
         cur = nx;
         pos = pos_n;
         ++kk;
+    }
+    };
+    if constexpr (KDMA) {
+        if (kstager) tile_loop(std::true_type{});
+        else tile_loop(std::false_type{});
+    } else {
+        tile_loop(std::false_type{});
     }
 }
 

@@ -29,6 +29,8 @@ Extra modes:
                           (H16 d128, B x ctx) instead of the step; one JSON line each
   --compare [OUT_MD]      time Parallax against softmax-only attention (rho = NULL) with the
                           same inputs and with twice the heads (equal matrix FLOPs)
+  --compare-grid [OUT_MD] the same decode comparisons (and Parallax at d = 64) on every decode
+                          grid cell, with the ratios' minimum and maximum
   --gqa [OUT_MD]          time the grouped-query decode (G = 1, 2, 4, 8 query heads per cache
                           head) on a 1x16x32768 cache
   --paged [OUT_MD]        time the paged-cache decode against the contiguous cache
@@ -684,6 +686,84 @@ def compare(out_md):
     return 0
 
 
+def compare_grid(out_md):
+    """The pages' decode comparison over their sweep (batch x context, the 18 grid cells, H16
+    d128, seqlens ~ U[ctx/2, ctx]) with our own kernels standing in for softmax attention:
+    Parallax against softmax only (rho = NULL) on the same cache (I/O-matched), against
+    softmax only with twice the heads (compute-matched: the same matrix FLOPs, twice the
+    cache), and Parallax at head dim 64 (the pages' compute-matched control: the FLOPs of
+    softmax attention at d 128, half its cache). Cold caches, HIP events, median of 10, the
+    automatic plan of each call. Ratios > 1 mean Parallax is faster."""
+    import torch
+
+    import attention_plx_attn_amd as plx
+    from plx_synth import decode_grid_cells
+    from plx_synth.inputs import draw_seqlens
+
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    stream = torch.cuda.current_stream(dev)
+    cold = ColdCaches(torch, dev)
+    g = torch.Generator(device=dev)
+    rows = []
+
+    def bf(shape, s=1.0):
+        return (s * torch.randn(shape, generator=g, device=dev)).to(torch.bfloat16)
+
+    def cache(B, H, L, d):
+        # per batch row, so that no float32 temporary of the whole cache is needed
+        out = torch.empty((B, H, L, d), dtype=torch.bfloat16, device=dev)
+        for b in range(B):
+            out[b] = torch.randn((H, L, d), generator=g, device=dev).to(torch.bfloat16)
+        return out
+
+    def timed(B, H, L, d, probe, sl):
+        q = bf((B, H, d))
+        rho = bf((B, H, d), 0.1) if probe else None
+        kc, vc = cache(B, H, L, d), cache(B, H, L, d)
+        o = torch.empty_like(q)
+        wsb = plx.decode_workspace_size(B, H, L, d, 0)
+        ws = torch.empty(max(wsb // 4, 1), dtype=torch.float32, device=dev)
+        st = timed_calls(torch, stream, lambda: plx.decode(q, rho, kc, vc, sl, d ** -0.5, out=o,
+                                                           workspace=ws), 10, cold=cold)
+        del q, rho, kc, vc, o, ws
+        torch.cuda.empty_cache()
+        return st["median_us"]
+
+    for cfg in decode_grid_cells():
+        g.manual_seed(cfg.B * 100003 + cfg.L_max)
+        sl = torch.from_numpy(draw_seqlens(cfg, 0)).to(dev)
+        B, H, L = cfg.B, cfg.H, cfg.L_max
+        t_plx = timed(B, H, L, 128, True, sl)
+        t_io = timed(B, H, L, 128, False, sl)
+        t_cm = timed(B, 2 * H, L, 128, False, sl)
+        t_64 = timed(B, H, L, 64, True, sl)
+        nbytes = decode_bytes(draw_seqlens(cfg, 0).tolist(), H, 128)
+        rows.append({"cell": f"B{B} ctx{L}", "bytes": nbytes, "parallax_us": t_plx,
+                     "softmax_io_us": t_io, "softmax_2h_us": t_cm, "parallax_d64_us": t_64,
+                     "io_ratio": round(t_io / t_plx, 3), "compute_ratio": round(t_cm / t_plx, 3),
+                     "d64_vs_softmax_d128": round(t_io / t_64, 3)})
+        print(json.dumps(rows[-1]), flush=True)
+    if out_md:
+        keys = ("io_ratio", "compute_ratio", "d64_vs_softmax_d128")
+        with open(out_md, "w") as fh:
+            fh.write("| cell (H16) | bytes | Parallax d128 us | softmax only, same cache us | "
+                     "softmax only, 2x heads us | Parallax d64 us | I/O-matched ratio | "
+                     "compute-matched ratio (2x heads) | compute-matched ratio (d64) |\n")
+            fh.write("|---|---|---|---|---|---|---|---|---|\n")
+            for r in rows:
+                fh.write(f"| {r['cell']} | {r['bytes'] / 1e6:.1f} MB | {r['parallax_us']} | "
+                         f"{r['softmax_io_us']} | {r['softmax_2h_us']} | {r['parallax_d64_us']} | "
+                         f"{r['io_ratio']} | {r['compute_ratio']} | {r['d64_vs_softmax_d128']} |\n")
+            for lab, sel in (("all 18 cells", rows),
+                             ("cells of 100 MB or more", [r for r in rows if r["bytes"] >= 1e8])):
+                fh.write(f"| min over {lab} | | | | | | " + " | ".join(
+                    str(min(r[k] for r in sel)) for k in keys) + " |\n")
+                fh.write(f"| max over {lab} | | | | | | " + " | ".join(
+                    str(max(r[k] for r in sel)) for k in keys) + " |\n")
+    return 0
+
+
 def gqa(out_md):
     """Decode with grouped query heads at a fixed cache (B=1, H_kv=16, 32768 rows, d=128):
     G = 1, 2, 4, 8 query heads per cache head, against the multi-head decode of the same
@@ -995,6 +1075,9 @@ def main():
     ap.add_argument("--backward", metavar="OUT_MD", nargs="?", const="",
                     help="time the prefill forward with statistics and its backward instead "
                          "of the step")
+    ap.add_argument("--compare-grid", metavar="OUT_MD", nargs="?", const="",
+                    help="the softmax-only comparisons on every decode grid cell instead of "
+                         "the step")
     ap.add_argument("--compare", metavar="OUT_MD", nargs="?", const="",
                     help="time Parallax against softmax-only attention (I/O- and "
                          "compute-matched) instead of the step")
@@ -1014,6 +1097,8 @@ def main():
         return sweep(args.sweep)
     if args.compare is not None:
         return compare(args.compare)
+    if args.compare_grid is not None:
+        return compare_grid(args.compare_grid)
     if args.probe_producer is not None:
         return probe_producer(args.probe_producer)
     if args.gqa is not None:

@@ -55,6 +55,7 @@ def check_grad(got, ref, what: str = "") -> dict:
     m = metrics(got, ref)
     assert m["finite"], f"{what}: non-finite output"
     scale = max(1.0, float(np.abs(to_f64(ref)).max())) if to_f64(ref).size else 1.0
+    m["excess_over_scale"] = m["excess_over_half_ulp"] / scale
     assert m["excess_over_half_ulp"] <= BF16_ABS * scale, f"{what}: {m}"
     assert m["rel_l2"] <= BF16_REL_L2, f"{what}: {m}"
     return m

@@ -57,7 +57,8 @@ def _check_grads(grads, x, what, sel=(slice(None), slice(None))):
             assert np.abs(to_f64(g[sel])).max() <= BF16_ABS, f"{what} {name}"
             continue
         out[name] = check_grad(g[sel], r, f"{what} {name}")
-    _say(what, {k: (round(m["max_abs"], 5), round(m["rel_l2"], 6)) for k, m in out.items()})
+    _say(what, {k: (round(m["max_abs"], 5), round(m["rel_l2"], 6),
+                    round(m["excess_over_scale"], 6)) for k, m in out.items()})
 
 
 @pytest.mark.parametrize("B,H,T,rho", [(1, 2, 1, "scaled"), (1, 2, 64, "scaled"),

@@ -19,8 +19,9 @@ fraction: the same prefill with split weights (`prefill_split_weights`), the lon
 B1 H32 T32768 (`prefill_long`) and every decode grid cell that moves at least 100 MB
 (`decode_grid`, cold caches, each beside the time a plain streaming-read kernel takes for
 the same bytes in the same run).
-`roofline` describes the dominant kernel (the prefill), timed with HIP events on the
-stream it runs on; `traffic` comes from committed rocprofv3 counter summaries and is
+`roofline` describes the dominant kernel (the prefill): its average launch duration is
+timed with HIP events on the stream it runs on around 20 back-to-back launches after the
+timed steps (an event pair around every launch adds its own dispatch gap, ~5 us); `traffic` comes from committed rocprofv3 counter summaries and is
 null when the kernel source changed since they were taken. `cpu_baseline` times the
 fp64 oracle's streaming form on the host cores.
 
@@ -1060,7 +1061,10 @@ def main():
     ap.add_argument("--copies", type=int, default=4, help="decode cache copies to rotate")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-grid", action="store_true",
-                    help="leave the decode grid cells out of the line (profiling runs)")
+                    help="leave the decode grid cells out of the line")
+    ap.add_argument("--step-only", action="store_true",
+                    help="time the step only, without the sub-records (profiling runs: the "
+                         "long prefill runs the same kernel instance as the step)")
     ap.add_argument("--calibrate-copy", action="store_true")
     ap.add_argument("--summarize-counters", nargs="+",
                     metavar="CSV_GLOB", help="FETCH_SIZE run, WRITE_SIZE run[, MFMA run]")
@@ -1181,25 +1185,49 @@ def main():
     avg = lambda xs: sum(xs) / len(xs)  # noqa: E731
     pct = lambda xs, p: xs[min(len(xs) - 1, int(p * len(xs)))]  # noqa: E731
 
+    # Average launch duration of each kernel: NB launches back to back between two events on
+    # the launch stream (the per-step event pairs above add the events' own dispatch gaps to
+    # every launch). The rooflines use these.
+    NB = 20
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record(stream)
+    for _ in range(NB):
+        run_prefill()
+    e1.record(stream)
+    torch.cuda.synchronize()
+    pre_b2b_us = e0.elapsed_time(e1) * 1e3 / NB
+    e0.record(stream)
+    for i in range(NB):
+        run_decode(i)
+    e1.record(stream)
+    torch.cuda.synchronize()
+    dec_b2b_us = e0.elapsed_time(e1) * 1e3 / NB
+
     flops = prefill_flops(pcfg.B, pcfg.H, pcfg.T, pcfg.d)
     pre_avg_s = avg(pre_ms) / 1e3
     tflops = flops / pre_avg_s / 1e12
     dbytes = decode_bytes(dx["seqlens"].tolist(), dcfg.H, dcfg.d)
     dec_avg_s = avg(dec_ms) / 1e3
     dec_gbps = dbytes / dec_avg_s / 1e9
+    tflops_b2b = flops / (pre_b2b_us * 1e-6) / 1e12
+    dec_gbps_b2b = dbytes / (dec_b2b_us * 1e-6) / 1e9
 
     traffic = committed_traffic()
     read_gbps = streaming_read_gbps(torch, dev, stream)
     # Sub-records after the timed steps: the split-weights prefill, the long prefill and the
     # bandwidth-dominated decode grid cells (each beside its streaming-read floor).
-    split_rec = prefill_split_record(torch, plx, stream, pd, pcfg, avg(pre_ms) * 1e3)
-    print(json.dumps(split_rec), file=sys.stderr, flush=True)
     n_copies = len(caches)
-    del caches
-    torch.cuda.empty_cache()
-    long_rec = prefill_long_record(torch, plx, dev, stream)
-    print(json.dumps(long_rec), file=sys.stderr, flush=True)
-    grid_recs = [] if args.no_grid else decode_grid_records(torch, plx, dev, stream)
+    split_rec = long_rec = None
+    grid_recs = []
+    if not args.step_only:
+        split_rec = prefill_split_record(torch, plx, stream, pd, pcfg, avg(pre_ms) * 1e3)
+        print(json.dumps(split_rec), file=sys.stderr, flush=True)
+        del caches
+        torch.cuda.empty_cache()
+        long_rec = prefill_long_record(torch, plx, dev, stream)
+        print(json.dumps(long_rec), file=sys.stderr, flush=True)
+        if not args.no_grid:
+            grid_recs = decode_grid_records(torch, plx, dev, stream)
     result = {
         "metric": "decode tokens/s & HBM GB/s frac; prefill TFLOP/s & MFMA util (B,H,T,d=128)",
         "value": round(tflops, 2),
@@ -1225,7 +1253,8 @@ def main():
                     "us_p90": round(pct(pre_ms, 0.9) * 1e3, 2),
                     "tflops": round(tflops, 2),
                     "mfma_frac": round(tflops / BF16_PEAK_TFLOPS, 4),
-                    "tokens_per_s": round(pcfg.B * pcfg.T / pre_avg_s, 1)},
+                    "tokens_per_s": round(pcfg.B * pcfg.T / pre_avg_s, 1),
+                    "us_back_to_back": round(pre_b2b_us, 2)},
         "decode": {"us_avg": round(avg(dec_ms) * 1e3, 2),
                    "us_p10": round(pct(dec_ms, 0.1) * 1e3, 2),
                    "us_p90": round(pct(dec_ms, 0.9) * 1e3, 2),
@@ -1233,18 +1262,20 @@ def main():
                    "hbm_gbps": round(dec_gbps, 1),
                    "hbm_frac": round(dec_gbps / HBM_PEAK_GBPS, 4),
                    "frac_of_torch_rowsum_read": round(dec_gbps / read_gbps, 4),
-                   "bytes": dbytes},
-        "roofline": {"bound": "mfma", "achieved": round(tflops, 2), "peak": BF16_PEAK_TFLOPS,
-                     "unit": "TFLOP/s", "frac": round(tflops / BF16_PEAK_TFLOPS, 4),
+                   "bytes": dbytes,
+                   "us_back_to_back": round(dec_b2b_us, 2)},
+        "roofline": {"bound": "mfma", "achieved": round(tflops_b2b, 2), "peak": BF16_PEAK_TFLOPS,
+                     "unit": "TFLOP/s", "frac": round(tflops_b2b / BF16_PEAK_TFLOPS, 4),
                      "traffic": traffic, "kernel": PREFILL_KERNEL,
-                     "work_per_launch": flops, "counters": counter_summary(flops, pre_avg_s)},
-        "roofline_decode": {"bound": "hbm", "achieved": round(dec_gbps, 1),
+                     "work_per_launch": flops, "launch_us": round(pre_b2b_us, 2),
+                     "counters": counter_summary(flops, pre_b2b_us * 1e-6)},
+        "roofline_decode": {"bound": "hbm", "achieved": round(dec_gbps_b2b, 1),
                             "peak": HBM_PEAK_GBPS, "unit": "GB/s",
-                            "frac": round(dec_gbps / HBM_PEAK_GBPS, 4),
+                            "frac": round(dec_gbps_b2b / HBM_PEAK_GBPS, 4),
                             "traffic": committed_decode_traffic(),
-                            "work_per_launch": dbytes},
+                            "work_per_launch": dbytes, "launch_us": round(dec_b2b_us, 2)},
         "prefill_split_weights": split_rec,
-        "prefill_long": dict(long_rec, roofline={
+        "prefill_long": None if long_rec is None else dict(long_rec, roofline={
             "bound": "mfma", "achieved": long_rec["tflops"], "peak": BF16_PEAK_TFLOPS,
             "unit": "TFLOP/s", "frac": long_rec["mfma_frac"], "traffic": None,
             "work_per_launch": long_rec["flops"]}),

@@ -48,15 +48,21 @@ def check_bf16(got, ref, what: str = "") -> dict:
     return m
 
 
+GRAD_REL = 6e-3  # elementwise gradient bar, relative to the tensor's scale
+
+
 def check_grad(got, ref, what: str = "") -> dict:
-    """Gradients of the bf16 backward: rel-L2 <= 5e-3 and |g - r| <= ulp(r)/2 + 1e-2 max(1,
-    max |r|) (the forward's elementwise bar taken relative to the tensor's scale: every error
-    source of the backward is relative, and gradients reach ~40)."""
+    """Gradients of the bf16 backward: rel-L2 <= 5e-3 and |g - r| <= ulp(r)/2 + GRAD_REL max(1,
+    max |r|). Every error source of the backward is relative (gradients reach ~40), so the
+    elementwise bar is taken relative to the tensor's scale. GRAD_REL = 6e-3 is 1.5x the worst
+    error an fp64 emulation of the backward kernels' roundings (backward_rounding_emulation)
+    gives on the test inputs (4.1e-3 of the scale over 17 workloads); the emulated roundings
+    themselves pass it (tests/test_parity_bars.py)."""
     m = metrics(got, ref)
     assert m["finite"], f"{what}: non-finite output"
     scale = max(1.0, float(np.abs(to_f64(ref)).max())) if to_f64(ref).size else 1.0
     m["excess_over_scale"] = m["excess_over_half_ulp"] / scale
-    assert m["excess_over_half_ulp"] <= BF16_ABS * scale, f"{what}: {m}"
+    assert m["excess_over_half_ulp"] <= GRAD_REL * scale, f"{what}: {m}"
     assert m["rel_l2"] <= BF16_REL_L2, f"{what}: {m}"
     return m
 
@@ -120,3 +126,45 @@ def sample_rows(B: int, H: int, T: int, n_random: int = 64, seed: int = 0) -> np
                                    rng.choice(per_head, 28, replace=False)])
         rows.append(bh * T + np.unique(np.concatenate([pick, rng.integers(0, T, n_random)])))
     return np.concatenate(rows)
+
+
+def _bf16(x: np.ndarray) -> np.ndarray:
+    """Round float64 values to bf16 (through fp32, RNE, as the kernels' conversions)."""
+    return torch.from_numpy(np.ascontiguousarray(x)).to(torch.float32).to(
+        torch.bfloat16).to(torch.float64).numpy()
+
+
+def backward_rounding_emulation(q, k, v, rho, scale, do):
+    """The causal prefill backward in fp64 with the backward kernels' rounding points, for
+    setting the gradient tolerance (not a reference: the reference is oracle.prefill_backward).
+
+    Rounded as in the kernels: the forward's saved vbar and o are bf16, and G_i = <dO_i,
+    vbar_i>, D_i = <dO_i, o_i> + tbar_i G_i are formed from them; the pair quantities
+    s_ij = p_ij (1 - t_ij + tbar_i), scale * da_ij and dt_ij are rounded to bf16 before the
+    products dV = s^T dO, dQ = (scale da) K, dK = (scale da)^T Q + dt^T R, dR = dt K. Everything
+    else (p from the saved lse, the sums) is exact here. Returns (dq, dk, dv, drho)."""
+    q, k, v, rho, do = (to_f64(a) for a in (q, k, v, rho, do))
+    B, H, T, _ = q.shape
+    out = [np.zeros_like(q), np.zeros_like(k), np.zeros_like(v), np.zeros_like(rho)]
+    visible = np.tril(np.ones((T, T), dtype=bool))
+    for b in range(B):
+        for h in range(H):
+            Q, K, V, R, dO = q[b, h], k[b, h], v[b, h], rho[b, h], do[b, h]
+            a = np.where(visible, scale * (Q @ K.T), -np.inf)
+            p = np.exp(a - a.max(axis=1, keepdims=True))
+            p /= p.sum(axis=1, keepdims=True)
+            t = np.where(visible, R @ K.T, 0.0)
+            tbar = (p * t).sum(axis=1, keepdims=True)
+            s = p * (1.0 - t + tbar)
+            vbar, o = _bf16(p @ V), _bf16(s @ V)
+            g = dO @ V.T
+            G = (dO * vbar).sum(axis=1, keepdims=True)
+            D = (dO * o).sum(axis=1, keepdims=True) + tbar * G
+            sb = _bf16(s)
+            dab = _bf16(scale * p * ((1.0 - t + tbar) * g + t * G - D))
+            dtb = _bf16(p * (G - g))
+            out[2][b, h] = sb.T @ dO
+            out[0][b, h] = dab @ K
+            out[1][b, h] = dab.T @ Q + dtb.T @ R
+            out[3][b, h] = dtb @ K
+    return tuple(out)

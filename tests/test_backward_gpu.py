@@ -2,14 +2,13 @@
 the fp64 oracle (oracle.prefill_stats, oracle.prefill_backward) on the same bf16 inputs.
 
 Tolerances. vbar uses the bf16 bar of the forward (parity.check_bf16: elementwise 1e-2 beyond
-half an output ulp, rel-L2 <= 5e-3). Gradients use the same two numbers with the elementwise
-one taken relative to the tensor's scale: |g - r| <= ulp(r)/2 + 1e-2 max(1, max |r|) and
-rel-L2 <= 5e-3. The forward's bar is for outputs of unit scale; gradients reach ~40 (drho sums
-dt_ij k_j with g_ij ~ N(0, d)), and every error source of the backward is relative: the pair
-quantities s, scale * da and dt are rounded to bf16 (2^-9) before their products, and G and D
-are formed from the forward's bf16 vbar and o (each element within 2^-9). Emulating those
-roundings in fp64 gives rel-L2 ~3e-3 and elementwise errors ~1e-3 of the tensor's largest
-value. A gradient that is exactly zero (dq, dk and drho with a single key) must be within 1e-2
+half an output ulp, rel-L2 <= 5e-3). Gradients: |g - r| <= ulp(r)/2 + 6e-3 max(1, max |r|)
+and rel-L2 <= 5e-3 (parity.check_grad). Gradients reach ~40 (drho sums dt_ij k_j with
+g_ij ~ N(0, d)) and every error source of the backward is relative: the pair quantities s,
+scale * da and dt are rounded to bf16 (2^-9) before their products, and G and D are formed
+from the forward's bf16 vbar and o. An fp64 emulation of exactly those roundings
+(parity.backward_rounding_emulation) gives elementwise errors of 1.4e-3 to 4.1e-3 of each
+tensor's largest value on these workloads; the bar is 1.5x the worst of them. A gradient that is exactly zero (dq, dk and drho with a single key) must be within 1e-2
 absolute. lse and tbar come from fp32 sums of the unrounded weights in the forward: within
 1e-3 absolute (fp32 sums over <= 2^15 terms and the hardware exp2, ~1e-5 in practice).
 """

@@ -42,11 +42,17 @@
 
 #include "plx_device.hpp"
 #include "plx_kernels.hpp"
+#include "prefill_sched.hpp"
 
 namespace plx {
 namespace {
 
-constexpr int BR = 128;  // query rows per work item
+using prefill::BR;
+using prefill::Item;
+using prefill::item_at;
+using prefill::item_position;
+using prefill::krow;
+using prefill::krow_inv;
 constexpr int NT = 512;  // threads per workgroup (8 waves x 16 query rows)
 constexpr int NBUF = 4;  // stream tiles s + 2 is staged while s is processed
 
@@ -83,40 +89,8 @@ struct Geo {
 };
 constexpr float kLazyTau = 8.0f;  // log2 headroom before the running max moves
 
-// K row of key k of a tile: inside each 32-key group, key 8 q + 4 b + i goes to row
-// 16 b + 4 q + i, so that the score blocks b = 0, 1 give each lane the 8 consecutive keys
-// 8 q .. 8 q + 7 that the value product's operand wants.
-__device__ __forceinline__ int krow(int k) {
-    return (k & ~31) | (((k >> 2) & 1) << 4) | (((k >> 3) & 3) << 2) | (k & 3);
-}
-
-// Key stored at LDS row r (the inverse of krow).
-__device__ __forceinline__ int krow_inv(int r) {
-    return (r & ~31) | (((r >> 2) & 3) << 3) | (((r >> 4) & 1) << 2) | (r & 3);
-}
-
 __device__ __forceinline__ f32x4 mfma16(bf16x8 a, bf16x8 b, f32x4 c) {
     return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
-}
-
-__device__ __forceinline__ int item_position(int kk, int j, int Wc) {
-    return kk * Wc + ((kk & 1) ? Wc - 1 - j : j);
-}
-
-struct Item {
-    int bh, q0, ntiles, nfull;
-};
-
-template <int BC>
-__device__ __forceinline__ Item item_at(int pos, int cls, int ncls, int nbh_c, int nqb, int T) {
-    Item it;
-    const int qb = nqb - 1 - pos / nbh_c;
-    it.bh = cls + ncls * (pos % nbh_c);
-    it.q0 = qb * BR;
-    const int kend = min(it.q0 + BR, T);
-    it.ntiles = (kend + BC - 1) / BC;
-    it.nfull = min(it.ntiles, it.q0 / BC);
-    return it;
 }
 
 __device__ __forceinline__ float max_across_row_groups(float x) {

@@ -1,8 +1,10 @@
-// stream_read.hip -- a read-only HBM streaming kernel for the benchmark (not part of the
-// attention library): it reads two device ranges once with non-temporal 16-byte loads, the
-// access the decode kernels make to a KV cache, and does nothing else. Its time for a given
-// byte count is the floor a decode call of the same bytes is measured against (launch, ramp
-// and the board's sustained read rate included).
+// stream_read.hip -- plain HBM streaming kernels for the benchmark (not part of the attention
+// library). The read kernel reads two device ranges once with non-temporal 16-byte loads, the
+// access the decode kernels make to a KV cache, and does nothing else; the write kernel writes
+// one range once with 16-byte stores, the access of a kernel whose output dominates its
+// traffic (the probe producer). Their times for a given byte count are the floors the
+// attention kernels of the same bytes are measured against (launch, ramp and the board's
+// sustained rate included).
 #include <hip/hip_runtime.h>
 #include <stddef.h>
 #include <stdint.h>
@@ -41,7 +43,30 @@ __global__ __launch_bounds__(256) void stream_read_kernel(const u32x4* __restric
     if (x == 0x9E3779B9u) sink[blockIdx.x & 1023] = x;
 }
 
+// Workgroup w writes tiles w, w + grid, ... of 32 KB (8 stores of 16 bytes per thread, each
+// store instruction covering 4 KB contiguously); the value written is the tile index.
+__global__ __launch_bounds__(256) void stream_write_kernel(u32x4* __restrict__ a, size_t n) {
+    constexpr size_t tile = (size_t)kUnroll * 256;
+    for (size_t t0 = (size_t)blockIdx.x * tile; t0 < n; t0 += (size_t)gridDim.x * tile) {
+        const uint32_t v = (uint32_t)(t0 / tile);
+#pragma unroll
+        for (int j = 0; j < kUnroll; ++j) {
+            const size_t i = t0 + (size_t)j * 256 + threadIdx.x;
+            if (i < n) a[i] = u32x4{v, v, v, v};
+        }
+    }
+}
+
 }  // namespace
+
+// Writes bytes (a multiple of 16) at a (16-byte aligned) with `grid` workgroups of 256 threads
+// on `stream`. Returns 0, or the HIP error code of the launch.
+extern "C" int plx_bench_stream_write(void* a, size_t bytes, int grid, void* stream) {
+    if (grid < 1 || bytes % 16 != 0) return (int)hipErrorInvalidValue;
+    hipLaunchKernelGGL(stream_write_kernel, dim3(grid), dim3(256), 0, (hipStream_t)stream,
+                       (u32x4*)a, bytes / 16);
+    return (int)hipGetLastError();
+}
 
 // Reads bytes_a bytes at a and bytes_b bytes at b (multiples of 16, 16-byte aligned) with
 // `grid` workgroups of 256 threads on `stream`; sink holds at least 1024 words. Returns 0, or

@@ -8,11 +8,11 @@
 // appears in the review's mechanism-analysis paragraph; here it is a per-head multiplier, the
 // sigmoid left to the caller.
 //
-// One workgroup (4 waves) computes 128 tokens x the 128 dims of one head as
+// One workgroup (4 waves) computes 64 UG tokens x the 128 dims of one head as
 // Y^T = W_R X^T on v_mfma_f32_16x16x32_bf16: per 32-wide K step the workgroup stages the
 // head's W_R slice (128 rows x 64 bytes, rows padded to 80 bytes so the operand reads are
 // free of bank conflicts) in LDS, double-buffered, and every wave reads its A operand blocks
-// there; the B operand is two 16-token groups of x rows read straight from global memory.
+// there; the B operand is UG 16-token groups of x rows read straight from global memory.
 // Each lane then holds 32 dims (4 consecutive dims of each 16-dim block) of one token per
 // group, so the RMSNorm sum of squares needs only 4 lanes, the RoPE pairs (i, i + 64) sit in
 // the same lane, and rho is written with 8-byte row pieces in the [B, H, T, d] layout the
@@ -27,14 +27,18 @@ namespace {
 
 constexpr int D = 128;
 constexpr int NT = 256;
-constexpr int TOK = 128;     // tokens per workgroup (32 per wave, two groups of 16)
 constexpr int WROW = 40;     // LDS row stride of the W_R slice (bf16): 80 bytes
 constexpr int WBUF = D * WROW;
+constexpr int kProbeNarrowC = 64;  // inputs up to this width take one token group per wave
 
 __device__ __forceinline__ f32x4 mfma16(bf16x8 a, bf16x8 b, f32x4 c) {
     return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
 }
 
+// UG groups of 16 tokens per wave, 64 UG tokens per workgroup: UG = 2 lets every W_R operand
+// read feed two products (wide inputs, matrix-bound); UG = 1 halves the accumulators so that
+// more waves are resident (narrow inputs, where the call is bound by latency and the writes).
+template <int UG>
 __global__ __launch_bounds__(NT) void probe_bf16_d128_kernel(
     const __bf16* __restrict__ x, const __bf16* __restrict__ wr, const float* __restrict__ gamma,
     const float* __restrict__ gate, const int32_t* __restrict__ positions, __bf16* __restrict__ rho,
@@ -45,14 +49,15 @@ __global__ __launch_bounds__(NT) void probe_bf16_d128_kernel(
     const int tid = threadIdx.x, lane = tid & 63;
     const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int c16 = lane & 15, g = lane >> 4;
+    constexpr int TOK = 64 * UG;  // tokens per workgroup
     const int h = blockIdx.y;
     const long long N = (long long)B * T;
-    long long tok[2];
-    bool tok_ok[2];
-    uint32_t xrow[2];
+    long long tok[UG];
+    bool tok_ok[UG];
+    uint32_t xrow[UG];
 #pragma unroll
-    for (int u = 0; u < 2; ++u) {
-        tok[u] = (long long)blockIdx.x * TOK + 32 * w + 16 * u + c16;
+    for (int u = 0; u < UG; ++u) {
+        tok[u] = (long long)blockIdx.x * TOK + 16 * UG * w + 16 * u + c16;
         tok_ok[u] = tok[u] < N;
         xrow[u] = tok_ok[u] ? (uint32_t)(tok[u] * C) * 2u : OOB;
     }
@@ -72,9 +77,32 @@ __global__ __launch_bounds__(NT) void probe_bf16_d128_kernel(
         for (int r = 0; r < 2; ++r) *(u32x4*)&wl[buf][(sr + 64 * r) * WROW + 8 * sp] = st[r];
     };
 
-    f32x4 acc[2][8];
+    // Everything the workgroup reads from memory besides the later K steps is requested up
+    // front, so that the W_R slice, the first x rows, gamma, the gate and the positions arrive
+    // in one round trip instead of one after another.
+    auto load_x = [&](int k0, bf16x8 (&bx)[UG]) {
+        const int kc = k0 + 8 * g;
 #pragma unroll
-    for (int u = 0; u < 2; ++u)
+        for (int u = 0; u < UG; ++u)
+            bx[u] = as_bf16x8(load16(rx, tok_ok[u] && kc < C ? xrow[u] + 2u * kc : OOB));
+    };
+    bf16x8 bx[UG];
+    load_x(0, bx);
+    f32x4 gmv[8];
+#pragma unroll
+    for (int j = 0; j < 8; ++j)
+        gmv[j] = gamma ? *(const f32x4*)(gamma + 16 * j + 4 * g) : f32x4{1.f, 1.f, 1.f, 1.f};
+    const float gh = gate ? gate[h] : 1.f;
+    int pos0[UG];
+#pragma unroll
+    for (int u = 0; u < UG; ++u) {
+        const long long tk = tok_ok[u] ? tok[u] : 0;
+        pos0[u] = positions ? positions[(int)(tk / T)] : 0;
+    }
+
+    f32x4 acc[UG][8];
+#pragma unroll
+    for (int u = 0; u < UG; ++u)
 #pragma unroll
         for (int j = 0; j < 8; ++j) acc[u][j] = f32x4{};
     u32x4 st[2];
@@ -85,16 +113,12 @@ __global__ __launch_bounds__(NT) void probe_bf16_d128_kernel(
     for (int k0 = 0; k0 < C; k0 += 32) {
         const bool more = k0 + 32 < C;
         if (more) stage(k0 + 32, st);
-        const int kc = k0 + 8 * g;
-        bf16x8 bx[2];
-#pragma unroll
-        for (int u = 0; u < 2; ++u)
-            bx[u] = as_bf16x8(load16(rx, tok_ok[u] && kc < C ? xrow[u] + 2u * kc : OOB));
+        if (k0 > 0) load_x(k0, bx);
 #pragma unroll
         for (int j = 0; j < 8; ++j) {
             const bf16x8 a = *(const bf16x8*)&wl[buf][(16 * j + c16) * WROW + 8 * g];
-            acc[0][j] = mfma16(a, bx[0], acc[0][j]);
-            acc[1][j] = mfma16(a, bx[1], acc[1][j]);
+#pragma unroll
+            for (int u = 0; u < UG; ++u) acc[u][j] = mfma16(a, bx[u], acc[u][j]);
         }
         if (more) put(buf ^ 1, st);
         __syncthreads();
@@ -102,13 +126,6 @@ __global__ __launch_bounds__(NT) void probe_bf16_d128_kernel(
     }
 
     // acc[u][j][i]: dim 16 j + 4 g + i of token tok[u].
-    float gm[8][4];
-#pragma unroll
-    for (int j = 0; j < 8; ++j) {
-        const f32x4 v = gamma ? *(const f32x4*)(gamma + 16 * j + 4 * g) : f32x4{1.f, 1.f, 1.f, 1.f};
-#pragma unroll
-        for (int i = 0; i < 4; ++i) gm[j][i] = v[i];
-    }
     // Turns per position of the 16 rotation pairs this lane holds: base^(-2 di / d) / (2 pi).
     float turns[4][4];
 #pragma unroll
@@ -117,9 +134,8 @@ __global__ __launch_bounds__(NT) void probe_bf16_d128_kernel(
         for (int i = 0; i < 4; ++i)
             turns[j][i] = exp2f(-(2.f * (16 * j + 4 * g + i) / D) * log2_base) *
                           0.15915494309189535f;
-    const float gh = gate ? gate[h] : 1.f;
 #pragma unroll
-    for (int u = 0; u < 2; ++u) {
+    for (int u = 0; u < UG; ++u) {
         float ss = 0.f;
 #pragma unroll
         for (int j = 0; j < 8; ++j)
@@ -134,9 +150,9 @@ __global__ __launch_bounds__(NT) void probe_bf16_d128_kernel(
 #pragma unroll
         for (int j = 0; j < 8; ++j)
 #pragma unroll
-            for (int i = 0; i < 4; ++i) n[j][i] = gm[j][i] * acc[u][j][i] * inv;
+            for (int i = 0; i < 4; ++i) n[j][i] = gmv[j][i] * acc[u][j][i] * inv;
         if (log2_base > 0.f) {
-            const float pos = (float)((positions ? positions[b] : 0) + t);
+            const float pos = (float)(pos0[u] + t);
 #pragma unroll
             for (int j = 0; j < 4; ++j)
 #pragma unroll
@@ -164,7 +180,7 @@ __global__ __launch_bounds__(NT) void probe_bf16_d128_kernel(
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
             const int row = 4 * r + g;
-            const long long tr = (long long)blockIdx.x * TOK + 32 * w + 16 * u + row;
+            const long long tr = (long long)blockIdx.x * TOK + 16 * UG * w + 16 * u + row;
             if (tr < N) {
                 const int br = (int)(tr / T), trr = (int)(tr - (long long)br * T);
                 *(u32x4*)(rho + (((size_t)br * H + h) * T + trr) * D + 8 * c16) =
@@ -181,13 +197,19 @@ __global__ __launch_bounds__(NT) void probe_bf16_d128_kernel(
 
 hipError_t launch_probe_bf16_d128(const ProbeArgs& a, hipStream_t stream) {
     const long long N = (long long)a.B * a.T;
-    const long long nblk = (N + TOK - 1) / TOK;
-    if (nblk > 0x7fffffffLL) return hipErrorInvalidConfiguration;
-    hipLaunchKernelGGL(probe_bf16_d128_kernel, dim3((unsigned)nblk, a.H), dim3(NT), 0, stream,
-                       (const __bf16*)a.x, (const __bf16*)a.w_r, a.gamma, a.gate, a.positions,
-                       (__bf16*)a.rho, a.B, a.T, a.C, a.H, a.eps,
-                       a.rope_base > 0.f ? log2f(a.rope_base) : 0.f);
-    return hipGetLastError();
+    const float lb = a.rope_base > 0.f ? log2f(a.rope_base) : 0.f;
+    auto go = [&](auto kernel, int tok) {
+        const long long nblk = (N + tok - 1) / tok;
+        if (nblk > 0x7fffffffLL) return hipErrorInvalidConfiguration;
+        hipLaunchKernelGGL(kernel, dim3((unsigned)nblk, a.H), dim3(NT), 0, stream,
+                           (const __bf16*)a.x, (const __bf16*)a.w_r, a.gamma, a.gate,
+                           a.positions, (__bf16*)a.rho, a.B, a.T, a.C, a.H, a.eps, lb);
+        return hipGetLastError();
+    };
+    // Narrow inputs (one K step or two): one token group per wave. Measured at 4 x 2048 tokens,
+    // H = 16: see the probe producer's profile.
+    if (a.C <= kProbeNarrowC) return go(probe_bf16_d128_kernel<1>, 64);
+    return go(probe_bf16_d128_kernel<2>, 128);
 }
 
 }  // namespace plx

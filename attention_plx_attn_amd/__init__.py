@@ -10,6 +10,7 @@ Python entry points over the C ABI of ``libplx_attn.so`` (include/plx_attn.h):
   callers that cannot allocate (split records in the library's fixed per-GPU scratch);
 * ``decode_gqa`` / ``decode_gqa_plan`` -- decode with grouped query heads (H_q = G H_kv);
 * ``decode_paged`` -- decode over a paged KV cache (block pool + block table);
+* ``decode_paged_gqa`` -- the same with grouped query heads;
 * ``prefill_fwd`` / ``prefill_bwd`` -- the prefill with saved statistics and its backward
   (gradients of q, k, v and rho);
 * ``probe(x, w_r, H, ...)`` -- the probe producer rho = gate * RoPE(RMSNorm(x W_R^T)).
@@ -25,6 +26,7 @@ from ._lib import (  # noqa: F401
     decode_noalloc,
     decode_num_splits,
     decode_paged,
+    decode_paged_gqa,
     decode_workspace_size,
     header_functions,
     load,

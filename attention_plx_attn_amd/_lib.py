@@ -67,6 +67,9 @@ def load() -> ctypes.CDLL:
     lib.plx_attn_decode_paged.argtypes = ([ctypes.c_int] + [i32] * 7 + [vp] * 7 +
                                           [f32, i32, vp, ctypes.c_size_t, vp])
     lib.plx_attn_decode_paged.restype = ctypes.c_int
+    lib.plx_attn_decode_paged_gqa.argtypes = ([ctypes.c_int] + [i32] * 8 + [vp] * 7 +
+                                              [f32, i32, vp, ctypes.c_size_t, vp])
+    lib.plx_attn_decode_paged_gqa.restype = ctypes.c_int
     lib.plx_attn_probe.argtypes = [ctypes.c_int] + [i32] * 5 + [vp] * 5 + [f32, f32, vp, vp]
     lib.plx_attn_probe.restype = ctypes.c_int
     lib.plx_attn_prefill_fwd.argtypes = [ctypes.c_int] + [i32] * 5 + [vp] * 7 + [f32, vp]
@@ -457,4 +460,51 @@ def decode_paged(q: torch.Tensor, rho: Optional[torch.Tensor], k_pool: torch.Ten
                                    _stream_handle(stream, q.device))
     if rc != 0:
         raise PlxError(rc, "plx_attn_decode_paged")
+    return out
+
+
+def decode_paged_gqa(q: torch.Tensor, rho: Optional[torch.Tensor], k_pool: torch.Tensor,
+                     v_pool: torch.Tensor, block_table: torch.Tensor, seqlens: torch.Tensor,
+                     scale: Optional[float] = None, num_splits: int = 0,
+                     out: Optional[torch.Tensor] = None,
+                     workspace: Optional[torch.Tensor] = None,
+                     stream: Optional[torch.cuda.Stream] = None) -> torch.Tensor:
+    """Paged decode with grouped query heads: q, rho [B,H_q,d]; pools
+    [num_blocks,H_kv,block_size,d] with H_q / H_kv in {1, 2, 4, 8}; block_table int32
+    [B, max_blocks]; seqlens int32 [B]. Query head h reads cache head h // (H_q / H_kv)."""
+    lib = load()
+    if q.dim() != 3 or k_pool.dim() != 4:
+        raise ValueError("q must be [B, H_q, d], the pools [num_blocks, H_kv, block_size, d]")
+    B, Hq, dqk = q.shape
+    nblk, Hkv, bs, dv = v_pool.shape
+    max_blocks = block_table.shape[1]
+    _check(q, "q", None, None)
+    if rho is not None:
+        _check(rho, "rho", q.dtype, q.device, (B, Hq, dqk))
+    _check(k_pool, "k_pool", q.dtype, q.device, (nblk, Hkv, bs, dqk))
+    _check(v_pool, "v_pool", q.dtype, q.device, (nblk, Hkv, bs, dv))
+    _check(block_table, "block_table", torch.int32, q.device, (B, max_blocks))
+    _check(seqlens, "seqlens", torch.int32, q.device, (B,))
+    if out is None:
+        out = torch.empty((B, Hq, dv), dtype=q.dtype, device=q.device)
+        _bind(stream, out)
+    _check(out, "out", q.dtype, q.device, (B, Hq, dv))
+    _, need = decode_gqa_plan(B, Hq, Hkv, max_blocks * bs, dv, num_splits)
+    if workspace is None and need > 0:
+        workspace = torch.empty(need // 4, dtype=torch.float32, device=q.device)
+        _bind(stream, workspace)
+    ws_ptr, ws_bytes = 0, 0
+    if workspace is not None:
+        _check(workspace, "workspace", None, q.device)
+        ws_ptr, ws_bytes = workspace.data_ptr(), workspace.numel() * workspace.element_size()
+    if scale is None:
+        scale = dqk ** -0.5
+    rc = lib.plx_attn_decode_paged_gqa(_dtype_code(q), B, Hq, Hkv, bs, max_blocks, nblk, dqk,
+                                       dv, q.data_ptr(), 0 if rho is None else rho.data_ptr(),
+                                       k_pool.data_ptr(), v_pool.data_ptr(),
+                                       block_table.data_ptr(), seqlens.data_ptr(),
+                                       out.data_ptr(), float(scale), int(num_splits), ws_ptr,
+                                       ws_bytes, _stream_handle(stream, q.device))
+    if rc != 0:
+        raise PlxError(rc, "plx_attn_decode_paged_gqa")
     return out

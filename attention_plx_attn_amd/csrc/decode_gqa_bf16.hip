@@ -21,7 +21,10 @@
 // loads in flight); each column keeps its own running max (lazy update by 2^8) and the fp32
 // sums l = sum w, beta = sum w t. The 4 wave states merge through LDS; with
 // one chunk per (b, h_kv) the kernel writes o, otherwise per-query-head partials (the record
-// of the split decode) that the split decode's combine kernel merges.
+// of the split decode) that the split decode's combine kernel merges. The PAGED instance reads
+// the cache from a pool of blocks through a per-sequence block table.
+#include <type_traits>
+
 #include "plx_device.hpp"
 #include "plx_kernels.hpp"
 
@@ -43,11 +46,17 @@ __device__ __forceinline__ f32x4 mfma16(bf16x8 a, bf16x8 b, f32x4 c) {
 // key of k-slot e of lane group g in a 32-key step
 __device__ __forceinline__ int slot_key(int g, int e) { return e < 4 ? 4 * g + e : 12 + 4 * g + e; }
 
-template <int G>
+// PAGED: the caches are pools of blocks [num_blocks, Hkv, 2^bs_log2, d] and table[b][i] names
+// the block of rows i 2^bs_log2 .. of sequence b (blocks of at least 32 rows, so a 32-row step
+// never crosses a block). Only blocks holding rows below the chunk end are looked up, one step
+// ahead of their loads; an entry outside [0, num_blocks) is never dereferenced and its steps
+// are skipped (its rows get no weight).
+template <int G, bool PAGED>
 __global__ __launch_bounds__(NT, 2) void decode_gqa_bf16_d128_kernel(
     const __bf16* __restrict__ q, const __bf16* __restrict__ rho, const __bf16* __restrict__ kc,
     const __bf16* __restrict__ vc, const int32_t* __restrict__ seqlens, __bf16* __restrict__ o,
-    float* __restrict__ ws, int Hkv, int L_max, int S, float c) {
+    float* __restrict__ ws, int Hkv, int L_max, int S, float c, const int32_t* __restrict__ table,
+    int max_blocks, int bs_log2, int num_blocks) {
     static_assert(G >= 1 && G <= 8, "up to 8 query heads per cache head");
     __shared__ __attribute__((aligned(16))) __bf16 vt[NW][D * VTS];            // 40 KB
     __shared__ __attribute__((aligned(16))) float st_m[NW][16], st_l[NW][16];  // per column
@@ -90,17 +99,45 @@ __global__ __launch_bounds__(NT, 2) void decode_gqa_bf16_d128_kernel(
         u32x4 k[2][4];
         u32x4 v[8];
     };
-    auto load = [&](int kb0, Frag& f) {
+    // Loads of the 32 rows from row r of the resources ck, cv.
+    auto load_rows = [&](__amdgpu_buffer_rsrc_t ck, __amdgpu_buffer_rsrc_t cv, int r, Frag& f) {
 #pragma unroll
         for (int t = 0; t < 2; ++t)
 #pragma unroll
             for (int st = 0; st < 4; ++st)
                 f.k[t][st] =
-                    load16_nt(rk, (uint32_t)(kb0 + 16 * t + col) * 256u + 64u * st + 16u * g);
+                    load16_nt(ck, (uint32_t)(r + 16 * t + col) * 256u + 64u * st + 16u * g);
 #pragma unroll
         for (int e = 0; e < 8; ++e)
-            f.v[e] = load16_nt(rv, (uint32_t)(kb0 + slot_key(g, e)) * 256u + 16u * col);
+            f.v[e] = load16_nt(cv, (uint32_t)(r + slot_key(g, e)) * 256u + 16u * col);
     };
+    // Block of the step at row kb0 (paged caches), or -1 past the chunk.
+    auto lookup = [&](int kb0) -> int {
+        if constexpr (!PAGED) return 0;
+        return kb0 < j1 ? __builtin_amdgcn_readfirstlane(
+                              table[(size_t)b * max_blocks + (kb0 >> bs_log2)])
+                        : -1;
+    };
+    // Loads of the step at row kb0: the contiguous cache, or the block that holds it.
+    auto load = [&](int kb0, int phys, Frag& f) {
+        if constexpr (!PAGED) {
+            load_rows(rk, rv, kb0, f);
+        } else {
+            // The resources span the step's block up to the block's or the chunk's end,
+            // whichever comes first.
+            uint32_t bytes = 0;
+            size_t base = 0;
+            const int rel = kb0 & ((1 << bs_log2) - 1);
+            if (kb0 < j1 && (unsigned)phys < (unsigned)num_blocks) {
+                base = (((size_t)phys * Hkv + hk) << bs_log2) * D;
+                bytes = (uint32_t)min(1 << bs_log2, j1 - (kb0 - rel)) * 256u;
+            }
+            load_rows(make_rsrc(kc + base, bytes), make_rsrc(vc + base, bytes), rel, f);
+        }
+    };
+    // Whether a step's rows take part: always, or when its block is in the pool (a step of 32
+    // rows lies in one block; a step with no weight leaves every sum unchanged).
+    auto in_pool = [&](int phys) { return !PAGED || (unsigned)phys < (unsigned)num_blocks; };
     __bf16* vtw = vt[w];
     auto consume = [&](int kb0, const Frag& f) {
         // V^T: lane (col, g) holds dims 8 col .. +7 of its 8 slot keys; row 8 col + d gets the
@@ -197,13 +234,19 @@ __global__ __launch_bounds__(NT, 2) void decode_gqa_bf16_d128_kernel(
     constexpr int STEP = KB * NW;
     Frag fa, fb;
     int kb0 = j0 + KB * w;
-    if (kb0 < j1) load(kb0, fa);
+    int pha = lookup(kb0);
+    if (kb0 < j1) load(kb0, pha, fa);
+    int ph1 = lookup(kb0 + STEP);
     for (; kb0 < j1; kb0 += 2 * STEP) {
-        load(kb0 + STEP, fb);
-        consume(kb0, fa);
+        load(kb0 + STEP, ph1, fb);
+        const int phb = ph1;
+        const int ph2 = lookup(kb0 + 2 * STEP);
+        if (in_pool(pha)) consume(kb0, fa);
         if (kb0 + STEP >= j1) break;
-        load(kb0 + 2 * STEP, fa);
-        consume(kb0 + STEP, fb);
+        load(kb0 + 2 * STEP, ph2, fa);
+        pha = ph2;
+        ph1 = lookup(kb0 + 3 * STEP);
+        if (in_pool(phb)) consume(kb0 + STEP, fb);
     }
 
     // Column totals of the weights (over the 4 row groups).
@@ -269,19 +312,26 @@ hipError_t launch_decode_gqa_bf16_d128(const DecodeArgs& a, int Hkv, hipStream_t
     const int G = a.H / Hkv;
     dim3 grid(a.splits, Hkv, a.B);
     const float c = a.scale * kLog2e;
-#define PLX_GQA_LAUNCH(GG)                                                                  \
-    hipLaunchKernelGGL(decode_gqa_bf16_d128_kernel<GG>, grid, dim3(NT), 0, stream,          \
-                       (const __bf16*)a.q, (const __bf16*)a.rho, (const __bf16*)a.k,        \
-                       (const __bf16*)a.v, a.seqlens, (__bf16*)a.o, a.ws, Hkv, a.L_max,     \
-                       a.splits, c)
+    auto go = [&](auto kernel) {
+        hipLaunchKernelGGL(kernel, grid, dim3(NT), 0, stream, (const __bf16*)a.q,
+                           (const __bf16*)a.rho, (const __bf16*)a.k, (const __bf16*)a.v,
+                           a.seqlens, (__bf16*)a.o, a.ws, Hkv, a.L_max, a.splits, c, a.table,
+                           a.max_blocks, a.block_log2, a.num_blocks);
+    };
+    auto pick = [&](auto g_tag) {
+        constexpr int GG = decltype(g_tag)::value;
+        if (a.table)
+            go(decode_gqa_bf16_d128_kernel<GG, true>);
+        else
+            go(decode_gqa_bf16_d128_kernel<GG, false>);
+    };
     switch (G) {
-        case 1: PLX_GQA_LAUNCH(1); break;
-        case 2: PLX_GQA_LAUNCH(2); break;
-        case 4: PLX_GQA_LAUNCH(4); break;
-        case 8: PLX_GQA_LAUNCH(8); break;
+        case 1: pick(std::integral_constant<int, 1>{}); break;
+        case 2: pick(std::integral_constant<int, 2>{}); break;
+        case 4: pick(std::integral_constant<int, 4>{}); break;
+        case 8: pick(std::integral_constant<int, 8>{}); break;
         default: return hipErrorInvalidValue;
     }
-#undef PLX_GQA_LAUNCH
     hipError_t e = hipGetLastError();
     if (e != hipSuccess || a.splits == 1) return e;
     return launch_decode_combine(a, stream);

@@ -389,6 +389,15 @@ plx_status_t decode_call(plx_dtype_t dtype, int32_t B, int32_t H, int32_t L_max,
     return e == hipSuccess ? PLX_OK : PLX_ERR_HIP;
 }
 
+// Paged decode, one query head per cache head (the split decode kernel) or grouped query
+// heads (the grouped kernel, also for one head per cache head when `grouped`).
+plx_status_t paged_call(plx_dtype_t dtype, int32_t B, int32_t H_q, int32_t H_kv,
+                        int32_t block_size, int32_t max_blocks, int32_t num_blocks, int32_t d_qk,
+                        int32_t d_v, const void* q, const void* rho, const void* k_pool,
+                        const void* v_pool, const int32_t* block_table, const int32_t* seqlens,
+                        void* o, float softmax_scale, int32_t num_splits, void* workspace,
+                        size_t workspace_bytes, void* stream, bool grouped);
+
 }  // namespace
 
 extern "C" {
@@ -466,39 +475,22 @@ plx_status_t plx_attn_decode_paged(plx_dtype_t dtype, int32_t B, int32_t H, int3
                                    const int32_t* block_table, const int32_t* seqlens, void* o,
                                    float softmax_scale, int32_t num_splits, void* workspace,
                                    size_t workspace_bytes, void* stream) {
-    if (dtype != PLX_F32 && dtype != PLX_BF16) return PLX_ERR_INVALID_ARG;
-    if (!q || !k_pool || !v_pool || !block_table || !seqlens || !o) return PLX_ERR_NULL_POINTER;
-    if (block_size < 32 || (block_size & (block_size - 1)) != 0 || max_blocks < 1 ||
-        num_blocks < 1)
-        return PLX_ERR_INVALID_SHAPE;
-    if ((long long)max_blocks * block_size > INT_MAX) return PLX_ERR_INVALID_SHAPE;
-    const int L_max = max_blocks * block_size;
-    plx_status_t st = check_decode_shape(B, H, L_max, d_v);
-    if (st != PLX_OK) return st;
-    if (d_qk < 1) return PLX_ERR_INVALID_SHAPE;
-    if (!std::isfinite(softmax_scale) || softmax_scale < 0.f) return PLX_ERR_INVALID_ARG;
-    if (num_splits < 0 || num_splits > kDecodeMaxSplits) return PLX_ERR_INVALID_ARG;
-    if (!(dtype == PLX_BF16 && d_qk == 128 && d_v == 128)) return PLX_ERR_UNSUPPORTED;
-    if (!aligned16(q) || !aligned16(rho) || !aligned16(k_pool) || !aligned16(v_pool) ||
-        !aligned16(o) || (reinterpret_cast<uintptr_t>(seqlens) & 3u) != 0 ||
-        (reinterpret_cast<uintptr_t>(block_table) & 3u) != 0)
-        return PLX_ERR_MISALIGNED;
-    int splits = 0;
-    size_t need = 0;
-    st = plx_attn_decode_gqa_plan(B, H, H, L_max, d_v, num_splits, &splits, &need);
-    if (st != PLX_OK) return st;
-    if (need > 0) {
-        if (!workspace) return PLX_ERR_NULL_POINTER;
-        if (workspace_bytes < need) return PLX_ERR_WORKSPACE_TOO_SMALL;
-        if (!aligned16(workspace)) return PLX_ERR_MISALIGNED;
-    }
-    int log2 = 0;
-    while ((1 << log2) < block_size) ++log2;
-    plx::DecodeArgs a{B, H, L_max, d_qk, q, rho, k_pool, v_pool, seqlens, o, softmax_scale,
-                      splits, 0, static_cast<float*>(workspace), 0, 0,
-                      block_table, max_blocks, log2, num_blocks};
-    const hipError_t e = plx::launch_decode_bf16_d128(a, static_cast<hipStream_t>(stream));
-    return e == hipSuccess ? PLX_OK : PLX_ERR_HIP;
+    return paged_call(dtype, B, H, H, block_size, max_blocks, num_blocks, d_qk, d_v, q, rho,
+                      k_pool, v_pool, block_table, seqlens, o, softmax_scale, num_splits,
+                      workspace, workspace_bytes, stream, false);
+}
+
+plx_status_t plx_attn_decode_paged_gqa(plx_dtype_t dtype, int32_t B, int32_t H_q, int32_t H_kv,
+                                       int32_t block_size, int32_t max_blocks,
+                                       int32_t num_blocks, int32_t d_qk, int32_t d_v,
+                                       const void* q, const void* rho, const void* k_pool,
+                                       const void* v_pool, const int32_t* block_table,
+                                       const int32_t* seqlens, void* o, float softmax_scale,
+                                       int32_t num_splits, void* workspace,
+                                       size_t workspace_bytes, void* stream) {
+    return paged_call(dtype, B, H_q, H_kv, block_size, max_blocks, num_blocks, d_qk, d_v, q, rho,
+                      k_pool, v_pool, block_table, seqlens, o, softmax_scale, num_splits,
+                      workspace, workspace_bytes, stream, true);
 }
 
 plx_status_t plx_attn_probe(plx_dtype_t dtype, int32_t B, int32_t T, int32_t C, int32_t H,
@@ -525,3 +517,53 @@ plx_status_t plx_attn_probe(plx_dtype_t dtype, int32_t B, int32_t T, int32_t C, 
 }
 
 }  // extern "C"
+
+namespace {
+
+plx_status_t paged_call(plx_dtype_t dtype, int32_t B, int32_t H_q, int32_t H_kv,
+                        int32_t block_size, int32_t max_blocks, int32_t num_blocks, int32_t d_qk,
+                        int32_t d_v, const void* q, const void* rho, const void* k_pool,
+                        const void* v_pool, const int32_t* block_table, const int32_t* seqlens,
+                        void* o, float softmax_scale, int32_t num_splits, void* workspace,
+                        size_t workspace_bytes, void* stream, bool grouped) {
+    if (dtype != PLX_F32 && dtype != PLX_BF16) return PLX_ERR_INVALID_ARG;
+    if (!q || !k_pool || !v_pool || !block_table || !seqlens || !o) return PLX_ERR_NULL_POINTER;
+    if (block_size < 32 || (block_size & (block_size - 1)) != 0 || max_blocks < 1 ||
+        num_blocks < 1)
+        return PLX_ERR_INVALID_SHAPE;
+    if ((long long)max_blocks * block_size > INT_MAX) return PLX_ERR_INVALID_SHAPE;
+    const int L_max = max_blocks * block_size;
+    plx_status_t st = check_decode_shape(B, H_q, L_max, d_v);
+    if (st != PLX_OK) return st;
+    if (d_qk < 1 || H_kv < 1 || H_q % H_kv != 0) return PLX_ERR_INVALID_SHAPE;
+    if (!std::isfinite(softmax_scale) || softmax_scale < 0.f) return PLX_ERR_INVALID_ARG;
+    if (num_splits < 0 || num_splits > kDecodeMaxSplits) return PLX_ERR_INVALID_ARG;
+    const int G = H_q / H_kv;
+    if (!(dtype == PLX_BF16 && d_qk == 128 && d_v == 128) ||
+        (G != 1 && G != 2 && G != 4 && G != 8))
+        return PLX_ERR_UNSUPPORTED;
+    if (!aligned16(q) || !aligned16(rho) || !aligned16(k_pool) || !aligned16(v_pool) ||
+        !aligned16(o) || (reinterpret_cast<uintptr_t>(seqlens) & 3u) != 0 ||
+        (reinterpret_cast<uintptr_t>(block_table) & 3u) != 0)
+        return PLX_ERR_MISALIGNED;
+    int splits = 0;
+    size_t need = 0;
+    st = plx_attn_decode_gqa_plan(B, H_q, H_kv, L_max, d_v, num_splits, &splits, &need);
+    if (st != PLX_OK) return st;
+    if (need > 0) {
+        if (!workspace) return PLX_ERR_NULL_POINTER;
+        if (workspace_bytes < need) return PLX_ERR_WORKSPACE_TOO_SMALL;
+        if (!aligned16(workspace)) return PLX_ERR_MISALIGNED;
+    }
+    int log2 = 0;
+    while ((1 << log2) < block_size) ++log2;
+    plx::DecodeArgs a{B, H_q, L_max, d_qk, q, rho, k_pool, v_pool, seqlens, o, softmax_scale,
+                      splits, 0, static_cast<float*>(workspace), 0, 0,
+                      block_table, max_blocks, log2, num_blocks};
+    const hipError_t e =
+        grouped ? plx::launch_decode_gqa_bf16_d128(a, H_kv, static_cast<hipStream_t>(stream))
+                : plx::launch_decode_bf16_d128(a, static_cast<hipStream_t>(stream));
+    return e == hipSuccess ? PLX_OK : PLX_ERR_HIP;
+}
+
+}  // namespace

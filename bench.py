@@ -859,9 +859,10 @@ def gqa(out_md):
 
 def paged(out_md):
     """Decode over a paged cache against the contiguous cache, same split plan: B=1, H=16,
-    32768 rows and B=16, H=16, 4096 rows (full lengths), blocks of 32, 64 and 256 rows in a
-    random order in the pool, and 64-row blocks in pool order. Cold caches (a 1 GiB read before each call), HIP events,
-    median of 20."""
+    32768 rows and B=16, H=16, 4096 rows (full lengths), and with grouped query heads B=16,
+    32 query heads over 8 cache heads, 4096 rows and B=1, 64 over 8, 32768 rows; blocks of 32,
+    64 and 256 rows in a random order in the pool, and 64-row blocks in pool order. Cold
+    caches (a 1 GiB read before each call), HIP events, median of 20."""
     import torch
 
     import attention_plx_attn_amd as plx
@@ -890,20 +891,24 @@ def paged(out_md):
 
     rows = []
     d = 128
-    for B, H, L in ((1, 16, 32768), (16, 16, 4096)):
-        q = torch.randn((B, H, d), generator=g, device=dev).to(torch.bfloat16)
-        r = (0.1 * torch.randn((B, H, d), generator=g, device=dev)).to(torch.bfloat16)
+    for B, Hq, H, L in ((1, 16, 16, 32768), (16, 16, 16, 4096), (16, 32, 8, 4096),
+                        (1, 64, 8, 32768)):
+        grouped = Hq != H
+        q = torch.randn((B, Hq, d), generator=g, device=dev).to(torch.bfloat16)
+        r = (0.1 * torch.randn((B, Hq, d), generator=g, device=dev)).to(torch.bfloat16)
         kc = torch.randn((B, H, L, d), generator=g, device=dev).to(torch.bfloat16)
         vc = torch.randn((B, H, L, d), generator=g, device=dev).to(torch.bfloat16)
         sl = torch.full((B,), L, dtype=torch.int32, device=dev)
         o = torch.empty_like(q)
-        S, need = plx.decode_gqa_plan(B, H, H, L, d)
+        S, need = plx.decode_gqa_plan(B, Hq, H, L, d)
         ws = torch.empty(max(need // 4, 1), dtype=torch.float32, device=dev)
-        nbytes = B * H * L * 2 * d * 2 + B * H * 3 * d * 2
-        us = timed(lambda: plx.decode(q, r, kc, vc, sl, d ** -0.5, num_splits=S, out=o,
+        nbytes = B * H * L * 2 * d * 2 + B * Hq * 3 * d * 2
+        name = (f"decode B{B} Hq{Hq} Hkv{H} ctx{L}" if grouped else f"decode B{B} H{H} ctx{L}")
+        contiguous = plx.decode_gqa if grouped else plx.decode
+        us = timed(lambda: contiguous(q, r, kc, vc, sl, d ** -0.5, num_splits=S, out=o,
                                       workspace=ws))
-        rows.append({"workload": f"decode B{B} H{H} ctx{L}", "cache": "contiguous",
-                     "splits": S, "median_us": us})
+        rows.append({"workload": name, "cache": "contiguous", "splits": S, "median_us": us})
+        paged_call = plx.decode_paged_gqa if grouped else plx.decode_paged
         for bs, shuffled in ((32, True), (64, True), (256, True), (64, False)):
             mb = L // bs
             perm = (torch.randperm(B * mb, generator=torch.Generator().manual_seed(bs))
@@ -913,12 +918,11 @@ def paged(out_md):
             vp = torch.empty_like(kp)
             kp[perm] = kc.view(B, H, mb, bs, d).permute(0, 2, 1, 3, 4).reshape(B * mb, H, bs, d)
             vp[perm] = vc.view(B, H, mb, bs, d).permute(0, 2, 1, 3, 4).reshape(B * mb, H, bs, d)
-            us = timed(lambda: plx.decode_paged(q, r, kp, vp, table, sl, d ** -0.5,
-                                                num_splits=S, out=o, workspace=ws))
+            us = timed(lambda: paged_call(q, r, kp, vp, table, sl, d ** -0.5, num_splits=S,
+                                          out=o, workspace=ws))
             order = "shuffled" if shuffled else "in pool order"
-            rows.append({"workload": f"decode B{B} H{H} ctx{L}",
-                         "cache": f"paged, {bs}-row blocks, {order}", "splits": S,
-                         "median_us": us})
+            rows.append({"workload": name, "cache": f"paged, {bs}-row blocks, {order}",
+                         "splits": S, "median_us": us})
             del kp, vp
         for r_ in rows[-5:]:
             r_["hbm_gbps"] = round(nbytes / r_["median_us"] / 1e3, 1)

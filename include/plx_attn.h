@@ -241,6 +241,28 @@ plx_status_t plx_attn_decode_paged(plx_dtype_t dtype, int32_t B, int32_t H, int3
                                    size_t workspace_bytes, void* stream);
 
 /*
+ * Paged decode with grouped query heads: plx_attn_decode_paged's pool and table over H_kv
+ * cache heads, read by H_q = G H_kv query heads as in plx_attn_decode_gqa (query head h reads
+ * cache head h / G; same split plan, plx_attn_decode_gqa_plan with L_max = max_blocks *
+ * block_size, and same workspace), with
+ *   q, rho         : [B, H_q, d_qk]          o : [B, H_q, d_v]
+ *   k_pool, v_pool : [num_blocks, H_kv, block_size, d] (dtype)
+ *   block_table    : device int32 [B, max_blocks], as for plx_attn_decode_paged
+ * A table entry outside [0, num_blocks) below n_b is never dereferenced and its rows get no
+ * weight, as for plx_attn_decode_paged. With the same plan the result is bitwise that of
+ * plx_attn_decode_gqa over the cache the table describes.
+ * Built combinations: (PLX_BF16, d_qk = d_v = 128, G in {1, 2, 4, 8}); rho may be NULL.
+ */
+plx_status_t plx_attn_decode_paged_gqa(plx_dtype_t dtype, int32_t B, int32_t H_q, int32_t H_kv,
+                                       int32_t block_size, int32_t max_blocks,
+                                       int32_t num_blocks, int32_t d_qk, int32_t d_v,
+                                       const void* q, const void* rho, const void* k_pool,
+                                       const void* v_pool, const int32_t* block_table,
+                                       const int32_t* seqlens, void* o, float softmax_scale,
+                                       int32_t num_splits, void* workspace,
+                                       size_t workspace_bytes, void* stream);
+
+/*
  * The probe producer: rho = gate_h * RoPE(gamma (.) RMSNorm_head(x W_R^T)), written in the
  * layout plx_attn_prefill / plx_attn_decode read (agihunt review, method paragraph: rho is one
  * matrix product W_R x from the layer input, with its own RMSNorm and, optionally, RoPE; the

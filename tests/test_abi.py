@@ -22,7 +22,8 @@ def test_exports_every_declared_symbol(lib):
                              "plx_attn_decode_noalloc", "plx_attn_decode_num_splits",
                              "plx_attn_decode_workspace_size", "plx_attn_probe",
                              "plx_attn_decode_gqa", "plx_attn_decode_gqa_plan",
-                             "plx_attn_decode_paged", "plx_attn_prefill_fwd",
+                             "plx_attn_decode_paged", "plx_attn_decode_paged_gqa",
+                             "plx_attn_prefill_fwd",
                              "plx_attn_prefill_bwd", "plx_attn_prefill_bwd_workspace_size",
                              "plx_status_string"}
     out = subprocess.run(["nm", "-D", "--defined-only", plx.LIB_PATH], capture_output=True,
@@ -199,6 +200,37 @@ def test_decode_paged_validation(lib):
     assert _paged(lib, dqk=64, dv=64) == 4
     assert _paged(lib, tab=A + 2) == 5
     assert _paged(lib, mb=16, splits=4) == 1               # workspace required
+
+
+def _paged_gqa(lib, dtype=1, B=2, Hq=8, Hkv=2, bs=64, mb=4, nb=8, dqk=128, dv=128, q=A, rho=A,
+               kp=A, vp=A, tab=A, sl=A, o=A, scale=0.1, splits=1, ws=0, wsb=0):
+    return lib.plx_attn_decode_paged_gqa(dtype, B, Hq, Hkv, bs, mb, nb, dqk, dv, q, rho, kp, vp,
+                                         tab, sl, o, ctypes.c_float(scale), splits, ws, wsb,
+                                         None)
+
+
+def test_decode_paged_gqa_validation(lib):
+    assert _paged_gqa(lib, kp=0) == 1
+    assert _paged_gqa(lib, tab=0) == 1
+    assert _paged_gqa(lib, B=0) == 2
+    assert _paged_gqa(lib, Hq=6, Hkv=4) == 2               # H_q a multiple of H_kv
+    assert _paged_gqa(lib, Hkv=0) == 2
+    assert _paged_gqa(lib, bs=96) == 2                     # block size a power of two
+    assert _paged_gqa(lib, bs=16) == 2                     # at least 32 rows
+    assert _paged_gqa(lib, mb=0) == 2
+    assert _paged_gqa(lib, nb=0) == 2
+    assert _paged_gqa(lib, splits=-1) == 3
+    assert _paged_gqa(lib, scale=float("nan")) == 3
+    assert _paged_gqa(lib, dtype=5) == 3
+    assert _paged_gqa(lib, Hq=6, Hkv=2) == 4               # G = 3 not built
+    assert _paged_gqa(lib, Hq=32, Hkv=2) == 4              # G = 16 not built
+    assert _paged_gqa(lib, dqk=64, dv=64) == 4
+    assert _paged_gqa(lib, dtype=0) == 4                   # fp32 not built
+    assert _paged_gqa(lib, vp=A + 8) == 5
+    assert _paged_gqa(lib, tab=A + 2) == 5
+    assert _paged_gqa(lib, mb=16, splits=4) == 1           # workspace required
+    need = 2 * 8 * 4 * (2 * 128 + 4) * 4
+    assert _paged_gqa(lib, mb=16, splits=4, ws=A, wsb=need - 4) == 6
 
 
 def _fwd(lib, dtype=1, B=1, H=2, T=64, dqk=128, dv=128, q=A, k=A, v=A, rho=A, o=A, vbar=A,

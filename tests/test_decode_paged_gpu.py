@@ -11,6 +11,7 @@ import torch
 
 import attention_plx_attn_amd as plx
 import oracle
+from paged_cache import paginate
 from parity import check_bf16
 from plx_synth import decode_inputs
 from plx_synth.inputs import DecodeConfig
@@ -20,25 +21,7 @@ DEV = "cuda:0"
 
 
 def _paged(x, bs, seed):
-    kc, vc, sl = x["k_cache"], x["v_cache"], x["seqlens"]
-    B, H, L, d = kc.shape
-    mb = L // bs
-    rng = np.random.default_rng(seed)
-    nblk = B * mb + 3
-    perm = rng.permutation(nblk)[: B * mb].reshape(B, mb)
-    kp = torch.full((nblk, H, bs, d), float("nan"), dtype=kc.dtype)
-    vp = torch.full((nblk, H, bs, d), float("nan"), dtype=vc.dtype)
-    table = torch.from_numpy(perm.astype(np.int32)).clone()
-    for b in range(B):
-        n = int(sl[b])
-        used = (n + bs - 1) // bs
-        for i in range(mb):
-            if i < used:
-                kp[perm[b, i]] = kc[b, :, i * bs:(i + 1) * bs]
-                vp[perm[b, i]] = vc[b, :, i * bs:(i + 1) * bs]
-            else:
-                table[b, i] = [-7, 1 << 30, nblk][i % 3]   # never dereferenced
-    return kp, vp, table
+    return paginate(x["k_cache"], x["v_cache"], x["seqlens"], bs, seed)
 
 
 @pytest.mark.parametrize("rho_kind", ["scaled", "proj32"])

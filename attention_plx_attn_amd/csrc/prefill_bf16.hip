@@ -17,9 +17,11 @@
 //   * K rows are stored in LDS in an order (key 8 q + 4 b + i of each 32-key group at row
 //     16 b + 4 q + i) that makes each lane's accumulator registers of two score blocks hold
 //     the 8 consecutive keys of its value-product operand: no cross-lane traffic;
-//   * V is stored transposed (d rows x BC keys, 16-byte key chunks XOR-swizzled with bits
-//     4..6 of d), so a value operand is one 16-byte LDS read whose address is a per-lane base
-//     plus a constant;
+//   * at d = 128 (single bf16 weights) the V tiles arrive in LDS row-major, by direct-to-LDS
+//     loads, and each value operand (8 consecutive keys of one dim) is two transposing LDS
+//     reads (ds_read_b64_tr_b16); otherwise the V stagers store V transposed (d rows x BC
+//     keys, 16-byte key chunks XOR-swizzled with bits 4..6 of d), so a value operand is one
+//     16-byte LDS read whose address is a per-lane base plus a constant;
 //   * P1 and P2 are rounded to bf16 and l = sum P1, beta = sum P2 are taken from the rounded
 //     values, so the effective corrected weights sum to exactly one; P2 = P1 * T is formed
 //     from the unrounded P1 (or, in the SPLIT instances, both go in as hi + lo bf16 terms
@@ -27,9 +29,9 @@
 //   * the running max is updated lazily (only when a row's tile max exceeds it by more than
 //     2^8); the result is the same exact expression, with far fewer rescales.
 // A tile holds BC = 64 keys at d = 128 and BC = 128 keys at d = 64 (the same bytes).
-// Waves 0-3 stage the K tiles and waves 4-7 the V tiles (with the transpose); the V stagers
-// issue at a higher priority, which balances the two waves of a SIMD (the hardware otherwise
-// favours the older wave for the matrix pipe, and the V stagers have the longer slot).
+// Waves 0-3 stage the K tiles and waves 4-7 the V tiles; the V stagers issue at a higher
+// priority, which balances the two waves of a SIMD (the hardware otherwise favours the older
+// wave for the matrix pipe).
 // Persistent launch: one workgroup per compute unit, each working through a static list of
 // items, longest first in snake order so that every workgroup gets the same number of tiles.
 // The items of one workgroup form a single stream of K/V tiles in a ring of four LDS
@@ -69,12 +71,14 @@ struct Geo {
     static constexpr int VS = BC + 8;        // LDS row stride of a transposed V tile
     // KDMA (d = 128): the K tiles are staged by direct-to-LDS loads into unpadded 256-byte
     // rows whose 16-byte chunks are XOR-swizzled by the row (chunk c of row r at position
-    // c ^ (r & 15)), which keeps the operand reads conflict-free without padding. Otherwise
-    // the stagers store through registers into rows padded by 16 bytes.
+    // c ^ (r & 15)), which keeps the operand reads conflict-free without padding; the V tiles
+    // the same way, row-major with their own chunk swizzle (vswz), read back transposed.
+    // Otherwise the stagers store through registers: K into rows padded by 16 bytes, V
+    // transposed (d rows of BC keys, stride VS).
     static constexpr bool KDMA = KDMA_;
     static constexpr int KS = KDMA ? D : D + 8;  // LDS row stride of a K tile (bf16 elements)
     static constexpr int K_ELEMS = BC * KS;      // 8192 bf16 at D = 128
-    static constexpr int V_ELEMS = D * VS;   // 9216 bf16 at D = 128
+    static constexpr int V_ELEMS = KDMA ? BC * D : D * VS;
     static constexpr int OFF_V = NBUF * K_ELEMS * 2;
     static constexpr int LDS_BYTES = OFF_V + NBUF * V_ELEMS * 2;
     static constexpr int NS = D / 32;    // 32-dim steps of a q.k product
@@ -92,6 +96,21 @@ constexpr float kLazyTau = 8.0f;  // log2 headroom before the running max moves
 __device__ __forceinline__ f32x4 mfma16(bf16x8 a, bf16x8 b, f32x4 c) {
     return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
 }
+
+typedef short i16x4_t __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) i16x4_t lds_i16x4_t;
+
+// Transposing LDS read (ds_read_b64_tr_b16): within each 16-lane group, lane 4 a + b receives
+// element b of the 4 consecutive 16-bit elements that lanes 4 j + a (j = 0..3) address.
+__device__ __forceinline__ i16x4_t lds_read_tr(const unsigned char* p) {
+    return __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+        (lds_i16x4_t*)(__attribute__((address_space(3))) unsigned char*)p);
+}
+
+// Swizzle of the row-major V tile: chunk c of key row r sits at position c ^ vswz(r). The
+// value operand reads of one half-wave touch rows 8 g + j (+ 4, + 32 G) for g = 0, 1 and
+// j = 0..3, 32 bytes each: vswz gives these 8 rows 8 distinct 32-byte spans of the banks.
+__device__ __forceinline__ int vswz(int r) { return 2 * ((r & 3) | (((r >> 3) & 1) << 2)); }
 
 __device__ __forceinline__ float max_across_row_groups(float x) {
     // max over the four lanes l, l ^ 16, l ^ 32, l ^ 48
@@ -179,11 +198,11 @@ __global__ __launch_bounds__(NT, 1) void prefill_bf16_kernel(
     const uint32_t voff =
         (uint32_t)(4 * (st >> CPR_LOG)) * ROWB + 16u * (st & (CPR - 1));  // + ROWB j
     u32x4 stg[4];
-    // Loads of tile kt of head bh, bound for ring slot t: direct-to-LDS for K at d = 128 (the
-    // LDS destination must be known now), into registers otherwise (stored by lstore).
-    // The staging role is a template argument of the tile loop (wave-uniform), so that the
-    // K stagers' direct-to-LDS loads never meet the V stagers' register staging at a join:
-    // there the compiler would drain every outstanding load before the V path's copies.
+    // Loads of tile kt of head bh, bound for ring slot t: direct-to-LDS for K and V at d = 128
+    // (the LDS destination must be known now), into registers otherwise (stored by lstore).
+    // In the KDMA instances the staging role is a template argument of the tile loop (the
+    // loop is compiled once per role, behind a wave-uniform branch): measured 3% faster than
+    // one loop that branches on the role at each staging point.
     // role: std::true_type / std::false_type (K / V stager) in the KDMA instances; elsewhere
     // the runtime role `kstager` decides and the argument is ignored.
     auto is_k = [&](auto role) {
@@ -215,13 +234,28 @@ __global__ __launch_bounds__(NT, 1) void prefill_bf16_kernel(
             }
         } else if (vactive) {
             const auto rv = make_rsrc(v + base, bytes);
+            if constexpr (KDMA) {
+                // Load j of V-stager wave w fills LDS rows 16 j + 4 (w - 4) .. +3 in lane
+                // order: lane (row r, position p) fetches chunk p ^ vswz(r) of key r.
+                unsigned char* Vl = vbuf(t);
+                const int p = lane & 15, wv = w - 4;
 #pragma unroll
-            for (int j = 0; j < 4; ++j) stg[j] = load16(rv, voff + ROWB * j);
+                for (int j = 0; j < KCH; ++j) {
+                    const int r = 16 * j + 4 * wv + (lane >> 4);
+                    const uint32_t src = (uint32_t)r * ROWB + 16u * (p ^ vswz(r));
+                    __builtin_amdgcn_raw_ptr_buffer_load_lds(
+                        rv, (__attribute__((address_space(3))) void*)(Vl + (16 * j + 4 * wv) * ROWB),
+                        16, src, 0, 0, 0);
+                }
+            } else {
+#pragma unroll
+                for (int j = 0; j < 4; ++j) stg[j] = load16(rv, voff + ROWB * j);
+            }
         }
     };
     auto lstore = [&](auto role, int t) {
+        if constexpr (KDMA) return;  // K and V are already in LDS
         if (is_k(role)) {
-            if constexpr (KDMA) return;  // already in LDS
             unsigned char* Kl = kbuf(t);
 #pragma unroll
             for (int j = 0; j < KCH; ++j) {
@@ -277,13 +311,31 @@ __global__ __launch_bounds__(NT, 1) void prefill_bf16_kernel(
     int vlane[4];
 #pragma unroll
     for (int x = 0; x < 4; ++x) vlane[x] = col * VS * 2 + 16 * (gq ^ x);
+    // KDMA: the operand of dim block db, step G is two transposing reads (keys 32 G + 8 gq +
+    // 0..3 and + 4..7); lane 4 j + a of a 16-lane group addresses row 32 G + 8 gq + j (+ 4),
+    // dims 16 db + 4 a .. +3, i.e. bytes 8 a of 32-byte span db ^ s at s = vswz(row) / 2.
+    int vtr[KDMA ? NDB : 1];
+    if constexpr (KDMA) {
+        const int j = col >> 2, sw = j | ((gq & 1) << 2);
+#pragma unroll
+        for (int db = 0; db < NDB; ++db)
+            vtr[db] = (8 * gq + j) * (int)ROWB + 32 * (db ^ sw) + 8 * (col & 3);
+    }
     // SPLIT: q1, q2 are the lo terms of p1, p2 (same V operand, two more products).
     auto values = [&](int t, int G, bf16x8 p1, bf16x8 p2, bf16x8 q1, bf16x8 q2) {
         const unsigned char* Vl = vbuf(t);
 #pragma unroll
         for (int db = 0; db < NDB; ++db) {
-            const bf16x8 vf = *(const bf16x8*)(Vl + vlane[db & 3] + 16 * db * VS * 2 +
-                                               64 * (G ^ (db >> 2)));
+            bf16x8 vf;
+            if constexpr (KDMA) {
+                const unsigned char* p = Vl + vtr[db] + 32 * G * ROWB;
+                const i16x4_t lo = lds_read_tr(p), hi = lds_read_tr(p + 4 * ROWB);
+                vf = __builtin_bit_cast(bf16x8,
+                                        __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
+            } else {
+                vf = *(const bf16x8*)(Vl + vlane[db & 3] + 16 * db * VS * 2 +
+                                      64 * (G ^ (db >> 2)));
+            }
             a1[db] = mfma16(vf, p1, a1[db]);
             if constexpr (PROBE) a2[db] = mfma16(vf, p2, a2[db]);
             if constexpr (SPLIT) {

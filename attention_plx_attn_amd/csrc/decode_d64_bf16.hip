@@ -334,6 +334,10 @@ hipError_t launch_decode_bf16_d64(const DecodeArgs& a, hipStream_t stream) {
                            a.splits, c);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess || a.splits == 1) return e;
+    return launch_decode_combine_d64(a, stream);
+}
+
+hipError_t launch_decode_combine_d64(const DecodeArgs& a, hipStream_t stream) {
     hipLaunchKernelGGL(decode_combine_d64_kernel, dim3(a.B * a.H), dim3(64), 0, stream,
                        (const float*)a.ws, (__bf16*)a.o, a.splits);
     return hipGetLastError();

@@ -31,12 +31,10 @@
 namespace plx {
 namespace {
 
-constexpr int D = 128;
 constexpr int NT = 256;
 constexpr int NW = 4;
 constexpr int KB = 32;       // keys per wave step
 constexpr int VTS = KB + 8;  // LDS row stride of V^T (bf16): 80 bytes, conflict-free reads
-constexpr int REC = kDecodeRecord;
 constexpr float kLazyTau = 8.0f;
 
 __device__ __forceinline__ f32x4 mfma16(bf16x8 a, bf16x8 b, f32x4 c) {
@@ -51,14 +49,23 @@ __device__ __forceinline__ int slot_key(int g, int e) { return e < 4 ? 4 * g + e
 // never crosses a block). Only blocks holding rows below the chunk end are looked up, one step
 // ahead of their loads; an entry outside [0, num_blocks) is never dereferenced and its steps
 // are skipped (its rows get no weight).
-template <int G, bool PAGED>
-__global__ __launch_bounds__(NT, 2) void decode_gqa_bf16_d128_kernel(
+// D = 128 or 64. At d = 64 a row is 8 chunks of 16 bytes: lanes col < 8 load the V rows of
+// k-slots 0..3 of their group and lanes col >= 8 those of k-slots 4..7, chunk col & 7 each.
+template <int D, int G, bool PAGED>
+__global__ __launch_bounds__(NT, 2) void decode_gqa_bf16_kernel(
     const __bf16* __restrict__ q, const __bf16* __restrict__ rho, const __bf16* __restrict__ kc,
     const __bf16* __restrict__ vc, const int32_t* __restrict__ seqlens, __bf16* __restrict__ o,
     float* __restrict__ ws, int Hkv, int L_max, int S, float c, const int32_t* __restrict__ table,
     int max_blocks, int bs_log2, int num_blocks) {
     static_assert(G >= 1 && G <= 8, "up to 8 query heads per cache head");
-    __shared__ __attribute__((aligned(16))) __bf16 vt[NW][D * VTS];            // 40 KB
+    static_assert(D == 128 || D == 64, "head dim");
+    constexpr int NS = D / 32;              // 32-dim steps of the scores
+    constexpr int NDB = D / 16;             // 16-dim blocks of the value products
+    constexpr int NV = D / 16;              // 16-byte V loads per lane and step
+    constexpr uint32_t ROWB = 2 * D;        // bytes per cache row
+    constexpr int REC = 2 * D + 4;          // split record: A1[D], A2[D], m, l, beta, pad
+    __shared__ __attribute__((aligned(16))) __bf16 vt[NW][D * VTS];            // 40 KB at 128
+    static_assert(NW * 16 * D * 4 <= (int)sizeof(vt), "merge area");
     __shared__ __attribute__((aligned(16))) float st_m[NW][16], st_l[NW][16];  // per column
 
     const int s = blockIdx.x, hk = blockIdx.y, b = blockIdx.z;
@@ -72,44 +79,47 @@ __global__ __launch_bounds__(NT, 2) void decode_gqa_bf16_d128_kernel(
     const int chunk = (((nb + S - 1) / S) + KB - 1) / KB * KB;
     const int j0 = s * chunk, j1 = min(j0 + chunk, nb);
     const size_t bk = (size_t)b * Hkv + hk;
-    const uint32_t range = j1 > 0 ? (uint32_t)j1 * 256u : 0u;
+    const uint32_t range = j1 > 0 ? (uint32_t)j1 * ROWB : 0u;
     const auto rk = make_rsrc(kc + bk * (size_t)L_max * D, range);
     const auto rv = make_rsrc(vc + bk * (size_t)L_max * D, range);
 
     // B operand of the scores: column col = 2 gq (q of query head hk G + gq) or 2 gq + 1 (its
     // rho); lane holds dims 32 st + 8 g .. +7. Columns from 2 G on, and rho when absent, are 0.
-    bf16x8 bqr[4];
+    bf16x8 bqr[NS];
     {
         const int gq = col >> 1;
         const bool live = gq < G && (!(col & 1) || rho != nullptr);
         const __bf16* src = (col & 1) ? rho : q;
         const auto r = make_rsrc(live ? src + ((size_t)b * Hq + (size_t)hk * G + gq) * D : q,
-                                 live ? 256u : 0u);
+                                 live ? ROWB : 0u);
 #pragma unroll
-        for (int st = 0; st < 4; ++st) bqr[st] = as_bf16x8(load16(r, 64u * st + 16u * g));
+        for (int st = 0; st < NS; ++st) bqr[st] = as_bf16x8(load16(r, 64u * st + 16u * g));
     }
 
-    f32x4 acc[8];  // acc[blk][i]: column 4 g + i, dim 16 blk + col
+    f32x4 acc[NDB];  // acc[blk][i]: column 4 g + i, dim 16 blk + col
 #pragma unroll
-    for (int blk = 0; blk < 8; ++blk) acc[blk] = f32x4{};
+    for (int blk = 0; blk < NDB; ++blk) acc[blk] = f32x4{};
     float m_run = -INFINITY;  // running max of this lane's column's head
     float rsum = 0.f;         // this lane's share of sum w (even columns) or sum w t (odd)
 
     struct Frag {
-        u32x4 k[2][4];
-        u32x4 v[8];
+        u32x4 k[2][NS];
+        u32x4 v[NV];
     };
+    // The V rows and the chunk a lane loads: k-slot vslot(e) of its group, chunk vchunk.
+    const int vhalf = D == 128 ? 0 : 4 * (col >> 3);
+    const int vchunk = D == 128 ? col : (col & 7);
     // Loads of the 32 rows from row r of the resources ck, cv.
     auto load_rows = [&](__amdgpu_buffer_rsrc_t ck, __amdgpu_buffer_rsrc_t cv, int r, Frag& f) {
 #pragma unroll
         for (int t = 0; t < 2; ++t)
 #pragma unroll
-            for (int st = 0; st < 4; ++st)
+            for (int st = 0; st < NS; ++st)
                 f.k[t][st] =
-                    load16_nt(ck, (uint32_t)(r + 16 * t + col) * 256u + 64u * st + 16u * g);
+                    load16_nt(ck, (uint32_t)(r + 16 * t + col) * ROWB + 64u * st + 16u * g);
 #pragma unroll
-        for (int e = 0; e < 8; ++e)
-            f.v[e] = load16_nt(cv, (uint32_t)(r + slot_key(g, e)) * 256u + 16u * col);
+        for (int e = 0; e < NV; ++e)
+            f.v[e] = load16_nt(cv, (uint32_t)(r + slot_key(g, vhalf + e)) * ROWB + 16u * vchunk);
     };
     // Block of the step at row kb0 (paged caches), or -1 past the chunk.
     auto lookup = [&](int kb0) -> int {
@@ -130,7 +140,7 @@ __global__ __launch_bounds__(NT, 2) void decode_gqa_bf16_d128_kernel(
             const int rel = kb0 & ((1 << bs_log2) - 1);
             if (kb0 < j1 && (unsigned)phys < (unsigned)num_blocks) {
                 base = (((size_t)phys * Hkv + hk) << bs_log2) * D;
-                bytes = (uint32_t)min(1 << bs_log2, j1 - (kb0 - rel)) * 256u;
+                bytes = (uint32_t)min(1 << bs_log2, j1 - (kb0 - rel)) * ROWB;
             }
             load_rows(make_rsrc(kc + base, bytes), make_rsrc(vc + base, bytes), rel, f);
         }
@@ -140,18 +150,25 @@ __global__ __launch_bounds__(NT, 2) void decode_gqa_bf16_d128_kernel(
     auto in_pool = [&](int phys) { return !PAGED || (unsigned)phys < (unsigned)num_blocks; };
     __bf16* vtw = vt[w];
     auto consume = [&](int kb0, const Frag& f) {
-        // V^T: lane (col, g) holds dims 8 col .. +7 of its 8 slot keys; row 8 col + d gets the
-        // 8 slots 8 g .. 8 g + 7 (two bf16 per dword: slots 2 p, 2 p + 1).
+        // V^T: lane (col, g) holds dims 8 vchunk .. +7 of its slot keys (slots vhalf ..
+        // vhalf + NV - 1 of its group); row 8 vchunk + d gets them at columns 8 g + vhalf ..
+        // (two bf16 per dword: slots 2 p, 2 p + 1).
 #pragma unroll
         for (int dd = 0; dd < 4; ++dd) {
-            u32x4 lo, hi;  // dims 8 col + 2 dd (low halves) and + 2 dd + 1 (high halves)
+            uint32_t lo[NV / 2], hi[NV / 2];  // dims 8 vchunk + 2 dd (low halves), + 1 (high)
 #pragma unroll
-            for (int p = 0; p < 4; ++p) {
+            for (int p = 0; p < NV / 2; ++p) {
                 lo[p] = __builtin_amdgcn_perm(f.v[2 * p + 1][dd], f.v[2 * p][dd], 0x05040100u);
                 hi[p] = __builtin_amdgcn_perm(f.v[2 * p + 1][dd], f.v[2 * p][dd], 0x07060302u);
             }
-            *(u32x4*)(vtw + (8 * col + 2 * dd) * VTS + 8 * g) = lo;
-            *(u32x4*)(vtw + (8 * col + 2 * dd + 1) * VTS + 8 * g) = hi;
+            __bf16* r0 = vtw + (8 * vchunk + 2 * dd) * VTS + 8 * g + vhalf;
+            if constexpr (NV == 8) {
+                *(u32x4*)r0 = u32x4{lo[0], lo[1], lo[2], lo[3]};
+                *(u32x4*)(r0 + VTS) = u32x4{hi[0], hi[1], hi[2], hi[3]};
+            } else {
+                *(u32x2*)r0 = u32x2{lo[0], lo[1]};
+                *(u32x2*)(r0 + VTS) = u32x2{hi[0], hi[1]};
+            }
         }
         // Scores and probe products: sc[t][i] = key 16 t + 4 g + i, column col.
         f32x4 sc[2];
@@ -159,7 +176,7 @@ __global__ __launch_bounds__(NT, 2) void decode_gqa_bf16_d128_kernel(
         for (int t = 0; t < 2; ++t) {
             sc[t] = f32x4{};
 #pragma unroll
-            for (int st = 0; st < 4; ++st) sc[t] = mfma16(as_bf16x8(f.k[t][st]), bqr[st], sc[t]);
+            for (int st = 0; st < NS; ++st) sc[t] = mfma16(as_bf16x8(f.k[t][st]), bqr[st], sc[t]);
         }
         // Column max of the scores; odd columns take their head's score column's max.
         float mx = -INFINITY;
@@ -183,7 +200,7 @@ __global__ __launch_bounds__(NT, 2) void decode_gqa_bf16_d128_kernel(
             for (int i = 0; i < 4; ++i) {
                 const float ai = shfl_xor(alpha, lane ^ (4 * g + i));
 #pragma unroll
-                for (int blk = 0; blk < 8; ++blk) acc[blk][i] *= ai;
+                for (int blk = 0; blk < NDB; ++blk) acc[blk][i] *= ai;
             }
         }
         // Weights: even columns w = exp2(s c - m), odd columns w t; 0 past the range and for
@@ -221,7 +238,7 @@ __global__ __launch_bounds__(NT, 2) void decode_gqa_bf16_d128_kernel(
         // O[c][dim] += P[c][slots] V^T[dim][slots]: B operand lane (col = dim, g) reads
         // V^T[16 blk + col][8 g .. 8 g + 7].
 #pragma unroll
-        for (int blk = 0; blk < 8; ++blk) {
+        for (int blk = 0; blk < NDB; ++blk) {
             const bf16x8 vb = *(const bf16x8*)(vtw + (16 * blk + col) * VTS + 8 * g);
             acc[blk] = mfma16(pa, vb, acc[blk]);
             acc[blk] = mfma16(pb, vb, acc[blk]);
@@ -262,13 +279,14 @@ __global__ __launch_bounds__(NT, 2) void decode_gqa_bf16_d128_kernel(
     float* ow = reinterpret_cast<float*>(&vt[0][0]);  // [NW][16][D]
     __syncthreads();
 #pragma unroll
-    for (int blk = 0; blk < 8; ++blk)
+    for (int blk = 0; blk < NDB; ++blk)
 #pragma unroll
         for (int i = 0; i < 4; ++i) ow[(w * 16 + 4 * g + i) * D + 16 * blk + col] = acc[blk][i];
     __syncthreads();
-    // Thread tid handles dims 2 (tid & 63) .. +1 of query heads gq = tid >> 6, tid >> 6 + 4.
-    for (int gq = tid >> 6; gq < G; gq += NW) {
-        const int d0 = 2 * (tid & 63);
+    // Thread tid handles dims 2 (tid % TPH) .. +1 of query heads tid / TPH, + NT / TPH, ...
+    constexpr int TPH = D / 2;  // threads per query head
+    for (int gq = tid / TPH; gq < G; gq += NT / TPH) {
+        const int d0 = 2 * (tid % TPH);
         float M = -INFINITY;
 #pragma unroll
         for (int v = 0; v < NW; ++v) M = fmaxf(M, st_m[v][2 * gq]);
@@ -308,7 +326,7 @@ __global__ __launch_bounds__(NT, 2) void decode_gqa_bf16_d128_kernel(
 
 }  // namespace
 
-hipError_t launch_decode_gqa_bf16_d128(const DecodeArgs& a, int Hkv, hipStream_t stream) {
+hipError_t launch_decode_gqa_bf16(const DecodeArgs& a, int Hkv, hipStream_t stream) {
     const int G = a.H / Hkv;
     dim3 grid(a.splits, Hkv, a.B);
     const float c = a.scale * kLog2e;
@@ -318,23 +336,29 @@ hipError_t launch_decode_gqa_bf16_d128(const DecodeArgs& a, int Hkv, hipStream_t
                            a.seqlens, (__bf16*)a.o, a.ws, Hkv, a.L_max, a.splits, c, a.table,
                            a.max_blocks, a.block_log2, a.num_blocks);
     };
-    auto pick = [&](auto g_tag) {
-        constexpr int GG = decltype(g_tag)::value;
+    auto pick = [&](auto d_tag, auto g_tag) {
+        constexpr int DD = decltype(d_tag)::value, GG = decltype(g_tag)::value;
         if (a.table)
-            go(decode_gqa_bf16_d128_kernel<GG, true>);
+            go(decode_gqa_bf16_kernel<DD, GG, true>);
         else
-            go(decode_gqa_bf16_d128_kernel<GG, false>);
+            go(decode_gqa_bf16_kernel<DD, GG, false>);
     };
-    switch (G) {
-        case 1: pick(std::integral_constant<int, 1>{}); break;
-        case 2: pick(std::integral_constant<int, 2>{}); break;
-        case 4: pick(std::integral_constant<int, 4>{}); break;
-        case 8: pick(std::integral_constant<int, 8>{}); break;
-        default: return hipErrorInvalidValue;
-    }
+    auto by_g = [&](auto d_tag) {
+        switch (G) {
+            case 1: pick(d_tag, std::integral_constant<int, 1>{}); return true;
+            case 2: pick(d_tag, std::integral_constant<int, 2>{}); return true;
+            case 4: pick(d_tag, std::integral_constant<int, 4>{}); return true;
+            case 8: pick(d_tag, std::integral_constant<int, 8>{}); return true;
+            default: return false;
+        }
+    };
+    bool ok = false;
+    if (a.d == 128) ok = by_g(std::integral_constant<int, 128>{});
+    else if (a.d == 64) ok = by_g(std::integral_constant<int, 64>{});
+    if (!ok) return hipErrorInvalidValue;
     hipError_t e = hipGetLastError();
     if (e != hipSuccess || a.splits == 1) return e;
-    return launch_decode_combine(a, stream);
+    return a.d == 64 ? launch_decode_combine_d64(a, stream) : launch_decode_combine(a, stream);
 }
 
 }  // namespace plx

@@ -389,8 +389,9 @@ plx_status_t decode_call(plx_dtype_t dtype, int32_t B, int32_t H, int32_t L_max,
     return e == hipSuccess ? PLX_OK : PLX_ERR_HIP;
 }
 
-// Paged decode, one query head per cache head (the split decode kernel) or grouped query
-// heads (the grouped kernel, also for one head per cache head when `grouped`).
+// Paged decode, one query head per cache head (the split decode kernel at d = 128) or grouped
+// query heads (the grouped kernel, also for one head per cache head when `grouped` or at
+// d = 64).
 plx_status_t paged_call(plx_dtype_t dtype, int32_t B, int32_t H_q, int32_t H_kv,
                         int32_t block_size, int32_t max_blocks, int32_t num_blocks, int32_t d_qk,
                         int32_t d_v, const void* q, const void* rho, const void* k_pool,
@@ -447,7 +448,7 @@ plx_status_t plx_attn_decode_gqa(plx_dtype_t dtype, int32_t B, int32_t H_q, int3
     if (!std::isfinite(softmax_scale) || softmax_scale < 0.f) return PLX_ERR_INVALID_ARG;
     if (num_splits < 0 || num_splits > kDecodeMaxSplits) return PLX_ERR_INVALID_ARG;
     const int G = H_q / H_kv;
-    if (!(dtype == PLX_BF16 && d_qk == 128 && d_v == 128) ||
+    if (!(dtype == PLX_BF16 && d_qk == d_v && (d_qk == 128 || d_qk == 64)) ||
         (G != 1 && G != 2 && G != 4 && G != 8))
         return PLX_ERR_UNSUPPORTED;
     if (!aligned16(q) || !aligned16(rho) || !aligned16(k_cache) || !aligned16(v_cache) ||
@@ -464,7 +465,7 @@ plx_status_t plx_attn_decode_gqa(plx_dtype_t dtype, int32_t B, int32_t H_q, int3
     }
     plx::DecodeArgs a{B, H_q, L_max, d_qk, q, rho, k_cache, v_cache, seqlens, o, softmax_scale,
                       splits, 0, static_cast<float*>(workspace), 0, 0};
-    const hipError_t e = plx::launch_decode_gqa_bf16_d128(a, H_kv, static_cast<hipStream_t>(stream));
+    const hipError_t e = plx::launch_decode_gqa_bf16(a, H_kv, static_cast<hipStream_t>(stream));
     return e == hipSuccess ? PLX_OK : PLX_ERR_HIP;
 }
 
@@ -539,7 +540,7 @@ plx_status_t paged_call(plx_dtype_t dtype, int32_t B, int32_t H_q, int32_t H_kv,
     if (!std::isfinite(softmax_scale) || softmax_scale < 0.f) return PLX_ERR_INVALID_ARG;
     if (num_splits < 0 || num_splits > kDecodeMaxSplits) return PLX_ERR_INVALID_ARG;
     const int G = H_q / H_kv;
-    if (!(dtype == PLX_BF16 && d_qk == 128 && d_v == 128) ||
+    if (!(dtype == PLX_BF16 && d_qk == d_v && (d_qk == 128 || d_qk == 64)) ||
         (G != 1 && G != 2 && G != 4 && G != 8))
         return PLX_ERR_UNSUPPORTED;
     if (!aligned16(q) || !aligned16(rho) || !aligned16(k_pool) || !aligned16(v_pool) ||
@@ -560,9 +561,11 @@ plx_status_t paged_call(plx_dtype_t dtype, int32_t B, int32_t H_q, int32_t H_kv,
     plx::DecodeArgs a{B, H_q, L_max, d_qk, q, rho, k_pool, v_pool, seqlens, o, softmax_scale,
                       splits, 0, static_cast<float*>(workspace), 0, 0,
                       block_table, max_blocks, log2, num_blocks};
+    // d = 64 runs the grouped kernel also with one query head per cache head
     const hipError_t e =
-        grouped ? plx::launch_decode_gqa_bf16_d128(a, H_kv, static_cast<hipStream_t>(stream))
-                : plx::launch_decode_bf16_d128(a, static_cast<hipStream_t>(stream));
+        grouped || d_qk == 64
+            ? plx::launch_decode_gqa_bf16(a, H_kv, static_cast<hipStream_t>(stream))
+            : plx::launch_decode_bf16_d128(a, static_cast<hipStream_t>(stream));
     return e == hipSuccess ? PLX_OK : PLX_ERR_HIP;
 }
 

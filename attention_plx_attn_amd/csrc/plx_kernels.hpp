@@ -79,10 +79,13 @@ hipError_t launch_decode_bf16_d128(const DecodeArgs& a, hipStream_t stream);
 // own combine when a.splits > 1 (records of 2 * 64 + 4 floats).
 hipError_t launch_decode_bf16_d64(const DecodeArgs& a, hipStream_t stream);
 hipError_t launch_probe_bf16_d128(const ProbeArgs& a, hipStream_t stream);
-// Grouped query heads: a.H query heads over Hkv cache heads (a.H / Hkv in {1, 2, 4, 8}), split
-// mode with a.splits chunks; partials in the split decode's record layout per query head.
-hipError_t launch_decode_gqa_bf16_d128(const DecodeArgs& a, int Hkv, hipStream_t stream);
-// The split decode's combine: merges a.splits records per (b, query head) into o.
+// Grouped query heads: a.H query heads over Hkv cache heads (a.H / Hkv in {1, 2, 4, 8}), a.d
+// 128 or 64, split mode with a.splits chunks; partials in the split decode's record layout
+// of that head dim, per query head; a paged cache when a.table is set.
+hipError_t launch_decode_gqa_bf16(const DecodeArgs& a, int Hkv, hipStream_t stream);
+// The split decode's combines: merge a.splits records per (b, query head) into o (d = 128,
+// d = 64).
 hipError_t launch_decode_combine(const DecodeArgs& a, hipStream_t stream);
+hipError_t launch_decode_combine_d64(const DecodeArgs& a, hipStream_t stream);
 
 }  // namespace plx

@@ -790,9 +790,10 @@ def compare_grid(out_md):
 
 
 def gqa(out_md):
-    """Decode with grouped query heads at a fixed cache (B=1, H_kv=16, 32768 rows, d=128):
-    G = 1, 2, 4, 8 query heads per cache head, against the multi-head decode of the same
-    cache (G = 1). Cold caches (a 1 GiB read before each call), HIP events, median of 20."""
+    """Decode with grouped query heads at a fixed cache (B=1, H_kv=16, 32768 rows, d=128, then
+    d=64): G = 1, 2, 4, 8 query heads per cache head, against the multi-head decode of the
+    same cache (G = 1). Cold caches (a 1 GiB read before each call), HIP events, median of
+    20."""
     import torch
 
     import attention_plx_attn_amd as plx
@@ -804,10 +805,6 @@ def gqa(out_md):
     g.manual_seed(17)
     flush = torch.ones(1024 * 1024 * 1024 // 4, dtype=torch.float32, device=dev)
     sink = torch.empty(8192, dtype=torch.float32, device=dev)
-    B, Hkv, L, d = 1, 16, 32768, 128
-    kc = torch.randn((B, Hkv, L, d), generator=g, device=dev).to(torch.bfloat16)
-    vc = torch.randn((B, Hkv, L, d), generator=g, device=dev).to(torch.bfloat16)
-    sl = torch.full((B,), L, dtype=torch.int32, device=dev)
 
     def timed(call):
         for _ in range(3):
@@ -824,23 +821,32 @@ def gqa(out_md):
         return _stats_us(ts)["median_us"]
 
     rows = []
-    q16 = torch.randn((B, Hkv, d), generator=g, device=dev).to(torch.bfloat16)
-    r16 = (0.1 * torch.randn((B, Hkv, d), generator=g, device=dev)).to(torch.bfloat16)
-    o16 = torch.empty_like(q16)
-    us = timed(lambda: plx.decode(q16, r16, kc, vc, sl, d ** -0.5, out=o16))
-    rows.append({"kernel": "multi-head decode (VALU value products)", "G": 1, "H_q": Hkv,
-                 "median_us": us})
-    for G in (1, 2, 4, 8):
-        Hq = Hkv * G
-        q = torch.randn((B, Hq, d), generator=g, device=dev).to(torch.bfloat16)
-        r = (0.1 * torch.randn((B, Hq, d), generator=g, device=dev)).to(torch.bfloat16)
-        o = torch.empty_like(q)
-        _, need = plx.decode_gqa_plan(B, Hq, Hkv, L, d)
-        ws = torch.empty(max(need // 4, 1), dtype=torch.float32, device=dev)
-        us = timed(lambda: plx.decode_gqa(q, r, kc, vc, sl, d ** -0.5, out=o, workspace=ws))
-        rows.append({"kernel": "grouped-query decode (MFMA value products)", "G": G,
-                     "H_q": Hq, "median_us": us})
+    B, Hkv, L = 1, 16, 32768
+    for d in (128, 64):
+        kc = torch.randn((B, Hkv, L, d), generator=g, device=dev).to(torch.bfloat16)
+        vc = torch.randn((B, Hkv, L, d), generator=g, device=dev).to(torch.bfloat16)
+        sl = torch.full((B,), L, dtype=torch.int32, device=dev)
+        q16 = torch.randn((B, Hkv, d), generator=g, device=dev).to(torch.bfloat16)
+        r16 = (0.1 * torch.randn((B, Hkv, d), generator=g, device=dev)).to(torch.bfloat16)
+        o16 = torch.empty_like(q16)
+        us = timed(lambda: plx.decode(q16, r16, kc, vc, sl, d ** -0.5, out=o16))
+        rows.append({"kernel": "multi-head decode (VALU value products)", "d": d, "G": 1,
+                     "H_q": Hkv, "median_us": us})
+        for G in (1, 2, 4, 8):
+            Hq = Hkv * G
+            q = torch.randn((B, Hq, d), generator=g, device=dev).to(torch.bfloat16)
+            r = (0.1 * torch.randn((B, Hq, d), generator=g, device=dev)).to(torch.bfloat16)
+            o = torch.empty_like(q)
+            _, need = plx.decode_gqa_plan(B, Hq, Hkv, L, d)
+            ws = torch.empty(max(need // 4, 1), dtype=torch.float32, device=dev)
+            us = timed(lambda: plx.decode_gqa(q, r, kc, vc, sl, d ** -0.5, out=o,
+                                              workspace=ws))
+            rows.append({"kernel": "grouped-query decode (MFMA value products)", "d": d,
+                         "G": G, "H_q": Hq, "median_us": us})
+        del kc, vc
+        torch.cuda.empty_cache()
     for r_ in rows:
+        d = r_["d"]
         nbytes = B * Hkv * L * 2 * d * 2 + B * r_["H_q"] * 3 * d * 2
         r_["hbm_gbps"] = round(nbytes / r_["median_us"] / 1e3, 1)
         r_["hbm_frac"] = round(r_["hbm_gbps"] / HBM_PEAK_GBPS, 4)
@@ -848,11 +854,11 @@ def gqa(out_md):
         print(json.dumps(r_), flush=True)
     if out_md:
         with open(out_md, "w") as fh:
-            fh.write("| kernel | G | H_q | median us | HBM GB/s | fraction of 8 TB/s | "
-                     "query-head rows / s |\n|---|---|---|---|---|---|---|\n")
+            fh.write("| kernel | d | G | H_q | median us | HBM GB/s | fraction of 8 TB/s | "
+                     "query-head rows / s |\n|---|---|---|---|---|---|---|---|\n")
             for r_ in rows:
-                fh.write(f"| {r_['kernel']} | {r_['G']} | {r_['H_q']} | {r_['median_us']} | "
-                         f"{r_['hbm_gbps']} | {100 * r_['hbm_frac']:.1f}% | "
+                fh.write(f"| {r_['kernel']} | {r_['d']} | {r_['G']} | {r_['H_q']} | "
+                         f"{r_['median_us']} | {r_['hbm_gbps']} | {100 * r_['hbm_frac']:.1f}% | "
                          f"{r_['query_heads_per_s']:,.0f} |\n")
     return 0
 

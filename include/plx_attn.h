@@ -196,8 +196,8 @@ plx_status_t plx_attn_decode_noalloc(plx_dtype_t dtype, int32_t B, int32_t H, in
                                      int32_t num_splits, void* stream);
 
 /*
- * Decode with grouped query heads: H_q query heads over H_kv cache heads, G = H_q / H_kv in {1, 2, 4, 8}; query head h reads cache head
- * h / G. Same conventions as plx_attn_decode, with
+ * Decode with grouped query heads: H_q query heads over H_kv cache heads, G = H_q / H_kv in
+ * {1, 2, 4, 8}; query head h reads cache head h / G. Same conventions as plx_attn_decode, with
  *   q, rho  : [B, H_q, d_qk]      k_cache : [B, H_kv, L_max, d_qk]
  *   v_cache : [B, H_kv, L_max, d_v]   o : [B, H_q, d_v]
  * One matrix instruction per 16 cache rows yields the scores and probe products of all G
@@ -205,6 +205,7 @@ plx_status_t plx_attn_decode_noalloc(plx_dtype_t dtype, int32_t B, int32_t H, in
  * idle rows of a decode step's matrix instructions carry extra work), and the value products
  * run on the matrix cores as well. Split mode only: num_splits 0 (heuristic) or > 0 chunks per
  * (b, h_kv); rho may be NULL (rho = 0).
+ * Built combinations: (PLX_BF16, d_qk = d_v in {64, 128}, G in {1, 2, 4, 8}).
  * plx_attn_decode_gqa_plan writes the split count and the workspace bytes a call with the
  * same arguments needs (B*H_q*S*(2*d_v + 4)*4 for S > 1, else 0).
  */
@@ -230,7 +231,9 @@ plx_status_t plx_attn_decode_gqa(plx_dtype_t dtype, int32_t B, int32_t H_q, int3
  * never dereferenced: the rows it would hold are skipped (they get no softmax weight, as if
  * they were not part of the sequence), so a sequence with such an entry below n_b attends to
  * its other rows only.
- * Built combination: (PLX_BF16, d_qk = d_v = 128); rho may be NULL (rho = 0).
+ * Built combinations: (PLX_BF16, d_qk = d_v in {64, 128}); rho may be NULL (rho = 0). At
+ * d = 128 the result is bitwise that of plx_attn_decode (split mode) over the cache the table
+ * describes, with the same split count; at d = 64 that of plx_attn_decode_gqa with H_q = H_kv.
  */
 plx_status_t plx_attn_decode_paged(plx_dtype_t dtype, int32_t B, int32_t H, int32_t block_size,
                                    int32_t max_blocks, int32_t num_blocks, int32_t d_qk,
@@ -251,7 +254,7 @@ plx_status_t plx_attn_decode_paged(plx_dtype_t dtype, int32_t B, int32_t H, int3
  * A table entry outside [0, num_blocks) below n_b is never dereferenced and its rows get no
  * weight, as for plx_attn_decode_paged. With the same plan the result is bitwise that of
  * plx_attn_decode_gqa over the cache the table describes.
- * Built combinations: (PLX_BF16, d_qk = d_v = 128, G in {1, 2, 4, 8}); rho may be NULL.
+ * Built combinations: (PLX_BF16, d_qk = d_v in {64, 128}, G in {1, 2, 4, 8}); rho may be NULL.
  */
 plx_status_t plx_attn_decode_paged_gqa(plx_dtype_t dtype, int32_t B, int32_t H_q, int32_t H_kv,
                                        int32_t block_size, int32_t max_blocks,

@@ -174,7 +174,8 @@ def test_decode_gqa_validation(lib):
     assert _gqa(lib, Hq=6, Hkv=2) == 4                     # G = 3 not built
     assert _gqa(lib, Hq=32, Hkv=2) == 4                    # G = 16 > 8
     assert _gqa(lib, splits=-4) == 3                       # split mode only
-    assert _gqa(lib, dqk=64, dv=64) == 4
+    assert _gqa(lib, dqk=32, dv=32) == 4
+    assert _gqa(lib, dqk=64, dv=128) == 4
     assert _gqa(lib, kc=A + 8) == 5
     assert _gqa(lib, L=1024, splits=4) == 1                # workspace required
     need = 2 * 8 * 4 * (2 * 128 + 4) * 4
@@ -197,7 +198,8 @@ def test_decode_paged_validation(lib):
     assert _paged(lib, mb=0) == 2
     assert _paged(lib, nb=0) == 2
     assert _paged(lib, splits=-1) == 3
-    assert _paged(lib, dqk=64, dv=64) == 4
+    assert _paged(lib, dqk=32, dv=32) == 4
+    assert _paged(lib, dqk=64, dv=128) == 4
     assert _paged(lib, tab=A + 2) == 5
     assert _paged(lib, mb=16, splits=4) == 1               # workspace required
 
@@ -224,7 +226,8 @@ def test_decode_paged_gqa_validation(lib):
     assert _paged_gqa(lib, dtype=5) == 3
     assert _paged_gqa(lib, Hq=6, Hkv=2) == 4               # G = 3 not built
     assert _paged_gqa(lib, Hq=32, Hkv=2) == 4              # G = 16 not built
-    assert _paged_gqa(lib, dqk=64, dv=64) == 4
+    assert _paged_gqa(lib, dqk=32, dv=32) == 4
+    assert _paged_gqa(lib, dqk=64, dv=128) == 4
     assert _paged_gqa(lib, dtype=0) == 4                   # fp32 not built
     assert _paged_gqa(lib, vp=A + 8) == 5
     assert _paged_gqa(lib, tab=A + 2) == 5

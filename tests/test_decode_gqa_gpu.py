@@ -80,3 +80,46 @@ def test_gqa_g1_equals_plain_decode_oracle_on_32k():
     ref = oracle.decode(x["q"], x["rho"], x["k_cache"], x["v_cache"], x["seqlens"], x["scale"],
                         form="sweighted")
     check_bf16(o, ref, "gqa G=1 decode_32k")
+
+
+def _inputs_d(B, Hq, G, L, d, seed, rho="scaled", poison=True):
+    cq = DecodeConfig("dq", 60, B, Hq, 1, d, "bf16", rho, "full")
+    ck = DecodeConfig("dk", 61, B, Hq // G, L, d, "bf16", rho, "uniform_half")
+    xq = decode_inputs(cq, seed=seed)
+    xk = decode_inputs(ck, seed=seed, poison=poison)
+    return xq["q"], xq["rho"], xk["k_cache"], xk["v_cache"], xk["seqlens"], xq["scale"]
+
+
+@pytest.mark.parametrize("G", [1, 2, 4, 8])
+@pytest.mark.parametrize("splits", [0, 1, 3])
+@pytest.mark.parametrize("L", [40, 700])
+def test_gqa_d64_matches_oracle(G, splits, L):
+    """Head dim 64 (the compute-matched head dim) with grouped query heads."""
+    B, Hkv = 3, 2
+    probe = "proj32" if (G + splits + L) % 2 else "scaled"
+    q, rho, kc, vc, sl, scale = _inputs_d(B, Hkv * G, G, L, 64, seed=G * 7 + L, rho=probe)
+    print("gqa d64", G, splits, L, probe, sl.tolist(), flush=True)
+    o = plx.decode_gqa(q.to(DEV), rho.to(DEV), kc.to(DEV), vc.to(DEV), sl.to(DEV), scale,
+                       num_splits=splits)
+    torch.cuda.synchronize()
+    check_bf16(o, _oracle(q, rho, kc, vc, sl, scale, G),
+               f"gqa d64 G={G} splits={splits} L={L} rho={probe}")
+
+
+@pytest.mark.parametrize("G", [1, 8])
+def test_gqa_d64_edges_and_softmax_only(G):
+    B, Hkv, L = 5, 2, 200
+    q, rho, kc, vc, _, scale = _inputs_d(B, Hkv * G, G, L, 64, seed=5, poison=False)
+    sl = torch.tensor([0, -3, 1, 200, 9999], dtype=torch.int32)
+    d = [t.to(DEV) for t in (q, rho, kc, vc, sl)]
+    o = plx.decode_gqa(d[0], d[1], d[2], d[3], d[4], scale, num_splits=2)
+    z = plx.decode_gqa(d[0], None, d[2], d[3], d[4], scale, num_splits=2)
+    z0 = plx.decode_gqa(d[0], torch.zeros_like(d[1]), d[2], d[3], d[4], scale, num_splits=2)
+    torch.cuda.synchronize()
+    assert torch.equal(z, z0)
+    o, z = o.cpu(), z.cpu()
+    assert torch.all(o[0] == 0) and torch.all(o[1] == 0)
+    for h in range(Hkv * G):
+        assert torch.equal(o[2, h], vc[2, h // G, 0])
+    check_bf16(o[3:], _oracle(q, rho, kc, vc, sl, scale, G)[3:], f"gqa d64 edges G={G}")
+    check_bf16(z[3:], _oracle(q, None, kc, vc, sl, scale, G)[3:], f"gqa d64 softmax-only G={G}")

@@ -86,3 +86,26 @@ def test_paged_invalid_entry_below_seqlens_is_skipped(splits):
         ref = oracle.decode(x["q"][b: b + 1], x["rho"][b: b + 1], k, v,
                             np.array([len(rows)], np.int32), x["scale"])
         check_bf16(o[b: b + 1], ref, f"paged invalid entry b={b} splits={splits}")
+
+
+@pytest.mark.parametrize("bs", [32, 256])
+@pytest.mark.parametrize("splits", [0, 3])
+def test_paged_d64_equals_grouped_and_oracle(bs, splits):
+    """Head dim 64: the paged decode runs the grouped kernel with one query head per cache
+    head, so it gives plx_attn_decode_gqa's bits on the contiguous cache."""
+    cfg = DecodeConfig("d64", 45, 4, 3, 1024, 64, "bf16", "proj32", "uniform_half")
+    x = decode_inputs(cfg, seed=bs + splits, poison=True)
+    kp, vp, table = _paged(x, bs, seed=bs + 1)
+    print("paged d64", bs, splits, x["seqlens"].tolist(), flush=True)
+    q, rho, sl = (x[k].to(DEV) for k in ("q", "rho", "seqlens"))
+    o = plx.decode_paged(q, rho, kp.to(DEV), vp.to(DEV), table.to(DEV), sl, x["scale"],
+                         num_splits=splits)
+    s = plx.decode_gqa_plan(4, 3, 3, 1024, 64, splits)[0]
+    ref_c = plx.decode_gqa(q, rho, x["k_cache"].to(DEV), x["v_cache"].to(DEV), sl, x["scale"],
+                           num_splits=s)
+    torch.cuda.synchronize()
+    assert torch.equal(o, ref_c)
+    k = torch.nan_to_num(x["k_cache"].float())
+    v = torch.nan_to_num(x["v_cache"].float())
+    ref = oracle.decode(x["q"], x["rho"], k, v, x["seqlens"], x["scale"], form="cov")
+    check_bf16(o, ref, f"paged d64 bs={bs} splits={splits}")

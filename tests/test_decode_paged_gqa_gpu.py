@@ -105,3 +105,26 @@ def test_paged_gqa_serving_shape():
     o = plx.decode_paged_gqa(*d, scale)
     torch.cuda.synchronize()
     check_bf16(o, _oracle(q, rho, kc, vc, sl, scale, G), "paged gqa serving shape")
+
+
+@pytest.mark.parametrize("G", [1, 4, 8])
+@pytest.mark.parametrize("bs", [32, 128])
+@pytest.mark.parametrize("splits", [0, 3])
+def test_paged_gqa_d64_equals_contiguous_and_oracle(G, bs, splits):
+    """Head dim 64: the paged pool gives the contiguous grouped decode's bits."""
+    B, Hkv, L = 3, 2, 1024
+    cq = DecodeConfig("pq64", 52, B, Hkv * G, 1, 64, "bf16", "proj32", "full")
+    ck = DecodeConfig("pk64", 53, B, Hkv, L, 64, "bf16", "proj32", "uniform_half")
+    xq, xk = decode_inputs(cq, seed=G + bs), decode_inputs(ck, seed=G + bs, poison=True)
+    q, rho, scale = xq["q"], xq["rho"], xq["scale"]
+    kc, vc, sl = xk["k_cache"], xk["v_cache"], xk["seqlens"]
+    kp, vp, table = paginate(kc, vc, sl, bs, seed=bs + 3 * G)
+    print("paged gqa d64", G, bs, splits, sl.tolist(), flush=True)
+    d = [t.to(DEV) for t in (q, rho, kp, vp, table, sl)]
+    o = plx.decode_paged_gqa(*d, scale, num_splits=splits)
+    s = plx.decode_gqa_plan(B, Hkv * G, Hkv, L, 64, splits)[0]
+    ref_c = plx.decode_gqa(d[0], d[1], kc.to(DEV), vc.to(DEV), d[5], scale, num_splits=s)
+    torch.cuda.synchronize()
+    assert torch.equal(o, ref_c)
+    check_bf16(o, _oracle(q, rho, kc, vc, sl, scale, G),
+               f"paged gqa d64 G={G} bs={bs} splits={splits}")

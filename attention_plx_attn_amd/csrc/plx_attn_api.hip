@@ -383,9 +383,10 @@ plx_status_t decode_call(plx_dtype_t dtype, int32_t B, int32_t H, int32_t L_max,
     plx::DecodeArgs a{B, H, L_max, d_qk, q, rho, k_cache, v_cache, seqlens, o, softmax_scale,
                       p.splits, p.chunk, static_cast<float*>(workspace), p.waves,
                       p.whole ? 1 : 0};
-    const hipError_t e = d_qk == 64
-                             ? plx::launch_decode_bf16_d64(a, static_cast<hipStream_t>(stream))
-                             : plx::launch_decode_bf16_d128(a, static_cast<hipStream_t>(stream));
+    // d = 64 (split mode): the grouped-head kernel with one query head per cache head
+    const hipError_t e =
+        d_qk == 64 ? plx::launch_decode_gqa_bf16(a, H, static_cast<hipStream_t>(stream))
+                   : plx::launch_decode_bf16_d128(a, static_cast<hipStream_t>(stream));
     return e == hipSuccess ? PLX_OK : PLX_ERR_HIP;
 }
 

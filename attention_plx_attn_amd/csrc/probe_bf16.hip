@@ -35,6 +35,13 @@ __device__ __forceinline__ f32x4 mfma16(bf16x8 a, bf16x8 b, f32x4 c) {
     return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
 }
 
+// Sequence b and position t of token n = b T + t. Token indices fit 31 bits (the host checks
+// B T C 2 < 2^31), so 32-bit division serves (a 64-bit one is a long instruction sequence).
+__device__ __forceinline__ void seq_pos(int n, int T, int& b, int& t) {
+    b = (int)((unsigned)n / (unsigned)T);
+    t = n - b * T;
+}
+
 // UG groups of 16 tokens per wave, 64 UG tokens per workgroup: UG = 2 lets every W_R operand
 // read feed two products (wide inputs, matrix-bound); UG = 1 halves the accumulators so that
 // more waves are resident (narrow inputs, where the call is bound by latency and the writes).
@@ -96,8 +103,8 @@ __global__ __launch_bounds__(NT) void probe_bf16_d128_kernel(
     int pos0[UG];
 #pragma unroll
     for (int u = 0; u < UG; ++u) {
-        const long long tk = tok_ok[u] ? tok[u] : 0;
-        pos0[u] = positions ? positions[(int)(tk / T)] : 0;
+        const int tk = tok_ok[u] ? (int)tok[u] : 0;
+        pos0[u] = positions ? positions[(unsigned)tk / (unsigned)T] : 0;
     }
 
     f32x4 acc[UG][8];
@@ -144,8 +151,8 @@ __global__ __launch_bounds__(NT) void probe_bf16_d128_kernel(
         ss += shfl_xor(ss, 16);
         ss += shfl_xor(ss, 32);
         const float inv = 1.f / sqrtf(ss * (1.f / D) + eps);
-        const long long tk = tok_ok[u] ? tok[u] : 0;
-        const int b = (int)(tk / T), t = (int)(tk - (long long)b * T);
+        int b, t;
+        seq_pos(tok_ok[u] ? (int)tok[u] : 0, T, b, t);
         float n[8][4];
 #pragma unroll
         for (int j = 0; j < 8; ++j)
@@ -182,7 +189,8 @@ __global__ __launch_bounds__(NT) void probe_bf16_d128_kernel(
             const int row = 4 * r + g;
             const long long tr = (long long)blockIdx.x * TOK + 16 * UG * w + 16 * u + row;
             if (tr < N) {
-                const int br = (int)(tr / T), trr = (int)(tr - (long long)br * T);
+                int br, trr;
+                seq_pos((int)tr, T, br, trr);
                 *(u32x4*)(rho + (((size_t)br * H + h) * T + trr) * D + 8 * c16) =
                     *(const u32x4*)&ot[w][row][8 * c16];
             }

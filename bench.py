@@ -331,6 +331,9 @@ def _bench_lib():
     lib.plx_bench_stream_write.argtypes = [ctypes.c_void_p, ctypes.c_size_t, ctypes.c_int,
                                            ctypes.c_void_p]
     lib.plx_bench_stream_write.restype = ctypes.c_int
+    lib.plx_bench_stream_read_rows.argtypes = ([ctypes.c_void_p] * 3 + [ctypes.c_int] * 3 +
+                                               [ctypes.c_void_p, ctypes.c_int, ctypes.c_void_p])
+    lib.plx_bench_stream_read_rows.restype = ctypes.c_int
     return lib
 
 
@@ -411,6 +414,26 @@ def stream_floor(torch, blib, stream, a, b, nbytes, cold, n=10):
     return best
 
 
+def rows_floor(torch, blib, stream, dx, B, H, L_max, cold, n=10):
+    """Time of the streaming-read kernel over exactly the cache rows a decode call reads (rows
+    below each sequence's length, in the caches' own [B, H, L_max, d] layout), cold caches,
+    best median over five grid sizes."""
+    sink = torch.zeros(1024, dtype=torch.int32, device=dx["k_cache"].device)
+    h = ctypes_stream(stream)
+    best = None
+    for grid in (512, 1024, 2048, 4096, 8192):
+        def call(grid=grid):
+            rc = blib.plx_bench_stream_read_rows(dx["k_cache"].data_ptr(), dx["v_cache"].data_ptr(),
+                                                 dx["seqlens"].data_ptr(), B, H, L_max,
+                                                 sink.data_ptr(), grid, h)
+            if rc != 0:
+                raise RuntimeError(f"plx_bench_stream_read_rows: HIP error {rc}")
+        st = timed_calls(torch, stream, call, n, cold=cold)
+        if best is None or st["median_us"] < best["median_us"]:
+            best = dict(st, grid=grid)
+    return best
+
+
 def ctypes_stream(stream) -> int:
     import ctypes
     return ctypes.c_void_p(stream.cuda_stream).value or 0
@@ -461,8 +484,9 @@ def prefill_long_record(torch, plx, dev, stream, n=5):
 
 def decode_grid_records(torch, plx, dev, stream, min_bytes=100e6, n=10):
     """Decode grid cells (H16 d128, B x ctx, seqlens ~ U[ctx/2, ctx]) that move at least
-    min_bytes, automatic plan, cold caches; each beside the streaming-read floor of its KV
-    bytes measured in the same run."""
+    min_bytes, automatic plan, cold caches; each beside two streaming-read floors measured in
+    the same run: the same number of KV bytes read contiguously, and exactly the rows the call
+    reads, in place (the ragged lengths leave every (b, h)'s rows past its end unread)."""
     from plx_synth import decode_grid_cells, decode_inputs
     from plx_synth.inputs import draw_seqlens
 
@@ -484,6 +508,7 @@ def decode_grid_records(torch, plx, dev, stream, min_bytes=100e6, n=10):
                          n, cold=cold)
         kv = nbytes - cfg.B * cfg.H * 3 * cfg.d * 2
         fl = stream_floor(torch, blib, stream, dx["k_cache"], dx["v_cache"], kv, cold)
+        fr = rows_floor(torch, blib, stream, dx, cfg.B, cfg.H, cfg.L_max, cold)
         gbps = nbytes / (st["median_us"] * 1e-6) / 1e9
         recs.append({"workload": f"decode B{cfg.B} H{cfg.H} ctx{cfg.L_max} d{cfg.d} bf16",
                      **st, "plan": splits, "bytes": nbytes, "hbm_gbps": round(gbps, 1),
@@ -491,7 +516,9 @@ def decode_grid_records(torch, plx, dev, stream, min_bytes=100e6, n=10):
                      "tokens_per_s": round(cfg.B / (st["median_us"] * 1e-6), 1),
                      "floor_us": fl["median_us"], "floor_bytes": fl["bytes"],
                      "floor_gbps": round(fl["bytes"] / (fl["median_us"] * 1e-6) / 1e9, 1),
-                     "time_over_floor": round(st["median_us"] / fl["median_us"], 4)})
+                     "time_over_floor": round(st["median_us"] / fl["median_us"], 4),
+                     "rows_floor_us": fr["median_us"],
+                     "time_over_rows_floor": round(st["median_us"] / fr["median_us"], 4)})
         print(json.dumps(recs[-1]), file=sys.stderr, flush=True)
         del dx, ws, od
         torch.cuda.empty_cache()

@@ -8,11 +8,14 @@
 // appears in the review's mechanism-analysis paragraph; here it is a per-head multiplier, the
 // sigmoid left to the caller.
 //
-// One workgroup (4 waves) computes 64 UG tokens x the 128 dims of one head as
+// One workgroup (4 waves) computes 64 UG tokens x the 128 dims of HG heads as
 // Y^T = W_R X^T on v_mfma_f32_16x16x32_bf16: per 32-wide K step the workgroup stages the
 // head's W_R slice (128 rows x 64 bytes, rows padded to 80 bytes so the operand reads are
 // free of bank conflicts) in LDS, double-buffered, and every wave reads its A operand blocks
 // there; the B operand is UG 16-token groups of x rows read straight from global memory.
+// Narrow calls are bound by the per-token vector work of the epilogue, so there the RoPE
+// frequencies come from a per-workgroup table, gamma from LDS, the gate is folded into the
+// norm's scale, and with one K step two heads share each token's sines and cosines.
 // Each lane then holds 32 dims (4 consecutive dims of each 16-dim block) of one token per
 // group, so the RMSNorm sum of squares needs only 4 lanes, the RoPE pairs (i, i + 64) sit in
 // the same lane, and rho is written with 8-byte row pieces in the [B, H, T, d] layout the
@@ -31,6 +34,17 @@ constexpr int WROW = 40;     // LDS row stride of the W_R slice (bf16): 80 bytes
 constexpr int WBUF = D * WROW;
 constexpr int kProbeNarrowC = 64;  // inputs up to this width take one token group per wave
 
+// gamma of a call that passes none (RMSNorm without a learned scale)
+__constant__ float kOnes[D] = {
+    1.f, 1.f, 1.f, 1.f, 1.f, 1.f, 1.f, 1.f, 1.f, 1.f, 1.f, 1.f, 1.f, 1.f, 1.f, 1.f,
+    1.f, 1.f, 1.f, 1.f, 1.f, 1.f, 1.f, 1.f, 1.f, 1.f, 1.f, 1.f, 1.f, 1.f, 1.f, 1.f,
+    1.f, 1.f, 1.f, 1.f, 1.f, 1.f, 1.f, 1.f, 1.f, 1.f, 1.f, 1.f, 1.f, 1.f, 1.f, 1.f,
+    1.f, 1.f, 1.f, 1.f, 1.f, 1.f, 1.f, 1.f, 1.f, 1.f, 1.f, 1.f, 1.f, 1.f, 1.f, 1.f,
+    1.f, 1.f, 1.f, 1.f, 1.f, 1.f, 1.f, 1.f, 1.f, 1.f, 1.f, 1.f, 1.f, 1.f, 1.f, 1.f,
+    1.f, 1.f, 1.f, 1.f, 1.f, 1.f, 1.f, 1.f, 1.f, 1.f, 1.f, 1.f, 1.f, 1.f, 1.f, 1.f,
+    1.f, 1.f, 1.f, 1.f, 1.f, 1.f, 1.f, 1.f, 1.f, 1.f, 1.f, 1.f, 1.f, 1.f, 1.f, 1.f,
+    1.f, 1.f, 1.f, 1.f, 1.f, 1.f, 1.f, 1.f, 1.f, 1.f, 1.f, 1.f, 1.f, 1.f, 1.f, 1.f};
+
 __device__ __forceinline__ f32x4 mfma16(bf16x8 a, bf16x8 b, f32x4 c) {
     return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
 }
@@ -44,20 +58,26 @@ __device__ __forceinline__ void seq_pos(int n, int T, int& b, int& t) {
 
 // UG groups of 16 tokens per wave, 64 UG tokens per workgroup: UG = 2 lets every W_R operand
 // read feed two products (wide inputs, matrix-bound); UG = 1 halves the accumulators so that
-// more waves are resident (narrow inputs, where the call is bound by latency and the writes).
-template <int UG>
-__global__ __launch_bounds__(NT) void probe_bf16_d128_kernel(
+// more waves are resident (narrow inputs). HG heads per workgroup, one after the other: for
+// inputs of at most 32 (one K step) both heads' W_R slices are staged at once, and the RoPE
+// sines and cosines, which depend on the token and not on the head, are evaluated once for
+// both (narrow calls are bound by this per-token vector work).
+template <int UG, int HG>
+__global__ __launch_bounds__(NT, UG == 1 ? 4 : 1) void probe_bf16_d128_kernel(
     const __bf16* __restrict__ x, const __bf16* __restrict__ wr, const float* __restrict__ gamma,
     const float* __restrict__ gate, const int32_t* __restrict__ positions, __bf16* __restrict__ rho,
     int B, int T, int C, int H, float eps, float log2_base) {
     constexpr uint32_t OOB = 0xFFFFFFF0u;  // past every resource: reads as zeros
     __shared__ __attribute__((aligned(16))) __bf16 wl[2][WBUF];
     __shared__ __attribute__((aligned(16))) __bf16 ot[NT / 64][16][D + 8];  // output rows
+    __shared__ __attribute__((aligned(16))) float turn_tab[D / 2];  // turns per position, per pair
+    __shared__ __attribute__((aligned(16))) float gam[D];           // gamma (ones if none)
+    static_assert(HG == 1 || HG == 2, "heads per workgroup");
     const int tid = threadIdx.x, lane = tid & 63;
     const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int c16 = lane & 15, g = lane >> 4;
     constexpr int TOK = 64 * UG;  // tokens per workgroup
-    const int h = blockIdx.y;
+    const int h0 = blockIdx.y * HG;
     const long long N = (long long)B * T;
     long long tok[UG];
     bool tok_ok[UG];
@@ -69,7 +89,8 @@ __global__ __launch_bounds__(NT) void probe_bf16_d128_kernel(
         xrow[u] = tok_ok[u] ? (uint32_t)(tok[u] * C) * 2u : OOB;
     }
     const auto rx = make_rsrc(x, (uint32_t)(N * C * 2));  // < 2^31 (checked on the host)
-    const auto rw = make_rsrc(wr + (size_t)h * D * C, (uint32_t)D * C * 2u);
+    auto rw_of = [&](int h) { return make_rsrc(wr + (size_t)h * D * C, (uint32_t)D * C * 2u); };
+    const auto rw = rw_of(h0);
 
     // Staging: thread tid copies 16-byte pieces (tid & 3) of rows tid >> 2 and 64 + (tid >> 2).
     const int sr = tid >> 2, sp = tid & 3;
@@ -95,29 +116,48 @@ __global__ __launch_bounds__(NT) void probe_bf16_d128_kernel(
     };
     bf16x8 bx[UG];
     load_x(0, bx);
-    f32x4 gmv[8];
-#pragma unroll
-    for (int j = 0; j < 8; ++j)
-        gmv[j] = gamma ? *(const f32x4*)(gamma + 16 * j + 4 * g) : f32x4{1.f, 1.f, 1.f, 1.f};
-    const float gh = gate ? gate[h] : 1.f;
+    if (tid < D) gam[tid] = (gamma ? gamma : kOnes)[tid];  // published by the K loop's barriers
+    // Token group u (16 consecutive tokens from tg0[u]) usually lies in one sequence (b0, from
+    // position t0): then a lane's position and the group's output rows follow by addition.
+    int tg0[UG], b0[UG], t0[UG];
+    bool one_seq[UG];
     int pos0[UG];
 #pragma unroll
     for (int u = 0; u < UG; ++u) {
-        const int tk = tok_ok[u] ? (int)tok[u] : 0;
-        pos0[u] = positions ? positions[(unsigned)tk / (unsigned)T] : 0;
+        tg0[u] = (int)((long long)blockIdx.x * TOK + 16 * UG * w + 16 * u);
+        seq_pos(tg0[u] < N ? tg0[u] : 0, T, b0[u], t0[u]);
+        one_seq[u] = tg0[u] + 15 < N && t0[u] + 15 < T;
+        int bl = b0[u];
+        if (!one_seq[u]) {
+            int tl;
+            seq_pos(tok_ok[u] ? (int)tok[u] : 0, T, bl, tl);
+        }
+        pos0[u] = positions ? positions[bl] : 0;
     }
+    // Turns per position of rotation pair p (dims p and p + 64): base^(-2 p / d) / (2 pi),
+    // the same for every token and head: formed once per workgroup.
+    if (tid < D / 2)
+        turn_tab[tid] = log2_base > 0.f
+                            ? exp2f(-(2.f * tid / D) * log2_base) * 0.15915494309189535f
+                            : 0.f;
 
     f32x4 acc[UG][8];
-#pragma unroll
-    for (int u = 0; u < UG; ++u)
-#pragma unroll
-        for (int j = 0; j < 8; ++j) acc[u][j] = f32x4{};
     u32x4 st[2];
     stage(0, st);
+    if constexpr (HG == 2) {  // C <= 32: the second head's slice goes to the other buffer
+        const int kc = 8 * sp;
+        const auto rw1 = rw_of(h0 + 1);
+        u32x4 st1[2];
+#pragma unroll
+        for (int r = 0; r < 2; ++r)
+            st1[r] = load16(rw1, kc < C ? (uint32_t)((sr + 64 * r) * C + kc) * 2u : OOB);
+        put(1, st1);
+    }
     put(0, st);
     __syncthreads();
     int buf = 0;
-    for (int k0 = 0; k0 < C; k0 += 32) {
+    // One K step; the first starts the accumulators from zero.
+    auto kstep = [&](int k0, bool first) {
         const bool more = k0 + 32 < C;
         if (more) stage(k0 + 32, st);
         if (k0 > 0) load_x(k0, bx);
@@ -125,79 +165,111 @@ __global__ __launch_bounds__(NT) void probe_bf16_d128_kernel(
         for (int j = 0; j < 8; ++j) {
             const bf16x8 a = *(const bf16x8*)&wl[buf][(16 * j + c16) * WROW + 8 * g];
 #pragma unroll
-            for (int u = 0; u < UG; ++u) acc[u][j] = mfma16(a, bx[u], acc[u][j]);
+            for (int u = 0; u < UG; ++u)
+                acc[u][j] = mfma16(a, bx[u], first ? f32x4{} : acc[u][j]);
         }
         if (more) put(buf ^ 1, st);
         __syncthreads();
         buf ^= 1;
+    };
+    if constexpr (HG == 1) {
+        kstep(0, true);
+        for (int k0 = 32; k0 < C; k0 += 32) kstep(k0, false);
     }
 
-    // acc[u][j][i]: dim 16 j + 4 g + i of token tok[u].
-    // Turns per position of the 16 rotation pairs this lane holds: base^(-2 di / d) / (2 pi).
-    float turns[4][4];
+    // acc[u][j][i]: dim 16 j + 4 g + i of token tok[u]. The lane's 16 rotation pairs are
+    // p = 16 j + 4 g + i, j < 4 (the table was published by the K loop's barriers).
+    f32x4 turns[4];
 #pragma unroll
-    for (int j = 0; j < 4; ++j)
+    for (int j = 0; j < 4; ++j) turns[j] = *(const f32x4*)&turn_tab[16 * j + 4 * g];
+    float rc[UG][4][4], rs[UG][4][4];  // cosine and sine of the lane's 16 rotation angles
 #pragma unroll
-        for (int i = 0; i < 4; ++i)
-            turns[j][i] = exp2f(-(2.f * (16 * j + 4 * g + i) / D) * log2_base) *
-                          0.15915494309189535f;
+    for (int hh = 0; hh < HG; ++hh) {
+        const int h = h0 + hh;
+        if constexpr (HG == 2) {  // the one K step of this head, from its staged slice
 #pragma unroll
-    for (int u = 0; u < UG; ++u) {
-        float ss = 0.f;
+            for (int j = 0; j < 8; ++j) {
+                const bf16x8 a = *(const bf16x8*)&wl[hh][(16 * j + c16) * WROW + 8 * g];
 #pragma unroll
-        for (int j = 0; j < 8; ++j)
-#pragma unroll
-            for (int i = 0; i < 4; ++i) ss = fmaf(acc[u][j][i], acc[u][j][i], ss);
-        ss += shfl_xor(ss, 16);
-        ss += shfl_xor(ss, 32);
-        const float inv = 1.f / sqrtf(ss * (1.f / D) + eps);
-        int b, t;
-        seq_pos(tok_ok[u] ? (int)tok[u] : 0, T, b, t);
-        float n[8][4];
-#pragma unroll
-        for (int j = 0; j < 8; ++j)
-#pragma unroll
-            for (int i = 0; i < 4; ++i) n[j][i] = gmv[j][i] * acc[u][j][i] * inv;
-        if (log2_base > 0.f) {
-            const float pos = (float)(pos0[u] + t);
-#pragma unroll
-            for (int j = 0; j < 4; ++j)
-#pragma unroll
-                for (int i = 0; i < 4; ++i) {
-                    // fraction of a turn: p + e = pos * turns exactly (e from the fma), less
-                    // the nearest whole number of turns
-                    const float p = pos * turns[j][i];
-                    const float e = fmaf(pos, turns[j][i], -p);
-                    const float fr = (p - rintf(p)) + e;
-                    const float sn = __builtin_amdgcn_sinf(fr), cs = __builtin_amdgcn_cosf(fr);
-                    const float lo = n[j][i], hi = n[j + 4][i];
-                    n[j][i] = lo * cs - hi * sn;
-                    n[j + 4][i] = hi * cs + lo * sn;
-                }
-        }
-        // The group's 16 rows go through LDS so that each store writes whole 256-byte rows:
-        // lane (c16, g) then stores 16-byte piece c16 of rows 4 r + g, r = 0..3.
-#pragma unroll
-        for (int j = 0; j < 8; ++j)
-            *(u32x2*)&ot[w][c16][16 * j + 4 * g] = u32x2{pack_bf16x2(gh * n[j][0], gh * n[j][1]),
-                                                      pack_bf16x2(gh * n[j][2], gh * n[j][3])};
-        __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
-        __builtin_amdgcn_wave_barrier();
-        __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
-#pragma unroll
-        for (int r = 0; r < 4; ++r) {
-            const int row = 4 * r + g;
-            const long long tr = (long long)blockIdx.x * TOK + 16 * UG * w + 16 * u + row;
-            if (tr < N) {
-                int br, trr;
-                seq_pos((int)tr, T, br, trr);
-                *(u32x4*)(rho + (((size_t)br * H + h) * T + trr) * D + 8 * c16) =
-                    *(const u32x4*)&ot[w][row][8 * c16];
+                for (int u = 0; u < UG; ++u) acc[u][j] = mfma16(a, bx[u], f32x4{});
             }
         }
-        __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
-        __builtin_amdgcn_wave_barrier();
-        __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+        const float gh = gate ? gate[h] : 1.f;
+#pragma unroll
+        for (int u = 0; u < UG; ++u) {
+            float ss = 0.f;
+#pragma unroll
+            for (int j = 0; j < 8; ++j)
+#pragma unroll
+                for (int i = 0; i < 4; ++i) ss = fmaf(acc[u][j][i], acc[u][j][i], ss);
+            ss += shfl_xor(ss, 16);
+            ss += shfl_xor(ss, 32);
+            // the gate is a scalar, so it commutes with the rotation: fold it into the norm
+            const float sc = gh * __builtin_amdgcn_rsqf(ss * (1.f / D) + eps);
+            int t = t0[u] + c16;
+            if (!one_seq[u]) {
+                int b;
+                seq_pos(tok_ok[u] ? (int)tok[u] : 0, T, b, t);
+            }
+            float n[8][4];
+#pragma unroll
+            for (int j = 0; j < 8; ++j) {
+                const f32x4 gmv = *(const f32x4*)&gam[16 * j + 4 * g];
+#pragma unroll
+                for (int i = 0; i < 4; ++i) n[j][i] = gmv[i] * acc[u][j][i] * sc;
+            }
+            if (log2_base > 0.f) {
+                if (hh == 0) {
+                    const float pos = (float)(pos0[u] + t);
+#pragma unroll
+                    for (int j = 0; j < 4; ++j)
+#pragma unroll
+                        for (int i = 0; i < 4; ++i) {
+                            // fraction of a turn: p + e = pos * turns exactly (e from the fma),
+                            // less the nearest whole number of turns
+                            const float p = pos * turns[j][i];
+                            const float e = fmaf(pos, turns[j][i], -p);
+                            const float fr = (p - rintf(p)) + e;
+                            rs[u][j][i] = __builtin_amdgcn_sinf(fr);
+                            rc[u][j][i] = __builtin_amdgcn_cosf(fr);
+                        }
+                }
+#pragma unroll
+                for (int j = 0; j < 4; ++j)
+#pragma unroll
+                    for (int i = 0; i < 4; ++i) {
+                        const float lo = n[j][i], hi = n[j + 4][i];
+                        n[j][i] = lo * rc[u][j][i] - hi * rs[u][j][i];
+                        n[j + 4][i] = hi * rc[u][j][i] + lo * rs[u][j][i];
+                    }
+            }
+            // The group's 16 rows go through LDS so that each store writes whole 256-byte rows:
+            // lane (c16, g) then stores 16-byte piece c16 of rows 4 r + g, r = 0..3.
+#pragma unroll
+            for (int j = 0; j < 8; ++j)
+                *(u32x2*)&ot[w][c16][16 * j + 4 * g] = u32x2{pack_bf16x2(n[j][0], n[j][1]),
+                                                          pack_bf16x2(n[j][2], n[j][3])};
+            __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+            __builtin_amdgcn_wave_barrier();
+            __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+            __bf16* const row0 = rho + (((size_t)b0[u] * H + h) * T + t0[u]) * D + 8 * c16;
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+                const int row = 4 * r + g;
+                const int tr = tg0[u] + row;
+                const u32x4 val = *(const u32x4*)&ot[w][row][8 * c16];
+                if (one_seq[u]) {
+                    *(u32x4*)(row0 + (size_t)row * D) = val;
+                } else if (tr < N) {
+                    int br, trr;
+                    seq_pos(tr, T, br, trr);
+                    *(u32x4*)(rho + (((size_t)br * H + h) * T + trr) * D + 8 * c16) = val;
+                }
+            }
+            __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+            __builtin_amdgcn_wave_barrier();
+            __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+        }
     }
 }
 
@@ -206,18 +278,20 @@ __global__ __launch_bounds__(NT) void probe_bf16_d128_kernel(
 hipError_t launch_probe_bf16_d128(const ProbeArgs& a, hipStream_t stream) {
     const long long N = (long long)a.B * a.T;
     const float lb = a.rope_base > 0.f ? log2f(a.rope_base) : 0.f;
-    auto go = [&](auto kernel, int tok) {
+    auto go = [&](auto kernel, int tok, int hg) {
         const long long nblk = (N + tok - 1) / tok;
         if (nblk > 0x7fffffffLL) return hipErrorInvalidConfiguration;
-        hipLaunchKernelGGL(kernel, dim3((unsigned)nblk, a.H), dim3(NT), 0, stream,
+        hipLaunchKernelGGL(kernel, dim3((unsigned)nblk, a.H / hg), dim3(NT), 0, stream,
                            (const __bf16*)a.x, (const __bf16*)a.w_r, a.gamma, a.gate,
                            a.positions, (__bf16*)a.rho, a.B, a.T, a.C, a.H, a.eps, lb);
         return hipGetLastError();
     };
-    // Narrow inputs (one K step or two): one token group per wave. Measured at 4 x 2048 tokens,
-    // H = 16: see the probe producer's profile.
-    if (a.C <= kProbeNarrowC) return go(probe_bf16_d128_kernel<1>, 64);
-    return go(probe_bf16_d128_kernel<2>, 128);
+    // Narrow inputs (one K step or two): one token group per wave; with one K step and an even
+    // head count, two heads per workgroup. Measured at 4 x 2048 tokens, H = 16: see the probe
+    // producer's profile.
+    if (a.C <= 32 && a.H % 2 == 0) return go(probe_bf16_d128_kernel<1, 2>, 64, 2);
+    if (a.C <= kProbeNarrowC) return go(probe_bf16_d128_kernel<1, 1>, 64, 1);
+    return go(probe_bf16_d128_kernel<2, 1>, 128, 1);
 }
 
 }  // namespace plx

@@ -26,10 +26,12 @@ def _inputs(seed, B, T, C, H, d=128):
 
 # (B, T, C, H): decode-like single tokens; ragged token counts (not a multiple of 64);
 # an input width that is not a multiple of 32; a wide input (many K steps); the widths on either
-# side of the switch from one to two token groups per wave (64 / 96)
+# side of the switch from one to two token groups per wave (64 / 96); two heads per workgroup
+# (one K step, even H) with 16-token groups inside one sequence (T = 160) and across
+# sequence ends (T = 77), and the odd-H and two-K-step cases that keep one head
 @pytest.mark.parametrize("B,T,C,H", [(4, 1, 32, 16), (2, 100, 32, 3), (3, 77, 40, 2),
                                      (1, 64, 2048, 2), (1, 300, 256, 1), (2, 130, 64, 2),
-                                     (1, 129, 96, 2)])
+                                     (1, 129, 96, 2), (2, 160, 32, 4), (3, 77, 24, 2)])
 @pytest.mark.parametrize("opts", ["plain", "gamma_gate", "rope"])
 def test_probe_matches_oracle(B, T, C, H, opts):
     x, w, gamma, gate = _inputs(B * 1000 + T + C, B, T, C, H)

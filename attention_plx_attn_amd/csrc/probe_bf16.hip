@@ -155,26 +155,56 @@ __global__ __launch_bounds__(NT, UG == 1 ? 4 : 1) void probe_bf16_d128_kernel(
     }
     put(0, st);
     __syncthreads();
-    int buf = 0;
     // One K step; the first starts the accumulators from zero.
-    auto kstep = [&](int k0, bool first) {
-        const bool more = k0 + 32 < C;
-        if (more) stage(k0 + 32, st);
-        if (k0 > 0) load_x(k0, bx);
+    // K steps of 32. Wide inputs (UG = 2, many steps) are software-pipelined: the W_R slice
+    // of step k is requested two steps ahead (alternating register sets) and written to its
+    // LDS buffer at the end of step k - 1; the x rows of step k are requested at the end of
+    // step k - 2 (alternating sets). Steps alternate between the buffers and register sets A
+    // (even) and B (odd), unrolled by two so that no register set is copied while its loads
+    // are in flight. Narrow inputs (one or two steps) request each step's data in the step
+    // before.
+    auto products = [&](int b, const bf16x8 (&x)[UG], bool first) {
 #pragma unroll
         for (int j = 0; j < 8; ++j) {
-            const bf16x8 a = *(const bf16x8*)&wl[buf][(16 * j + c16) * WROW + 8 * g];
+            const bf16x8 a = *(const bf16x8*)&wl[b][(16 * j + c16) * WROW + 8 * g];
 #pragma unroll
             for (int u = 0; u < UG; ++u)
-                acc[u][j] = mfma16(a, bx[u], first ? f32x4{} : acc[u][j]);
+                acc[u][j] = mfma16(a, x[u], first ? f32x4{} : acc[u][j]);
         }
-        if (more) put(buf ^ 1, st);
-        __syncthreads();
-        buf ^= 1;
     };
-    if constexpr (HG == 1) {
-        kstep(0, true);
-        for (int k0 = 32; k0 < C; k0 += 32) kstep(k0, false);
+    if constexpr (HG == 1 && UG == 1) {
+        int buf = 0;
+        for (int k0 = 0; k0 < C; k0 += 32) {
+            const bool more = k0 + 32 < C;
+            if (more) stage(k0 + 32, st);
+            if (k0 > 0) load_x(k0, bx);
+            products(buf, bx, k0 == 0);
+            if (more) put(buf ^ 1, st);
+            __syncthreads();
+            buf ^= 1;
+        }
+    } else if constexpr (HG == 1) {
+        u32x4 stb[2];
+        bf16x8 bxb[UG];
+        if (C > 32) {
+            stage(32, stb);
+            load_x(32, bxb);
+        }
+        for (int k0 = 0; k0 < C; k0 += 64) {
+            // step k0: buffer 0, set A (st, bx)
+            if (k0 + 64 < C) stage(k0 + 64, st);
+            products(0, bx, k0 == 0);
+            if (k0 + 64 < C) load_x(k0 + 64, bx);
+            if (k0 + 32 < C) put(1, stb);
+            __syncthreads();
+            if (k0 + 32 >= C) break;
+            // step k0 + 32: buffer 1, set B
+            if (k0 + 96 < C) stage(k0 + 96, stb);
+            products(1, bxb, false);
+            if (k0 + 96 < C) load_x(k0 + 96, bxb);
+            if (k0 + 64 < C) put(0, st);
+            __syncthreads();
+        }
     }
 
     // acc[u][j][i]: dim 16 j + 4 g + i of token tok[u]. The lane's 16 rotation pairs are

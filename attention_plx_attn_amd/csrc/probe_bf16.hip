@@ -184,25 +184,27 @@ __global__ __launch_bounds__(NT, UG == 1 ? 4 : 1) void probe_bf16_d128_kernel(
             buf ^= 1;
         }
     } else if constexpr (HG == 1) {
+        // The loads are issued whether or not their step exists: past C they read zeros
+        // without touching memory, and the same loads outstanding on every path let each
+        // step wait only for its own data (a conditional load would make the compiler wait
+        // for every load in flight after the join).
         u32x4 stb[2];
         bf16x8 bxb[UG];
-        if (C > 32) {
-            stage(32, stb);
-            load_x(32, bxb);
-        }
+        stage(32, stb);
+        load_x(32, bxb);
         for (int k0 = 0; k0 < C; k0 += 64) {
             // step k0: buffer 0, set A (st, bx)
-            if (k0 + 64 < C) stage(k0 + 64, st);
+            stage(k0 + 64, st);
             products(0, bx, k0 == 0);
-            if (k0 + 64 < C) load_x(k0 + 64, bx);
-            if (k0 + 32 < C) put(1, stb);
+            load_x(k0 + 64, bx);
+            put(1, stb);
             __syncthreads();
             if (k0 + 32 >= C) break;
             // step k0 + 32: buffer 1, set B
-            if (k0 + 96 < C) stage(k0 + 96, stb);
+            stage(k0 + 96, stb);
             products(1, bxb, false);
-            if (k0 + 96 < C) load_x(k0 + 96, bxb);
-            if (k0 + 64 < C) put(0, st);
+            load_x(k0 + 96, bxb);
+            put(0, st);
             __syncthreads();
         }
     }

@@ -23,9 +23,10 @@
 //     keys, 16-byte key chunks XOR-swizzled with bits 4..6 of d), so a value operand is one
 //     16-byte LDS read whose address is a per-lane base plus a constant;
 //   * P1 and P2 are rounded to bf16 and l = sum P1, beta = sum P2 are taken from the rounded
-//     values, so the effective corrected weights sum to exactly one; P2 = P1 * T is formed
-//     from the unrounded P1 (or, in the SPLIT instances, both go in as hi + lo bf16 terms
-//     and l, beta are fp32 sums of the unrounded weights);
+//     values, so the effective corrected weights sum to exactly one; the sums run on the
+//     matrix cores as one more value product each, against a block of ones; P2 = P1 * T is
+//     formed from the unrounded P1 (or, in the SPLIT instances, both go in as hi + lo bf16
+//     terms and l, beta are fp32 sums of the unrounded weights);
 //   * the running max is updated lazily (only when a row's tile max exceeds it by more than
 //     2^8); the result is the same exact expression, with far fewer rescales.
 // A tile holds BC = 64 keys at d = 128 and BC = 128 keys at d = 64 (the same bytes).
@@ -184,6 +185,13 @@ __global__ __launch_bounds__(NT, 1) void prefill_bf16_kernel(
 
     f32x4 a1[NDB], a2[NDB];  // O1^T, O2^T: dim block db (16 dims), lane: dims 16 db + 4 gq + i
     float lsum = 0.f, bsum = 0.f;
+    // Single bf16 weights: l and beta are summed on the matrix cores, as the value products of
+    // a block of ones (every row of the accumulator holds the column sums of P1^T and P2^T);
+    // each lane then holds the full sums of its query. The split instances sum fp32 weights.
+    f32x4 al = {}, ab = {};
+    bf16x8 ones;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) ones[i] = (__bf16)1.0f;
     float lsx = 0.f, bsx = 0.f;  // STATS: the same sums of the unrounded weights and products
     float m_run = -INFINITY;
 
@@ -343,6 +351,10 @@ __global__ __launch_bounds__(NT, 1) void prefill_bf16_kernel(
                 if constexpr (PROBE) a2[db] = mfma16(vf, q2, a2[db]);
             }
         }
+        if constexpr (!SPLIT) {
+            al = mfma16(ones, p1, al);
+            if constexpr (PROBE) ab = mfma16(ones, p2, ab);
+        }
         __builtin_amdgcn_iglp_opt(1);
     };
 
@@ -386,8 +398,13 @@ __global__ __launch_bounds__(NT, 1) void prefill_bf16_kernel(
                 a1[db] *= alpha;
                 if constexpr (PROBE) a2[db] *= alpha;
             }
-            lsum *= alpha;
-            if constexpr (PROBE) bsum *= alpha;
+            if constexpr (SPLIT) {
+                lsum *= alpha;
+                if constexpr (PROBE) bsum *= alpha;
+            } else {
+                al *= alpha;
+                if constexpr (PROBE) ab *= alpha;
+            }
             if constexpr (STATS) {
                 lsx *= alpha;
                 bsx *= alpha;
@@ -410,8 +427,6 @@ __global__ __launch_bounds__(NT, 1) void prefill_bf16_kernel(
                 if constexpr (SPLIT) {
                     q1[e] = pack_bf16x2(w0 - bf16_lo(p1[e]), w1 - bf16_hi(p1[e]));
                     lsum += w0 + w1;
-                } else {
-                    lsum = add_bf16x2(p1[e], lsum);
                 }
                 if constexpr (STATS) {
                     lsx += w0 + w1;
@@ -423,8 +438,6 @@ __global__ __launch_bounds__(NT, 1) void prefill_bf16_kernel(
                     if constexpr (SPLIT) {
                         q2[e] = pack_bf16x2(u0 - bf16_lo(p2[e]), u1 - bf16_hi(p2[e]));
                         bsum += u0 + u1;
-                    } else {
-                        bsum = add_bf16x2(p2[e], bsum);
                     }
                 } else {
                     p2[e] = 0u;
@@ -505,6 +518,7 @@ __global__ __launch_bounds__(NT, 1) void prefill_bf16_kernel(
 #pragma unroll
         for (int db = 0; db < NDB; ++db) a1[db] = a2[db] = f32x4{};  // a2 stays 0 without PROBE
         lsum = bsum = 0.f;
+        al = ab = f32x4{};
         lsx = bsx = 0.f;
         m_run = -INFINITY;
         const int qi = cur.q0 + 16 * w + col;
@@ -537,15 +551,18 @@ __global__ __launch_bounds__(NT, 1) void prefill_bf16_kernel(
             slot_end(kt);
         }
         __builtin_amdgcn_s_waitcnt(0x0F70);
-        // ---- epilogue: l and beta over the four lanes of each query; o = (A1/l)(1 + beta/l)
-        // - A2/l, rounded to bf16.
-        lsum += __int_as_float(__builtin_amdgcn_ds_swizzle(__float_as_int(lsum), 0x401F));
-        {
+        // ---- epilogue: l and beta (split instances: over the four lanes of each query);
+        // o = (A1/l)(1 + beta/l) - A2/l, rounded to bf16.
+        if constexpr (!SPLIT) {
+            lsum = al[0];
+            bsum = PROBE ? ab[0] : 0.f;
+        } else {
+            lsum += __int_as_float(__builtin_amdgcn_ds_swizzle(__float_as_int(lsum), 0x401F));
             const auto r1 = __builtin_amdgcn_permlane32_swap(__float_as_int(lsum),
                                                              __float_as_int(lsum), false, false);
             lsum = __int_as_float(r1[0]) + __int_as_float(r1[1]);
         }
-        if constexpr (PROBE) {
+        if constexpr (PROBE && SPLIT) {
             bsum += __int_as_float(__builtin_amdgcn_ds_swizzle(__float_as_int(bsum), 0x401F));
             const auto r2 = __builtin_amdgcn_permlane32_swap(__float_as_int(bsum),
                                                              __float_as_int(bsum), false, false);

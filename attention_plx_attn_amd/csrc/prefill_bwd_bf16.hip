@@ -31,8 +31,10 @@
 //     (B), then dV^T += dO^T s, dK^T += Q^T (scale da) + R^T dt, whose A operands (8 queries
 //     of one dim per lane) come from the same row-major tiles through gfx950's transposing
 //     LDS read, so the tiles are stored once.
-// Both kernels double-buffer their tiles in LDS: tile n + 1 is loaded into registers while
-// tile n is processed and written to the other buffer afterwards; one barrier per tile.
+// Both kernels double-buffer their tiles in LDS with one barrier per tile: tile n + 1 is
+// requested while tile n is processed. The dk kernel at d = 128 loads its Q, R and dO tiles
+// straight into LDS (direct-to-LDS loads into unpadded, chunk-swizzled rows); otherwise tile
+// n + 1 goes through registers and is written to the other buffer after tile n.
 // Work items are dispatched longest first; with B*H a multiple of 8, item n (dispatched to
 // XCD n % 8) serves head n % (B*H), so all items of a head share one XCD's L2.
 #include "plx_device.hpp"
@@ -96,6 +98,82 @@ __device__ __forceinline__ i16x4 read_tr(const unsigned char* p) {
 __device__ __forceinline__ bf16x8 read_tr_operand(const unsigned char* p, int row_bytes) {
     const i16x4 lo = read_tr(p), hi = read_tr(p + 16 * row_bytes);
     return __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
+}
+
+// ---- direct-to-LDS tiles (d = 128): 64 rows of 256 bytes, unpadded. Chunk c (16 bytes) of
+// LDS row r sits at position c ^ swz(r), swz(r) = 2 (r & 7) + bit 3 of r. For one chunk, the
+// 16 rows of a row-operand read (r & 15 = 0..15) get 16 distinct positions; for the chunk
+// pair 2 db, 2 db + 1 of a transposing read, rows 0..7 (and 8..15) of each 16 get 8 distinct
+// 32-byte spans (db ^ (r & 7)).
+__device__ __forceinline__ int swz(int r) { return 2 * (r & 7) | ((r >> 3) & 1); }
+
+// Inverse of prow: the tile element stored at LDS row r.
+__device__ __forceinline__ int prow_inv(int r) {
+    return (r & 32) | (((r >> 2) & 3) << 3) | (((r >> 4) & 1) << 2) | (r & 3);
+}
+
+typedef int i32x4 __attribute__((ext_vector_type(4)));
+
+__device__ __forceinline__ i32x4 raw_rsrc(const void* base, uint32_t bytes) {
+    const uint64_t a = (uint64_t)base;
+    return i32x4{(int)(uint32_t)a, (int)((uint32_t)(a >> 32) & 0xFFFFu), (int)bytes, 0x00020000};
+}
+
+__device__ __forceinline__ uint32_t lds_addr(const void* p) {
+    return (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) void*)p;
+}
+
+// Six 16-byte direct-to-LDS loads: from each of three raw buffers (bounds-checked, zeros past
+// the end) byte offsets o0 and o1 of this lane, into LDS bytes lds + TB t + 1024 i + 16 lane
+// (t = buffer, i = offset). Issued from one asm block so that the compiler's wait accounting
+// does not track them (it would otherwise make the LDS reads that follow wait for them); the
+// caller waits (vmcnt) before the barrier that publishes the tile. M0 is restored on exit;
+// the leading s_nop covers a VALU write of the resources' SGPRs just before.
+template <int TB>
+__device__ __forceinline__ void dma3x2(i32x4 r0, i32x4 r1, i32x4 r2, uint32_t lds, uint32_t o0,
+                                       uint32_t o1) {
+    uint32_t saved;
+    asm volatile(
+        "s_nop 4\n\t"
+        "s_mov_b32 %0, m0\n\t"
+        "s_mov_b32 m0, %1\n\t"
+        "s_nop 0\n\t"
+        "buffer_load_dwordx4 %5, %2, 0 offen lds\n\t"
+        "s_add_u32 m0, %1, 0x400\n\t"
+        "s_nop 0\n\t"
+        "buffer_load_dwordx4 %6, %2, 0 offen lds\n\t"
+        "s_add_u32 m0, %1, %7\n\t"
+        "s_nop 0\n\t"
+        "buffer_load_dwordx4 %5, %3, 0 offen lds\n\t"
+        "s_add_u32 m0, %1, %8\n\t"
+        "s_nop 0\n\t"
+        "buffer_load_dwordx4 %6, %3, 0 offen lds\n\t"
+        "s_add_u32 m0, %1, %9\n\t"
+        "s_nop 0\n\t"
+        "buffer_load_dwordx4 %5, %4, 0 offen lds\n\t"
+        "s_add_u32 m0, %1, %10\n\t"
+        "s_nop 0\n\t"
+        "buffer_load_dwordx4 %6, %4, 0 offen lds\n\t"
+        "s_mov_b32 m0, %0"
+        : "=&s"(saved)
+        : "s"(lds), "s"(r0), "s"(r1), "s"(r2), "v"(o0), "v"(o1), "n"(TB), "n"(TB + 0x400),
+          "n"(2 * TB), "n"(2 * TB + 0x400)
+        : "memory", "scc");
+}
+
+// One 16-byte direct-to-LDS load: byte offset o of raw buffer r into LDS bytes lds + 16 lane.
+__device__ __forceinline__ void dma1(i32x4 r, uint32_t lds, uint32_t o) {
+    uint32_t saved;
+    asm volatile(
+        "s_nop 4\n\t"
+        "s_mov_b32 %0, m0\n\t"
+        "s_mov_b32 m0, %1\n\t"
+        "s_nop 0\n\t"
+        "buffer_load_dwordx4 %3, %2, 0 offen lds\n\t"
+        "s_mov_b32 m0, %0"
+        : "=&s"(saved)
+        : "s"(lds), "s"(r), "v"(o)
+        : "memory", "scc");
 }
 
 // Item n of a launch of BH * nblk items, longest first: block index and (b, h).
@@ -292,7 +370,12 @@ __global__ __launch_bounds__(NT, 1) void prefill_bwd_dk_kernel(
     using G_ = BG<D>;
     constexpr int RS = G_::RS, NS = G_::NS, NDB = G_::NDB, CPR = G_::CPR, CPR_LOG = G_::CPR_LOG;
     constexpr uint32_t ROWB = G_::ROWB;
-    constexpr int K_R = QBC * RS * 2;  // bytes of one row-major tile (Q, R or dO)
+    // DMA: the Q, R and dO tiles (and the row records) arrive by direct-to-LDS loads into
+    // unpadded, chunk-swizzled rows (swz); otherwise through registers into rows padded by 16
+    // bytes.
+    constexpr bool DMA = D == 128;
+    constexpr int RB = DMA ? 2 * D : RS * 2;  // LDS bytes per tile row
+    constexpr int K_R = QBC * RB;              // bytes of one row-major tile (Q, R or dO)
     constexpr int K_BUF = 3 * K_R + K_REC;
     static_assert(2 * K_BUF <= 160 * 1024, "LDS budget");
     __shared__ __attribute__((aligned(16))) unsigned char lds[2 * K_BUF];
@@ -356,10 +439,42 @@ __global__ __launch_bounds__(NT, 1) void prefill_bwd_dk_kernel(
                 stg[m];
         if (w == 0) *(u32x4*)(base + 3 * K_R + 16 * lane) = srec;
     };
+    // DMA: wave w fills LDS rows 8 w .. 8 w + 7 of each tile (two 1 KB loads per tensor, 16
+    // bytes per lane in lane order): lane (row r, position p) fetches chunk p ^ swz(r) of
+    // tile element prow_inv(r). Wave 0 also loads the 64 row records. Rows past T read as
+    // zero.
+    uint32_t dsrc[2];
+#pragma unroll
+    for (int i = 0; i < 2; ++i) {
+        const int r = 8 * w + 4 * i + (lane >> 4);
+        dsrc[i] = (uint32_t)prow_inv(r) * ROWB + 16u * ((lane & 15) ^ swz(r));
+    }
+    auto stage = [&](int n, int buf) {
+        const int r0 = (qt0 + n) * QBC;
+        const uint32_t rem = slice_bytes - (uint32_t)r0 * ROWB;
+        const size_t at = slice + (size_t)r0 * D;
+        unsigned char* base = lds + buf * K_BUF;
+        dma3x2<K_R>(raw_rsrc(q + at, rem), raw_rsrc(rho + at, rem), raw_rsrc(dout + at, rem),
+                    lds_addr(base) + 8 * w * RB, dsrc[0], dsrc[1]);
+        if (w == 0)
+            dma1(raw_rsrc(rec + (size_t)bh * T + r0, (uint32_t)(T - r0) * 16u),
+                 lds_addr(base + 3 * K_R), 16u * lane);
+    };
 
     // transposed-read lane base: source lane (4 j + a) of group gq addresses tile row
-    // 4 gq + j (+ 32 G + 16 h), dims 4 a .. +3 (+ 16 db)
-    const int trl = (4 * gq + (col >> 2)) * RS * 2 + 8 * (col & 3);
+    // 4 gq + j (+ 32 G + 16 h), dims 4 a .. +3 (+ 16 db). DMA: the dims' 32-byte span db sits
+    // at span db ^ (r & 7) of the row, with its two chunks swapped when bit 3 of r is set.
+    const int trl = (4 * gq + (col >> 2)) * RB + 8 * (col & 3);
+    int trd[DMA ? NDB : 1];
+    int rowc[DMA ? NS : 1];  // DMA: byte of chunk 4 s + gq in LDS row col
+    if constexpr (DMA) {
+        const int r = 4 * gq + (col >> 2), f = swz(r);
+#pragma unroll
+        for (int db = 0; db < NDB; ++db)
+            trd[db] = r * RB + 16 * ((2 * db + ((col & 3) >> 1)) ^ f) + 8 * (col & 1);
+#pragma unroll
+        for (int s = 0; s < NS; ++s) rowc[s] = col * RB + 16 * ((4 * s + gq) ^ swz(col));
+    }
 
     auto tile = [&](int n, int buf, bool mask) {
         const unsigned char* base = lds + buf * K_BUF;
@@ -370,10 +485,11 @@ __global__ __launch_bounds__(NT, 1) void prefill_bwd_dk_kernel(
             S[b] = Tp[b] = Gm[b] = f32x4{};
 #pragma unroll
             for (int s = 0; s < NS; ++s) {
-                const int o = 16 * b * RS * 2 + 64 * s;
-                S[b] = mfma16(*(const bf16x8*)(Qr + o), xk[s], S[b]);
-                Tp[b] = mfma16(*(const bf16x8*)(Qr + K_R + o), xk[s], Tp[b]);
-                Gm[b] = mfma16(*(const bf16x8*)(Qr + 2 * K_R + o), xv[s], Gm[b]);
+                const unsigned char* a =
+                    DMA ? base + rowc[s] + 16 * b * RB : Qr + 16 * b * RS * 2 + 64 * s;
+                S[b] = mfma16(*(const bf16x8*)a, xk[s], S[b]);
+                Tp[b] = mfma16(*(const bf16x8*)(a + K_R), xk[s], Tp[b]);
+                Gm[b] = mfma16(*(const bf16x8*)(a + 2 * K_R), xv[s], Gm[b]);
             }
         }
         // register i of block b: query (qt0 + n) * 64 + 32 (b >> 1) + 8 gq + 4 (b & 1) + i
@@ -398,11 +514,11 @@ __global__ __launch_bounds__(NT, 1) void prefill_bwd_dk_kernel(
                     fa[4 * bb + i] = scale * p * (fmaf(one, g, t * rw[2]) - rw[3]);
                 }
             const bf16x8 ps = pack8(fs), pa = pack8(fa), pt = pack8(ft);
-            const unsigned char* Tr = base + trl + 32 * G2 * RS * 2;
+            const unsigned char* Tr = base + (DMA ? 0 : trl) + 32 * G2 * RB;
 #pragma unroll
             for (int db = 0; db < NDB; ++db) {
-                const int o = 32 * db;
-                auto op = [&](int tensor) { return read_tr_operand(Tr + tensor * K_R + o, RS * 2); };
+                const int o = DMA ? trd[db] : 32 * db;
+                auto op = [&](int tensor) { return read_tr_operand(Tr + tensor * K_R + o, RB); };
                 av[db] = mfma16(op(2), ps, av[db]);
                 ak[db] = mfma16(op(0), pa, ak[db]);
                 ak[db] = mfma16(op(1), pt, ak[db]);
@@ -411,17 +527,32 @@ __global__ __launch_bounds__(NT, 1) void prefill_bwd_dk_kernel(
     };
 
     const int tail = (T - 1) / QBC - qt0;
-    gload(0);
-    lstore(0);
-    __syncthreads();
-    for (int n = 0; n < ntiles; ++n) {
-        const int buf = n & 1;
-        const bool more = n + 1 < ntiles;
-        if (more) gload(n + 1);
-        const int r0 = (qt0 + n) * QBC;
-        if (r0 + QBC - 1 >= k0 + 16 * w) tile(n, buf, r0 < k0 + KBR || n == tail);
-        if (more) lstore(buf ^ 1);
+    if constexpr (DMA) {
+        stage(0, 0);
+        __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0): this wave's loads are in LDS
         __syncthreads();
+        for (int n = 0; n < ntiles; ++n) {
+            const int buf = n & 1;
+            const bool more = n + 1 < ntiles;
+            if (more) stage(n + 1, buf ^ 1);
+            const int r0 = (qt0 + n) * QBC;
+            if (r0 + QBC - 1 >= k0 + 16 * w) tile(n, buf, r0 < k0 + KBR || n == tail);
+            __builtin_amdgcn_s_waitcnt(0x0F70);
+            __syncthreads();
+        }
+    } else {
+        gload(0);
+        lstore(0);
+        __syncthreads();
+        for (int n = 0; n < ntiles; ++n) {
+            const int buf = n & 1;
+            const bool more = n + 1 < ntiles;
+            if (more) gload(n + 1);
+            const int r0 = (qt0 + n) * QBC;
+            if (r0 + QBC - 1 >= k0 + 16 * w) tile(n, buf, r0 < k0 + KBR || n == tail);
+            if (more) lstore(buf ^ 1);
+            __syncthreads();
+        }
     }
 
     if (kj < T) {

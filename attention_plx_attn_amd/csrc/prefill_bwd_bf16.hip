@@ -32,9 +32,9 @@
 //     of one dim per lane) come from the same row-major tiles through gfx950's transposing
 //     LDS read, so the tiles are stored once.
 // Both kernels double-buffer their tiles in LDS with one barrier per tile: tile n + 1 is
-// requested while tile n is processed. The dk kernel at d = 128 loads its Q, R and dO tiles
-// straight into LDS (direct-to-LDS loads into unpadded, chunk-swizzled rows); otherwise tile
-// n + 1 goes through registers and is written to the other buffer after tile n.
+// requested while tile n is processed. At d = 128 both kernels load their tiles (K and V; Q,
+// R and dO) straight into LDS (direct-to-LDS loads into unpadded, chunk-swizzled rows); at
+// d = 64 tile n + 1 goes through registers and is written to the other buffer after tile n.
 // Work items are dispatched longest first; with B*H a multiple of 8, item n (dispatched to
 // XCD n % 8) serves head n % (B*H), so all items of a head share one XCD's L2.
 #include "plx_device.hpp"
@@ -161,6 +161,32 @@ __device__ __forceinline__ void dma3x2(i32x4 r0, i32x4 r1, i32x4 r2, uint32_t ld
         : "memory", "scc");
 }
 
+// Four such loads from two buffers (as dma3x2 with two).
+template <int TB>
+__device__ __forceinline__ void dma2x2(i32x4 r0, i32x4 r1, uint32_t lds, uint32_t o0,
+                                       uint32_t o1) {
+    uint32_t saved;
+    asm volatile(
+        "s_nop 4\n\t"
+        "s_mov_b32 %0, m0\n\t"
+        "s_mov_b32 m0, %1\n\t"
+        "s_nop 0\n\t"
+        "buffer_load_dwordx4 %4, %2, 0 offen lds\n\t"
+        "s_add_u32 m0, %1, 0x400\n\t"
+        "s_nop 0\n\t"
+        "buffer_load_dwordx4 %5, %2, 0 offen lds\n\t"
+        "s_add_u32 m0, %1, %6\n\t"
+        "s_nop 0\n\t"
+        "buffer_load_dwordx4 %4, %3, 0 offen lds\n\t"
+        "s_add_u32 m0, %1, %7\n\t"
+        "s_nop 0\n\t"
+        "buffer_load_dwordx4 %5, %3, 0 offen lds\n\t"
+        "s_mov_b32 m0, %0"
+        : "=&s"(saved)
+        : "s"(lds), "s"(r0), "s"(r1), "v"(o0), "v"(o1), "n"(TB), "n"(TB + 0x400)
+        : "memory", "scc");
+}
+
 // One 16-byte direct-to-LDS load: byte offset o of raw buffer r into LDS bytes lds + 16 lane.
 __device__ __forceinline__ void dma1(i32x4 r, uint32_t lds, uint32_t o) {
     uint32_t saved;
@@ -198,7 +224,11 @@ __global__ __launch_bounds__(NT, 1) void prefill_bwd_dq_kernel(
     using G_ = BG<D>;
     constexpr int RS = G_::RS, NS = G_::NS, NDB = G_::NDB, CPR = G_::CPR, CPR_LOG = G_::CPR_LOG;
     constexpr uint32_t ROWB = G_::ROWB;
-    constexpr int Q_KR = KBC * RS * 2;  // bytes of a row-major K (or V) tile
+    // DMA: the K and V tiles arrive by direct-to-LDS loads into unpadded, chunk-swizzled rows
+    // (swz); otherwise through registers into rows padded by 16 bytes.
+    constexpr bool DMA = D == 128;
+    constexpr int RB = DMA ? 2 * D : RS * 2;  // LDS bytes per tile row
+    constexpr int Q_KR = KBC * RB;             // bytes of a row-major K (or V) tile
     constexpr int Q_BUF = 2 * Q_KR;
     static_assert(2 * Q_BUF <= 160 * 1024, "LDS budget");
     __shared__ __attribute__((aligned(16))) unsigned char lds[2 * Q_BUF];
@@ -279,22 +309,50 @@ __global__ __launch_bounds__(NT, 1) void prefill_bwd_dq_kernel(
         for (int j = 0; j < KPT; ++j)
             *(u32x4*)(base + prow(KPT * skg + j) * RS * 2 + 16 * sdc) = stg[j];
     };
+    // DMA: wave w fills LDS rows 8 w .. 8 w + 7 of the K and the V tile (two 1 KB loads each,
+    // 16 bytes per lane in lane order): lane (row r, position p) fetches chunk p ^ swz(r) of
+    // key prow_inv(r). Rows past T read as zero.
+    uint32_t dsrc[2];
+#pragma unroll
+    for (int i = 0; i < 2; ++i) {
+        const int r = 8 * w + 4 * i + (lane >> 4);
+        dsrc[i] = (uint32_t)prow_inv(r) * ROWB + 16u * ((lane & 15) ^ swz(r));
+    }
+    auto stage = [&](int kt, int buf) {
+        const uint32_t rem = slice_bytes - (uint32_t)kt * KBC * ROWB;
+        const size_t at = slice + (size_t)kt * KBC * D;
+        dma2x2<Q_KR>(raw_rsrc(k + at, rem), raw_rsrc(v + at, rem),
+                     lds_addr(lds + buf * Q_BUF) + 8 * w * RB, dsrc[0], dsrc[1]);
+    };
     // K^T operands through the transposing read: source lane (4 j + a) of group gq addresses
-    // K tile row 4 gq + j (+ 32 G + 16 h), dims 4 a .. +3 (+ 16 db)
-    const int trl = (4 * gq + (col >> 2)) * RS * 2 + 8 * (col & 3);
+    // K tile row 4 gq + j (+ 32 G + 16 h), dims 4 a .. +3 (+ 16 db). DMA: the dims' 32-byte
+    // span db sits at span db ^ (r & 7) of the row, its two chunks swapped when bit 3 of r is
+    // set.
+    const int trl = (4 * gq + (col >> 2)) * RB + 8 * (col & 3);
+    int trd[DMA ? NDB : 1];
+    int rowc[DMA ? NS : 1];  // DMA: byte of chunk 4 s + gq in LDS row col
+    if constexpr (DMA) {
+        const int r = 4 * gq + (col >> 2), f = swz(r);
+#pragma unroll
+        for (int db = 0; db < NDB; ++db)
+            trd[db] = r * RB + 16 * ((2 * db + ((col & 3) >> 1)) ^ f) + 8 * (col & 1);
+#pragma unroll
+        for (int s = 0; s < NS; ++s) rowc[s] = col * RB + 16 * ((4 * s + gq) ^ swz(col));
+    }
 
     auto tile = [&](int kt, int buf, bool diag) {
         const unsigned char* Kr = lds + buf * Q_BUF + col * RS * 2 + 16 * gq;
-        const unsigned char* Vr = Kr + Q_KR;
-        const unsigned char* Kt = lds + buf * Q_BUF + trl;
+        const unsigned char* Kt = lds + buf * Q_BUF + (DMA ? 0 : trl);
         f32x4 S[4], Tp[4], Gm[4];
 #pragma unroll
         for (int kb = 0; kb < 4; ++kb) {
             S[kb] = Tp[kb] = Gm[kb] = f32x4{};
 #pragma unroll
             for (int s = 0; s < NS; ++s) {
-                const bf16x8 kf = *(const bf16x8*)(Kr + 16 * kb * RS * 2 + 64 * s);
-                const bf16x8 vf = *(const bf16x8*)(Vr + 16 * kb * RS * 2 + 64 * s);
+                const unsigned char* a = DMA ? lds + buf * Q_BUF + rowc[s] + 16 * kb * RB
+                                             : Kr + 16 * kb * RS * 2 + 64 * s;
+                const bf16x8 kf = *(const bf16x8*)a;
+                const bf16x8 vf = *(const bf16x8*)(a + Q_KR);
                 S[kb] = mfma16(kf, xq[s], S[kb]);
                 Tp[kb] = mfma16(kf, xr[s], Tp[kb]);
                 Gm[kb] = mfma16(vf, xdo[s], Gm[kb]);
@@ -321,7 +379,8 @@ __global__ __launch_bounds__(NT, 1) void prefill_bwd_dq_kernel(
             const bf16x8 da = pack8(fa), dt = pack8(ft);
 #pragma unroll
             for (int db = 0; db < NDB; ++db) {
-                const bf16x8 kf = read_tr_operand(Kt + 32 * G2 * RS * 2 + 32 * db, RS * 2);
+                const bf16x8 kf =
+                    read_tr_operand(Kt + 32 * G2 * RB + (DMA ? trd[db] : 32 * db), RB);
                 aq[db] = mfma16(kf, da, aq[db]);
                 ar[db] = mfma16(kf, dt, ar[db]);
             }
@@ -329,17 +388,31 @@ __global__ __launch_bounds__(NT, 1) void prefill_bwd_dq_kernel(
         }
     };
 
-    gload(0);
-    lstore(0);
-    __syncthreads();
-    for (int kt = 0; kt < ntiles; ++kt) {
-        const int buf = kt & 1;
-        const bool more = kt + 1 < ntiles;
-        if (more) gload(kt + 1);
-        // a wave whose rows all precede the tile's first key has nothing to add
-        if (kt * KBC <= q0 + 16 * w + 15) tile(kt, buf, kt >= nfull);
-        if (more) lstore(buf ^ 1);
+    if constexpr (DMA) {
+        stage(0, 0);
+        __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0): this wave's loads are in LDS
         __syncthreads();
+        for (int kt = 0; kt < ntiles; ++kt) {
+            const int buf = kt & 1;
+            if (kt + 1 < ntiles) stage(kt + 1, buf ^ 1);
+            // a wave whose rows all precede the tile's first key has nothing to add
+            if (kt * KBC <= q0 + 16 * w + 15) tile(kt, buf, kt >= nfull);
+            __builtin_amdgcn_s_waitcnt(0x0F70);
+            __syncthreads();
+        }
+    } else {
+        gload(0);
+        lstore(0);
+        __syncthreads();
+        for (int kt = 0; kt < ntiles; ++kt) {
+            const int buf = kt & 1;
+            const bool more = kt + 1 < ntiles;
+            if (more) gload(kt + 1);
+            // a wave whose rows all precede the tile's first key has nothing to add
+            if (kt * KBC <= q0 + 16 * w + 15) tile(kt, buf, kt >= nfull);
+            if (more) lstore(buf ^ 1);
+            __syncthreads();
+        }
     }
 
     if (qi < T) {

@@ -387,10 +387,14 @@ __global__ __launch_bounds__(NT, 1) void prefill_bf16_kernel(
             mt = max3(mt, S[kb + 1][0], S[kb + 1][1]);
             mt = max3(mt, S[kb + 1][2], S[kb + 1][3]);
         }
-        mt = max_across_row_groups(mt);
-        const float ms = mt > -INFINITY ? mt * c : -INFINITY;
-        const bool need = ms > m_run + kLazyTau;
-        if (wave_any(need)) {
+        // The running max moves only when some score of the row exceeds it by more than tau:
+        // each lane tests its own keys, and the max across the row's four lanes is formed
+        // only when some lane of the wave passes (the same decisions as testing the row max).
+        const bool need_lane = (mt > -INFINITY ? mt * c : -INFINITY) > m_run + kLazyTau;
+        if (wave_any(need_lane)) {
+            mt = max_across_row_groups(mt);
+            const float ms = mt > -INFINITY ? mt * c : -INFINITY;
+            const bool need = ms > m_run + kLazyTau;
             const float mn = need ? ms : m_run;
             const float alpha = exp2_fast(m_run - mn);
 #pragma unroll

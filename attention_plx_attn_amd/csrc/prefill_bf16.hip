@@ -17,7 +17,7 @@
 //   * K rows are stored in LDS in an order (key 8 q + 4 b + i of each 32-key group at row
 //     16 b + 4 q + i) that makes each lane's accumulator registers of two score blocks hold
 //     the 8 consecutive keys of its value-product operand: no cross-lane traffic;
-//   * at d = 128 (single bf16 weights) the V tiles arrive in LDS row-major, by direct-to-LDS
+//   * with single bf16 weights the V tiles arrive in LDS row-major, by direct-to-LDS
 //     loads, and each value operand (8 consecutive keys of one dim) is two transposing LDS
 //     reads (ds_read_b64_tr_b16); otherwise the V stagers store V transposed (d rows x BC
 //     keys, 16-byte key chunks XOR-swizzled with bits 4..6 of d), so a value operand is one
@@ -70,12 +70,12 @@ struct Geo {
     static constexpr int NKB = BC / 16;      // 16-key score blocks per tile
     static constexpr int NG = BC / 32;       // 32-key value steps per tile
     static constexpr int VS = BC + 8;        // LDS row stride of a transposed V tile
-    // KDMA (d = 128): the K tiles are staged by direct-to-LDS loads into unpadded 256-byte
-    // rows whose 16-byte chunks are XOR-swizzled by the row (chunk c of row r at position
-    // c ^ (r & 15)), which keeps the operand reads conflict-free without padding; the V tiles
-    // the same way, row-major with their own chunk swizzle (vswz), read back transposed.
-    // Otherwise the stagers store through registers: K into rows padded by 16 bytes, V
-    // transposed (d rows of BC keys, stride VS).
+    // KDMA (single bf16 weights): the K tiles are staged by direct-to-LDS loads into unpadded
+    // rows whose 16-byte chunks are XOR-swizzled by the row (kswz), which keeps the operand
+    // reads conflict-free without padding; the V tiles the same way, row-major with their own
+    // chunk swizzle (vswz), read back transposed. Otherwise (split weights) the stagers store
+    // through registers: K into rows padded by 16 bytes, V transposed (d rows of BC keys,
+    // stride VS).
     static constexpr bool KDMA = KDMA_;
     static constexpr int KS = KDMA ? D : D + 8;  // LDS row stride of a K tile (bf16 elements)
     static constexpr int K_ELEMS = BC * KS;      // 8192 bf16 at D = 128
@@ -108,10 +108,23 @@ __device__ __forceinline__ i16x4_t lds_read_tr(const unsigned char* p) {
         (lds_i16x4_t*)(__attribute__((address_space(3))) unsigned char*)p);
 }
 
-// Swizzle of the row-major V tile: chunk c of key row r sits at position c ^ vswz(r). The
-// value operand reads of one half-wave touch rows 8 g + j (+ 4, + 32 G) for g = 0, 1 and
-// j = 0..3, 32 bytes each: vswz gives these 8 rows 8 distinct 32-byte spans of the banks.
-__device__ __forceinline__ int vswz(int r) { return 2 * ((r & 3) | (((r >> 3) & 1) << 2)); }
+// Chunk swizzles of the direct-to-LDS tiles: chunk c of row r sits at position c ^ kswz(r)
+// in a K tile and c ^ vswz(r) in a V tile (rows of 16 chunks at d = 128, 8 at d = 64, so two
+// d = 64 rows share one 256-byte line of the 64 banks).
+//  * K: a score operand read touches rows 16 kb + 0..15 at one chunk: the 16 rows get 16
+//    distinct positions in the banks (d = 64: the 8 rows of either parity 8 distinct ones).
+//  * V: the value operand reads of one half-wave touch rows 8 g + j (+ 4, + 32 G) for g = 0, 1
+//    and j = 0..3, 32 bytes (a chunk pair) each: vswz is even, so pairs stay together, and
+//    it gives these 8 rows 8 distinct 32-byte spans of the banks.
+template <int D>
+__device__ __forceinline__ int kswz(int r) {
+    return D == 128 ? (r & 15) : ((r >> 1) & 7);
+}
+template <int D>
+__device__ __forceinline__ int vswz(int r) {
+    return D == 128 ? 2 * ((r & 3) | (((r >> 3) & 1) << 2))
+                    : 2 * (((r >> 1) & 1) | (((r >> 3) & 1) << 1));
+}
 
 __device__ __forceinline__ float max_across_row_groups(float x) {
     // max over the four lanes l, l ^ 16, l ^ 32, l ^ 48
@@ -141,15 +154,16 @@ __global__ __launch_bounds__(NT, 1) void prefill_bf16_kernel(
     const __bf16* __restrict__ rho, __bf16* __restrict__ o, __bf16* __restrict__ vbar,
     float* __restrict__ stats, int BH, int T, int nqb, float c, int ncls) {
     static_assert(!(STATS && SPLIT), "the statistics instances keep single bf16 weights");
-    // Direct-to-LDS K staging where it fits the register budget: at d = 128 without split
-    // weights (the split instances need the registers the role-specialised tile loops cost).
-    constexpr bool KDMA = D == 128 && !SPLIT;
+    // Direct-to-LDS K and V staging where it fits the register budget: without split weights
+    // (the split instances need the registers the role-specialised tile loops cost).
+    constexpr bool KDMA = !SPLIT;
     using G_ = Geo<D, KDMA>;
     constexpr int KS = G_::KS, K_ELEMS = G_::K_ELEMS, V_ELEMS = G_::V_ELEMS, OFF_V = G_::OFF_V;
     constexpr int BC = G_::BC, NKB = G_::NKB, NG = G_::NG, VS = G_::VS;
     constexpr int NS = G_::NS, NDB = G_::NDB, CPR = G_::CPR, CPR_LOG = G_::CPR_LOG;
     constexpr int KCH = G_::KCH;
     constexpr uint32_t ROWB = G_::ROWB;
+    constexpr int RPL = 1024 / (int)ROWB;  // LDS rows per 1 KB direct-to-LDS load
     __shared__ __attribute__((aligned(16))) unsigned char lds[G_::LDS_BYTES];
 
     const int tid = threadIdx.x;
@@ -223,17 +237,19 @@ __global__ __launch_bounds__(NT, 1) void prefill_bf16_kernel(
         if (is_k(role)) {
             const auto rk = make_rsrc(k + base, bytes);
             if constexpr (KDMA) {
-                // Load j of K-stager wave w fills LDS rows 16 j + 4 w .. +3 (1 KB, 16 bytes per
-                // lane in lane order): lane (row r, position p) fetches chunk p ^ (r & 15) of
-                // key krow_inv(r). Rows past T read as zero.
+                // Load j of K-stager wave w fills the RPL rows from LDS row RPL (4 j + w) on
+                // (1 KB, 16 bytes per lane in lane order; RPL = 1024 / ROWB): lane (row r,
+                // position p) fetches chunk p ^ kswz(r) of key krow_inv(r). Rows past T read
+                // as zero.
                 unsigned char* Kl = kbuf(t);
-                const int p = lane & 15;
+                const int p = lane & (CPR - 1);
 #pragma unroll
                 for (int j = 0; j < KCH; ++j) {
-                    const int r = 16 * j + 4 * w + (lane >> 4);
-                    const uint32_t src = (uint32_t)krow_inv(r) * ROWB + 16u * (p ^ (r & 15));
+                    const int r = RPL * (4 * j + w) + (lane >> CPR_LOG);
+                    const uint32_t src =
+                        (uint32_t)krow_inv(r) * ROWB + 16u * (p ^ kswz<D>(r));
                     __builtin_amdgcn_raw_ptr_buffer_load_lds(
-                        rk, (__attribute__((address_space(3))) void*)(Kl + (16 * j + 4 * w) * ROWB),
+                        rk, (__attribute__((address_space(3))) void*)(Kl + RPL * (4 * j + w) * ROWB),
                         16, src, 0, 0, 0);
                 }
             } else {
@@ -243,16 +259,16 @@ __global__ __launch_bounds__(NT, 1) void prefill_bf16_kernel(
         } else if (vactive) {
             const auto rv = make_rsrc(v + base, bytes);
             if constexpr (KDMA) {
-                // Load j of V-stager wave w fills LDS rows 16 j + 4 (w - 4) .. +3 in lane
-                // order: lane (row r, position p) fetches chunk p ^ vswz(r) of key r.
+                // Load j of V-stager wave w fills the RPL rows from LDS row RPL (4 j + w - 4)
+                // on in lane order: lane (row r, position p) fetches chunk p ^ vswz(r) of key r.
                 unsigned char* Vl = vbuf(t);
-                const int p = lane & 15, wv = w - 4;
+                const int p = lane & (CPR - 1), wv = w - 4;
 #pragma unroll
                 for (int j = 0; j < KCH; ++j) {
-                    const int r = 16 * j + 4 * wv + (lane >> 4);
-                    const uint32_t src = (uint32_t)r * ROWB + 16u * (p ^ vswz(r));
+                    const int r = RPL * (4 * j + wv) + (lane >> CPR_LOG);
+                    const uint32_t src = (uint32_t)r * ROWB + 16u * (p ^ vswz<D>(r));
                     __builtin_amdgcn_raw_ptr_buffer_load_lds(
-                        rv, (__attribute__((address_space(3))) void*)(Vl + (16 * j + 4 * wv) * ROWB),
+                        rv, (__attribute__((address_space(3))) void*)(Vl + RPL * (4 * j + wv) * ROWB),
                         16, src, 0, 0, 0);
                 }
             } else {
@@ -296,7 +312,7 @@ __global__ __launch_bounds__(NT, 1) void prefill_bf16_kernel(
     int klane[NS];
 #pragma unroll
     for (int s = 0; s < NS; ++s)
-        klane[s] = KDMA ? col * KS * 2 + 16 * (gq ^ (col & 3)) + 64 * (s ^ (col >> 2))
+        klane[s] = KDMA ? col * KS * 2 + 16 * ((4 * s + gq) ^ kswz<D>(col))
                         : col * KS * 2 + 16 * gq;  // + 64 s as an immediate offset below
     auto products = [&](int t, f32x4 (&S)[NKB], f32x4 (&Tp)[NKB]) {
         const unsigned char* Kl = kbuf(t);
@@ -324,7 +340,7 @@ __global__ __launch_bounds__(NT, 1) void prefill_bf16_kernel(
     // dims 16 db + 4 a .. +3, i.e. bytes 8 a of 32-byte span db ^ s at s = vswz(row) / 2.
     int vtr[KDMA ? NDB : 1];
     if constexpr (KDMA) {
-        const int j = col >> 2, sw = j | ((gq & 1) << 2);
+        const int j = col >> 2, sw = vswz<D>(8 * gq + j) / 2;
 #pragma unroll
         for (int db = 0; db < NDB; ++db)
             vtr[db] = (8 * gq + j) * (int)ROWB + 32 * (db ^ sw) + 8 * (col & 3);

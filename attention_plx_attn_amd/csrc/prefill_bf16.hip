@@ -17,11 +17,11 @@
 //   * K rows are stored in LDS in an order (key 8 q + 4 b + i of each 32-key group at row
 //     16 b + 4 q + i) that makes each lane's accumulator registers of two score blocks hold
 //     the 8 consecutive keys of its value-product operand: no cross-lane traffic;
-//   * with single bf16 weights the V tiles arrive in LDS row-major, by direct-to-LDS
-//     loads, and each value operand (8 consecutive keys of one dim) is two transposing LDS
-//     reads (ds_read_b64_tr_b16); otherwise the V stagers store V transposed (d rows x BC
-//     keys, 16-byte key chunks XOR-swizzled with bits 4..6 of d), so a value operand is one
-//     16-byte LDS read whose address is a per-lane base plus a constant;
+//   * the V tiles arrive in LDS row-major, by direct-to-LDS loads (all but the split-weights
+//     instances at d = 64), and each value operand (8 consecutive keys of one dim) is two
+//     transposing LDS reads (ds_read_b64_tr_b16); otherwise the V stagers store V transposed
+//     (d rows x BC keys, 16-byte key chunks XOR-swizzled with bits 4..6 of d), so a value
+//     operand is one 16-byte LDS read whose address is a per-lane base plus a constant;
 //   * P1 and P2 are rounded to bf16 and l = sum P1, beta = sum P2 are taken from the rounded
 //     values, so the effective corrected weights sum to exactly one; the sums run on the
 //     matrix cores as one more value product each, against a block of ones; P2 = P1 * T is
@@ -70,12 +70,12 @@ struct Geo {
     static constexpr int NKB = BC / 16;      // 16-key score blocks per tile
     static constexpr int NG = BC / 32;       // 32-key value steps per tile
     static constexpr int VS = BC + 8;        // LDS row stride of a transposed V tile
-    // KDMA (single bf16 weights): the K tiles are staged by direct-to-LDS loads into unpadded
-    // rows whose 16-byte chunks are XOR-swizzled by the row (kswz), which keeps the operand
-    // reads conflict-free without padding; the V tiles the same way, row-major with their own
-    // chunk swizzle (vswz), read back transposed. Otherwise (split weights) the stagers store
-    // through registers: K into rows padded by 16 bytes, V transposed (d rows of BC keys,
-    // stride VS).
+    // KDMA (all but the split-weights instances at d = 64): the K tiles are staged by
+    // direct-to-LDS loads into unpadded rows whose 16-byte chunks are XOR-swizzled by the row
+    // (kswz), which keeps the operand reads conflict-free without padding; the V tiles the same
+    // way, row-major with their own chunk swizzle (vswz), read back transposed. Otherwise the
+    // stagers store through registers: K into rows padded by 16 bytes, V transposed (d rows of
+    // BC keys, stride VS).
     static constexpr bool KDMA = KDMA_;
     static constexpr int KS = KDMA ? D : D + 8;  // LDS row stride of a K tile (bf16 elements)
     static constexpr int K_ELEMS = BC * KS;      // 8192 bf16 at D = 128
@@ -154,9 +154,9 @@ __global__ __launch_bounds__(NT, 1) void prefill_bf16_kernel(
     const __bf16* __restrict__ rho, __bf16* __restrict__ o, __bf16* __restrict__ vbar,
     float* __restrict__ stats, int BH, int T, int nqb, float c, int ncls) {
     static_assert(!(STATS && SPLIT), "the statistics instances keep single bf16 weights");
-    // Direct-to-LDS K and V staging where it fits the register budget: without split weights
-    // (the split instances need the registers the role-specialised tile loops cost).
-    constexpr bool KDMA = !SPLIT;
+    // Direct-to-LDS K and V staging where it fits the register budget: everywhere but the
+    // split instances at d = 64 (there the role-specialised tile loops would spill).
+    constexpr bool KDMA = !SPLIT || D == 128;
     using G_ = Geo<D, KDMA>;
     constexpr int KS = G_::KS, K_ELEMS = G_::K_ELEMS, V_ELEMS = G_::V_ELEMS, OFF_V = G_::OFF_V;
     constexpr int BC = G_::BC, NKB = G_::NKB, NG = G_::NG, VS = G_::VS;

@@ -32,9 +32,8 @@
 //     of one dim per lane) come from the same row-major tiles through gfx950's transposing
 //     LDS read, so the tiles are stored once.
 // Both kernels double-buffer their tiles in LDS with one barrier per tile: tile n + 1 is
-// requested while tile n is processed. At d = 128 both kernels load their tiles (K and V; Q,
-// R and dO) straight into LDS (direct-to-LDS loads into unpadded, chunk-swizzled rows); at
-// d = 64 tile n + 1 goes through registers and is written to the other buffer after tile n.
+// requested while tile n is processed, by direct-to-LDS loads (K and V; Q, R and dO) into
+// unpadded, chunk-swizzled rows.
 // Work items are dispatched longest first; with B*H a multiple of 8, item n (dispatched to
 // XCD n % 8) serves head n % (B*H), so all items of a head share one XCD's L2.
 #include "plx_device.hpp"
@@ -48,7 +47,6 @@ constexpr int NT = 512;   // 8 waves
 // Sizes that follow from the head dim D (64 or 128).
 template <int D>
 struct BG {
-    static constexpr int RS = D + 8;     // LDS row stride of a row-major tile (bf16)
     static constexpr int NS = D / 32;    // 32-dim steps of a product over d
     static constexpr int NDB = D / 16;   // 16-dim blocks of an accumulator
     static constexpr int CPR = D / 8;    // 16-byte chunks per row
@@ -61,13 +59,10 @@ __device__ __forceinline__ f32x4 mfma16(bf16x8 a, bf16x8 b, f32x4 c) {
     return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
 }
 
-// LDS row of element k (0..63) of a tile: inside each 32-element group, element
-// 8 q + 4 b + i goes to row 16 b + 4 q + i. A product whose A operand is read from these rows
-// leaves, in lane (column, g) of its row blocks 2 G and 2 G + 1, the elements
-// 32 G + 8 g .. 32 G + 8 g + 7: the k-slots of the lane in the next product.
-__device__ __forceinline__ int prow(int k) {
-    return (k & 32) | (((k >> 2) & 1) << 4) | (((k >> 3) & 3) << 2) | (k & 3);
-}
+// Row order of a tile in LDS: inside each 32-element group, element 8 q + 4 b + i sits at row
+// 16 b + 4 q + i. A product whose A operand is read from these rows leaves, in lane
+// (column, g) of its row blocks 2 G and 2 G + 1, the elements 32 G + 8 g .. 32 G + 8 g + 7:
+// the k-slots of the lane in the next product.
 
 __device__ __forceinline__ bf16x8 pack8(const float (&x)[8]) {
     return __builtin_bit_cast(bf16x8, u32x4{pack_bf16x2(x[0], x[1]), pack_bf16x2(x[2], x[3]),
@@ -100,14 +95,18 @@ __device__ __forceinline__ bf16x8 read_tr_operand(const unsigned char* p, int ro
     return __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
 }
 
-// ---- direct-to-LDS tiles (d = 128): 64 rows of 256 bytes, unpadded. Chunk c (16 bytes) of
-// LDS row r sits at position c ^ swz(r), swz(r) = 2 (r & 7) + bit 3 of r. For one chunk, the
-// 16 rows of a row-operand read (r & 15 = 0..15) get 16 distinct positions; for the chunk
-// pair 2 db, 2 db + 1 of a transposing read, rows 0..7 (and 8..15) of each 16 get 8 distinct
-// 32-byte spans (db ^ (r & 7)).
-__device__ __forceinline__ int swz(int r) { return 2 * (r & 7) | ((r >> 3) & 1); }
+// ---- direct-to-LDS tiles: 64 rows of 2 d bytes, unpadded. Chunk c (16 bytes) of LDS row r
+// sits at position c ^ swz(r): at d = 128, swz(r) = 2 (r & 7) + bit 3 of r; at d = 64 (two
+// rows per 256-byte line of the 64 banks), swz(r) = 2 ((r >> 1) & 3) + bit 3 of r. For one
+// chunk, the 16 rows of a row-operand read (r & 15 = 0..15) get 16 distinct bank positions;
+// for the chunk pair 2 db, 2 db + 1 of a transposing read, rows 0..7 (and 8..15) of each 16
+// get 8 distinct 32-byte spans.
+template <int D>
+__device__ __forceinline__ int swz(int r) {
+    return D == 128 ? (2 * (r & 7) | ((r >> 3) & 1)) : (2 * ((r >> 1) & 3) | ((r >> 3) & 1));
+}
 
-// Inverse of prow: the tile element stored at LDS row r.
+// The tile element stored at LDS row r (0..63).
 __device__ __forceinline__ int prow_inv(int r) {
     return (r & 32) | (((r >> 2) & 3) << 3) | (((r >> 4) & 1) << 2) | (r & 3);
 }
@@ -222,13 +221,11 @@ __global__ __launch_bounds__(NT, 1) void prefill_bwd_dq_kernel(
     const __bf16* __restrict__ dout, __bf16* __restrict__ dq, __bf16* __restrict__ dr,
     f32x4* __restrict__ rec, int BH, int T, int nqb, float c, float scale) {
     using G_ = BG<D>;
-    constexpr int RS = G_::RS, NS = G_::NS, NDB = G_::NDB, CPR = G_::CPR, CPR_LOG = G_::CPR_LOG;
+    constexpr int NS = G_::NS, NDB = G_::NDB, CPR = G_::CPR, CPR_LOG = G_::CPR_LOG;
     constexpr uint32_t ROWB = G_::ROWB;
-    // DMA: the K and V tiles arrive by direct-to-LDS loads into unpadded, chunk-swizzled rows
-    // (swz); otherwise through registers into rows padded by 16 bytes.
-    constexpr bool DMA = D == 128;
-    constexpr int RB = DMA ? 2 * D : RS * 2;  // LDS bytes per tile row
-    constexpr int Q_KR = KBC * RB;             // bytes of a row-major K (or V) tile
+    // The K and V tiles arrive by direct-to-LDS loads into unpadded, chunk-swizzled rows (swz).
+    constexpr int RB = 2 * D;       // LDS bytes per tile row
+    constexpr int Q_KR = KBC * RB;  // bytes of a row-major K (or V) tile
     constexpr int Q_BUF = 2 * Q_KR;
     static_assert(2 * Q_BUF <= 160 * 1024, "LDS budget");
     __shared__ __attribute__((aligned(16))) unsigned char lds[2 * Q_BUF];
@@ -287,70 +284,53 @@ __global__ __launch_bounds__(NT, 1) void prefill_bwd_dq_kernel(
 #pragma unroll
     for (int db = 0; db < NDB; ++db) aq[db] = ar[db] = f32x4{};
 
-    // ---- staging: waves 0-3 K, waves 4-7 V (row-major, rows in prow order). Thread st loads
-    // keys KPT (st / CPR) .. + KPT - 1, dims 8 (st % CPR) .. +7 (KPT = 4 at d = 128, 2 at 64).
-    constexpr int KPT = CPR / 4;
-    const bool kst = w < 4;
-    const int st = tid & 255, sdc = st & (CPR - 1), skg = st >> CPR_LOG;
-    const uint32_t soff = (uint32_t)(KPT * skg) * ROWB + 16u * sdc;
-    u32x4 stg[KPT];
     const int kend = min(q0 + QBR, T);
     const int ntiles = (kend + KBC - 1) / KBC;
     const int nfull = min(ntiles, q0 / KBC);
-    auto gload = [&](int kt) {
-        const uint32_t rem = slice_bytes - (uint32_t)kt * KBC * ROWB;
-        const auto r = make_rsrc((kst ? k : v) + slice + (size_t)kt * KBC * D, rem);
-#pragma unroll
-        for (int j = 0; j < KPT; ++j) stg[j] = load16(r, soff + ROWB * j);
-    };
-    auto lstore = [&](int buf) {
-        unsigned char* base = lds + buf * Q_BUF + (kst ? 0 : Q_KR);
-#pragma unroll
-        for (int j = 0; j < KPT; ++j)
-            *(u32x4*)(base + prow(KPT * skg + j) * RS * 2 + 16 * sdc) = stg[j];
-    };
-    // DMA: wave w fills LDS rows 8 w .. 8 w + 7 of the K and the V tile (two 1 KB loads each,
-    // 16 bytes per lane in lane order): lane (row r, position p) fetches chunk p ^ swz(r) of
-    // key prow_inv(r). Rows past T read as zero.
+    // ---- staging: wave w fills LDS rows 8 w .. 8 w + 7 of the K and the V tile (rows in prow
+    // order; at d = 128 two 1 KB loads each, at d = 64 one; 16 bytes per lane in lane order):
+    // lane (row r, position p) fetches chunk p ^ swz(r) of key prow_inv(r). Rows past T read
+    // as zero.
     uint32_t dsrc[2];
 #pragma unroll
     for (int i = 0; i < 2; ++i) {
-        const int r = 8 * w + 4 * i + (lane >> 4);
-        dsrc[i] = (uint32_t)prow_inv(r) * ROWB + 16u * ((lane & 15) ^ swz(r));
+        const int r = 8 * w + (1024 / RB) * i + (lane >> CPR_LOG);
+        dsrc[i] = (uint32_t)prow_inv(r) * ROWB + 16u * ((lane & (CPR - 1)) ^ swz<D>(r));
     }
     auto stage = [&](int kt, int buf) {
         const uint32_t rem = slice_bytes - (uint32_t)kt * KBC * ROWB;
         const size_t at = slice + (size_t)kt * KBC * D;
-        dma2x2<Q_KR>(raw_rsrc(k + at, rem), raw_rsrc(v + at, rem),
-                     lds_addr(lds + buf * Q_BUF) + 8 * w * RB, dsrc[0], dsrc[1]);
+        const uint32_t dst = lds_addr(lds + buf * Q_BUF) + 8 * w * RB;
+        if constexpr (D == 128) {
+            dma2x2<Q_KR>(raw_rsrc(k + at, rem), raw_rsrc(v + at, rem), dst, dsrc[0], dsrc[1]);
+        } else {
+            dma1(raw_rsrc(k + at, rem), dst, dsrc[0]);
+            dma1(raw_rsrc(v + at, rem), dst + Q_KR, dsrc[0]);
+        }
     };
     // K^T operands through the transposing read: source lane (4 j + a) of group gq addresses
-    // K tile row 4 gq + j (+ 32 G + 16 h), dims 4 a .. +3 (+ 16 db). DMA: the dims' 32-byte
-    // span db sits at span db ^ (r & 7) of the row, its two chunks swapped when bit 3 of r is
-    // set.
-    const int trl = (4 * gq + (col >> 2)) * RB + 8 * (col & 3);
-    int trd[DMA ? NDB : 1];
-    int rowc[DMA ? NS : 1];  // DMA: byte of chunk 4 s + gq in LDS row col
-    if constexpr (DMA) {
-        const int r = 4 * gq + (col >> 2), f = swz(r);
+    // K tile row r = 4 gq + j (+ 32 G + 16 h), dims 4 a .. +3 (+ 16 db), i.e. byte 8 (a & 1)
+    // of chunk (2 db + (a >> 1)) ^ swz(r) (trd). Row operands: chunk 4 s + gq of row col
+    // (+ 16 kb) sits at position (4 s + gq) ^ swz(col) (rowc).
+    int trd[NDB], rowc[NS];
+    {
+        const int r = 4 * gq + (col >> 2), f = swz<D>(r);
 #pragma unroll
         for (int db = 0; db < NDB; ++db)
             trd[db] = r * RB + 16 * ((2 * db + ((col & 3) >> 1)) ^ f) + 8 * (col & 1);
 #pragma unroll
-        for (int s = 0; s < NS; ++s) rowc[s] = col * RB + 16 * ((4 * s + gq) ^ swz(col));
+        for (int s = 0; s < NS; ++s) rowc[s] = col * RB + 16 * ((4 * s + gq) ^ swz<D>(col));
     }
 
     auto tile = [&](int kt, int buf, bool diag) {
-        const unsigned char* Kr = lds + buf * Q_BUF + col * RS * 2 + 16 * gq;
-        const unsigned char* Kt = lds + buf * Q_BUF + (DMA ? 0 : trl);
+        const unsigned char* Kt = lds + buf * Q_BUF;
         f32x4 S[4], Tp[4], Gm[4];
 #pragma unroll
         for (int kb = 0; kb < 4; ++kb) {
             S[kb] = Tp[kb] = Gm[kb] = f32x4{};
 #pragma unroll
             for (int s = 0; s < NS; ++s) {
-                const unsigned char* a = DMA ? lds + buf * Q_BUF + rowc[s] + 16 * kb * RB
-                                             : Kr + 16 * kb * RS * 2 + 64 * s;
+                const unsigned char* a = Kt + rowc[s] + 16 * kb * RB;
                 const bf16x8 kf = *(const bf16x8*)a;
                 const bf16x8 vf = *(const bf16x8*)(a + Q_KR);
                 S[kb] = mfma16(kf, xq[s], S[kb]);
@@ -379,8 +359,7 @@ __global__ __launch_bounds__(NT, 1) void prefill_bwd_dq_kernel(
             const bf16x8 da = pack8(fa), dt = pack8(ft);
 #pragma unroll
             for (int db = 0; db < NDB; ++db) {
-                const bf16x8 kf =
-                    read_tr_operand(Kt + 32 * G2 * RB + (DMA ? trd[db] : 32 * db), RB);
+                const bf16x8 kf = read_tr_operand(Kt + 32 * G2 * RB + trd[db], RB);
                 aq[db] = mfma16(kf, da, aq[db]);
                 ar[db] = mfma16(kf, dt, ar[db]);
             }
@@ -388,31 +367,16 @@ __global__ __launch_bounds__(NT, 1) void prefill_bwd_dq_kernel(
         }
     };
 
-    if constexpr (DMA) {
-        stage(0, 0);
-        __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0): this wave's loads are in LDS
+    stage(0, 0);
+    __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0): this wave's loads are in LDS
+    __syncthreads();
+    for (int kt = 0; kt < ntiles; ++kt) {
+        const int buf = kt & 1;
+        if (kt + 1 < ntiles) stage(kt + 1, buf ^ 1);
+        // a wave whose rows all precede the tile's first key has nothing to add
+        if (kt * KBC <= q0 + 16 * w + 15) tile(kt, buf, kt >= nfull);
+        __builtin_amdgcn_s_waitcnt(0x0F70);  // the next tile's loads, before it is published
         __syncthreads();
-        for (int kt = 0; kt < ntiles; ++kt) {
-            const int buf = kt & 1;
-            if (kt + 1 < ntiles) stage(kt + 1, buf ^ 1);
-            // a wave whose rows all precede the tile's first key has nothing to add
-            if (kt * KBC <= q0 + 16 * w + 15) tile(kt, buf, kt >= nfull);
-            __builtin_amdgcn_s_waitcnt(0x0F70);
-            __syncthreads();
-        }
-    } else {
-        gload(0);
-        lstore(0);
-        __syncthreads();
-        for (int kt = 0; kt < ntiles; ++kt) {
-            const int buf = kt & 1;
-            const bool more = kt + 1 < ntiles;
-            if (more) gload(kt + 1);
-            // a wave whose rows all precede the tile's first key has nothing to add
-            if (kt * KBC <= q0 + 16 * w + 15) tile(kt, buf, kt >= nfull);
-            if (more) lstore(buf ^ 1);
-            __syncthreads();
-        }
     }
 
     if (qi < T) {
@@ -441,14 +405,12 @@ __global__ __launch_bounds__(NT, 1) void prefill_bwd_dk_kernel(
     const f32x4* __restrict__ rec, __bf16* __restrict__ dk, __bf16* __restrict__ dv, int BH,
     int T, int nkb, float c, float scale) {
     using G_ = BG<D>;
-    constexpr int RS = G_::RS, NS = G_::NS, NDB = G_::NDB, CPR = G_::CPR, CPR_LOG = G_::CPR_LOG;
+    constexpr int NS = G_::NS, NDB = G_::NDB, CPR = G_::CPR, CPR_LOG = G_::CPR_LOG;
     constexpr uint32_t ROWB = G_::ROWB;
-    // DMA: the Q, R and dO tiles (and the row records) arrive by direct-to-LDS loads into
-    // unpadded, chunk-swizzled rows (swz); otherwise through registers into rows padded by 16
-    // bytes.
-    constexpr bool DMA = D == 128;
-    constexpr int RB = DMA ? 2 * D : RS * 2;  // LDS bytes per tile row
-    constexpr int K_R = QBC * RB;              // bytes of one row-major tile (Q, R or dO)
+    // The Q, R and dO tiles (and the row records) arrive by direct-to-LDS loads into
+    // unpadded, chunk-swizzled rows (swz).
+    constexpr int RB = 2 * D;      // LDS bytes per tile row
+    constexpr int K_R = QBC * RB;  // bytes of one row-major tile (Q, R or dO)
     constexpr int K_BUF = 3 * K_R + K_REC;
     static_assert(2 * K_BUF <= 160 * 1024, "LDS budget");
     __shared__ __attribute__((aligned(16))) unsigned char lds[2 * K_BUF];
@@ -477,89 +439,60 @@ __global__ __launch_bounds__(NT, 1) void prefill_bwd_dk_kernel(
 #pragma unroll
     for (int db = 0; db < NDB; ++db) ak[db] = av[db] = f32x4{};
 
-    // ---- staging: chunk m (0 .. 3 NP - 1) of thread t is tensor m / NP (Q, R, dO), row
-    // t / CPR + RPP (m % NP), dims 8 (t % CPR) .. +7, with RPP = 512 / CPR rows per pass and
-    // NP = 64 / RPP passes (2 at d = 128, 1 at 64); threads 0..63 also stage the row records.
-    constexpr int RPP = 512 / CPR, NP = QBC / RPP;
-    u32x4 stg[3 * NP];
-    u32x4 srec = u32x4{};
     const int qt0 = k0 / QBC;
     const int ntiles = (T + QBC - 1) / QBC - qt0;
-    const int srow = tid >> CPR_LOG, sc = tid & (CPR - 1);
-    auto gload = [&](int n) {
-        const int r0 = (qt0 + n) * QBC;
-        const uint32_t rem = slice_bytes - (uint32_t)r0 * ROWB;
-        const auto r_q = make_rsrc(q + slice + (size_t)r0 * D, rem);
-        const auto r_r = make_rsrc(rho + slice + (size_t)r0 * D, rem);
-        const auto r_d = make_rsrc(dout + slice + (size_t)r0 * D, rem);
-#pragma unroll
-        for (int h = 0; h < NP; ++h) {
-            const uint32_t off = (uint32_t)(srow + RPP * h) * ROWB + 16u * sc;
-            stg[h] = load16(r_q, off);
-            stg[NP + h] = load16(r_r, off);
-            stg[2 * NP + h] = load16(r_d, off);
-        }
-        if (w == 0) {
-            const auto r = make_rsrc(rec + (size_t)bh * T + r0, (uint32_t)(T - r0) * 16u);
-            srec = load16(r, 16u * lane);
-        }
-    };
-    auto lstore = [&](int buf) {
-        unsigned char* base = lds + buf * K_BUF;
-#pragma unroll
-        for (int m = 0; m < 3 * NP; ++m)
-            *(u32x4*)(base + (m / NP) * K_R + prow(srow + RPP * (m % NP)) * RS * 2 + 16 * sc) =
-                stg[m];
-        if (w == 0) *(u32x4*)(base + 3 * K_R + 16 * lane) = srec;
-    };
-    // DMA: wave w fills LDS rows 8 w .. 8 w + 7 of each tile (two 1 KB loads per tensor, 16
-    // bytes per lane in lane order): lane (row r, position p) fetches chunk p ^ swz(r) of
-    // tile element prow_inv(r). Wave 0 also loads the 64 row records. Rows past T read as
-    // zero.
+    // ---- staging: wave w fills LDS rows 8 w .. 8 w + 7 of each tile (rows in prow order; at
+    // d = 128 two 1 KB loads per tensor, at d = 64 one; 16 bytes per lane in lane order):
+    // lane (row r, position p) fetches chunk p ^ swz(r) of tile element prow_inv(r). Wave 0
+    // also loads the 64 row records. Rows past T read as zero.
     uint32_t dsrc[2];
 #pragma unroll
     for (int i = 0; i < 2; ++i) {
-        const int r = 8 * w + 4 * i + (lane >> 4);
-        dsrc[i] = (uint32_t)prow_inv(r) * ROWB + 16u * ((lane & 15) ^ swz(r));
+        const int r = 8 * w + (1024 / RB) * i + (lane >> CPR_LOG);
+        dsrc[i] = (uint32_t)prow_inv(r) * ROWB + 16u * ((lane & (CPR - 1)) ^ swz<D>(r));
     }
     auto stage = [&](int n, int buf) {
         const int r0 = (qt0 + n) * QBC;
         const uint32_t rem = slice_bytes - (uint32_t)r0 * ROWB;
         const size_t at = slice + (size_t)r0 * D;
         unsigned char* base = lds + buf * K_BUF;
-        dma3x2<K_R>(raw_rsrc(q + at, rem), raw_rsrc(rho + at, rem), raw_rsrc(dout + at, rem),
-                    lds_addr(base) + 8 * w * RB, dsrc[0], dsrc[1]);
+        const uint32_t dst = lds_addr(base) + 8 * w * RB;
+        if constexpr (D == 128) {
+            dma3x2<K_R>(raw_rsrc(q + at, rem), raw_rsrc(rho + at, rem), raw_rsrc(dout + at, rem),
+                        dst, dsrc[0], dsrc[1]);
+        } else {
+            dma1(raw_rsrc(q + at, rem), dst, dsrc[0]);
+            dma1(raw_rsrc(rho + at, rem), dst + K_R, dsrc[0]);
+            dma1(raw_rsrc(dout + at, rem), dst + 2 * K_R, dsrc[0]);
+        }
         if (w == 0)
             dma1(raw_rsrc(rec + (size_t)bh * T + r0, (uint32_t)(T - r0) * 16u),
                  lds_addr(base + 3 * K_R), 16u * lane);
     };
 
-    // transposed-read lane base: source lane (4 j + a) of group gq addresses tile row
-    // 4 gq + j (+ 32 G + 16 h), dims 4 a .. +3 (+ 16 db). DMA: the dims' 32-byte span db sits
-    // at span db ^ (r & 7) of the row, with its two chunks swapped when bit 3 of r is set.
-    const int trl = (4 * gq + (col >> 2)) * RB + 8 * (col & 3);
-    int trd[DMA ? NDB : 1];
-    int rowc[DMA ? NS : 1];  // DMA: byte of chunk 4 s + gq in LDS row col
-    if constexpr (DMA) {
-        const int r = 4 * gq + (col >> 2), f = swz(r);
+    // Transposed reads: source lane (4 j + a) of group gq addresses tile row r = 4 gq + j
+    // (+ 32 G + 16 h), dims 4 a .. +3 (+ 16 db), i.e. byte 8 (a & 1) of chunk
+    // (2 db + (a >> 1)) ^ swz(r) (trd). Row operands: chunk 4 s + gq of row col (+ 16 b) sits
+    // at position (4 s + gq) ^ swz(col) (rowc).
+    int trd[NDB], rowc[NS];
+    {
+        const int r = 4 * gq + (col >> 2), f = swz<D>(r);
 #pragma unroll
         for (int db = 0; db < NDB; ++db)
             trd[db] = r * RB + 16 * ((2 * db + ((col & 3) >> 1)) ^ f) + 8 * (col & 1);
 #pragma unroll
-        for (int s = 0; s < NS; ++s) rowc[s] = col * RB + 16 * ((4 * s + gq) ^ swz(col));
+        for (int s = 0; s < NS; ++s) rowc[s] = col * RB + 16 * ((4 * s + gq) ^ swz<D>(col));
     }
 
     auto tile = [&](int n, int buf, bool mask) {
         const unsigned char* base = lds + buf * K_BUF;
-        const unsigned char* Qr = base + col * RS * 2 + 16 * gq;
         f32x4 S[4], Tp[4], Gm[4];
 #pragma unroll
         for (int b = 0; b < 4; ++b) {
             S[b] = Tp[b] = Gm[b] = f32x4{};
 #pragma unroll
             for (int s = 0; s < NS; ++s) {
-                const unsigned char* a =
-                    DMA ? base + rowc[s] + 16 * b * RB : Qr + 16 * b * RS * 2 + 64 * s;
+                const unsigned char* a = base + rowc[s] + 16 * b * RB;
                 S[b] = mfma16(*(const bf16x8*)a, xk[s], S[b]);
                 Tp[b] = mfma16(*(const bf16x8*)(a + K_R), xk[s], Tp[b]);
                 Gm[b] = mfma16(*(const bf16x8*)(a + 2 * K_R), xv[s], Gm[b]);
@@ -587,10 +520,10 @@ __global__ __launch_bounds__(NT, 1) void prefill_bwd_dk_kernel(
                     fa[4 * bb + i] = scale * p * (fmaf(one, g, t * rw[2]) - rw[3]);
                 }
             const bf16x8 ps = pack8(fs), pa = pack8(fa), pt = pack8(ft);
-            const unsigned char* Tr = base + (DMA ? 0 : trl) + 32 * G2 * RB;
+            const unsigned char* Tr = base + 32 * G2 * RB;
 #pragma unroll
             for (int db = 0; db < NDB; ++db) {
-                const int o = DMA ? trd[db] : 32 * db;
+                const int o = trd[db];
                 auto op = [&](int tensor) { return read_tr_operand(Tr + tensor * K_R + o, RB); };
                 av[db] = mfma16(op(2), ps, av[db]);
                 ak[db] = mfma16(op(0), pa, ak[db]);
@@ -600,32 +533,16 @@ __global__ __launch_bounds__(NT, 1) void prefill_bwd_dk_kernel(
     };
 
     const int tail = (T - 1) / QBC - qt0;
-    if constexpr (DMA) {
-        stage(0, 0);
-        __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0): this wave's loads are in LDS
+    stage(0, 0);
+    __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0): this wave's loads are in LDS
+    __syncthreads();
+    for (int n = 0; n < ntiles; ++n) {
+        const int buf = n & 1;
+        if (n + 1 < ntiles) stage(n + 1, buf ^ 1);
+        const int r0 = (qt0 + n) * QBC;
+        if (r0 + QBC - 1 >= k0 + 16 * w) tile(n, buf, r0 < k0 + KBR || n == tail);
+        __builtin_amdgcn_s_waitcnt(0x0F70);  // the next tile's loads, before it is published
         __syncthreads();
-        for (int n = 0; n < ntiles; ++n) {
-            const int buf = n & 1;
-            const bool more = n + 1 < ntiles;
-            if (more) stage(n + 1, buf ^ 1);
-            const int r0 = (qt0 + n) * QBC;
-            if (r0 + QBC - 1 >= k0 + 16 * w) tile(n, buf, r0 < k0 + KBR || n == tail);
-            __builtin_amdgcn_s_waitcnt(0x0F70);
-            __syncthreads();
-        }
-    } else {
-        gload(0);
-        lstore(0);
-        __syncthreads();
-        for (int n = 0; n < ntiles; ++n) {
-            const int buf = n & 1;
-            const bool more = n + 1 < ntiles;
-            if (more) gload(n + 1);
-            const int r0 = (qt0 + n) * QBC;
-            if (r0 + QBC - 1 >= k0 + 16 * w) tile(n, buf, r0 < k0 + KBR || n == tail);
-            if (more) lstore(buf ^ 1);
-            __syncthreads();
-        }
     }
 
     if (kj < T) {

@@ -9,10 +9,11 @@
 // sigmoid left to the caller.
 //
 // One workgroup (4 waves) computes 64 UG tokens x the 128 dims of HG heads as
-// Y^T = W_R X^T on v_mfma_f32_16x16x32_bf16: per 32-wide K step the workgroup stages the
-// head's W_R slice (128 rows x 64 bytes, rows padded to 80 bytes so the operand reads are
-// free of bank conflicts) in LDS, double-buffered, and every wave reads its A operand blocks
-// there; the B operand is UG 16-token groups of x rows read straight from global memory.
+// Y^T = W_R X^T on v_mfma_f32_16x16x32_bf16: per K step (32 wide for narrow inputs, 64 for
+// wide ones) the workgroup stages the head's W_R slice (128 rows, padded by 16 bytes so the
+// operand reads are free of bank conflicts) in LDS, double-buffered, and every wave reads its
+// A operand blocks there; the B operand is UG 16-token groups of x rows read straight from
+// global memory.
 // Narrow calls are bound by the per-token vector work of the epilogue, so there the RoPE
 // frequencies come from a per-workgroup table, gamma from LDS, the gate is folded into the
 // norm's scale, and with one K step two heads share each token's sines and cosines.
@@ -30,8 +31,6 @@ namespace {
 
 constexpr int D = 128;
 constexpr int NT = 256;
-constexpr int WROW = 40;     // LDS row stride of the W_R slice (bf16): 80 bytes
-constexpr int WBUF = D * WROW;
 constexpr int kProbeNarrowC = 64;  // inputs up to this width take one token group per wave
 
 // gamma of a call that passes none (RMSNorm without a learned scale)
@@ -63,12 +62,16 @@ __device__ __forceinline__ void seq_pos(int n, int T, int& b, int& t) {
 // sines and cosines, which depend on the token and not on the head, are evaluated once for
 // both (narrow calls are bound by this per-token vector work).
 template <int UG, int HG>
-__global__ __launch_bounds__(NT, UG == 1 ? 4 : 1) void probe_bf16_d128_kernel(
+__global__ __launch_bounds__(NT, UG == 1 ? 4 : 2) void probe_bf16_d128_kernel(
     const __bf16* __restrict__ x, const __bf16* __restrict__ wr, const float* __restrict__ gamma,
     const float* __restrict__ gate, const int32_t* __restrict__ positions, __bf16* __restrict__ rho,
     int B, int T, int C, int H, float eps, float log2_base) {
     constexpr uint32_t OOB = 0xFFFFFFF0u;  // past every resource: reads as zeros
-    __shared__ __attribute__((aligned(16))) __bf16 wl[2][WBUF];
+    // K step: 32 (narrow), 64 (wide: half the barriers and staging rounds per product); W_R
+    // slice rows padded to 80 or 144 bytes so that the operand reads are free of bank conflicts.
+    constexpr int KS = UG == 2 ? 64 : 32;
+    constexpr int WR = KS + 8;  // LDS row stride of the W_R slice (bf16)
+    __shared__ __attribute__((aligned(16))) __bf16 wl[2][D * WR];
     __shared__ __attribute__((aligned(16))) __bf16 ot[NT / 64][16][D + 8];  // output rows
     __shared__ __attribute__((aligned(16))) float turn_tab[D / 2];  // turns per position, per pair
     __shared__ __attribute__((aligned(16))) float gam[D];           // gamma (ones if none)
@@ -92,29 +95,37 @@ __global__ __launch_bounds__(NT, UG == 1 ? 4 : 1) void probe_bf16_d128_kernel(
     auto rw_of = [&](int h) { return make_rsrc(wr + (size_t)h * D * C, (uint32_t)D * C * 2u); };
     const auto rw = rw_of(h0);
 
-    // Staging: thread tid copies 16-byte pieces (tid & 3) of rows tid >> 2 and 64 + (tid >> 2).
-    const int sr = tid >> 2, sp = tid & 3;
-    auto stage = [&](int k0, u32x4 (&st)[2]) {
+    // Staging: thread tid copies 16-byte piece tid % PR (PR = KS / 8 pieces per row) of rows
+    // tid / PR + (256 / PR) r, r = 0 .. NR - 1.
+    constexpr int PR = KS / 8, NR = 2 * PR / 4;
+    const int sr = tid / PR, sp = tid % PR;
+    auto stage = [&](int k0, u32x4 (&st)[NR]) {
         const int kc = k0 + 8 * sp;
 #pragma unroll
-        for (int r = 0; r < 2; ++r)
-            st[r] = load16(rw, kc < C ? (uint32_t)((sr + 64 * r) * C + kc) * 2u : OOB);
+        for (int r = 0; r < NR; ++r)
+            st[r] = load16(rw, kc < C ? (uint32_t)((sr + (256 / PR) * r) * C + kc) * 2u : OOB);
     };
-    auto put = [&](int buf, const u32x4 (&st)[2]) {
+    auto put = [&](int buf, const u32x4 (&st)[NR]) {
 #pragma unroll
-        for (int r = 0; r < 2; ++r) *(u32x4*)&wl[buf][(sr + 64 * r) * WROW + 8 * sp] = st[r];
+        for (int r = 0; r < NR; ++r)
+            *(u32x4*)&wl[buf][(sr + (256 / PR) * r) * WR + 8 * sp] = st[r];
     };
 
     // Everything the workgroup reads from memory besides the later K steps is requested up
     // front, so that the W_R slice, the first x rows, gamma, the gate and the positions arrive
     // in one round trip instead of one after another.
-    auto load_x = [&](int k0, bf16x8 (&bx)[UG]) {
-        const int kc = k0 + 8 * g;
+    // x rows of one K step: lane (token c16, g) holds k-slots 32 h + 8 g .. +7, h < KS / 32.
+    constexpr int KH = KS / 32;
+    auto load_x = [&](int k0, bf16x8 (&bx)[UG][KH]) {
 #pragma unroll
-        for (int u = 0; u < UG; ++u)
-            bx[u] = as_bf16x8(load16(rx, tok_ok[u] && kc < C ? xrow[u] + 2u * kc : OOB));
+        for (int h = 0; h < KH; ++h) {
+            const int kc = k0 + 32 * h + 8 * g;
+#pragma unroll
+            for (int u = 0; u < UG; ++u)
+                bx[u][h] = as_bf16x8(load16(rx, tok_ok[u] && kc < C ? xrow[u] + 2u * kc : OOB));
+        }
     };
-    bf16x8 bx[UG];
+    bf16x8 bx[UG][KH];
     load_x(0, bx);
     if (tid < D) gam[tid] = (gamma ? gamma : kOnes)[tid];  // published by the K loop's barriers
     // Token group u (16 consecutive tokens from tg0[u]) usually lies in one sequence (b0, from
@@ -142,41 +153,42 @@ __global__ __launch_bounds__(NT, UG == 1 ? 4 : 1) void probe_bf16_d128_kernel(
                             : 0.f;
 
     f32x4 acc[UG][8];
-    u32x4 st[2];
+    u32x4 st[NR];
     stage(0, st);
     if constexpr (HG == 2) {  // C <= 32: the second head's slice goes to the other buffer
         const int kc = 8 * sp;
         const auto rw1 = rw_of(h0 + 1);
-        u32x4 st1[2];
+        u32x4 st1[NR];
 #pragma unroll
-        for (int r = 0; r < 2; ++r)
+        for (int r = 0; r < NR; ++r)
             st1[r] = load16(rw1, kc < C ? (uint32_t)((sr + 64 * r) * C + kc) * 2u : OOB);
         put(1, st1);
     }
     put(0, st);
     __syncthreads();
     // One K step; the first starts the accumulators from zero.
-    // K steps of 32. Wide inputs (UG = 2, many steps) are software-pipelined: the W_R slice
-    // of step k is requested two steps ahead (alternating register sets) and written to its
-    // LDS buffer at the end of step k - 1; the x rows of step k are requested at the end of
-    // step k - 2 (alternating sets). Steps alternate between the buffers and register sets A
-    // (even) and B (odd), unrolled by two so that no register set is copied while its loads
-    // are in flight. Narrow inputs (one or two steps) request each step's data in the step
-    // before.
-    auto products = [&](int b, const bf16x8 (&x)[UG], bool first) {
+    // Wide inputs (UG = 2, many steps) are software-pipelined: the W_R slice of step k is
+    // requested two steps ahead (alternating register sets) and written to its LDS buffer at
+    // the end of step k - 1; the x rows of step k are requested at the end of step k - 2
+    // (alternating sets). Steps alternate between the buffers and register sets A (even) and
+    // B (odd), unrolled by two so that no register set is copied while its loads are in
+    // flight. Narrow inputs (one or two steps) request each step's data in the step before.
+    auto products = [&](int b, const bf16x8 (&x)[UG][KH], bool first) {
 #pragma unroll
-        for (int j = 0; j < 8; ++j) {
-            const bf16x8 a = *(const bf16x8*)&wl[b][(16 * j + c16) * WROW + 8 * g];
+        for (int h = 0; h < KH; ++h)
 #pragma unroll
-            for (int u = 0; u < UG; ++u)
-                acc[u][j] = mfma16(a, x[u], first ? f32x4{} : acc[u][j]);
-        }
+            for (int j = 0; j < 8; ++j) {
+                const bf16x8 a = *(const bf16x8*)&wl[b][(16 * j + c16) * WR + 32 * h + 8 * g];
+#pragma unroll
+                for (int u = 0; u < UG; ++u)
+                    acc[u][j] = mfma16(a, x[u][h], first && h == 0 ? f32x4{} : acc[u][j]);
+            }
     };
     if constexpr (HG == 1 && UG == 1) {
         int buf = 0;
-        for (int k0 = 0; k0 < C; k0 += 32) {
-            const bool more = k0 + 32 < C;
-            if (more) stage(k0 + 32, st);
+        for (int k0 = 0; k0 < C; k0 += KS) {
+            const bool more = k0 + KS < C;
+            if (more) stage(k0 + KS, st);
             if (k0 > 0) load_x(k0, bx);
             products(buf, bx, k0 == 0);
             if (more) put(buf ^ 1, st);
@@ -188,22 +200,22 @@ __global__ __launch_bounds__(NT, UG == 1 ? 4 : 1) void probe_bf16_d128_kernel(
         // without touching memory, and the same loads outstanding on every path let each
         // step wait only for its own data (a conditional load would make the compiler wait
         // for every load in flight after the join).
-        u32x4 stb[2];
-        bf16x8 bxb[UG];
-        stage(32, stb);
-        load_x(32, bxb);
-        for (int k0 = 0; k0 < C; k0 += 64) {
+        u32x4 stb[NR];
+        bf16x8 bxb[UG][KH];
+        stage(KS, stb);
+        load_x(KS, bxb);
+        for (int k0 = 0; k0 < C; k0 += 2 * KS) {
             // step k0: buffer 0, set A (st, bx)
-            stage(k0 + 64, st);
+            stage(k0 + 2 * KS, st);
             products(0, bx, k0 == 0);
-            load_x(k0 + 64, bx);
+            load_x(k0 + 2 * KS, bx);
             put(1, stb);
             __syncthreads();
-            if (k0 + 32 >= C) break;
-            // step k0 + 32: buffer 1, set B
-            stage(k0 + 96, stb);
+            if (k0 + KS >= C) break;
+            // step k0 + KS: buffer 1, set B
+            stage(k0 + 3 * KS, stb);
             products(1, bxb, false);
-            load_x(k0 + 96, bxb);
+            load_x(k0 + 3 * KS, bxb);
             put(0, st);
             __syncthreads();
         }
@@ -221,9 +233,9 @@ __global__ __launch_bounds__(NT, UG == 1 ? 4 : 1) void probe_bf16_d128_kernel(
         if constexpr (HG == 2) {  // the one K step of this head, from its staged slice
 #pragma unroll
             for (int j = 0; j < 8; ++j) {
-                const bf16x8 a = *(const bf16x8*)&wl[hh][(16 * j + c16) * WROW + 8 * g];
+                const bf16x8 a = *(const bf16x8*)&wl[hh][(16 * j + c16) * WR + 8 * g];
 #pragma unroll
-                for (int u = 0; u < UG; ++u) acc[u][j] = mfma16(a, bx[u], f32x4{});
+                for (int u = 0; u < UG; ++u) acc[u][j] = mfma16(a, bx[u][0], f32x4{});
             }
         }
         const float gh = gate ? gate[h] : 1.f;

@@ -319,6 +319,9 @@ __global__ __launch_bounds__(UG == 2 ? 512 : 256, UG == 1 ? 4 : 2) void probe_bf
                         acc[u][j] = mfma16(a, b[u], k == 0 && h == 0 ? f32x4{} : acc[u][j]);
                 }
             }
+            // interleave the step's LDS reads with its products (measured: 73.7 -> 69.5 us at
+            // C = 2048)
+            __builtin_amdgcn_iglp_opt(0);
             if (ahead) __builtin_amdgcn_s_waitcnt(0x0F76);  // vmcnt(6)
             else __builtin_amdgcn_s_waitcnt(0x0F70);        // vmcnt(0)
             __syncthreads();

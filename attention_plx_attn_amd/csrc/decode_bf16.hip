@@ -113,8 +113,13 @@ __device__ __forceinline__ void store_merged(const Merge& st, __bf16* o_bh, int 
 // names the block of rows i 2^bs_log2 .. of sequence b (blocks of at least 32 rows, so a step
 // never crosses a block). Only blocks holding rows below the chunk end are looked up; an entry
 // outside [0, num_blocks) is never dereferenced and its rows get no weight (skipped).
-template <bool PROBE, bool PAGED>
-__global__ __launch_bounds__(NT, 2) void decode_split_bf16_d128_kernel(
+// DEEP: each wave keeps its next step's loads in flight while it consumes the current one
+// (two register sets, two waves per SIMD). Without it each wave holds one step (one register
+// set, four waves per SIMD): for chunks of at most one step per wave (short contexts) the
+// second set is never used, and the doubled occupancy keeps twice the workgroups resident.
+// Both consume the same steps in the same order, so their outputs are bit-identical.
+template <bool PROBE, bool PAGED, bool DEEP>
+__global__ __launch_bounds__(NT, DEEP ? 2 : 4) void decode_split_bf16_d128_kernel(
     const __bf16* __restrict__ q, const __bf16* __restrict__ rho, const __bf16* __restrict__ kc,
     const __bf16* __restrict__ vc, const int32_t* __restrict__ seqlens, __bf16* __restrict__ o,
     float* __restrict__ ws, int H, int L_max, int S, float c, const int32_t* __restrict__ table,
@@ -182,7 +187,16 @@ __global__ __launch_bounds__(NT, 2) void decode_split_bf16_d128_kernel(
     constexpr int STEP = KB * NW;
     Frag fa, fb;
     int kb0 = j0 + KB * w;
-    if constexpr (PAGED) {
+    if constexpr (!DEEP) {
+        // One step per pass; a step whose table entry lies outside [0, num_blocks) reads
+        // zeros and gets no weight (its row limit is its own first row).
+        for (; kb0 < j1; kb0 += STEP) {
+            const int ph = lookup(kb0);
+            load_at(kb0, ph, fa);
+            const int lim = PAGED && (unsigned)ph >= (unsigned)num_blocks ? kb0 : j1;
+            decode::consume<PROBE>(acc, fa, bqr, kb0, lim, c, ush[w], col, g);
+        }
+    } else if constexpr (PAGED) {
         // A step whose table entry lies outside [0, num_blocks) has no rows: its loads read
         // zeros and its row limit is its own first row, so none of its rows gets a weight.
         auto limit = [&](int phys, int at) {
@@ -534,16 +548,20 @@ hipError_t launch_decode(const DecodeArgs& a, hipStream_t stream) {
     }
     const int BH = a.B * a.H;
     dim3 grid(a.splits, a.H, a.B);
+    // Chunks of at most one step per wave run the one-register-set instance.
+    const bool deep = a.chunk > KB * NW;
+    auto split = [&](auto kern, const int32_t* table) {
+        hipLaunchKernelGGL(kern, grid, dim3(NT), 0, stream, (const __bf16*)a.q, rho,
+                           (const __bf16*)a.k, (const __bf16*)a.v, a.seqlens, (__bf16*)a.o, a.ws,
+                           a.H, a.L_max, a.splits, c, table, table ? a.max_blocks : 0,
+                           table ? a.block_log2 : 0, table ? a.num_blocks : 0);
+    };
     if (a.table)
-        hipLaunchKernelGGL((decode_split_bf16_d128_kernel<PROBE, true>), grid, dim3(NT), 0,
-                           stream, (const __bf16*)a.q, rho, (const __bf16*)a.k,
-                           (const __bf16*)a.v, a.seqlens, (__bf16*)a.o, a.ws, a.H, a.L_max,
-                           a.splits, c, a.table, a.max_blocks, a.block_log2, a.num_blocks);
+        deep ? split(decode_split_bf16_d128_kernel<PROBE, true, true>, a.table)
+             : split(decode_split_bf16_d128_kernel<PROBE, true, false>, a.table);
     else
-        hipLaunchKernelGGL((decode_split_bf16_d128_kernel<PROBE, false>), grid, dim3(NT), 0,
-                           stream, (const __bf16*)a.q, rho, (const __bf16*)a.k,
-                           (const __bf16*)a.v, a.seqlens, (__bf16*)a.o, a.ws, a.H, a.L_max,
-                           a.splits, c, nullptr, 0, 0, 0);
+        deep ? split(decode_split_bf16_d128_kernel<PROBE, false, true>, nullptr)
+             : split(decode_split_bf16_d128_kernel<PROBE, false, false>, nullptr);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess || a.splits == 1) return e;
     hipLaunchKernelGGL(decode_combine_kernel, dim3(BH), dim3(64), 0, stream, (const float*)a.ws,

@@ -51,15 +51,12 @@ constexpr int kDecodeWgPerCu = 1;        // one streaming workgroup per compute 
 // us at 2; contexts up to 2048 rows, and B H >= 32 CUs, keep one chunk.
 constexpr int kDecodeBalanceWgPerCu = 32;
 constexpr int kDecodeBalanceRows = 2048;
-// Wave-range mode: slices end at (b, h) starts once there are 2 (b, h) per wave. The automatic
-// plan uses it only in that form, for short contexts with enough (b, h) for at least 2 and at
-// most 4 (the register limit) 4-wave workgroups per compute unit. Measured on MI355X: ahead
-// of split mode for B x ctx = 512 x 128 and 2048 x 128; behind it once a combine of cut (b, h)
-// runs, or when the contexts are long enough for one workgroup per (b, h).
+// Wave-range mode: slices end at (b, h) starts once there are 2 (b, h) per wave; it runs only
+// when asked for (num_splits < 0). Short contexts use split mode with one chunk per (b, h):
+// chunks of at most one step per wave run the one-register-set split kernel (four waves per
+// SIMD), which measured ahead of wave-range mode on MI355X (B x ctx = 128 x 128: 23.1 vs
+// 36.8 us; 512 x 128: 67.4 vs 76.6 us; 2048 x 128: 258.8 vs 280.0 us).
 constexpr int kRangeWholeBhPerWave = 2;
-constexpr int kRangeWgPerCu = 4;
-constexpr int kRangeMinWgPerCu = 2;
-constexpr int kRangeMaxAutoLmax = 512;
 
 int ceil_div(long long a, long long b) { return (int)((a + b - 1) / b); }
 
@@ -100,22 +97,16 @@ plx_status_t plan_decode(int B, int H, int L_max, int d_v, int num_splits, Decod
         int cus = 0;
         const plx_status_t st = current_cu_count(&cus);
         if (st != PLX_OK) return st;
-        long long wg = bh / (4LL * kRangeWholeBhPerWave);
-        if (wg > (long long)kRangeWgPerCu * cus) wg = (long long)kRangeWgPerCu * cus;
-        if (range_built && range_mode_fits(B, H, L_max) && L_max <= kRangeMaxAutoLmax &&
-            wg >= (long long)kRangeMinWgPerCu * cus)
-            waves = (int)(4 * wg);
-        if (!waves) {  // split mode: fill the chip once with (b, h, chunk) workgroups
-            long long s = (kDecodeWgPerCu * (long long)cus + bh - 1) / bh;
-            long long s_bal = (kDecodeBalanceWgPerCu * (long long)cus + bh - 1) / bh;
-            if (s_bal > L_max / kDecodeBalanceRows) s_bal = L_max / kDecodeBalanceRows;
-            if (s < s_bal) s = s_bal;
-            const long long smax = (L_max + kDecodeMinChunk - 1) / kDecodeMinChunk;
-            if (s > smax) s = smax;
-            if (s < 1) s = 1;
-            if (s > kDecodeMaxSplits) s = kDecodeMaxSplits;
-            splits = (int)s;
-        }
+        // split mode: fill the chip once with (b, h, chunk) workgroups
+        long long s = (kDecodeWgPerCu * (long long)cus + bh - 1) / bh;
+        long long s_bal = (kDecodeBalanceWgPerCu * (long long)cus + bh - 1) / bh;
+        if (s_bal > L_max / kDecodeBalanceRows) s_bal = L_max / kDecodeBalanceRows;
+        if (s < s_bal) s = s_bal;
+        const long long smax = (L_max + kDecodeMinChunk - 1) / kDecodeMinChunk;
+        if (s > smax) s = smax;
+        if (s < 1) s = 1;
+        if (s > kDecodeMaxSplits) s = kDecodeMaxSplits;
+        splits = (int)s;
     }
     if (waves > 0) {
         p->waves = waves;
@@ -417,17 +408,6 @@ plx_status_t plx_attn_decode_gqa_plan(int32_t B, int32_t H_q, int32_t H_kv, int3
     DecodePlan p;
     st = plan_decode(B, H_kv, L_max, d_v, num_splits == 0 ? 0 : num_splits, &p);
     if (st != PLX_OK) return st;
-    if (p.waves > 0) {  // the automatic plan of the grouped kernel is always split mode
-        int cus = 0;
-        st = current_cu_count(&cus);
-        if (st != PLX_OK) return st;
-        const long long bh = (long long)B * H_kv;
-        long long s = (kDecodeWgPerCu * (long long)cus + bh - 1) / bh;
-        const long long smax = (L_max + kDecodeMinChunk - 1) / kDecodeMinChunk;
-        s = s > smax ? smax : (s < 1 ? 1 : s);
-        p = DecodePlan{};
-        chunk_plan(L_max, (int)s, &p.chunk, &p.splits);
-    }
     *splits_out = p.splits;
     *workspace_bytes_out = p.splits > 1 ? (size_t)B * H_q * p.splits *
                                               (size_t)(2 * d_v + 4) * sizeof(float)
@@ -559,8 +539,10 @@ plx_status_t paged_call(plx_dtype_t dtype, int32_t B, int32_t H_q, int32_t H_kv,
     }
     int log2 = 0;
     while ((1 << log2) < block_size) ++log2;
+    int chunk = 0, launched = 0;
+    chunk_plan(L_max, splits, &chunk, &launched);
     plx::DecodeArgs a{B, H_q, L_max, d_qk, q, rho, k_pool, v_pool, seqlens, o, softmax_scale,
-                      splits, 0, static_cast<float*>(workspace), 0, 0,
+                      splits, chunk, static_cast<float*>(workspace), 0, 0,
                       block_table, max_blocks, log2, num_blocks};
     // d = 64 runs the grouped kernel also with one query head per cache head
     const hipError_t e =

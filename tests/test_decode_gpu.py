@@ -130,10 +130,11 @@ def test_wave_range_permuted_batch():
 
 
 def test_auto_plan_modes():
-    # Automatic choice (needs the device's compute-unit count): many short sequences use
-    # wave-range mode with whole (b, h) per slice (no workspace); the rest use split mode.
-    assert plx.decode_num_splits(2048, 16, 128, 0) < 0
+    # Automatic choice (needs the device's compute-unit count): split mode everywhere; many
+    # short sequences get one chunk per (b, h) (no workspace, the one-step-per-wave kernel).
+    assert plx.decode_num_splits(2048, 16, 128, 0) == 1
     assert plx.decode_workspace_size(2048, 16, 128, 128, 0) == 0
+    assert plx.decode_num_splits(128, 16, 128, 0) == 1
     assert plx.decode_num_splits(1, 16, 32768, 0) > 0
     assert plx.decode_num_splits(16, 16, 1024, 0) > 0
     assert plx.decode_num_splits(2048, 16, 1024, 0) > 0

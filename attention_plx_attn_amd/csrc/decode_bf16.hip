@@ -548,8 +548,9 @@ hipError_t launch_decode(const DecodeArgs& a, hipStream_t stream) {
     }
     const int BH = a.B * a.H;
     dim3 grid(a.splits, a.H, a.B);
-    // Chunks of at most one step per wave run the one-register-set instance.
-    const bool deep = a.chunk > KB * NW;
+    // Chunks of at most one step per wave run the one-register-set instance (the kernel's
+    // chunk of a sequence is at most that of L_max).
+    const bool deep = ((a.L_max + a.splits - 1) / a.splits + KB - 1) / KB * KB > KB * NW;
     auto split = [&](auto kern, const int32_t* table) {
         hipLaunchKernelGGL(kern, grid, dim3(NT), 0, stream, (const __bf16*)a.q, rho,
                            (const __bf16*)a.k, (const __bf16*)a.v, a.seqlens, (__bf16*)a.o, a.ws,

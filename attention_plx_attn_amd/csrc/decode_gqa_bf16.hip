@@ -51,8 +51,13 @@ __device__ __forceinline__ int slot_key(int g, int e) { return e < 4 ? 4 * g + e
 // are skipped (its rows get no weight).
 // D = 128 or 64. At d = 64 a row is 8 chunks of 16 bytes: lanes col < 8 load the V rows of
 // k-slots 0..3 of their group and lanes col >= 8 those of k-slots 4..7, chunk col & 7 each.
-template <int D, int G, bool PAGED>
-__global__ __launch_bounds__(NT, 2) void decode_gqa_bf16_kernel(
+// DEEP: each wave keeps its next step's loads in flight while it consumes the current one
+// (two register sets, two waves per SIMD); without it (d = 64 only) one step per pass with one
+// register set and five waves per SIMD, for chunks of at most one step per wave, where the
+// second set is never used. (At d = 128 the per-wave V^T buffers hold the occupancy at two
+// waves per SIMD either way.) Same steps in the same order: bit-identical outputs.
+template <int D, int G, bool PAGED, bool DEEP>
+__global__ __launch_bounds__(NT, DEEP ? 2 : 4) void decode_gqa_bf16_kernel(
     const __bf16* __restrict__ q, const __bf16* __restrict__ rho, const __bf16* __restrict__ kc,
     const __bf16* __restrict__ vc, const int32_t* __restrict__ seqlens, __bf16* __restrict__ o,
     float* __restrict__ ws, int Hkv, int L_max, int S, float c, const int32_t* __restrict__ table,
@@ -251,19 +256,27 @@ __global__ __launch_bounds__(NT, 2) void decode_gqa_bf16_kernel(
     constexpr int STEP = KB * NW;
     Frag fa, fb;
     int kb0 = j0 + KB * w;
-    int pha = lookup(kb0);
-    if (kb0 < j1) load(kb0, pha, fa);
-    int ph1 = lookup(kb0 + STEP);
-    for (; kb0 < j1; kb0 += 2 * STEP) {
-        load(kb0 + STEP, ph1, fb);
-        const int phb = ph1;
-        const int ph2 = lookup(kb0 + 2 * STEP);
-        if (in_pool(pha)) consume(kb0, fa);
-        if (kb0 + STEP >= j1) break;
-        load(kb0 + 2 * STEP, ph2, fa);
-        pha = ph2;
-        ph1 = lookup(kb0 + 3 * STEP);
-        if (in_pool(phb)) consume(kb0 + STEP, fb);
+    if constexpr (!DEEP) {
+        for (; kb0 < j1; kb0 += STEP) {
+            const int ph = lookup(kb0);
+            load(kb0, ph, fa);
+            if (in_pool(ph)) consume(kb0, fa);
+        }
+    } else {
+        int pha = lookup(kb0);
+        if (kb0 < j1) load(kb0, pha, fa);
+        int ph1 = lookup(kb0 + STEP);
+        for (; kb0 < j1; kb0 += 2 * STEP) {
+            load(kb0 + STEP, ph1, fb);
+            const int phb = ph1;
+            const int ph2 = lookup(kb0 + 2 * STEP);
+            if (in_pool(pha)) consume(kb0, fa);
+            if (kb0 + STEP >= j1) break;
+            load(kb0 + 2 * STEP, ph2, fa);
+            pha = ph2;
+            ph1 = lookup(kb0 + 3 * STEP);
+            if (in_pool(phb)) consume(kb0 + STEP, fb);
+        }
     }
 
     // Column totals of the weights (over the 4 row groups).
@@ -336,12 +349,18 @@ hipError_t launch_decode_gqa_bf16(const DecodeArgs& a, int Hkv, hipStream_t stre
                            a.seqlens, (__bf16*)a.o, a.ws, Hkv, a.L_max, a.splits, c, a.table,
                            a.max_blocks, a.block_log2, a.num_blocks);
     };
+    // Chunks of at most one step per wave run the one-register-set instance (the kernel's
+    // chunk of a sequence is at most that of L_max).
+    const bool deep = ((a.L_max + a.splits - 1) / a.splits + KB - 1) / KB * KB > KB * NW;
     auto pick = [&](auto d_tag, auto g_tag) {
         constexpr int DD = decltype(d_tag)::value, GG = decltype(g_tag)::value;
+        constexpr bool SHALLOW = DD == 64;  // built at d = 64 only
         if (a.table)
-            go(decode_gqa_bf16_kernel<DD, GG, true>);
+            deep || !SHALLOW ? go(decode_gqa_bf16_kernel<DD, GG, true, true>)
+                             : go(decode_gqa_bf16_kernel<DD, GG, true, !SHALLOW>);
         else
-            go(decode_gqa_bf16_kernel<DD, GG, false>);
+            deep || !SHALLOW ? go(decode_gqa_bf16_kernel<DD, GG, false, true>)
+                             : go(decode_gqa_bf16_kernel<DD, GG, false, !SHALLOW>);
     };
     auto by_g = [&](auto d_tag) {
         switch (G) {

@@ -539,10 +539,8 @@ plx_status_t paged_call(plx_dtype_t dtype, int32_t B, int32_t H_q, int32_t H_kv,
     }
     int log2 = 0;
     while ((1 << log2) < block_size) ++log2;
-    int chunk = 0, launched = 0;
-    chunk_plan(L_max, splits, &chunk, &launched);
     plx::DecodeArgs a{B, H_q, L_max, d_qk, q, rho, k_pool, v_pool, seqlens, o, softmax_scale,
-                      splits, chunk, static_cast<float*>(workspace), 0, 0,
+                      splits, 0, static_cast<float*>(workspace), 0, 0,
                       block_table, max_blocks, log2, num_blocks};
     // d = 64 runs the grouped kernel also with one query head per cache head
     const hipError_t e =

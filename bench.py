@@ -482,7 +482,7 @@ def prefill_long_record(torch, plx, dev, stream, n=5):
             "tokens_per_s": round(cfg.B * cfg.T / (st["median_us"] * 1e-6), 0)}
 
 
-def decode_grid_records(torch, plx, dev, stream, min_bytes=100e6, n=10):
+def decode_grid_records(torch, plx, dev, stream, min_bytes=100e6, n=10, only=None):
     """Decode grid cells (H16 d128, B x ctx, seqlens ~ U[ctx/2, ctx]) that move at least
     min_bytes, automatic plan, cold caches; each beside two streaming-read floors measured in
     the same run: the same number of KV bytes read contiguously, and exactly the rows the call
@@ -495,7 +495,7 @@ def decode_grid_records(torch, plx, dev, stream, min_bytes=100e6, n=10):
     recs = []
     for cfg in decode_grid_cells():
         nbytes = decode_bytes(draw_seqlens(cfg, 0).tolist(), cfg.H, cfg.d)
-        if nbytes < min_bytes:
+        if nbytes < min_bytes or (only is not None and (cfg.B, cfg.L_max) not in only):
             continue
         dx = decode_inputs(cfg, seed=0, device=str(dev), device_draw=True)
         splits = plx.decode_num_splits(cfg.B, cfg.H, cfg.L_max, 0)
@@ -1141,6 +1141,10 @@ def main():
     ap.add_argument("--compare-grid", metavar="OUT_MD", nargs="?", const="",
                     help="the softmax-only comparisons on every decode grid cell instead of "
                          "the step")
+    ap.add_argument("--decode-cells", metavar="BxCTX[,BxCTX...]",
+                    help="time only these decode grid cells (automatic plan, cold caches, "
+                         "beside their streaming floors; one JSON line each) instead of the "
+                         "step, e.g. for a kernel trace")
     ap.add_argument("--compare", metavar="OUT_MD", nargs="?", const="",
                     help="time Parallax against softmax-only attention (I/O- and "
                          "compute-matched) instead of the step")
@@ -1170,6 +1174,16 @@ def main():
         return paged(args.paged)
     if args.backward is not None:
         return backward(args.backward)
+    if args.decode_cells:
+        import torch
+
+        import attention_plx_attn_amd as plx
+        cells = {tuple(int(v) for v in c.split("x")) for c in args.decode_cells.split(",")}
+        dev = torch.device("cuda:0")
+        torch.cuda.set_device(dev)
+        decode_grid_records(torch, plx, dev, torch.cuda.current_stream(dev), min_bytes=0,
+                            only=cells)
+        return 0
 
     import torch
 

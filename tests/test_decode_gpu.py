@@ -42,6 +42,30 @@ def test_small_decode_with_poisoned_tail(L, splits, rho):
     check_bf16(o, ref, f"L={L} splits={splits} rho={rho}")
 
 
+@pytest.mark.parametrize("probe", [True, False])
+@pytest.mark.parametrize("d", [128, 64])
+def test_one_register_set_instance_matches_two_set_bitwise(d, probe):
+    """Sequences of at most 128 rows, one chunk each: with a cache of L_max = 128 every wave has
+    at most one 32-row step and the one-register-set instance runs; the same rows in a cache of
+    L_max = 256 run the two-set (prefetching) instance. Both consume the same steps in the same
+    order, so the outputs must be the same bits (and within the bar of the oracle)."""
+    cfg = DecodeConfig("d", 24, 6, 4, 256, d, "bf16", "proj32", "full")
+    x = decode_inputs(cfg, seed=2)
+    sl = torch.tensor([1, 33, 64, 100, 127, 128], dtype=torch.int32)
+    q, rho = x["q"].to(DEV), (x["rho"].to(DEV) if probe else None)
+    outs = []
+    for L in (256, 128):
+        kc = x["k_cache"][:, :, :L].contiguous().to(DEV)
+        vc = x["v_cache"][:, :, :L].contiguous().to(DEV)
+        assert plx.decode_num_splits(6, 4, L, 1) == 1
+        outs.append(plx.decode(q, rho, kc, vc, sl.to(DEV), x["scale"], num_splits=1))
+    torch.cuda.synchronize()
+    assert torch.equal(outs[0], outs[1])
+    r = x["rho"] if probe else torch.zeros_like(x["rho"])
+    ref = oracle.decode(x["q"], r, x["k_cache"], x["v_cache"], sl, x["scale"], form="cov")
+    check_bf16(outs[1], ref, f"one-register-set instance d={d} probe={probe}")
+
+
 def test_seqlens_edge_cases():
     cfg = DecodeConfig("d", 22, 5, 2, 200, 128, "bf16", "proj32", "full")
     x = decode_inputs(cfg, seed=1)

@@ -26,7 +26,7 @@ def _paged(x, bs, seed):
 
 @pytest.mark.parametrize("rho_kind", ["scaled", "proj32"])
 @pytest.mark.parametrize("bs", [32, 64, 256])
-@pytest.mark.parametrize("splits", [0, 1, 3])
+@pytest.mark.parametrize("splits", [0, 1, 3, 8])  # 8: chunks of 128 rows, one step per wave
 def test_paged_equals_contiguous_and_oracle(bs, splits, rho_kind):
     cfg = DecodeConfig("d", 42, 4, 3, 1024, 128, "bf16", rho_kind, "uniform_half")
     x = decode_inputs(cfg, seed=bs + splits, poison=True)
@@ -64,7 +64,7 @@ def test_paged_seqlens_edges_and_softmax_only():
     check_bf16(o[3:], ref[3:], "paged edges")
 
 
-@pytest.mark.parametrize("splits", [1, 3])
+@pytest.mark.parametrize("splits", [1, 3, 4, 8])  # 4, 8: one step per wave
 def test_paged_invalid_entry_below_seqlens_is_skipped(splits):
     """A table entry outside [0, num_blocks) inside a sequence's valid range: those rows get
     no weight, so the output equals the oracle over the sequence without them."""
@@ -89,7 +89,7 @@ def test_paged_invalid_entry_below_seqlens_is_skipped(splits):
 
 
 @pytest.mark.parametrize("bs", [32, 256])
-@pytest.mark.parametrize("splits", [0, 3])
+@pytest.mark.parametrize("splits", [0, 3, 8])  # 8: one step per wave
 def test_paged_d64_equals_grouped_and_oracle(bs, splits):
     """Head dim 64: the paged decode runs the grouped kernel with one query head per cache
     head, so it gives plx_attn_decode_gqa's bits on the contiguous cache."""

@@ -109,7 +109,7 @@ def test_paged_gqa_serving_shape():
 
 @pytest.mark.parametrize("G", [1, 4, 8])
 @pytest.mark.parametrize("bs", [32, 128])
-@pytest.mark.parametrize("splits", [0, 3])
+@pytest.mark.parametrize("splits", [0, 3, 8])  # 8: chunks of 128 rows, one step per wave
 def test_paged_gqa_d64_equals_contiguous_and_oracle(G, bs, splits):
     """Head dim 64: the paged pool gives the contiguous grouped decode's bits."""
     B, Hkv, L = 3, 2, 1024
@@ -128,3 +128,26 @@ def test_paged_gqa_d64_equals_contiguous_and_oracle(G, bs, splits):
     assert torch.equal(o, ref_c)
     check_bf16(o, _oracle(q, rho, kc, vc, sl, scale, G),
                f"paged gqa d64 G={G} bs={bs} splits={splits}")
+
+
+@pytest.mark.parametrize("splits", [1, 4, 8])  # 4, 8: one step per wave
+def test_paged_gqa_d64_invalid_entry_below_seqlens_is_skipped(splits):
+    """Head dim 64, an entry outside [0, num_blocks) inside a sequence's valid range: those
+    rows get no weight."""
+    B, Hkv, G, L, bs = 3, 2, 4, 512, 64
+    cq = DecodeConfig("pq64", 54, B, Hkv * G, 1, 64, "bf16", "proj32", "full")
+    ck = DecodeConfig("pk64", 55, B, Hkv, L, 64, "bf16", "proj32", "full")
+    xq, xk = decode_inputs(cq, seed=splits), decode_inputs(ck, seed=splits)
+    q, rho, scale = xq["q"], xq["rho"], xq["scale"]
+    kc, vc, sl = xk["k_cache"], xk["v_cache"], xk["seqlens"]
+    kp, vp, table = paginate(kc, vc, sl, bs, seed=19)
+    bad = {0: (1, -1), 1: (3, 1 << 30), 2: (0, kp.shape[0])}  # b: (block index, entry)
+    for b, (i, entry) in bad.items():
+        table[b, i] = entry
+    d = [t.to(DEV) for t in (q, rho, kp, vp, table, sl)]
+    o = plx.decode_paged_gqa(*d, scale, num_splits=splits).cpu()
+    for b, (i, _) in bad.items():
+        rows = np.r_[0:i * bs, (i + 1) * bs:L]
+        ref = _oracle(q[b:b + 1], rho[b:b + 1], kc[b:b + 1, :, rows], vc[b:b + 1, :, rows],
+                      np.array([len(rows)], np.int32), scale, G)
+        check_bf16(o[b:b + 1], ref, f"paged gqa d64 invalid entry b={b} splits={splits}")

@@ -114,8 +114,8 @@ plx_status_t plx_attn_prefill_ex(plx_dtype_t dtype, int32_t B, int32_t H, int32_
  * The plan a decode call with these arguments will use at d = 128, written to *splits_out in
  * the encoding of num_splits: S > 0 for split mode with S chunks per (b, h), or -G for
  * wave-range mode with G waves. num_splits > 0 and < 0 are taken as given (a negative count
- * is rounded up to a multiple of 4); 0 picks from B*H, L_max and the current device's
- * compute-unit count. At d = 64 only split mode exists: 0 then picks the split count the
+ * is rounded up to a multiple of 4); 0 picks a split-mode plan from B*H, L_max and the current
+ * device's compute-unit count. At d = 64 only split mode exists: 0 then picks the split count the
  * split heuristic gives (plx_attn_decode_workspace_size, which takes d_v, sizes it).
  */
 plx_status_t plx_attn_decode_num_splits(int32_t B, int32_t H, int32_t L_max,

@@ -208,3 +208,30 @@ def test_decode_grid_cell(cell):
          check_bf16(torch.cat(got), np.concatenate(refs), f"{cell.name} ({len(pick)} seqs)"))
     del x
     torch.cuda.empty_cache()
+
+
+@pytest.mark.parametrize("d", [128, 64])
+def test_decode_at_the_largest_cache(d):
+    """The largest cache the ABI accepts for one (b, h): L_max * 256 < 2^31, so 8,388,607 rows
+    (2 GiB of keys at d = 128), every row valid, automatic plan. Seven keys spread over the
+    range, the last ones at its end, are scaled copies of q so that their scores (about
+    2.5-3.5 sqrt(d)) outweigh the 8.4 million others: the output is then of order one and any
+    addressing mistake near the 2 GiB offsets shows. Compared with the oracle over all rows."""
+    L = (1 << 31) // 256 - 1
+    g = torch.Generator(device=DEV)
+    g.manual_seed(100 + d)
+    q = torch.randn(1, 1, d, generator=g, device=DEV, dtype=torch.bfloat16)
+    rho = torch.randn(1, 1, d, generator=g, device=DEV, dtype=torch.bfloat16)
+    kc = torch.randn(1, 1, L, d, generator=g, device=DEV, dtype=torch.bfloat16)
+    vc = torch.randn(1, 1, L, d, generator=g, device=DEV, dtype=torch.bfloat16)
+    spikes = [0, 1, L // 2, L - 1000, L - 33, L - 2, L - 1]
+    for i, j in enumerate(spikes):
+        kc[0, 0, j] = (q[0, 0].float() * (2.5 + i / 6)).to(torch.bfloat16)
+    sl = torch.tensor([L], dtype=torch.int32, device=DEV)
+    scale = d ** -0.5
+    _say("largest cache d", d, "rows", L, "plan", plx.decode_num_splits(1, 1, L, 0))
+    o = plx.decode(q, rho, kc, vc, sl, scale)
+    torch.cuda.synchronize()
+    ref = oracle.decode(q, rho, kc, vc, sl, scale, form="sweighted")
+    _say(check_bf16(o, ref, f"largest cache d={d}"))
+    assert float(np.abs(ref).max()) > 0.3  # the spike rows dominate: a meaningful comparison

@@ -240,3 +240,31 @@ def test_bf16_config_prefill_long_zero_probe_heads_bitwise():
     o0 = _run(x0).cpu()
     assert torch.equal(o[:, : cfg.H // 2], o0[:, : cfg.H // 2])
     _LONG.clear()
+
+
+def test_bf16_tensors_beyond_4_gib():
+    """300,000 (b, h) slices of T = 100 rows (one full and one ragged 64-key tile each): each of
+    q, k, v, rho and o spans 7.7 GB, so the slices past 4 GiB are addressed through 64-bit
+    offsets. Row 0 of every slice must be its v_0 exactly; 32 seeded slices and the last 8
+    (the largest offsets) are compared with the oracle on all rows."""
+    B, H, T, d = 5, 60000, 100, 128
+    BH = B * H
+    g = torch.Generator(device=DEV)
+    g.manual_seed(11)
+    x = {n: torch.randn(B, H, T, d, generator=g, device=DEV, dtype=torch.bfloat16)
+         for n in ("q", "k", "v")}
+    x["rho"] = torch.randn(B, H, T, d, generator=g, device=DEV, dtype=torch.bfloat16)
+    x["rho"].mul_(0.1)
+    assert x["q"].numel() * 2 > 1 << 32
+    scale = d ** -0.5
+    o = plx.prefill(x["q"], x["k"], x["v"], x["rho"], scale)
+    torch.cuda.synchronize()
+    assert torch.equal(o[:, :, 0], x["v"][:, :, 0])
+    assert bool(torch.isfinite(o).all())
+    rng = np.random.default_rng(12)
+    pick = np.unique(np.concatenate([rng.choice(BH, 32, replace=False), np.arange(BH - 8, BH)]))
+    idx = torch.from_numpy(pick).to(DEV)
+    sub = {n: t.view(BH, T, d)[idx].unsqueeze(0).cpu() for n, t in x.items()}
+    ref = oracle.prefill(sub["q"], sub["k"], sub["v"], sub["rho"], scale, form="cov")
+    got = o.view(BH, T, d)[idx].unsqueeze(0)
+    _say(check_bf16(got, ref, "prefill beyond 4 GiB per tensor"))

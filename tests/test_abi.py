@@ -294,3 +294,14 @@ def test_decode_noalloc_validation(lib):
     assert lib.plx_attn_decode_noalloc(*args(scale=-1.0)) == 3
     assert lib.plx_attn_decode_noalloc(*args(dtype=0)) == 4
     assert lib.plx_attn_decode_noalloc(*args(splits=5000)) == 3
+
+
+def test_missing_library_fails_loudly(monkeypatch):
+    """With the HIP library absent there is no fallback: every entry point raises."""
+    from attention_plx_attn_amd import _lib
+    monkeypatch.setattr(_lib, "_lib", None)
+    monkeypatch.setattr(_lib, "LIB_PATH", "/nonexistent/libplx_attn.so")
+    with pytest.raises(RuntimeError, match="is missing"):
+        _lib.load()
+    with pytest.raises(RuntimeError, match="is missing"):
+        _lib.decode_num_splits(1, 16, 32768, 0)

@@ -52,12 +52,12 @@ __device__ __forceinline__ int slot_key(int g, int e) { return e < 4 ? 4 * g + e
 // D = 128 or 64. At d = 64 a row is 8 chunks of 16 bytes: lanes col < 8 load the V rows of
 // k-slots 0..3 of their group and lanes col >= 8 those of k-slots 4..7, chunk col & 7 each.
 // DEEP: each wave keeps its next step's loads in flight while it consumes the current one
-// (two register sets, two waves per SIMD); without it (d = 64 only) one step per pass with one
-// register set and five waves per SIMD, for chunks of at most one step per wave, where the
-// second set is never used. (At d = 128 the per-wave V^T buffers hold the occupancy at two
-// waves per SIMD either way.) Same steps in the same order: bit-identical outputs.
+// (two register sets, two waves per SIMD); without it one step per pass with one register set,
+// for chunks of at most one step per wave, where the second set is never used: five waves per
+// SIMD at d = 64, three at d = 128 (where the per-wave V^T buffers, 40 KB per workgroup, allow
+// three workgroups per compute unit). Same steps in the same order: bit-identical outputs.
 template <int D, int G, bool PAGED, bool DEEP>
-__global__ __launch_bounds__(NT, DEEP ? 2 : 4) void decode_gqa_bf16_kernel(
+__global__ __launch_bounds__(NT, DEEP ? 2 : (D == 128 ? 3 : 4)) void decode_gqa_bf16_kernel(
     const __bf16* __restrict__ q, const __bf16* __restrict__ rho, const __bf16* __restrict__ kc,
     const __bf16* __restrict__ vc, const int32_t* __restrict__ seqlens, __bf16* __restrict__ o,
     float* __restrict__ ws, int Hkv, int L_max, int S, float c, const int32_t* __restrict__ table,
@@ -354,13 +354,12 @@ hipError_t launch_decode_gqa_bf16(const DecodeArgs& a, int Hkv, hipStream_t stre
     const bool deep = ((a.L_max + a.splits - 1) / a.splits + KB - 1) / KB * KB > KB * NW;
     auto pick = [&](auto d_tag, auto g_tag) {
         constexpr int DD = decltype(d_tag)::value, GG = decltype(g_tag)::value;
-        constexpr bool SHALLOW = DD == 64;  // built at d = 64 only
         if (a.table)
-            deep || !SHALLOW ? go(decode_gqa_bf16_kernel<DD, GG, true, true>)
-                             : go(decode_gqa_bf16_kernel<DD, GG, true, !SHALLOW>);
+            deep ? go(decode_gqa_bf16_kernel<DD, GG, true, true>)
+                 : go(decode_gqa_bf16_kernel<DD, GG, true, false>);
         else
-            deep || !SHALLOW ? go(decode_gqa_bf16_kernel<DD, GG, false, true>)
-                             : go(decode_gqa_bf16_kernel<DD, GG, false, !SHALLOW>);
+            deep ? go(decode_gqa_bf16_kernel<DD, GG, false, true>)
+                 : go(decode_gqa_bf16_kernel<DD, GG, false, false>);
     };
     auto by_g = [&](auto d_tag) {
         switch (G) {

@@ -123,3 +123,24 @@ def test_gqa_d64_edges_and_softmax_only(G):
         assert torch.equal(o[2, h], vc[2, h // G, 0])
     check_bf16(o[3:], _oracle(q, rho, kc, vc, sl, scale, G)[3:], f"gqa d64 edges G={G}")
     check_bf16(z[3:], _oracle(q, None, kc, vc, sl, scale, G)[3:], f"gqa d64 softmax-only G={G}")
+
+
+@pytest.mark.parametrize("G", [1, 4, 8])
+def test_gqa_one_register_set_instance_matches_two_set_bitwise(G):
+    """Sequences of at most 128 rows, one chunk each: a cache of L_max = 128 runs the
+    one-register-set instance of the grouped kernel, the same rows in a cache of L_max = 256
+    the two-set one; the outputs must be the same bits and within the oracle's bar."""
+    B, Hkv, L = 6, 2, 256
+    q, rho, kc, vc, _, scale = _inputs(B, Hkv * G, G, L, seed=G + 70, rho="proj32",
+                                       poison=False)
+    sl = torch.tensor([1, 33, 64, 100, 127, 128], dtype=torch.int32)
+    outs = []
+    for Lm in (256, 128):
+        k = kc[:, :, :Lm].contiguous().to(DEV)
+        v = vc[:, :, :Lm].contiguous().to(DEV)
+        assert plx.decode_gqa_plan(B, Hkv * G, Hkv, Lm, 128, 1)[0] == 1
+        outs.append(plx.decode_gqa(q.to(DEV), rho.to(DEV), k, v, sl.to(DEV), scale,
+                                   num_splits=1))
+    torch.cuda.synchronize()
+    assert torch.equal(outs[0], outs[1])
+    check_bf16(outs[1], _oracle(q, rho, kc, vc, sl, scale, G), f"gqa one-register-set G={G}")

@@ -75,7 +75,7 @@ def test_paged_gqa_seqlens_edges_and_softmax_only(G):
                f"paged gqa softmax-only G={G}")
 
 
-@pytest.mark.parametrize("splits", [1, 3])
+@pytest.mark.parametrize("splits", [1, 3, 4, 8])  # 4, 8: one step per wave
 def test_paged_gqa_invalid_entry_below_seqlens_is_skipped(splits):
     """An entry outside [0, num_blocks) inside a sequence's valid range: those rows get no
     weight, so the output is the oracle's over the sequence without them."""

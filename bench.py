@@ -819,8 +819,8 @@ def compare_grid(out_md):
 def gqa(out_md):
     """Decode with grouped query heads at a fixed cache (B=1, H_kv=16, 32768 rows, d=128, then
     d=64): G = 1, 2, 4, 8 query heads per cache head, against the multi-head decode of the
-    same cache (G = 1). Cold caches (a 1 GiB read before each call), HIP events, median of
-    20."""
+    same cache (G = 1); then short contexts (B=2048, H_kv=8, 64-128 rows each) at G = 1, 4, 8.
+    Cold caches (a 1 GiB read before each call), HIP events, median of 20."""
     import torch
 
     import attention_plx_attn_amd as plx
@@ -873,11 +873,35 @@ def gqa(out_md):
         del kc, vc
         torch.cuda.empty_cache()
     for r_ in rows:
-        d = r_["d"]
-        nbytes = B * Hkv * L * 2 * d * 2 + B * r_["H_q"] * 3 * d * 2
+        r_["bytes"] = B * Hkv * L * 2 * r_["d"] * 2 + B * r_["H_q"] * 3 * r_["d"] * 2
+    # Short contexts: many sequences of 64-128 rows (chunks of one step per wave, the
+    # one-register-set instances), B = 2048, H_kv = 8.
+    Bs, Hs, Ls = 2048, 8, 128
+    sls = torch.randint(Ls // 2, Ls + 1, (Bs,), generator=g, device=dev, dtype=torch.int32)
+    for d in (128, 64):
+        kc = torch.randn((Bs, Hs, Ls, d), generator=g, device=dev).to(torch.bfloat16)
+        vc = torch.randn((Bs, Hs, Ls, d), generator=g, device=dev).to(torch.bfloat16)
+        for G in (1, 4, 8):
+            Hq = Hs * G
+            q = torch.randn((Bs, Hq, d), generator=g, device=dev).to(torch.bfloat16)
+            r = (0.1 * torch.randn((Bs, Hq, d), generator=g, device=dev)).to(torch.bfloat16)
+            o = torch.empty_like(q)
+            _, need = plx.decode_gqa_plan(Bs, Hq, Hs, Ls, d)
+            ws = torch.empty(max(need // 4, 1), dtype=torch.float32, device=dev)
+            us = timed(lambda: plx.decode_gqa(q, r, kc, vc, sls, d ** -0.5, out=o,
+                                              workspace=ws))
+            rows.append({"kernel": f"grouped-query decode, B{Bs} H_kv{Hs} ctx{Ls} "
+                                   f"(seqlens U[{Ls // 2}, {Ls}])", "d": d, "G": G, "H_q": Hq,
+                         "B": Bs,
+                         "median_us": us,
+                         "bytes": int(sls.sum()) * Hs * 2 * d * 2 + Bs * Hq * 3 * d * 2})
+        del kc, vc
+        torch.cuda.empty_cache()
+    for r_ in rows:
+        nbytes = r_["bytes"]
         r_["hbm_gbps"] = round(nbytes / r_["median_us"] / 1e3, 1)
         r_["hbm_frac"] = round(r_["hbm_gbps"] / HBM_PEAK_GBPS, 4)
-        r_["query_heads_per_s"] = round(r_["H_q"] / (r_["median_us"] * 1e-6), 0)
+        r_["query_heads_per_s"] = round(r_.get("B", B) * r_["H_q"] / (r_["median_us"] * 1e-6), 0)
         print(json.dumps(r_), flush=True)
     if out_md:
         with open(out_md, "w") as fh:
